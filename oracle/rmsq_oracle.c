@@ -1,0 +1,339 @@
+/*
+ * rmsq_oracle.c -- plain, slow, obviously correct CPU oracle (TEST INFRASTRUCTURE ONLY).
+ *
+ * What is computed, per token row t (sources cited in rmsq_oracle.h):
+ *   1. residual add ([P1] "RMSNorm + quantization", fused-add variant; [P2] key source
+ *      snippet, x and residual fed to the norm together): h = bf16(x + r), written back as the
+ *      new residual.  Without a residual, h = x.
+ *   2. RMSNorm ([P3] "Pattern matching structure": rms_norm(input, weight, epsilon)); the
+ *      pages never print the formula, the textbook one is used:
+ *      y = h / sqrt(mean(h^2) + eps) * w.
+ *   3. quantization, one of ([P3] fused-op map and "Why this design"; [P2] "Motivation"):
+ *      FP8 static per-tensor, FP8 dynamic per-token, FP8 dynamic per-token-group (64/128,
+ *      row- or column-major scales, optional power-of-two E8M0 scales), FP4 e2m1 with
+ *      16-element blocks, an e4m3 scale per block and a caller-supplied f32 global scale.
+ *
+ * Nothing here is blocked, fused or reordered: one row at a time, one element at a time,
+ * index order, encoders by exhaustive nearest-value search over the decoded code values.
+ */
+#include "rmsq_oracle.h"
+
+#include <math.h>
+#include <stddef.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ bit helpers */
+static float u32_as_f32(uint32_t u) {
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+static uint32_t f32_as_u32(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return u;
+}
+
+/* ------------------------------------------------------------------ bf16 */
+/* bf16 is the upper half of a binary32 pattern. */
+float orc_bf16_to_f32(uint16_t b) { return u32_as_f32((uint32_t)b << 16); }
+
+/* Value of a bf16 pattern for rounding-distance purposes: infinity counts as 2^128, the
+ * value one step beyond the largest finite bf16 (IEEE overflow rule). */
+static double bf16_distance_value(uint16_t b) {
+  if ((b & 0x7FFFu) == 0x7F80u) return ldexp(1.0, 128);
+  return fabs((double)orc_bf16_to_f32(b));
+}
+
+/* Round to nearest bf16 by comparing the two bf16 neighbours of v; ties go to the one whose
+ * significand is even (lowest bit 0).  NaN stays NaN (quiet), infinities stay infinite. */
+uint16_t orc_f32_to_bf16(float v) {
+  uint32_t u = f32_as_u32(v);
+  uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+  if (isnan(v)) return (uint16_t)(sign | 0x7FC0u);
+  if (isinf(v)) return (uint16_t)(sign | 0x7F80u);
+  uint16_t lo = (uint16_t)((u >> 16) & 0x7FFFu); /* magnitude truncated toward zero */
+  if (((uint32_t)lo << 16) == (u & 0x7FFFFFFFu)) return (uint16_t)(sign | lo); /* exact */
+  uint16_t hi = (uint16_t)(lo + 1); /* next magnitude away from zero (may be infinity) */
+  double a = fabs((double)v);
+  double dlo = a - bf16_distance_value(lo);
+  double dhi = bf16_distance_value(hi) - a;
+  uint16_t pick;
+  if (dlo < dhi) pick = lo;
+  else if (dhi < dlo) pick = hi;
+  else pick = (lo & 1u) ? hi : lo;
+  return (uint16_t)(sign | pick);
+}
+
+/* ------------------------------------------------------------------ e4m3fn (OCP FP8) */
+/* 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits; exponent field 0 is subnormal
+ * (m * 2^-9); S.1111.111 is NaN; there is no infinity.  Largest finite magnitude 448. */
+float orc_e4m3_decode(uint8_t c) {
+  int s = (c >> 7) & 1, e = (c >> 3) & 0xF, m = c & 7;
+  double mag;
+  if (e == 0xF && m == 7) return NAN;
+  if (e == 0) mag = ldexp((double)m, -9);
+  else mag = ldexp(1.0 + m / 8.0, e - 7);
+  return (float)(s ? -mag : mag);
+}
+
+/* Nearest of the 127 non-negative finite magnitudes (codes 0x00..0x7E), ties to the even
+ * code; |v| >= 448 saturates to 448; the sign bit is copied from v (so -0 and negative
+ * values that round to zero give 0x80); NaN gives 0x7F. */
+uint8_t orc_e4m3_encode(float v) {
+  if (isnan(v)) return 0x7F;
+  uint8_t sign = signbit(v) ? 0x80 : 0x00;
+  double a = fabs((double)v);
+  if (a >= 448.0) return (uint8_t)(sign | 0x7E);
+  int best = 0;
+  double bestd = INFINITY;
+  for (int k = 0; k <= 0x7E; ++k) {
+    double d = fabs(a - (double)orc_e4m3_decode((uint8_t)k));
+    if (d < bestd || (d == bestd && (k & 1) == 0)) {
+      best = k;
+      bestd = d;
+    }
+  }
+  return (uint8_t)(sign | best);
+}
+
+/* ------------------------------------------------------------------ e2m1 (FP4) */
+/* 1 sign bit (bit 3), 2 exponent bits (bias 1), 1 mantissa bit; exponent field 0 is
+ * subnormal (m * 0.5).  Magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; no infinity or NaN. */
+float orc_e2m1_decode(uint8_t c) {
+  int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+  double mag = (e == 0) ? 0.5 * m : ldexp(1.0 + m / 2.0, e - 1);
+  return (float)(s ? -mag : mag);
+}
+
+uint8_t orc_e2m1_encode(float v) {
+  if (isnan(v)) return 0x7;
+  uint8_t sign = signbit(v) ? 0x8 : 0x0;
+  double a = fabs((double)v);
+  if (a >= 6.0) return (uint8_t)(sign | 0x7);
+  int best = 0;
+  double bestd = INFINITY;
+  for (int k = 0; k <= 7; ++k) {
+    double d = fabs(a - (double)orc_e2m1_decode((uint8_t)k));
+    if (d < bestd || (d == bestd && (k & 1) == 0)) {
+      best = k;
+      bestd = d;
+    }
+  }
+  return (uint8_t)(sign | best);
+}
+
+/* ------------------------------------------------------------------ E8M0 */
+/* E8M0 holds only a biased exponent: byte b means 2^(b-127).  A scale is rounded UP to
+ * the next power of two so that no scaled element exceeds the FP8 range. */
+int orc_e8m0_ceil_exp(float s) {
+  for (int k = -127; k < 127; ++k)
+    if (ldexp(1.0, k) >= (double)s) return k;
+  return 127;
+}
+
+void orc_e4m3_encode_n(const float* v, uint8_t* c, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) c[i] = orc_e4m3_encode(v[i]);
+}
+void orc_e2m1_encode_n(const float* v, uint8_t* c, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) c[i] = orc_e2m1_encode(v[i]);
+}
+void orc_f32_to_bf16_n(const float* v, uint16_t* b, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) b[i] = orc_f32_to_bf16(v[i]);
+}
+void orc_e8m0_ceil_exp_n(const float* s, int32_t* k, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) k[i] = orc_e8m0_ceil_exp(s[i]);
+}
+
+/* ------------------------------------------------------------------ row steps */
+void orc_residual_add(const uint16_t* x, const uint16_t* r, uint16_t* h, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) {
+    float sum = orc_bf16_to_f32(x[i]) + orc_bf16_to_f32(r[i]);
+    h[i] = orc_f32_to_bf16(sum);
+  }
+}
+
+float orc_inv_rms(const uint16_t* h, int64_t n, float eps) {
+  double ss = 0.0;
+  for (int64_t i = 0; i < n; ++i) {
+    double v = (double)orc_bf16_to_f32(h[i]);
+    ss += v * v;
+  }
+  return (float)(1.0 / sqrt(ss / (double)n + (double)eps));
+}
+
+void orc_normalize(const uint16_t* h, const uint16_t* w, float inv, float* y, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) {
+    float t = orc_bf16_to_f32(h[i]) * inv;
+    y[i] = t * orc_bf16_to_f32(w[i]);
+  }
+}
+
+static float absmax(const float* y, int64_t n) {
+  float a = 0.0f;
+  for (int64_t i = 0; i < n; ++i)
+    if (fabsf(y[i]) > a) a = fabsf(y[i]);
+  return a;
+}
+
+/* ------------------------------------------------------------------ quantizers (one row) */
+static void quant_static(const float* y, int64_t H, float scale, uint8_t* q, float* pre) {
+  float r = 1.0f / scale;
+  for (int64_t i = 0; i < H; ++i) {
+    float v = y[i] * r;
+    q[i] = orc_e4m3_encode(v);
+    if (pre) pre[i] = v;
+  }
+}
+
+/* Shared by the per-token (one group = the row) and per-group modes: the scale is the
+ * group's absmax over the FP8 maximum 448; a zero scale gives zero codes. */
+static float quant_group_fp8(const float* y, int64_t n, int e8m0, uint8_t* q, float* pre,
+                             int* e8m0_byte) {
+  float a = absmax(y, n);
+  float s = a / 448.0f;
+  float s_raw = s;
+  if (e8m0) {
+    int k = orc_e8m0_ceil_exp(s);
+    s = ldexpf(1.0f, k);
+    *e8m0_byte = k + 127;
+  }
+  if (s_raw == 0.0f) {
+    for (int64_t i = 0; i < n; ++i) {
+      q[i] = 0x00;
+      if (pre) pre[i] = 0.0f;
+    }
+    return s;
+  }
+  float r = 1.0f / s;
+  for (int64_t i = 0; i < n; ++i) {
+    float v = y[i] * r;
+    q[i] = orc_e4m3_encode(v);
+    if (pre) pre[i] = v;
+  }
+  return s;
+}
+
+/* FP4: block scale sf = e4m3(absmax * gs / 6), element multiplier m = gs / decode(sf). */
+static void quant_fp4(const float* y, int64_t H, float gs, uint8_t* qrow, uint8_t* sfrow,
+                      float* pre) {
+  for (int64_t b = 0; b < H / 16; ++b) {
+    const float* yb = y + b * 16;
+    float a = absmax(yb, 16);
+    uint8_t sf = orc_e4m3_encode((a * gs) / 6.0f);
+    float d = orc_e4m3_decode(sf);
+    sfrow[b] = sf;
+    uint8_t codes[16];
+    if (d > 0.0f) {
+      float m = gs / d;
+      for (int i = 0; i < 16; ++i) {
+        float v = yb[i] * m;
+        codes[i] = orc_e2m1_encode(v);
+        if (pre) pre[b * 16 + i] = v;
+      }
+    } else {
+      for (int i = 0; i < 16; ++i) {
+        codes[i] = 0;
+        if (pre) pre[b * 16 + i] = 0.0f;
+      }
+    }
+    for (int k = 0; k < 8; ++k)
+      qrow[b * 8 + k] = (uint8_t)(codes[2 * k] | (codes[2 * k + 1] << 4));
+  }
+}
+
+/* ------------------------------------------------------------------ one row's quantizer */
+int orc_quantize_row(const float* y, int64_t H, int mode, float scale_in, int group_size,
+                     unsigned flags, uint8_t* q, void* row_scales, float* pre) {
+  if (mode == ORC_FP8_STATIC) {
+    quant_static(y, H, scale_in, q, pre);
+  } else if (mode == ORC_FP8_TOKEN) {
+    int unused = 0;
+    ((float*)row_scales)[0] = quant_group_fp8(y, H, 0, q, pre, &unused);
+  } else if (mode == ORC_FP8_GROUP) {
+    if ((group_size != 64 && group_size != 128) || H % group_size) return -1;
+    int e8m0 = (flags & (ORC_SCALE_E8M0 | ORC_SCALE_E8M0_U8)) != 0;
+    int64_t G = group_size;
+    for (int64_t g = 0; g < H / G; ++g) {
+      int byte = 0;
+      float s = quant_group_fp8(y + g * G, G, e8m0, q + g * G, pre ? pre + g * G : NULL, &byte);
+      if (flags & ORC_SCALE_E8M0_U8) ((uint8_t*)row_scales)[g] = (uint8_t)byte;
+      else ((float*)row_scales)[g] = s;
+    }
+  } else if (mode == ORC_FP4_BLOCK16) {
+    if (group_size != 16 || H % 16) return -1;
+    quant_fp4(y, H, scale_in, q, (uint8_t*)row_scales, pre);
+  } else {
+    return -1;
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------ whole operation */
+int orc_fused(const uint16_t* x, const uint16_t* residual, const uint16_t* weight, float eps,
+              int mode, float scale_in, uint8_t* out_q, void* out_scales, uint16_t* residual_out,
+              int64_t T, int64_t H, int group_size, unsigned flags, int64_t scale_ld,
+              float* pre_q) {
+  if (T < 0 || H <= 0 || !x || !weight || !out_q) return -1;
+  if ((residual == NULL) != (residual_out == NULL)) return -1;
+  if (!(eps >= 0.0f) || isinf(eps)) return -1;
+  if (scale_ld == 0) scale_ld = T;
+  switch (mode) {
+    case ORC_FP8_STATIC:
+      break;
+    case ORC_FP8_TOKEN:
+      if (!out_scales) return -1;
+      break;
+    case ORC_FP8_GROUP:
+      if (!out_scales || (group_size != 64 && group_size != 128) || H % group_size) return -1;
+      if (scale_ld < T) return -1;
+      break;
+    case ORC_FP4_BLOCK16:
+      if (!out_scales || group_size != 16 || H % 16) return -1;
+      break;
+    default:
+      return -1;
+  }
+
+  uint16_t* h = (uint16_t*)malloc((size_t)H * sizeof(uint16_t));
+  float* y = (float*)malloc((size_t)H * sizeof(float));
+  float* sc = (float*)malloc((size_t)H * sizeof(float)); /* one row's scales */
+  if (!h || !y || !sc) {
+    free(h);
+    free(y);
+    free(sc);
+    return -1;
+  }
+
+  for (int64_t t = 0; t < T; ++t) {
+    if (residual) {
+      orc_residual_add(x + t * H, residual + t * H, h, H);
+      memcpy(residual_out + t * H, h, (size_t)H * sizeof(uint16_t));
+    } else {
+      memcpy(h, x + t * H, (size_t)H * sizeof(uint16_t));
+    }
+    float inv = orc_inv_rms(h, H, eps);
+    orc_normalize(h, weight, inv, y, H);
+    uint8_t* qrow = out_q + t * (mode == ORC_FP4_BLOCK16 ? H / 2 : H);
+    orc_quantize_row(y, H, mode, scale_in, group_size, flags, qrow, sc, pre_q ? pre_q + t * H : NULL);
+
+    /* place this row's scales */
+    if (mode == ORC_FP8_TOKEN) {
+      ((float*)out_scales)[t] = sc[0];
+    } else if (mode == ORC_FP8_GROUP) {
+      int64_t ng = H / group_size;
+      for (int64_t g = 0; g < ng; ++g) {
+        int64_t idx = (flags & ORC_SCALE_COLMAJOR) ? g * scale_ld + t : t * ng + g;
+        if (flags & ORC_SCALE_E8M0_U8) ((uint8_t*)out_scales)[idx] = ((uint8_t*)sc)[g];
+        else ((float*)out_scales)[idx] = sc[g];
+      }
+    } else if (mode == ORC_FP4_BLOCK16) {
+      memcpy((uint8_t*)out_scales + t * (H / 16), sc, (size_t)(H / 16));
+    }
+  }
+  free(h);
+  free(y);
+  free(sc);
+  return 0;
+}

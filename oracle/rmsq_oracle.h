@@ -1,0 +1,103 @@
+/*
+ * rmsq_oracle.h -- plain CPU oracle for fused (residual add ->) RMSNorm -> FP8/FP4 quantization.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This library exists to check the GPU library against the plain
+ * definition of the operation.  Only the test suite, the package smoke check and the CPU-baseline
+ * leg of the benchmark may load it; the product path never does.  It shares no code, header,
+ * table or constant with the HIP library: every format is decoded here from its bit-field
+ * definition and every encoder is a nearest-value search over those decoded values.
+ *
+ * Sources (cited by page and section; the pages never write the formulas, so the plain
+ * textbook readings are used and listed in the design notes):
+ *   [P1]  vLLM docs, "Fusion torch.compile passes", section "RMSNorm + quantization
+ *         (fuse_norm_quant)": plain RMSNorm -> quant and fused-add RMSNorm -> quant, the latter
+ *         updating the residual in place; FP8 static per-tensor, dynamic per-token and dynamic
+ *         per-token-group (128/64) schemes.
+ *   [P2]  prhub summary of vLLM PR #51925, "Motivation" and "Key source snippet": add-RMSNorm
+ *         followed by NVFP4 quantization (block scales, then FP4 conversion, with a global
+ *         activation scale supplied by the caller).
+ *   [P3]  Blog "[vLLM] Compilation Fusion Passes", sections "Pattern matching structure"
+ *         (rms_norm(input, weight, epsilon) -> quant, out-parameter result), the fused-op map
+ *         (static per-tensor, dynamic per-token, per-block 128 keys, with and without fused add),
+ *         "Type check" (input and weight share one dtype) and "Why this design" (E8M0 and
+ *         column-major scale options).
+ *
+ * Precision: the sum of squares and the reciprocal RMS are taken in binary64; everything that
+ * decides a quantized code (the normalized value, the scales, the scaled value fed to the
+ * encoder) is binary32, the precision the GPU kernel takes those decisions in.
+ * Build with -O2 -ffp-contract=off and without -ffast-math (no FMA contraction, no FTZ/DAZ).
+ */
+#ifndef RMSQ_ORACLE_H
+#define RMSQ_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Quantization modes (the oracle's own numbering; the GPU library's header is independent). */
+enum {
+  ORC_FP8_STATIC = 0, /* per-tensor static scale: q = e4m3(y * (1/scale))            [P1][P3] */
+  ORC_FP8_TOKEN = 1,  /* dynamic per-token: s = absmax(row)/448                       [P1][P3] */
+  ORC_FP8_GROUP = 2,  /* dynamic per-token-group, G in {64,128}: s = absmax(group)/448 [P1][P3] */
+  ORC_FP4_BLOCK16 = 3 /* e2m1 codes, 16-element blocks, e4m3 block scale, f32 global  [P2]     */
+};
+/* Flags for ORC_FP8_GROUP scales ([P3] "Why this design": E8M0 scales, column-major scales). */
+enum {
+  ORC_SCALE_COLMAJOR = 1u << 0, /* scales stored [H/G][scale_ld], element (t,g) at g*ld + t   */
+  ORC_SCALE_E8M0 = 1u << 1,     /* scale rounded up to a power of two, stored as f32           */
+  ORC_SCALE_E8M0_U8 = 1u << 2   /* scale rounded up to a power of two, stored as its E8M0 byte */
+};
+
+/* ---- formats (decoded from bit fields; encoders are nearest-value searches) ---- */
+float orc_bf16_to_f32(uint16_t b);
+uint16_t orc_f32_to_bf16(float v);  /* round to nearest, ties to even significand */
+float orc_e4m3_decode(uint8_t c);   /* OCP e4m3fn; 0x7F/0xFF decode to NaN */
+uint8_t orc_e4m3_encode(float v);   /* nearest, ties -> even code, saturate at 448, NaN -> 0x7F */
+float orc_e2m1_decode(uint8_t c);   /* low 4 bits used */
+uint8_t orc_e2m1_encode(float v);   /* nearest, ties -> even code, saturate at 6, NaN -> 0x7 */
+int orc_e8m0_ceil_exp(float s);     /* smallest k >= -127 with 2^k >= s (s >= 0), capped at 127 */
+
+/* Array forms of the converters (for exhaustive checks from the test suite). */
+void orc_e4m3_encode_n(const float* v, uint8_t* c, int64_t n);
+void orc_e2m1_encode_n(const float* v, uint8_t* c, int64_t n);
+void orc_f32_to_bf16_n(const float* v, uint16_t* b, int64_t n);
+void orc_e8m0_ceil_exp_n(const float* s, int32_t* k, int64_t n);
+
+/* ---- steps of one row ---- */
+/* h = bf16(f32(x) + f32(r)) elementwise; residual_out takes h. */
+void orc_residual_add(const uint16_t* x, const uint16_t* r, uint16_t* h, int64_t n);
+/* inv = 1 / sqrt(mean(h^2) + eps), sum in index order in binary64, result rounded to f32. */
+float orc_inv_rms(const uint16_t* h, int64_t n, float eps);
+/* y_i = (h_i * inv) * w_i, two binary32 products in that order. */
+void orc_normalize(const uint16_t* h, const uint16_t* w, float inv, float* y, int64_t n);
+
+/* Quantize one normalized row y[H] (the step after normalize).  row_scales receives this row's
+ * scales contiguously: FP8_TOKEN 1 f32; FP8_GROUP H/G f32 (H/G bytes with E8M0_U8);
+ * FP4 H/16 e4m3 bytes; FP8_STATIC none.  q gets H bytes (FP8) or H/2 packed bytes (FP4).
+ * Returns 0, or -1 on an invalid mode/group size. */
+int orc_quantize_row(const float* y, int64_t H, int mode, float scale_in, int group_size,
+                     unsigned flags, uint8_t* q, void* row_scales, float* pre);
+
+/* ---- the whole operation ----
+ * x            [T,H] bf16 bits, row-major
+ * residual     [T,H] bf16 bits or NULL (plain RMSNorm)
+ * weight       [H]   bf16 bits
+ * scale_in     FP8_STATIC: the dequant scale (q = y / scale); FP4: the global encode scale gs;
+ *              otherwise ignored
+ * out_q        FP8: [T,H] e4m3fn bytes; FP4: [T,H/2] bytes, element 2k in the low nibble
+ * out_scales   FP8_TOKEN [T] f32; FP8_GROUP [T,H/G] or [H/G,scale_ld] f32 (u8 with E8M0_U8);
+ *              FP4 [T,H/16] e4m3 bytes; FP8_STATIC: ignored (may be NULL)
+ * residual_out [T,H] bf16 or NULL; must be non-NULL when residual is non-NULL
+ * pre_q        optional [T,H] f32: the value each element's code was encoded from (diagnosis)
+ * Returns 0 on success, -1 on an invalid argument. */
+int orc_fused(const uint16_t* x, const uint16_t* residual, const uint16_t* weight, float eps,
+              int mode, float scale_in, uint8_t* out_q, void* out_scales, uint16_t* residual_out,
+              int64_t T, int64_t H, int group_size, unsigned flags, int64_t scale_ld,
+              float* pre_q);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,301 @@
+"""Pins for the oracle's operation (CPU only): hand rows, library cross-checks, invariants.
+
+What the operation is, from the pages: vLLM docs "Fusion torch.compile passes", section
+"RMSNorm + quantization (fuse_norm_quant)" (rms_norm / fused_add_rms_norm followed by FP8
+static per-tensor, dynamic per-token or dynamic per-token-group 128/64 quantization; the
+fused-add form updates the residual in place); PR #51925 summary, "Motivation" and "Key source
+snippet" (add-RMSNorm followed by NVFP4 block-scale quantization with a caller-supplied global
+scale); blog "[vLLM] Compilation Fusion Passes", "Pattern matching structure", fused-op map and
+"Why this design" (E8M0 and column-major scales).  Every test below would fail on a plausible
+slip in the oracle: eps outside the root, sum instead of mean, a dropped weight, a wrong
+rounding direction, a transposed scale layout, a swapped nibble.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from rmsnorm_quantization_amd import synth
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_rows.json")))
+
+
+def bf16_bits(a):
+    return synth.bits(torch.tensor(np.asarray(a, np.float32)).to(torch.bfloat16))
+
+
+def torch_e4m3(v):
+    v = np.ascontiguousarray(v, np.float32)
+    c = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    big = np.abs(v) > 464
+    c[big] = np.where(np.signbit(v[big]), 0xFE, 0x7E)
+    return c
+
+
+# ------------------------------------------------------------------ hand rows (golden)
+def test_hand_row_fp8_per_token(orc):
+    g = GOLDEN["fp8_token_row"]
+    x = bf16_bits(g["x"])[None, :]
+    w = bf16_bits(np.ones(8))
+    out = orc.fused(x, None, w, g["eps"], orc.FP8_TOKEN)
+    assert out["q"][0].tolist() == g["codes"]
+    assert hex(int(out["scales"].view(np.uint32)[0])) == g["scale_bits"].lower()
+
+
+def test_hand_row_fp8_static(orc):
+    g = GOLDEN["fp8_static_row"]
+    x = bf16_bits(g["x"])[None, :]
+    w = bf16_bits(np.ones(8))
+    out = orc.fused(x, None, w, g["eps"], orc.FP8_STATIC, scale_in=g["scale"])
+    assert out["q"][0].tolist() == g["codes"]
+
+
+def test_fp4_worked_block(orc):
+    g = GOLDEN["fp4_block"]
+    y = np.array(g["y"], np.float32)
+    q, sf, _ = orc.quantize_row(y, orc.FP4_BLOCK16, scale_in=np.float32(g["gs"]), group_size=16)
+    assert sf.tolist() == [g["sf"]]
+    nib = orc.unpack_fp4(q)
+    assert nib.tolist() == g["nibbles"]
+    assert q[0] == (g["nibbles"][0] | (g["nibbles"][1] << 4))  # element 0 in the low nibble
+    d = orc.e4m3_decode(sf)[0]
+    deq = orc.e2m1_decode(nib) * d / np.float32(g["gs"])
+    assert np.allclose(deq, g["dequant"], rtol=1e-6, atol=0)
+
+
+def test_constant_row(orc):
+    g = GOLDEN["constant_row"]
+    H = 64
+    x = bf16_bits(np.full(H, g["value"]))[None, :]
+    w = bf16_bits(np.ones(H))
+    y = orc.rms_y(x, None, w, g["eps"])
+    assert np.all(y == np.float32(g["y"]))
+    st = orc.fused(x, None, w, g["eps"], orc.FP8_STATIC, scale_in=1.0)
+    assert np.all(st["q"] == g["static_code"])
+    tk = orc.fused(x, None, w, g["eps"], orc.FP8_TOKEN)
+    assert np.all(tk["q"] == g["token_code"])
+    # with a general weight the row is +-(1-delta)*w
+    wr = bf16_bits(np.linspace(0.5, 1.5, H))
+    y2 = orc.rms_y(x, None, wr, g["eps"])
+    assert np.allclose(y2, synth.from_bits(wr).float().numpy() * np.float32(g["y"]), rtol=2e-7)
+
+
+# ------------------------------------------------------------------ library cross-checks
+@pytest.mark.parametrize("H,eps", [(64, 1e-5), (4096, 1e-6), (520, 1e-5)])
+def test_rmsnorm_matches_torch_float64(orc, H, eps):
+    rng = np.random.default_rng(H)
+    xf = (rng.standard_normal((6, H)) * rng.uniform(0.01, 30, (6, 1))).astype(np.float32)
+    x = bf16_bits(xf)
+    w = bf16_bits(rng.uniform(0.5, 1.5, H))
+    y = orc.rms_y(x, None, w, eps)
+    xt = synth.from_bits(x).double()
+    wt = synth.from_bits(w).double()
+    ref = torch.nn.functional.rms_norm(xt, (H,), wt, eps).numpy()
+    # three binary32 roundings (inv, h*inv, *w): relative error below 2^-22
+    assert np.all(np.abs(y - ref) <= 2.0 ** -22 * np.abs(ref) + 1e-30)
+
+
+def test_residual_add_matches_torch(orc):
+    rng = np.random.default_rng(1)
+    x = bf16_bits(rng.standard_normal(100_000) * 3)
+    r = bf16_bits(rng.standard_normal(100_000) * 3)
+    h = orc.residual_add(x, r)
+    ref = (synth.from_bits(x).float() + synth.from_bits(r).float()).to(torch.bfloat16)
+    assert np.array_equal(h, synth.bits(ref))
+
+
+def test_fused_add_uses_the_rounded_sum(orc):
+    rng = np.random.default_rng(2)
+    T, H = 5, 256
+    x = bf16_bits(rng.standard_normal((T, H)))
+    r = bf16_bits(rng.standard_normal((T, H)))
+    w = bf16_bits(rng.uniform(0.5, 1.5, H))
+    out = orc.fused(x, r, w, 1e-6, orc.FP8_TOKEN)
+    assert np.array_equal(out["residual_out"], orc.residual_add(x, r))
+    plain = orc.fused(out["residual_out"], None, w, 1e-6, orc.FP8_TOKEN)
+    assert np.array_equal(out["q"], plain["q"])
+    assert np.array_equal(out["scales"], plain["scales"])
+
+
+def _workload_y(orc, T=8, H=512, seed=0):
+    rng = np.random.default_rng(seed)
+    x = bf16_bits(rng.standard_normal((T, H)))
+    r = bf16_bits(rng.standard_normal((T, H)))
+    w = bf16_bits(rng.uniform(0.5, 1.5, H))
+    return x, r, w, orc.rms_y(x, r, w, 1e-6)
+
+
+def test_static_codes_match_torch_conversion(orc):
+    x, r, w, y = _workload_y(orc)
+    scale = np.float32(0.0137)
+    out = orc.fused(x, r, w, 1e-6, orc.FP8_STATIC, scale_in=scale)
+    assert np.array_equal(out["q"], torch_e4m3(y * (np.float32(1) / scale)))
+
+
+def test_per_token_scales_and_codes(orc):
+    x, r, w, y = _workload_y(orc, seed=3)
+    out = orc.fused(x, r, w, 1e-6, orc.FP8_TOKEN)
+    a = np.abs(y).max(axis=1)
+    s = a / np.float32(448)
+    assert np.array_equal(out["scales"], s)  # bit-exact absmax/448
+    exp = torch_e4m3(y * (np.float32(1) / s)[:, None])
+    assert np.array_equal(out["q"], exp)
+    # every non-zero row holds a +-448 code at its absmax element
+    assert np.all(np.any((out["q"] & 0x7F) == 0x7E, axis=1))
+
+
+@pytest.mark.parametrize("G", [64, 128])
+@pytest.mark.parametrize("flags", [0, 1, 2, 3, 4, 5])
+def test_per_group_layouts_scales_codes(orc, G, flags):
+    T, H = 6, 640
+    x, r, w, y = _workload_y(orc, T, H, seed=G + flags)
+    ld = T + 3 if flags & orc.SCALE_COLMAJOR else 0
+    out = orc.fused(x, r, w, 1e-6, orc.FP8_GROUP, group_size=G, flags=flags, scale_ld=ld)
+    yg = y.reshape(T, H // G, G)
+    s = np.abs(yg).max(axis=2) / np.float32(448)           # [T, ng]
+    if flags & (orc.SCALE_E8M0 | orc.SCALE_E8M0_U8):
+        k = np.ceil(np.log2(s.astype(np.float64))).astype(np.int64)
+        s = np.ldexp(np.float32(1), k).astype(np.float32)
+        assert np.all(s >= np.abs(yg).max(axis=2) / np.float32(448))
+    stored = out["scales"]
+    if flags & orc.SCALE_COLMAJOR:
+        assert stored.shape == (H // G, ld)
+        stored = stored[:, :T].T
+    if flags & orc.SCALE_E8M0_U8:
+        assert stored.dtype == np.uint8
+        assert np.array_equal(stored.astype(np.int64) - 127, k)
+    else:
+        assert np.array_equal(stored, s)
+    exp = torch_e4m3(yg * (np.float32(1) / s)[:, :, None]).reshape(T, H)
+    assert np.array_equal(out["q"], exp)
+    if flags & (orc.SCALE_E8M0 | orc.SCALE_E8M0_U8):
+        assert np.all((out["q"] & 0x7F) <= 0x7E)
+
+
+def test_colmajor_padding_untouched(orc):
+    T, H, G = 3, 256, 128
+    x, r, w, _ = _workload_y(orc, T, H, seed=9)
+    out = orc.fused(x, r, w, 1e-6, orc.FP8_GROUP, group_size=G, flags=orc.SCALE_COLMAJOR,
+                    scale_ld=8)
+    assert np.all(out["scales"][:, T:] == 0)
+    assert np.all(out["scales"][:, :T] > 0)
+
+
+def test_fp4_row_properties(orc):
+    x, r, w, y = _workload_y(orc, 4, 512, seed=21)
+    gs = np.float32(448 * 6) / np.abs(y).max()
+    out = orc.fused(x, r, w, 1e-6, orc.FP4_BLOCK16, scale_in=gs, group_size=16, want_pre=True)
+    sf = out["scales"]
+    nib = orc.unpack_fp4(out["q"])
+    d = orc.e4m3_decode(sf)                                # [T, H/16]
+    deq = orc.e2m1_decode(nib).reshape(4, 32, 16) * (d / gs)[:, :, None]
+    yb = y.reshape(4, 32, 16)
+    # block scale: e4m3 of absmax*gs/6, matched by torch's conversion
+    assert np.array_equal(sf, torch_e4m3((np.abs(yb).max(axis=2) * gs) / np.float32(6)))
+    # the block holding the global max gets the top scale and a +-6 code
+    t, i = np.unravel_index(np.abs(y).argmax(), y.shape)
+    assert sf[t, i // 16] == 0x7E
+    assert (nib[t, i] & 7) == 7
+    # dequantized value within one e2m1 step of y; the step at a code is the larger gap to
+    # its neighbouring magnitudes (0, .5, 1, 1.5, 2, 3, 4, 6)
+    gap = np.array([0.5, 0.5, 0.5, 0.5, 1.0, 1.0, 2.0, 2.0], np.float32)
+    unit = (d / gs)[:, :, None]
+    assert np.all(np.abs(deq - yb) <= gap[nib & 7].reshape(4, 32, 16) * unit + 1e-7)
+
+
+# ------------------------------------------------------------------ invariants
+@pytest.mark.parametrize("mode", ["static", "token", "group"])
+def test_half_step_invariant(orc, mode):
+    x, r, w, y = _workload_y(orc, 8, 1024, seed=31)
+    t8 = orc.e4m3_table().astype(np.float64)
+    if mode == "static":
+        scale = np.float32(0.02)
+        out = orc.fused(x, r, w, 1e-6, orc.FP8_STATIC, scale_in=scale, want_pre=True)
+        s = np.full(y.shape, scale, np.float64)
+    elif mode == "token":
+        out = orc.fused(x, r, w, 1e-6, orc.FP8_TOKEN, want_pre=True)
+        s = np.repeat(out["scales"].astype(np.float64)[:, None], y.shape[1], 1)
+    else:
+        out = orc.fused(x, r, w, 1e-6, orc.FP8_GROUP, group_size=128, want_pre=True)
+        s = np.repeat(out["scales"].astype(np.float64), 128, axis=1)
+    q = out["q"]
+    dq = t8[q] * s
+    mag = np.abs(t8[q & 0x7F])
+    # e4m3 spacing at the code: 2^(e-3) for normal codes, 2^-9 for subnormals
+    e = (q >> 3) & 0xF
+    spacing = np.where(e == 0, 2.0 ** -9, 2.0 ** (e.astype(np.float64) - 10))
+    sat = mag >= 448
+    err = np.abs(dq - y.astype(np.float64))
+    # half a step of the scaled value, plus the rounding of y*(1/s) itself
+    bound = 0.5 * spacing * s + np.abs(y) * 2.0 ** -23
+    assert np.all(err[~sat] <= bound[~sat])
+
+
+def test_zero_residual_equals_plain(orc):
+    rng = np.random.default_rng(41)
+    T, H = 4, 384
+    x = bf16_bits(rng.standard_normal((T, H)))
+    w = bf16_bits(rng.uniform(0.5, 1.5, H))
+    zeros = np.zeros((T, H), np.uint16)
+    a = orc.fused(x, zeros, w, 1e-5, orc.FP8_GROUP, group_size=128)
+    b = orc.fused(x, None, w, 1e-5, orc.FP8_GROUP, group_size=128)
+    assert np.array_equal(a["q"], b["q"]) and np.array_equal(a["scales"], b["scales"])
+    assert np.array_equal(a["residual_out"], x)
+
+
+@pytest.mark.parametrize("k", [-3, 5])
+def test_power_of_two_equivariance(orc, k):
+    rng = np.random.default_rng(51)
+    T, H = 3, 256
+    xf = rng.standard_normal((T, H)).astype(np.float32)
+    rf = rng.standard_normal((T, H)).astype(np.float32)
+    x, r = bf16_bits(xf), bf16_bits(rf)
+    xs = bf16_bits(synth.from_bits(x).float().numpy() * np.float32(2.0 ** k))
+    rs = bf16_bits(synth.from_bits(r).float().numpy() * np.float32(2.0 ** k))
+    w = bf16_bits(rng.uniform(0.5, 1.5, H))
+    for mode, gsz in ((orc.FP8_TOKEN, 0), (orc.FP8_GROUP, 64), (orc.FP4_BLOCK16, 16)):
+        a = orc.fused(x, r, w, 0.0, mode, scale_in=100.0, group_size=gsz)
+        b = orc.fused(xs, rs, w, 0.0, mode, scale_in=100.0, group_size=gsz)
+        assert np.array_equal(a["q"], b["q"]) and np.array_equal(a["scales"], b["scales"])
+
+
+def test_rows_are_independent(orc):
+    rng = np.random.default_rng(61)
+    T, H = 7, 128
+    x = bf16_bits(rng.standard_normal((T, H)))
+    r = bf16_bits(rng.standard_normal((T, H)))
+    w = bf16_bits(rng.uniform(0.5, 1.5, H))
+    perm = rng.permutation(T)
+    a = orc.fused(x, r, w, 1e-6, orc.FP8_GROUP, group_size=64, flags=orc.SCALE_COLMAJOR)
+    b = orc.fused(x[perm], r[perm], w, 1e-6, orc.FP8_GROUP, group_size=64,
+                  flags=orc.SCALE_COLMAJOR)
+    assert np.array_equal(a["q"][perm], b["q"])
+    assert np.array_equal(a["scales"][:, perm], b["scales"])
+    assert np.array_equal(a["residual_out"][perm], b["residual_out"])
+
+
+def test_zero_row_gives_zero_codes(orc):
+    H = 256
+    x = np.zeros((2, H), np.uint16)
+    w = bf16_bits(np.ones(H))
+    tk = orc.fused(x, None, w, 1e-6, orc.FP8_TOKEN)
+    assert np.all(tk["q"] == 0) and np.all(tk["scales"] == 0)
+    gp = orc.fused(x, None, w, 1e-6, orc.FP8_GROUP, group_size=128, flags=orc.SCALE_E8M0_U8)
+    assert np.all(gp["q"] == 0) and np.all(gp["scales"] == 0)  # E8M0 byte 0 = 2^-127
+    f4 = orc.fused(x, None, w, 1e-6, orc.FP4_BLOCK16, scale_in=10.0, group_size=16)
+    assert np.all(f4["q"] == 0) and np.all(f4["scales"] == 0)
+
+
+def test_empty_and_invalid(orc):
+    w = bf16_bits(np.ones(64))
+    out = orc.fused(np.zeros((0, 64), np.uint16), None, w, 1e-6, orc.FP8_TOKEN)
+    assert out["q"].shape == (0, 64)
+    with pytest.raises(ValueError):
+        orc.fused(np.zeros((2, 96), np.uint16), None, bf16_bits(np.ones(96)), 1e-6,
+                  orc.FP8_GROUP, group_size=64)  # 96 % 64 != 0
+    with pytest.raises(ValueError):
+        orc.fused(np.zeros((2, 64), np.uint16), None, w, 1e-6, orc.FP8_GROUP, group_size=32)
+    with pytest.raises(ValueError):
+        orc.fused(np.zeros((2, 64), np.uint16), None, w, 1e-6, 7)

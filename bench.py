@@ -1,0 +1,322 @@
+"""Benchmark of the fused add + RMSNorm + quantization kernel family on one MI355X.
+
+Default workload: fused residual add + RMSNorm -> FP8 static per-tensor quant, 4096 tokens x
+hidden 4096, bf16 inputs ~N(0,1), weight ~U(0.5,1.5), eps 1e-5, static scale from a fixed
+512x4096 warm-up batch.  One step = one launch of the fused kernel over the whole batch
+(residual add, sum of squares, normalize, scale, quantize, stores).
+
+Inputs are resident in HBM before timing starts.  Launches rotate over several buffer sets
+whose total footprint is well above the 256 MB last-level cache, so each launch reads cold
+data.  Prints ONE JSON line:
+  value          algorithmic GB/s over the timed region (bytes each launch must move)
+  roofline       HBM roofline of the fused kernel: algorithmic bytes / average launch duration
+                 (per-launch HIP events on the launch stream), against 8 TB/s; traffic = HBM
+                 bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE (scaled by a plain
+                 copy's counters) when the committed counters match the current kernel source
+  cpu_baseline   the CPU oracle on a bounded sample of the same workload, one core
+
+Other workloads (--workload w0..w4) and forced launch shapes (--launch tpr,vpt,rpb) are for
+exploration; only one GPU is supported (--gpus above 1 exits with a message).
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+FOOTPRINT_BYTES = 1536 << 20   # rotating buffer sets: at least 6x the 256 MB MALL
+MODE_NAMES = {0: "fp8_static", 1: "fp8_per_token", 2: "fp8_per_group", 3: "fp4_block16"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in ("rmsnorm_quantization_amd/csrc/rmsq.hip", "rmsnorm_quantization_amd/csrc/rmsq_device.hpp",
+              "include/rmsq.h", "rmsnorm_quantization_amd/build.py"):
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def workload_spec(args):
+    from rmsnorm_quantization_amd import binding as B
+    from rmsnorm_quantization_amd import synth
+
+    wl = synth.WORKLOADS[int(args.workload[1:])]
+    T = args.tokens or max(wl.tokens)
+    H = args.hidden or (7168 if wl.index == 3 else wl.hidden[0])
+    mode = {0: B.RMSQ_FP8_STATIC, 1: B.RMSQ_FP8_STATIC, 2: B.RMSQ_FP8_TOKEN,
+            3: B.RMSQ_FP8_GROUP, 4: B.RMSQ_FP4_BLOCK16}[wl.index]
+    G = {2: args.group, 3: 16}.get(mode, 0)
+    flags = 0
+    if mode == B.RMSQ_FP8_GROUP:
+        for f in (args.flags or "").split(","):
+            flags |= {"": 0, "col": B.RMSQ_SCALE_COLMAJOR, "e8m0": B.RMSQ_SCALE_E8M0,
+                      "e8m0u8": B.RMSQ_SCALE_E8M0_U8}[f]
+    return wl, T, H, mode, G, flags
+
+
+def algorithmic_bytes(mode, T, H, G, flags, residual):
+    """Bytes one launch must move: every input read once, every output written once, the
+    weight once per launch."""
+    rd = 2 * T * H + (2 * T * H if residual else 0) + 2 * H + (4 if mode in (0, 3) else 0)
+    wr = (2 * T * H if residual else 0) + (T * H // 2 if mode == 3 else T * H)
+    if mode == 1:
+        wr += 4 * T
+    elif mode == 2:
+        wr += T * (H // G) * (1 if flags & 4 else 4)
+    elif mode == 3:
+        wr += T * (H // 16)
+    return rd, wr
+
+
+def scale_layout(mode, T, H, G, flags):
+    import torch
+
+    if mode == 0:
+        return None, None
+    if mode == 1:
+        return (T,), torch.float32
+    if mode == 2:
+        dt = torch.uint8 if flags & 4 else torch.float32
+        return ((H // G, T) if flags & 1 else (T, H // G)), dt
+    return (T, H // 16), torch.uint8
+
+
+def gpu_leg(args, wl, T, H, mode, G, flags):
+    import torch
+
+    from rmsnorm_quantization_amd import binding as B
+    from rmsnorm_quantization_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x, r, w = synth.make_inputs(wl.index, T, H)
+    residual = r is not None
+    rd, wr = algorithmic_bytes(mode, T, H, G, flags, residual)
+    set_bytes = rd + wr
+    nsets = max(2, math.ceil(FOOTPRINT_BYTES / set_bytes))
+    xd, rdv, wd = x.to(dev), (r.to(dev) if residual else None), w.to(dev)
+    sshape, sdt = scale_layout(mode, T, H, G, flags)
+    qcols = H // 2 if mode == 3 else H
+    sets = []
+    for _ in range(nsets):
+        s = {"x": xd.clone(), "r": rdv.clone() if residual else None,
+             "ro": torch.empty_like(xd) if residual else None,
+             "q": torch.empty((T, qcols), dtype=torch.uint8, device=dev),
+             "s": torch.empty(sshape, dtype=sdt, device=dev) if sshape else None}
+        sets.append(s)
+    wd = wd.contiguous()
+
+    # per-tensor input scale: the static scale from the workload's warm-up batch (max|y|/448,
+    # computed on the GPU with the per-token mode), the FP4 global scale 448*6/max|y|
+    scale_in = None
+    if mode == 0:
+        if wl.static_scale is not None:
+            sval = wl.static_scale
+        else:
+            xw, rw = synth.make_warmup(wl.index, H)
+            xw, rw = xw.to(dev), rw.to(dev)
+            q = torch.empty(xw.shape, dtype=torch.uint8, device=dev)
+            st = torch.empty((xw.shape[0],), dtype=torch.float32, device=dev)
+            B.rmsq_fused(xw, rw, wd, wl.eps, B.RMSQ_FP8_TOKEN, None, q, st, torch.empty_like(xw))
+            sval = float(st.max())
+        scale_in = torch.tensor([sval], dtype=torch.float32, device=dev)
+    elif mode == 3:
+        q = torch.empty((T, H), dtype=torch.uint8, device=dev)
+        st = torch.empty((T,), dtype=torch.float32, device=dev)
+        B.rmsq_fused(xd, rdv, wd, wl.eps, B.RMSQ_FP8_TOKEN, None, q, st,
+                     torch.empty_like(xd) if residual else None)
+        amax = float(st.max()) * 448.0
+        scale_in = torch.tensor([448.0 * 6.0 / amax], dtype=torch.float32, device=dev)
+
+    launch = None
+    if args.launch:
+        tpr, vpt, rpb = (int(v) for v in args.launch.split(","))
+        launch = B.rmsq_launch(tpr, vpt, rpb, 0)
+    shape = launch.as_tuple() if launch else B.rmsq_query_launch(mode, T, H, G, residual)[0].as_tuple()
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        s = sets[i % nsets]
+        B.rmsq_fused(s["x"], s["r"], wd, wl.eps, mode, scale_in, s["q"], s["s"], s["ro"],
+                     group_size=G, flags=flags, launch=launch, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K back-to-back launches bracketed by one event pair
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    # per-launch durations: each launch between its own event pair on the launch stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        step(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in evs)
+    avg_launch_ms = sum(per) / len(per)
+    med_launch_ms = per[len(per) // 2]
+
+    # a plain device copy of the same footprint, for context (practical HBM ceiling)
+    copy_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    copy_dst = torch.empty_like(copy_src)
+    for _ in range(3):
+        copy_dst.copy_(copy_src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    c0.record(stream)
+    for _ in range(10):
+        copy_dst.copy_(copy_src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * copy_src.numel() * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+
+    return {"ms_per_step": ms_per_step, "avg_launch_ms": avg_launch_ms,
+            "median_launch_ms": med_launch_ms, "bytes": rd + wr, "read": rd, "write": wr,
+            "sets": nsets, "launch": shape, "copy_gbs": copy_gbs,
+            "device": torch.cuda.get_device_name(dev)}
+
+
+def cpu_leg(wl, T, H, mode, G, flags, budget_s=12.0):
+    """The oracle as it stands (single thread) on whole rows of the same workload, processed
+    in chunks until about budget_s seconds of CPU work; returns GB/s with the same
+    algorithmic byte count per row."""
+    import numpy as np
+
+    import oracle as O
+    from rmsnorm_quantization_amd import synth
+
+    x, r, w = synth.make_inputs(wl.index, T, H)
+    xb, rb, wb = synth.bits(x), (synth.bits(r) if r is not None else None), synth.bits(w)
+    if mode == 0:
+        if wl.static_scale is not None:
+            s_in = wl.static_scale
+        else:
+            xw, rw = synth.make_warmup(wl.index, H)
+            y = O.rms_y(synth.bits(xw), synth.bits(rw), wb, wl.eps)
+            s_in = float(np.abs(y).max() / np.float32(448))
+    elif mode == 3:
+        s_in = float(np.float32(448 * 6) / np.abs(O.rms_y(xb[:256], None if rb is None else rb[:256],
+                                                        wb, wl.eps)).max())
+    else:
+        s_in = 0.0
+    chunk = max(1, min(T, 64))
+    rows = 0
+    t0 = time.perf_counter()
+    while rows < T and time.perf_counter() - t0 < budget_s:
+        n = min(chunk, T - rows)
+        O.fused(xb[rows:rows + n], None if rb is None else rb[rows:rows + n], wb, wl.eps, mode,
+                scale_in=s_in, group_size=G, flags=flags & ~1)
+        rows += n
+    dt = time.perf_counter() - t0
+    rd, wr = algorithmic_bytes(mode, rows, H, G, flags, rb is not None)
+    return {"value": (rd + wr) / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {rows} of {T} rows ({rows * H} elements), {dt:.1f} s, "
+                      f"single thread, {os.cpu_count()} host CPUs visible",
+            "tokens_per_s": rows / dt}
+
+
+def load_traffic(key):
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    e = t.get(key)
+    if not e or e.get("kernel_source") != kernel_source_hash():
+        return None
+    return e
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="w1", choices=["w0", "w1", "w2", "w3", "w4"])
+    ap.add_argument("--tokens", type=int, default=0)
+    ap.add_argument("--hidden", type=int, default=0)
+    ap.add_argument("--group", type=int, default=128)
+    ap.add_argument("--flags", default="")
+    ap.add_argument("--launch", default="")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
+              f"supported (token rows shard with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    wl, T, H, mode, G, flags = workload_spec(args)
+    g = gpu_leg(args, wl, T, H, mode, G, flags)
+    gbs = g["bytes"] / (g["ms_per_step"] * 1e-3) / 1e9
+    achieved = g["bytes"] / (g["avg_launch_ms"] * 1e-3) / 1e9
+    key = f"{args.workload}_T{T}_H{H}_{MODE_NAMES[mode]}_G{G}_f{flags}"
+    tr = load_traffic(key)
+    out = {
+        "metric": "fused add+RMSNorm+quant GB/s & % of MI355X HBM peak; tokens/s",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(g["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: {T} tokens x hidden {H}, "
+                        f"{'residual add, ' if wl.residual else ''}{MODE_NAMES[mode]}"
+                        f"{f' G={G}' if mode == 2 else ''}{f' flags={flags}' if flags else ''}",
+            "tokens": T, "hidden": H, "mode": MODE_NAMES[mode], "group_size": G,
+            "flags": flags, "residual": wl.residual, "eps": wl.eps,
+            "io": "bf16 in; " + ("e2m1 + e4m3 block scales out" if mode == 3 else "e4m3fn out"),
+            "launch": {"threads_per_row": g["launch"][0], "chunks_per_thread": g["launch"][1],
+                       "rows_per_block": g["launch"][2]},
+            "rotating_sets": g["sets"], "parallelism": "single GPU",
+        },
+        "tokens_per_s": round(T / (g["ms_per_step"] * 1e-3), 1),
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "bytes_per_step": g["bytes"],
+        "avg_launch_us": round(g["avg_launch_ms"] * 1e3, 3),
+        "median_launch_us": round(g["median_launch_ms"] * 1e3, 3),
+        "copy_kernel_GBs": round(g["copy_gbs"], 1),
+        "device": g["device"],
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None if tr is None else tr["bytes_per_launch"],
+        },
+        "cpu_baseline": None,
+    }
+    if tr is not None:
+        out["roofline"]["traffic_detail"] = {k: tr[k] for k in ("fetch_bytes", "write_bytes",
+                                                                "calibration") if k in tr}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_leg(wl, T, H, mode, G, flags, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

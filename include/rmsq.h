@@ -1,0 +1,173 @@
+/*
+ * rmsq.h -- C ABI of librmsq: fused (residual add ->) RMSNorm -> FP8 / FP4 quantization on
+ * AMD MI355X (gfx950).
+ *
+ * The operation, per token row t of a row-major [T, H] bf16 activation (sources: vLLM docs
+ * "Fusion torch.compile passes", section "RMSNorm + quantization (fuse_norm_quant)"; blog
+ * "[vLLM] Compilation Fusion Passes", sections "Pattern matching structure", the fused-op map
+ * and "Why this design"; prhub summary of vLLM PR #51925, "Motivation" and "Key source
+ * snippet"):
+ *
+ *   h      = bf16(x + residual)          fused-add form; h is written back as the new residual
+ *          = x                           plain form (residual == NULL)
+ *   inv    = 1 / sqrt(sum(h^2)/H + eps)  sum and root in binary64, inv rounded to binary32
+ *   y      = (h * inv) * weight          binary32, never stored
+ *   codes  = quantize(y)                 FP8 e4m3fn (OCP, max 448) or FP4 e2m1 (max 6), round to
+ *                                        nearest even, saturating
+ *
+ * Quantization modes (the pages' quant keys: static per-tensor, dynamic per-token, dynamic
+ * per-token-group 128/64; NVFP4-style block-16):
+ *   RMSQ_FP8_STATIC   q = e4m3(y * (1/scale)); scale = *scale_in, the dequant scale
+ *   RMSQ_FP8_TOKEN    s_t = absmax(y_t)/448 (f32), q = e4m3(y * (1/s_t)); s_t = 0 gives 0 codes
+ *   RMSQ_FP8_GROUP    per group of G in {64,128}: s = absmax/448, optionally rounded up to a
+ *                     power of two (E8M0); a zero group (absmax/448 == 0) gives 0 codes
+ *   RMSQ_FP4_BLOCK16  per 16-element block: sf = e4m3(absmax * gs / 6), d = decode(sf),
+ *                     q = e2m1(y * (gs / d)), 0 codes when d == 0; gs = *scale_in, the global
+ *                     encode scale (dequant: value = e2m1 * d / gs)
+ *
+ * Ownership and threading: the caller owns every buffer.  The library never allocates, frees
+ * or synchronizes; work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and all
+ * pointers except where noted are DEVICE pointers.  Argument errors are returned synchronously
+ * before anything is enqueued.  No C++ exception crosses this boundary.  Calls are thread-safe.
+ */
+#ifndef RMSQ_H
+#define RMSQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define RMSQ_API __attribute__((visibility("default")))
+#else
+#define RMSQ_API
+#endif
+
+#define RMSQ_ABI_VERSION 1
+#define RMSQ_MAX_HIDDEN 65536 /* largest H one workgroup keeps in registers */
+
+/* ---- status codes ---- */
+enum {
+  RMSQ_OK = 0,
+  RMSQ_EINVAL = -1,       /* bad size, null pointer, bad group size, eps <= 0, ld < T, ... */
+  RMSQ_EALIGN = -2,       /* a pointer is not aligned as documented below */
+  RMSQ_EALIAS = -3,       /* an output overlaps an input or another output */
+  RMSQ_EUNSUPPORTED = -4, /* flag not valid for the mode, or the device is not gfx950 */
+  RMSQ_ELAUNCH = -5,      /* the kernel launch was refused by the HIP runtime */
+  RMSQ_EDEVICE = -6       /* no current HIP device could be queried */
+};
+
+/* ---- quantization modes ---- */
+typedef enum {
+  RMSQ_FP8_STATIC = 0,
+  RMSQ_FP8_TOKEN = 1,
+  RMSQ_FP8_GROUP = 2,
+  RMSQ_FP4_BLOCK16 = 3
+} rmsq_mode;
+
+/* ---- scale-layout flags, RMSQ_FP8_GROUP only (blog "Why this design": E8M0 scales and
+ *      column-major scales) ---- */
+enum {
+  RMSQ_SCALE_COLMAJOR = 1u << 0, /* scales stored [H/G][scale_ld]: element (t,g) at g*ld + t */
+  RMSQ_SCALE_E8M0 = 1u << 1,     /* scale rounded up to 2^ceil(log2 s), stored as f32        */
+  RMSQ_SCALE_E8M0_U8 = 1u << 2   /* same rounding, stored as the E8M0 byte (exponent + 127)  */
+};
+
+/*
+ * rmsq_fused -- one launch of the fused kernel family.
+ *
+ *  x            [T,H] bf16, row stride H, 16-byte aligned.  Read only; must not overlap any
+ *               output.
+ *  residual     [T,H] bf16, 16-byte aligned, or NULL for plain RMSNorm (vLLM rms_norm ->
+ *               quant); non-NULL selects the fused-add form (fused_add_rms_norm -> quant).
+ *  weight       [H] bf16, 16-byte aligned (same dtype as x: the blog's "Type check" rejects
+ *               mixed input/weight dtypes; bf16 is the one dtype supported).
+ *  eps          finite, > 0 (the pages' patterns use 1e-5 and 1e-6).
+ *  mode         rmsq_mode.
+ *  scale_in     device f32, 4-byte aligned: FP8_STATIC the per-tensor dequant scale (positive,
+ *               finite); FP4_BLOCK16 the global encode scale gs (positive, finite); must be
+ *               NULL for FP8_TOKEN and FP8_GROUP.
+ *  out_q        FP8: [T,H] e4m3fn bytes, 8-byte aligned.  FP4: [T,H/2] bytes, 4-byte aligned,
+ *               element 2k in the low nibble of byte k.
+ *  out_scales   FP8_STATIC: must be NULL.  FP8_TOKEN: [T] f32.  FP8_GROUP: [T,H/G] f32
+ *               row-major, or [H/G, scale_ld] f32 with RMSQ_SCALE_COLMAJOR, or bytes with
+ *               RMSQ_SCALE_E8M0_U8.  FP4_BLOCK16: [T,H/16] e4m3 bytes, row-major.  f32 scales
+ *               need 4-byte alignment.  Column-major padding (columns T..ld-1) is not written.
+ *  residual_out [T,H] bf16, 16-byte aligned; receives h.  Must be non-NULL iff residual is;
+ *               may equal residual exactly (in-place update, as vLLM's fused_add_rms_norm
+ *               does), must not otherwise overlap anything.
+ *  tokens       T >= 0; T == 0 is a successful no-op (pointers are then not checked).
+ *  hidden       H: 8 <= H <= RMSQ_MAX_HIDDEN, H % 8 == 0, and H % group_size == 0.
+ *  group_size   FP8_GROUP: 64 or 128.  FP4_BLOCK16: 16.  Otherwise 0.
+ *  flags        RMSQ_SCALE_* for FP8_GROUP (E8M0 and E8M0_U8 are exclusive); 0 otherwise.
+ *  scale_ld     FP8_GROUP with RMSQ_SCALE_COLMAJOR: leading dimension >= T (0 means T).
+ *               Otherwise 0.
+ *  stream       hipStream_t to enqueue on.
+ * Returns RMSQ_OK or a negative status (see rmsq_status_string).
+ */
+RMSQ_API int rmsq_fused(const void* x, const void* residual, const void* weight, float eps, int mode,
+               const float* scale_in, void* out_q, void* out_scales, void* residual_out,
+               int64_t tokens, int64_t hidden, int group_size, unsigned flags, int64_t scale_ld,
+               void* stream);
+
+/* Host-only argument check of rmsq_fused: returns exactly the status rmsq_fused would return
+ * for these arguments before it touches the device (RMSQ_OK when they are valid).  Makes no HIP
+ * call and dereferences no pointer. */
+RMSQ_API int rmsq_validate(const void* x, const void* residual, const void* weight, float eps,
+                           int mode, const float* scale_in, const void* out_q,
+                           const void* out_scales, const void* residual_out, int64_t tokens,
+                           int64_t hidden, int group_size, unsigned flags, int64_t scale_ld);
+
+/*
+ * Launch shape of the kernel family: one row of H elements is spread over threads_per_row
+ * threads (a multiple of 64, <= 1024), each holding chunks_per_thread 16-byte chunks (1, 2, 4
+ * or 8) of the row in registers; rows_per_block rows share one workgroup
+ * (rows_per_block * threads_per_row <= 1024).  threads_per_row * chunks_per_thread * 8 >= H.
+ */
+typedef struct rmsq_launch {
+  int32_t threads_per_row;
+  int32_t chunks_per_thread;
+  int32_t rows_per_block;
+  int32_t reserved; /* must be 0 */
+} rmsq_launch;
+
+/* rmsq_fused with an explicit launch shape (for tuning sweeps); launch == NULL behaves as
+ * rmsq_fused.  Results are identical for every valid shape. */
+RMSQ_API int rmsq_fused_with_launch(const void* x, const void* residual, const void* weight, float eps,
+                           int mode, const float* scale_in, void* out_q, void* out_scales,
+                           void* residual_out, int64_t tokens, int64_t hidden, int group_size,
+                           unsigned flags, int64_t scale_ld, const rmsq_launch* launch,
+                           void* stream);
+
+/* The launch shape rmsq_fused picks for (mode, T, H, group_size, residual?) and its grid size
+ * (number of workgroups).  Host only; makes no HIP call.  Returns RMSQ_OK or RMSQ_EINVAL. */
+RMSQ_API int rmsq_query_launch(int mode, int64_t tokens, int64_t hidden, int group_size,
+                      int has_residual, rmsq_launch* launch, int64_t* grid);
+
+/* Which block of rows workgroup `block` of a `grid`-workgroup launch processes.  Workgroups are
+ * dispatched round-robin over the MI355X's 8 accelerator dies (XCDs); this map hands each die
+ * a contiguous range of row blocks.  Host copy of the device mapping, for tests. */
+RMSQ_API int64_t rmsq_block_to_rowblock(int64_t block, int64_t grid);
+
+/* Diagnostic: run the kernels' own converters over n f32 values (device pointers).
+ *  RMSQ_CVT_E4M3  out: n bytes, saturating e4m3fn (the FP8 epilogue's conversion)
+ *  RMSQ_CVT_E2M1  out: n/2 bytes, element 2k in the low nibble (the FP4 epilogue's conversion);
+ *                 n must be a multiple of 8
+ *  RMSQ_CVT_BF16  out: n uint16 bf16 patterns (the residual-add rounding)
+ *  n must be a multiple of 8; in/out 16-byte aligned.  Used to pin gfx950's conversion
+ *  instructions against the reference definitions of the formats. */
+enum { RMSQ_CVT_E4M3 = 0, RMSQ_CVT_E2M1 = 1, RMSQ_CVT_BF16 = 2 };
+RMSQ_API int rmsq_convert(int format, const float* in, void* out, int64_t n, void* stream);
+
+/* Human-readable text for a status code (static storage). */
+RMSQ_API const char* rmsq_status_string(int status);
+
+/* RMSQ_ABI_VERSION of the loaded library. */
+RMSQ_API int rmsq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RMSQ_H */

@@ -1,0 +1,229 @@
+"""Thin ctypes binding of librmsq (include/rmsq.h), argument marshalling only.
+
+torch supplies device memory and the stream; every step of the computation runs in the HIP
+kernels of librmsq.so.  The library is loaded from this package directory; if it is missing
+the binding raises -- there is no fallback path.
+
+Function names match the C ABI (rmsq_fused, rmsq_fused_with_launch, rmsq_validate,
+rmsq_query_launch, rmsq_block_to_rowblock, rmsq_convert, rmsq_status_string,
+rmsq_abi_version).  A few allocating helpers named after the fused ops of the vLLM fusion
+pages (rms_norm_static_fp8_quant, fused_add_rms_norm_static_fp8_quant,
+rms_norm_dynamic_per_token_quant, rms_norm_per_block_quant, fused_add_rms_norm_fp4_quant)
+sit on top for callers who want tensors back.
+"""
+import ctypes as C
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librmsq.so")
+
+# ---- constants mirrored from include/rmsq.h ----
+RMSQ_OK, RMSQ_EINVAL, RMSQ_EALIGN, RMSQ_EALIAS, RMSQ_EUNSUPPORTED, RMSQ_ELAUNCH, RMSQ_EDEVICE = (
+    0, -1, -2, -3, -4, -5, -6)
+RMSQ_FP8_STATIC, RMSQ_FP8_TOKEN, RMSQ_FP8_GROUP, RMSQ_FP4_BLOCK16 = 0, 1, 2, 3
+RMSQ_SCALE_COLMAJOR, RMSQ_SCALE_E8M0, RMSQ_SCALE_E8M0_U8 = 1, 2, 4
+RMSQ_CVT_E4M3, RMSQ_CVT_E2M1, RMSQ_CVT_BF16 = 0, 1, 2
+RMSQ_MAX_HIDDEN = 65536
+
+
+class RmsqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {rmsq_status_string(status)} (status {status})")
+        self.status = status
+
+
+class rmsq_launch(C.Structure):
+    _fields_ = [("threads_per_row", C.c_int32), ("chunks_per_thread", C.c_int32),
+                ("rows_per_block", C.c_int32), ("reserved", C.c_int32)]
+
+    def as_tuple(self):
+        return (self.threads_per_row, self.chunks_per_thread, self.rows_per_block)
+
+
+_lib = None
+
+
+def lib():
+    """The loaded librmsq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
+                f"g.build()'` (or python rmsnorm_quantization_amd/build.py)")
+        L = C.CDLL(LIB_PATH)
+        p, i64, f32, i32, u32 = C.c_void_p, C.c_int64, C.c_float, C.c_int, C.c_uint
+        fused_args = [p, p, p, f32, i32, p, p, p, p, i64, i64, i32, u32, i64]
+        L.rmsq_fused.argtypes = fused_args + [p]
+        L.rmsq_fused.restype = i32
+        L.rmsq_fused_with_launch.argtypes = fused_args + [C.POINTER(rmsq_launch), p]
+        L.rmsq_fused_with_launch.restype = i32
+        L.rmsq_validate.argtypes = fused_args
+        L.rmsq_validate.restype = i32
+        L.rmsq_query_launch.argtypes = [i32, i64, i64, i32, i32, C.POINTER(rmsq_launch),
+                                        C.POINTER(i64)]
+        L.rmsq_query_launch.restype = i32
+        L.rmsq_block_to_rowblock.argtypes = [i64, i64]
+        L.rmsq_block_to_rowblock.restype = i64
+        L.rmsq_convert.argtypes = [i32, p, p, i64, p]
+        L.rmsq_convert.restype = i32
+        L.rmsq_status_string.argtypes = [i32]
+        L.rmsq_status_string.restype = C.c_char_p
+        L.rmsq_abi_version.argtypes = []
+        L.rmsq_abi_version.restype = i32
+        _lib = L
+    return _lib
+
+
+def _ptr(t) -> Optional[int]:
+    """Device pointer of a tensor (or None); raw integers pass through."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("rmsq: tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("rmsq: tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != RMSQ_OK:
+        raise RmsqError(status, where)
+
+
+# ---------------------------------------------------------------- C ABI, same names
+def rmsq_status_string(status: int) -> str:
+    return lib().rmsq_status_string(int(status)).decode()
+
+
+def rmsq_abi_version() -> int:
+    return lib().rmsq_abi_version()
+
+
+def rmsq_fused(x, residual, weight, eps, mode, scale_in, out_q, out_scales, residual_out,
+               tokens=None, hidden=None, group_size=0, flags=0, scale_ld=0, stream=None,
+               launch: Optional[rmsq_launch] = None, check=True) -> int:
+    """Enqueue one fused launch.  Tensors are passed by device pointer; sizes default to x's
+    shape.  Raises RmsqError on a non-zero status unless check=False."""
+    T = x.shape[0] if tokens is None else tokens
+    H = x.shape[-1] if hidden is None else hidden
+    args = (_ptr(x), _ptr(residual), _ptr(weight), float(eps), int(mode), _ptr(scale_in),
+            _ptr(out_q), _ptr(out_scales), _ptr(residual_out), int(T), int(H), int(group_size),
+            int(flags), int(scale_ld))
+    if launch is None:
+        st = lib().rmsq_fused(*args, _stream(stream))
+    else:
+        st = lib().rmsq_fused_with_launch(*args, C.byref(launch), _stream(stream))
+    if check:
+        _check(st, "rmsq_fused")
+    return st
+
+
+def rmsq_fused_with_launch(x, residual, weight, eps, mode, scale_in, out_q, out_scales,
+                           residual_out, tokens=None, hidden=None, group_size=0, flags=0,
+                           scale_ld=0, launch=None, stream=None, check=True) -> int:
+    return rmsq_fused(x, residual, weight, eps, mode, scale_in, out_q, out_scales, residual_out,
+                      tokens, hidden, group_size, flags, scale_ld, stream, launch, check)
+
+
+def rmsq_validate(x, residual, weight, eps, mode, scale_in, out_q, out_scales, residual_out,
+                  tokens, hidden, group_size=0, flags=0, scale_ld=0) -> int:
+    """Host-only argument check; pointers are plain integers (or None) and never dereferenced."""
+    return lib().rmsq_validate(x, residual, weight, float(eps), int(mode), scale_in, out_q,
+                               out_scales, residual_out, int(tokens), int(hidden),
+                               int(group_size), int(flags), int(scale_ld))
+
+
+def rmsq_query_launch(mode, tokens, hidden, group_size=0, has_residual=True):
+    l = rmsq_launch()
+    grid = C.c_int64(0)
+    _check(lib().rmsq_query_launch(int(mode), int(tokens), int(hidden), int(group_size),
+                                   int(bool(has_residual)), C.byref(l), C.byref(grid)),
+           "rmsq_query_launch")
+    return l, grid.value
+
+
+def rmsq_block_to_rowblock(block: int, grid: int) -> int:
+    return lib().rmsq_block_to_rowblock(int(block), int(grid))
+
+
+def rmsq_convert(fmt, inp, out, n=None, stream=None, check=True) -> int:
+    n = inp.numel() if n is None else n
+    st = lib().rmsq_convert(int(fmt), _ptr(inp), _ptr(out), int(n), _stream(stream))
+    if check:
+        _check(st, "rmsq_convert")
+    return st
+
+
+# ---------------------------------------------------------------- allocating helpers
+def _scalar(v, dev) -> torch.Tensor:
+    if isinstance(v, torch.Tensor):
+        return v.to(device=dev, dtype=torch.float32).reshape(1).contiguous()
+    return torch.tensor([float(v)], dtype=torch.float32, device=dev)
+
+
+def rms_norm_static_fp8_quant(x, weight, scale, eps, residual=None, inplace=True):
+    """(q [T,H] float8_e4m3fn, residual_out or None).  With a residual, the new residual is
+    written into `residual` itself when inplace=True (as the fused-add op does)."""
+    q = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
+    rout = None if residual is None else (residual if inplace else torch.empty_like(residual))
+    rmsq_fused(x, residual, weight, eps, RMSQ_FP8_STATIC, _scalar(scale, x.device),
+               q.view(torch.uint8), None, rout)
+    return q, rout
+
+
+def fused_add_rms_norm_static_fp8_quant(x, residual, weight, scale, eps):
+    """Fused add + RMSNorm + FP8 static quant; `residual` is updated in place.  Returns q."""
+    return rms_norm_static_fp8_quant(x, weight, scale, eps, residual=residual, inplace=True)[0]
+
+
+def rms_norm_dynamic_per_token_quant(x, weight, eps, residual=None, inplace=True):
+    """(q float8_e4m3fn [T,H], scales f32 [T], residual_out or None)."""
+    T = x.shape[0]
+    q = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
+    s = torch.empty((T,), dtype=torch.float32, device=x.device)
+    rout = None if residual is None else (residual if inplace else torch.empty_like(residual))
+    rmsq_fused(x, residual, weight, eps, RMSQ_FP8_TOKEN, None, q.view(torch.uint8), s, rout)
+    return q, s, rout
+
+
+def rms_norm_per_block_quant(x, weight, eps, group_size=128, residual=None, inplace=True,
+                             col_major=False, e8m0=False, e8m0_bytes=False, scale_ld=0):
+    """(q float8_e4m3fn [T,H], scales, residual_out or None).  Scales are [T,H/G] f32, or
+    [H/G, ld] with col_major, or uint8 E8M0 bytes with e8m0_bytes."""
+    T, H = x.shape
+    ng = H // group_size
+    flags = (RMSQ_SCALE_COLMAJOR if col_major else 0) | (RMSQ_SCALE_E8M0 if e8m0 else 0) | (
+        RMSQ_SCALE_E8M0_U8 if e8m0_bytes else 0)
+    ld = scale_ld or T
+    shape = (ng, ld) if col_major else (T, ng)
+    s = torch.empty(shape, dtype=torch.uint8 if e8m0_bytes else torch.float32, device=x.device)
+    q = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
+    rout = None if residual is None else (residual if inplace else torch.empty_like(residual))
+    rmsq_fused(x, residual, weight, eps, RMSQ_FP8_GROUP, None, q.view(torch.uint8), s, rout,
+               group_size=group_size, flags=flags, scale_ld=scale_ld if col_major else 0)
+    return q, s, rout
+
+
+def fused_add_rms_norm_fp4_quant(x, residual, weight, global_scale, eps, inplace=True):
+    """(packed e2m1 uint8 [T,H/2], e4m3 block scales uint8 [T,H/16], residual_out).
+    global_scale is the encode multiplier gs (dequant value = e2m1 * decode(sf) / gs)."""
+    T, H = x.shape
+    q = torch.empty((T, H // 2), dtype=torch.uint8, device=x.device)
+    sf = torch.empty((T, H // 16), dtype=torch.uint8, device=x.device)
+    rout = residual if inplace else torch.empty_like(residual)
+    rmsq_fused(x, residual, weight, eps, RMSQ_FP4_BLOCK16, _scalar(global_scale, x.device), q,
+               sf, rout, group_size=16)
+    return q, sf, rout

@@ -1,0 +1,58 @@
+"""Build librmsq.so (the HIP kernels + C ABI) in-tree for gfx950 with hipcc.
+
+Flags that matter for results:
+  -ffp-contract=off                          no FMA contraction of the binary32 steps
+  -fhip-fp32-correctly-rounded-divide-sqrt   IEEE f32 division (scales, reciprocals)
+  -Xclang -target-feature -Xclang -packed-fp32-ops
+                                             no packed-f32 VALU instructions
+"""
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SRC = [os.path.join(PKG, "csrc", "rmsq.hip")]
+DEPS = SRC + [os.path.join(PKG, "csrc", "rmsq_device.hpp"), os.path.join(ROOT, "include", "rmsq.h")]
+LIB = os.path.join(PKG, "librmsq.so")
+ARCH = "gfx950"
+
+
+def hipcc():
+    for c in ("/opt/rocm/bin/hipcc", "hipcc"):
+        if os.path.sep not in c or os.path.exists(c):
+            return c
+    return "hipcc"
+
+
+def command(out=LIB, extra=()):
+    return [
+        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-fvisibility=hidden", "-Wall", "-I", os.path.join(ROOT, "include"),
+        *extra, *SRC, "-o", out,
+    ]
+
+
+def build_library(verbose: bool = False) -> str:
+    cmd = command(LIB + ".tmp")
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed to build librmsq.so")
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+def is_stale() -> bool:
+    if not os.path.exists(LIB):
+        return True
+    t = os.path.getmtime(LIB)
+    return any(os.path.getmtime(p) > t for p in DEPS)
+
+
+if __name__ == "__main__":
+    print(build_library(verbose=True))

@@ -1,0 +1,132 @@
+// rmsq_device.hpp -- gfx950 device helpers for the fused RMSNorm + quantization kernels:
+// bf16 unpack/pack, hardware FP8 (OCP e4m3fn) / FP4 (e2m1) conversion, DPP group reductions.
+//
+// Formats (the pages name FP8 e4m3 and NVFP4-style e2m1 outputs -- vLLM docs "Fusion
+// torch.compile passes", "RMSNorm + quantization"; PR #51925 summary, "Motivation" -- but not
+// their bit layouts; the OCP definitions are used): e4m3fn saturates at 448, e2m1 at 6, both
+// round to nearest even.  The hardware converters are fed values already clamped to the
+// format's range, so saturation never depends on the instruction's overflow behaviour.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rmsq {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kFp8Max = 448.0f;
+constexpr float kFp4Max = 6.0f;
+
+// ---- bf16 ------------------------------------------------------------------------------
+// A dword holds two bf16 values, element 2j in the low half.  bf16 is the upper half of an
+// f32 pattern, so widening is a shift or a mask.
+__device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
+
+// Round two f32 to bf16 (nearest even; v_cvt_pk_bf16_f32), a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2 r = __builtin_convertvector((f32x2){a, b}, bf16x2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// ---- FP8 e4m3fn --------------------------------------------------------------------------
+__device__ __forceinline__ float clamp_sym(float v, float m) {
+  return __builtin_amdgcn_fmed3f(v, -m, m);
+}
+
+// Four f32 -> four e4m3fn bytes, element 0 in the lowest byte (v_cvt_pk_fp8_f32).
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_sym(a, kFp8Max), clamp_sym(b, kFp8Max), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_sym(c, kFp8Max), clamp_sym(d, kFp8Max), w, true);
+  return (uint32_t)w;
+}
+
+// One f32 -> one e4m3fn byte.
+__device__ __forceinline__ uint32_t fp8x1(float a) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp_sym(a, kFp8Max), 0.0f, 0, false) & 0xFFu;
+}
+
+// e4m3fn byte -> f32 (exact; v_cvt_f32_fp8).
+__device__ __forceinline__ float fp8_decode(uint32_t byte) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
+}
+
+// ---- FP4 e2m1 ----------------------------------------------------------------------------
+// Eight f32 -> eight e2m1 nibbles in one dword, element 2k in the low nibble of byte k
+// (v_cvt_scalef32_pk_fp4_f32 with a unit scale, so the instruction's scale does nothing).
+__device__ __forceinline__ uint32_t fp4x8(const float* v) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clamp_sym(v[0], kFp4Max),
+                                               clamp_sym(v[1], kFp4Max), 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clamp_sym(v[2], kFp4Max),
+                                               clamp_sym(v[3], kFp4Max), 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clamp_sym(v[4], kFp4Max),
+                                               clamp_sym(v[5], kFp4Max), 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clamp_sym(v[6], kFp4Max),
+                                               clamp_sym(v[7], kFp4Max), 1.0f, 3);
+  return w;
+}
+
+// ---- E8M0 ---------------------------------------------------------------------------------
+// Round a non-negative f32 scale up to the next power of two 2^k, k in [-127, 127], from its
+// bit pattern: a normal s with a non-zero mantissa moves up one binade; s == 0 and the
+// subnormals at or below 2^-127 give 2^-127 (E8M0 byte 0).  Returns the E8M0 byte (k + 127)
+// and the power of two as f32 in *p2.
+__device__ __forceinline__ uint32_t e8m0_ceil(float s, float* p2) {
+  const uint32_t b = __float_as_uint(s);
+  const uint32_t e = b >> 23, m = b & 0x7FFFFFu;
+  uint32_t byte;
+  if (e == 0) byte = (m > 0x400000u) ? 1u : 0u;  // subnormal: 2^-126 or 2^-127
+  else byte = e + (m != 0u ? 1u : 0u);
+  if (byte > 254u) byte = 254u;
+  *p2 = byte == 0u ? __uint_as_float(0x00400000u) : __uint_as_float(byte << 23);
+  return byte;
+}
+
+// ---- cross-lane reductions ---------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Max over aligned groups of LANES consecutive lanes (2, 4, 8 or 16: one DPP row at most);
+// every lane of a group ends with the group's max.  Must run with all lanes of the wave active.
+template <int LANES>
+__device__ __forceinline__ float group_max(float v) {
+  static_assert(LANES == 1 || LANES == 2 || LANES == 4 || LANES == 8 || LANES == 16, "lanes");
+  if (LANES >= 2) v = fmaxf(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]: lane ^ 1
+  if (LANES >= 4) v = fmaxf(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]: lane ^ 2
+  if (LANES >= 8) v = fmaxf(v, dpp<0x141>(v));  // row_half_mirror: other quad of the 8
+  if (LANES >= 16) v = fmaxf(v, dpp<0x140>(v)); // row_mirror: other half of the 16
+  return v;
+}
+
+// Butterfly sum / max over the 64 lanes of a wave.  IEEE addition is commutative, so every
+// lane ends with the bit-identical result.
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+// ---- XCD-aware block order -------------------------------------------------------------
+// Workgroups are handed to the 8 XCDs round-robin (workgroup b runs on XCD b % 8).  Giving
+// XCD x the contiguous range of row blocks [x*q + min(x,r), ...) keeps neighbouring rows in
+// one L2, where the partial-line writes of small per-row scales merge.
+constexpr uint32_t kNumXcd = 8;
+__host__ __device__ __forceinline__ uint32_t rowblock_of(uint32_t b, uint32_t n) {
+  const uint32_t x = b % kNumXcd, i = b / kNumXcd;
+  const uint32_t q = n / kNumXcd, r = n % kNumXcd;
+  return x * q + (x < r ? x : r) + i;
+}
+
+}  // namespace rmsq

@@ -1,0 +1,173 @@
+"""GPU-vs-oracle comparison rule for fused RMSNorm + quantization (test infrastructure).
+
+The bar, per output:
+  residual_out   bit-exact.
+  codes          equal, or the adjacent magnitude with the same sign (+0 and -0 count as
+                 equal); a mismatch is only accepted where the oracle's pre-rounding value lies
+                 within 1e-5 (relative) of the rounding midpoint between the two codes, and
+                 mismatches may total at most 0.01% of the elements.  Elements of a group whose
+                 scale differs are judged by the dequantized rule instead.
+  f32 scales     within 1e-6 relative.  E8M0 scales: equal, or a x2 flip where the unrounded
+                 scale is within 1e-6 of a power of two.  FP4 e4m3 block scales: equal or +-1
+                 code, counted as mismatches.
+  dequantized    FP8: per row (per group in group mode) max |dq_gpu - dq_ref| <=
+                 1e-2 * max |dq_ref|.  FP4: per element within one e2m1 step * d / gs.
+Why ties can differ at all: the GPU sums squares in a different order than the oracle, so
+inv_rms may differ in its last bit, and a value sitting on a rounding midpoint can then land
+on either neighbour.  In practice the binary64 sums agree after rounding to f32 and the
+counts below come out zero; the rule is what is asserted.
+"""
+from dataclasses import dataclass, field
+
+import numpy as np
+
+import oracle as O
+
+MAX_MISMATCH_FRAC = 1e-4
+MID_REL = 1e-5
+SCALE_REL = 1e-6
+DEQ_REL = 1e-2
+
+_E4 = None
+_E2 = None
+
+
+def e4_table():
+    global _E4
+    if _E4 is None:
+        _E4 = O.e4m3_table().astype(np.float64)
+    return _E4
+
+
+def e2_table():
+    global _E2
+    if _E2 is None:
+        _E2 = O.e2m1_table().astype(np.float64)
+    return _E2
+
+
+@dataclass
+class Report:
+    elements: int = 0
+    code_mismatch: int = 0
+    scale_mismatch: int = 0
+    residual_mismatch: int = 0
+    max_dequant_rel: float = 0.0
+    notes: list = field(default_factory=list)
+
+    def __str__(self):
+        return (f"elements={self.elements} code_mismatch={self.code_mismatch} "
+                f"scale_mismatch={self.scale_mismatch} residual_mismatch={self.residual_mismatch} "
+                f"max_dequant_rel={self.max_dequant_rel:.3g}")
+
+
+def _codes_ok(qg, qr, pre, fmt, excluded, rep: Report):
+    """Rule 2 on [T,H] code arrays (FP4 as nibbles); `excluded` masks elements judged by
+    rule 4 only (their group's scale differs)."""
+    signbit = 0x80 if fmt == "e4m3" else 0x8
+    magmask = 0x7F if fmt == "e4m3" else 0x7
+    tab = e4_table() if fmt == "e4m3" else e2_table()
+    qg = qg.astype(np.int64)
+    qr = qr.astype(np.int64)
+    mg, mr = qg & magmask, qr & magmask
+    same = (qg == qr) | ((mg == 0) & (mr == 0))
+    bad = ~same & ~excluded
+    n = int(bad.sum())
+    rep.code_mismatch += n
+    if n == 0:
+        return
+    sg, sr = qg[bad] & signbit, qr[bad] & signbit
+    assert np.all((sg == sr) | (mg[bad] == 0) | (mr[bad] == 0)), "code mismatch with sign flip"
+    assert np.all(np.abs(mg[bad] - mr[bad]) == 1), "code mismatch by more than one code"
+    lo = np.minimum(mg[bad], mr[bad])
+    mid = (tab[lo] + tab[lo + 1]) / 2
+    p = np.abs(pre[bad].astype(np.float64))
+    assert np.all(np.abs(p - mid) <= MID_REL * mid), "code mismatch away from a rounding midpoint"
+
+
+def compare(mode, gpu, ref, *, T, H, group_size=0, flags=0, scale_in=0.0, rows=None,
+            raw_group_scales=None) -> Report:
+    """Assert the rule above.  gpu/ref are dicts with q, scales, residual_out (numpy, as the
+    oracle lays them out); ref also has pre.  rows: which of the T rows were computed (the
+    arrays are then already restricted to them; col-major scales are [H/G, len(rows)])."""
+    rep = Report(elements=T * H)
+    if ref.get("residual_out") is not None:
+        rb = int((gpu["residual_out"] != ref["residual_out"]).sum())
+        rep.residual_mismatch = rb
+        assert rb == 0, f"residual_out differs in {rb} elements"
+
+    pre = ref["pre"]
+    excluded = np.zeros((T, H), bool)
+
+    if mode == O.FP4_BLOCK16:
+        sg, sr = gpu["scales"].astype(np.int64), ref["scales"].astype(np.int64)  # [T, H/16]
+        diff = sg != sr
+        rep.scale_mismatch = int(diff.sum())
+        if rep.scale_mismatch:
+            assert np.all(np.abs(sg[diff] - sr[diff]) == 1), "FP4 block scale off by > 1 code"
+        excluded = np.repeat(diff, 16, axis=1)
+        ng, nr = O.unpack_fp4(gpu["q"]), O.unpack_fp4(ref["q"])
+        _codes_ok(ng, nr, pre, "e2m1", excluded, rep)
+        # rule 4: per element within one e2m1 step * d / gs
+        gs = np.float64(np.float32(scale_in))
+        dg = np.repeat(e4_table()[sg] / gs, 16, axis=1)
+        dr = np.repeat(e4_table()[sr] / gs, 16, axis=1)
+        vg = e2_table()[ng] * dg
+        vr = e2_table()[nr] * dr
+        gap = np.array([0.5, 0.5, 0.5, 0.5, 1.0, 1.0, 2.0, 2.0])
+        step = gap[nr & 7] * np.maximum(dg, dr)
+        assert np.all(np.abs(vg - vr) <= step + 1e-30), "FP4 dequantized value off by > one step"
+        rel = np.abs(vg - vr) / np.maximum(np.abs(vr).max(), 1e-30)
+        rep.max_dequant_rel = float(rel.max()) if rel.size else 0.0
+    else:
+        qg, qr = gpu["q"], ref["q"]
+        if mode == O.FP8_STATIC:
+            s_g = s_r = np.full((T, 1), np.float32(scale_in), np.float64)
+            G = H
+        elif mode == O.FP8_TOKEN:
+            s_g = gpu["scales"].astype(np.float64)[:, None]
+            s_r = ref["scales"].astype(np.float64)[:, None]
+            G = H
+        else:
+            G = group_size
+            sg, sr = gpu["scales"], ref["scales"]
+            if flags & O.SCALE_COLMAJOR:
+                sg, sr = sg.T, sr.T
+            if flags & O.SCALE_E8M0_U8:
+                s_g = np.ldexp(1.0, sg.astype(np.int64) - 127)
+                s_r = np.ldexp(1.0, sr.astype(np.int64) - 127)
+            else:
+                s_g, s_r = sg.astype(np.float64), sr.astype(np.float64)
+        if mode != O.FP8_STATIC:
+            e8 = mode == O.FP8_GROUP and bool(flags & (O.SCALE_E8M0 | O.SCALE_E8M0_U8))
+            if e8:
+                diff = s_g != s_r
+                if diff.any():
+                    assert raw_group_scales is not None, "E8M0 scale flip: unrounded scale needed"
+                    raw = np.asarray(raw_group_scales, np.float64)
+                    if flags & O.SCALE_COLMAJOR:
+                        raw = raw.T
+                    ratio = np.maximum(s_g[diff], s_r[diff]) / np.minimum(s_g[diff], s_r[diff])
+                    assert np.all(ratio == 2.0), "E8M0 scale differs by more than a factor 2"
+                    p2 = np.ldexp(1.0, np.round(np.log2(raw[diff])).astype(np.int64))
+                    assert np.all(np.abs(raw[diff] - p2) <= SCALE_REL * p2), "E8M0 flip off a power of two"
+            else:
+                rel = np.abs(s_g - s_r) / np.maximum(np.abs(s_r), 1e-38)
+                diff = rel > 0
+                assert np.all(rel <= SCALE_REL), f"scale off by {rel.max():.3g} relative"
+            rep.scale_mismatch = int(diff.sum())
+            excluded = np.repeat(diff, G, axis=1) if diff.shape[1] * G == H else excluded
+        _codes_ok(qg, qr, pre, "e4m3", excluded, rep)
+        # rule 4: dequantized, per row (static/token) or per group
+        dqg = e4_table()[qg].reshape(T, H // G, G) * s_g[:, :, None]
+        dqr = e4_table()[qr].reshape(T, H // G, G) * s_r[:, :, None]
+        err = np.abs(dqg - dqr).max(axis=2)
+        ref_max = np.abs(dqr).max(axis=2)
+        ok = err <= DEQ_REL * ref_max
+        assert np.all(ok | (ref_max == 0) & (err == 0)), "dequantized output off by > 1e-2 relative"
+        rel = err / np.maximum(ref_max, 1e-38)
+        rep.max_dequant_rel = float(rel.max()) if rel.size else 0.0
+
+    assert rep.code_mismatch <= MAX_MISMATCH_FRAC * rep.elements, \
+        f"{rep.code_mismatch} code mismatches exceed 0.01% of {rep.elements}"
+    return rep

@@ -1,0 +1,153 @@
+"""The C ABI on the CPU: the library loads, exports every function include/rmsq.h declares,
+and the host-side argument checks return the documented status for each kind of bad call.
+
+Nothing here touches a device: rmsq_validate makes no HIP call, and rmsq_fused is only called
+with arguments rmsq_validate has already rejected (it then returns the same status before
+reaching the device)."""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rmsq.h")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from rmsnorm_quantization_amd import binding, build
+
+    if build.is_stale():
+        build.build_library()
+    binding.lib()
+    return binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"RMSQ_API\s+[\w\s\*]*?\b(rmsq_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("rmsq_fused", "rmsq_fused_with_launch", "rmsq_validate", "rmsq_query_launch",
+              "rmsq_block_to_rowblock", "rmsq_convert", "rmsq_status_string",
+              "rmsq_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(B):
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
+    for n in declared_functions():
+        assert n in exported, n
+        assert hasattr(B.lib(), n)
+    # nothing else leaks out of the library under an rmsq name
+    assert {e for e in exported if "rmsq" in e} == set(declared_functions())
+
+
+def test_abi_version_and_status_strings(B):
+    assert B.rmsq_abi_version() == 1
+    for st in (0, -1, -2, -3, -4, -5, -6):
+        assert B.rmsq_status_string(st) and B.rmsq_status_string(st) != "unknown status"
+    assert B.rmsq_status_string(-99) == "unknown status"
+
+
+# ------------------------------------------------------------------ argument checks
+# Fake, well-separated, 256-byte-aligned addresses: never dereferenced.
+X, R, W, Q, S, RO, SC = (0x10000000 * (i + 1) for i in range(7))
+T, H = 4, 256
+
+
+def V(B, x=X, r=R, w=W, eps=1e-6, mode=1, sc=None, q=Q, s=S, ro=RO, t=T, h=H, g=0, f=0, ld=0):
+    return B.rmsq_validate(x, r, w, eps, mode, sc, q, s, ro, t, h, g, f, ld)
+
+
+def test_valid_calls(B):
+    assert V(B) == B.RMSQ_OK
+    assert V(B, mode=0, sc=SC, s=None) == B.RMSQ_OK
+    assert V(B, mode=2, g=128) == B.RMSQ_OK
+    assert V(B, mode=2, g=64, f=B.RMSQ_SCALE_COLMAJOR | B.RMSQ_SCALE_E8M0, ld=8) == B.RMSQ_OK
+    assert V(B, mode=3, g=16, sc=SC) == B.RMSQ_OK
+    assert V(B, r=None, ro=None) == B.RMSQ_OK
+    assert V(B, ro=R) == B.RMSQ_OK  # in-place residual
+    assert V(B, t=0, x=None, q=None) == B.RMSQ_OK  # empty batch
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(t=-1), "EINVAL"), (dict(h=0), "EINVAL"), (dict(h=12), "EINVAL"),
+    (dict(h=65536 + 8), "EINVAL"), (dict(eps=0.0), "EINVAL"), (dict(eps=-1e-6), "EINVAL"),
+    (dict(eps=float("inf")), "EINVAL"), (dict(eps=float("nan")), "EINVAL"),
+    (dict(mode=4), "EINVAL"), (dict(mode=-1), "EINVAL"),
+    (dict(x=None), "EINVAL"), (dict(w=None), "EINVAL"), (dict(q=None), "EINVAL"),
+    (dict(ro=None), "EINVAL"), (dict(r=None), "EINVAL"),
+    (dict(s=None), "EINVAL"), (dict(sc=SC), "EINVAL"),                    # token mode
+    (dict(mode=0, s=None), "EINVAL"), (dict(mode=0, sc=SC), "EINVAL"),    # static: scales
+    (dict(mode=0, sc=SC, s=None, g=64), "EINVAL"),
+    (dict(mode=2, g=32), "EINVAL"), (dict(mode=2, g=128, h=192), "EINVAL"),
+    (dict(mode=2, g=0), "EINVAL"), (dict(mode=3, g=16), "EINVAL"),         # fp4 needs gs
+    (dict(mode=3, sc=SC, g=8), "EINVAL"), (dict(mode=3, sc=SC, g=16, h=264), "EINVAL"),
+    (dict(mode=2, g=64, f=1, ld=3), "EINVAL"),                    # ld < T
+    (dict(mode=2, g=64, ld=8), "EINVAL"),                                  # ld without colmajor
+    (dict(f=1), "EUNSUPPORTED"), (dict(mode=3, sc=SC, g=16, f=2), "EUNSUPPORTED"),
+    (dict(mode=2, g=64, f=8), "EUNSUPPORTED"), (dict(mode=2, g=64, f=6), "EUNSUPPORTED"),
+    (dict(x=X + 8), "EALIGN"), (dict(w=W + 4), "EALIGN"), (dict(r=R + 2), "EALIGN"),
+    (dict(ro=RO + 8), "EALIGN"), (dict(q=Q + 4), "EALIGN"), (dict(s=S + 2), "EALIGN"),
+    (dict(mode=0, s=None, sc=SC + 1), "EALIGN"), (dict(mode=3, g=16, sc=SC, q=Q + 2), "EALIGN"),
+    (dict(q=X), "EALIAS"), (dict(s=X + 16), "EALIAS"), (dict(ro=X), "EALIAS"),
+    (dict(q=W), "EALIAS"), (dict(q=R), "EALIAS"), (dict(ro=R + 16), "EALIAS"),
+    (dict(s=Q + 16), "EALIAS"), (dict(ro=Q), "EALIAS"), (dict(mode=0, s=None, sc=Q), "EALIAS"),
+    (dict(s=R), "EALIAS"),
+])
+def test_bad_arguments(B, kw, status):
+    code = getattr(B, "RMSQ_" + status)
+    assert V(B, **kw) == code
+    # rmsq_fused returns the same status without going near a device
+    assert B.lib().rmsq_fused(kw.get("x", X), kw.get("r", R), kw.get("w", W),
+                              kw.get("eps", 1e-6), kw.get("mode", 1), kw.get("sc", None),
+                              kw.get("q", Q), kw.get("s", S), kw.get("ro", RO), kw.get("t", T),
+                              kw.get("h", H), kw.get("g", 0), kw.get("f", 0), kw.get("ld", 0),
+                              None) == code
+
+
+def test_colmajor_scale_extent_is_checked(B):
+    # col-major scales [H/G, ld]: the last column of the last group ends at ((ng-1)*ld + T)*4
+    ng, ld = H // 64, 16
+    end = ((ng - 1) * ld + T) * 4
+    assert V(B, mode=2, g=64, f=1, ld=ld, s=S, q=S + end) == B.RMSQ_OK
+    assert V(B, mode=2, g=64, f=1, ld=ld, s=S, q=S + end - 16) == B.RMSQ_EALIAS
+
+
+def test_query_launch(B):
+    for h in (8, 64, 1024, 2048, 2880, 4096, 5120, 7168, 8192, 16384, 65536):
+        l, grid = B.rmsq_query_launch(1, 1000, h)
+        tpr, vpt, rpb = l.as_tuple()
+        assert tpr % 64 == 0 and 64 <= tpr <= 1024
+        assert vpt in (1, 2, 4, 8) and tpr * vpt * 8 >= h
+        assert rpb >= 1 and rpb * tpr <= 1024
+        assert grid == -(-1000 // rpb)
+    with pytest.raises(B.RmsqError):
+        B.rmsq_query_launch(1, 10, 12)
+
+
+@pytest.mark.parametrize("grid", [1, 2, 7, 8, 9, 15, 16, 17, 255, 256, 1000, 4096, 16385])
+def test_block_to_rowblock_is_a_bijection(B, grid):
+    got = [B.rmsq_block_to_rowblock(b, grid) for b in range(grid)]
+    assert sorted(got) == list(range(grid))
+    # each XCD (b % 8) gets one contiguous run of row blocks
+    for x in range(8):
+        mine = [got[b] for b in range(x, grid, 8)]
+        assert mine == list(range(mine[0], mine[0] + len(mine))) if mine else True
+    assert B.rmsq_block_to_rowblock(grid, grid) == -1
+
+
+def test_convert_argument_checks(B):
+    L = B.lib()
+    assert L.rmsq_convert(7, X, Q, 8, None) == B.RMSQ_EINVAL
+    assert L.rmsq_convert(0, X, Q, 12, None) == B.RMSQ_EINVAL
+    assert L.rmsq_convert(0, X, Q, 0, None) == B.RMSQ_OK
+    assert L.rmsq_convert(0, X + 4, Q, 8, None) == B.RMSQ_EALIGN
+    assert L.rmsq_convert(0, X, X + 16, 8, None) == B.RMSQ_EALIAS

@@ -1,0 +1,88 @@
+"""Pin gfx950's conversion instructions, as the kernels use them, against the oracle's formats.
+
+rmsq_convert runs the kernels' own helpers (clamp + v_cvt_pk_fp8_f32; clamp +
+v_cvt_scalef32_pk_fp4_f32 with a unit scale and the nibble packing; v_cvt_pk_bf16_f32) over
+arbitrary f32 inputs.  Checked on every bf16 value, every rounding midpoint of the target
+format and +-1 ulp around it, saturation, signed zeros, and a large random sample of f32 bit
+patterns.  NaN inputs are outside the contract and are left out.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from rmsnorm_quantization_amd import binding as B
+from tests import gpu_harness as GH
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    GH.require_gpu()
+
+
+def _pad8(v):
+    n = (-len(v)) % 8
+    return np.concatenate([v, np.zeros(n, np.float32)]).astype(np.float32)
+
+
+def _midpoints(table):
+    t = np.sort(np.unique(table[np.isfinite(table) & (table >= 0)].astype(np.float64)))
+    mids = ((t[:-1] + t[1:]) / 2).astype(np.float32)
+    lo, hi = np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(np.inf))
+    v = np.concatenate([t.astype(np.float32), mids, lo, hi])
+    return np.concatenate([v, -v])
+
+
+def _inputs(table, sat):
+    rng = np.random.default_rng(1234)
+    bf = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32)
+    rnd = rng.integers(0, 2 ** 32, 2_000_000, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    near = (rng.standard_normal(1_000_000) * sat / 3).astype(np.float32)
+    special = np.array([0.0, -0.0, sat, -sat, sat * 1.01, -sat * 1.01, 1e30, -1e30, np.inf,
+                        -np.inf, 1e-40, -1e-40], np.float32)
+    v = np.concatenate([bf, rnd, near, _midpoints(table), special])
+    return _pad8(v[~np.isnan(v)])
+
+
+def _convert(fmt, v):
+    vin = torch.from_numpy(v).to("cuda")
+    n = v.size
+    nbytes = {B.RMSQ_CVT_E4M3: n, B.RMSQ_CVT_E2M1: n // 2, B.RMSQ_CVT_BF16: 2 * n}[fmt]
+    g = GH.Guarded(nbytes)
+    print(f"[convert] fmt={fmt} n={n}", flush=True)
+    B.rmsq_convert(fmt, vin, g.data, n)
+    torch.cuda.synchronize()
+    g.check("convert out")
+    return g.data.cpu().numpy()
+
+
+def test_e4m3_conversion_matches_oracle():
+    v = _inputs(O.e4m3_table(), 448.0)
+    got = _convert(B.RMSQ_CVT_E4M3, v)
+    exp = O.e4m3_encode(v)
+    bad = got != exp
+    assert not bad.any(), f"{bad.sum()} mismatches, e.g. {v[bad][:8]} -> {got[bad][:8]} vs {exp[bad][:8]}"
+
+
+def test_e2m1_conversion_and_packing_match_oracle():
+    v = _inputs(O.e2m1_table(), 6.0)
+    got = _convert(B.RMSQ_CVT_E2M1, v)
+    exp = O.e2m1_encode(v)
+    nib = O.unpack_fp4(got)
+    bad = nib != exp
+    assert not bad.any(), f"{bad.sum()} mismatches, e.g. {v[bad][:8]} -> {nib[bad][:8]} vs {exp[bad][:8]}"
+
+
+def test_bf16_rounding_matches_oracle():
+    rng = np.random.default_rng(99)
+    hi = np.arange(65536, dtype=np.uint32) << 16
+    ties = np.concatenate([hi | 0x8000, hi | 0x7FFF, hi | 0x8001]).view(np.float32)
+    rnd = rng.integers(0, 2 ** 32, 2_000_000, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    v = np.concatenate([ties, rnd])
+    v = _pad8(v[~np.isnan(v)])
+    got = _convert(B.RMSQ_CVT_BF16, v).view(np.uint16)
+    exp = O.f32_to_bf16(v)
+    bad = got != exp
+    assert not bad.any(), f"{bad.sum()} mismatches, e.g. {v[bad][:8]} -> {got[bad][:8]} vs {exp[bad][:8]}"

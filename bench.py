@@ -9,8 +9,9 @@ Inputs are resident in HBM before timing starts.  Launches rotate over several b
 whose total footprint is well above the 256 MB last-level cache, so each launch reads cold
 data.  Prints ONE JSON line:
   value          algorithmic GB/s over the timed region (bytes each launch must move)
-  roofline       HBM roofline of the fused kernel: algorithmic bytes / average launch duration
-                 (per-launch HIP events on the launch stream), against 8 TB/s; traffic = HBM
+  roofline       HBM roofline of the fused kernel: algorithmic bytes / the kernel's average
+                 duration (HIP events stamped by each dispatch itself on the launch stream),
+                 against 8 TB/s; traffic = HBM
                  bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE (scaled by a plain
                  copy's counters) when the committed counters match the current kernel source
   cpu_baseline   the CPU oracle on a bounded sample of the same workload, one core
@@ -38,8 +39,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for p in ("rmsnorm_quantization_amd/csrc/rmsq.hip", "rmsnorm_quantization_amd/csrc/rmsq_device.hpp",
-              "include/rmsq.h", "rmsnorm_quantization_amd/build.py"):
+    for p in ("rmsnorm_quantization_amd/csrc/rmsq_kernels.hpp",
+              "rmsnorm_quantization_amd/csrc/rmsq_device.hpp", "rmsnorm_quantization_amd/build.py"):
         h.update(open(os.path.join(ROOT, p), "rb").read())
     return h.hexdigest()[:16]
 
@@ -138,15 +139,27 @@ def gpu_leg(args, wl, T, H, mode, G, flags):
 
     launch = None
     if args.launch:
-        tpr, vpt, rpb = (int(v) for v in args.launch.split(","))
-        launch = B.rmsq_launch(tpr, vpt, rpb, 0)
+        vals = [int(v) for v in args.launch.split(",")]
+        launch = B.rmsq_launch(*(vals + [0] * (4 - len(vals))))
     shape = launch.as_tuple() if launch else B.rmsq_query_launch(mode, T, H, G, residual)[0].as_tuple()
     stream = torch.cuda.current_stream()
 
+    # argument tuples marshalled once, so the launch loop is one C call per step
+    import ctypes
+
+    lib = B.lib()
+    ptr = (lambda t: None if t is None else t.data_ptr())
+    argsets = [(ptr(s["x"]), ptr(s["r"]), wd.data_ptr(), float(wl.eps), mode, ptr(scale_in),
+                ptr(s["q"]), ptr(s["s"]), ptr(s["ro"]), T, H, G, flags, 0) for s in sets]
+    sh = stream.cuda_stream
+    lref = ctypes.byref(launch) if launch is not None else None
+    status = []
+
     def step(i):
-        s = sets[i % nsets]
-        B.rmsq_fused(s["x"], s["r"], wd, wl.eps, mode, scale_in, s["q"], s["s"], s["ro"],
-                     group_size=G, flags=flags, launch=launch, stream=stream)
+        a = argsets[i % nsets]
+        st = lib.rmsq_fused_with_launch(*a, lref, sh) if lref else lib.rmsq_fused(*a, sh)
+        if st:
+            status.append(st)
 
     for i in range(args.warmup):
         step(i)
@@ -162,15 +175,22 @@ def gpu_leg(args, wl, T, H, mode, G, flags):
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
 
-    # per-launch durations: each launch between its own event pair on the launch stream
+    # per-launch kernel durations: each launch carries its own event pair, stamped by the
+    # dispatch itself at kernel start and end (rmsq_fused_timed)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
+    for a_, b_ in evs:  # create the underlying HIP events
+        a_.record(stream)
+        b_.record(stream)
     torch.cuda.synchronize()
     for i in range(args.steps):
-        evs[i][0].record(stream)
-        step(i)
-        evs[i][1].record(stream)
+        a = argsets[i % nsets]
+        st = lib.rmsq_fused_timed(*a, lref, evs[i][0].cuda_event, evs[i][1].cuda_event, sh)
+        if st:
+            status.append(st)
     torch.cuda.synchronize()
+    if status:
+        raise RuntimeError(f"rmsq_fused failed: {B.rmsq_status_string(status[0])}")
     per = sorted(a.elapsed_time(b) for a, b in evs)
     avg_launch_ms = sum(per) / len(per)
     med_launch_ms = per[len(per) // 2]
@@ -245,6 +265,84 @@ def load_traffic(key):
     return e
 
 
+# ---------------------------------------------------------------- rocprofv3 summaries
+COPY_BYTES = 256 << 20  # the plain copy bench.py runs for calibration (copy_src above)
+
+
+def _db_rows(db, sql):
+    import sqlite3
+
+    con = sqlite3.connect(db)
+    try:
+        return con.execute(sql).fetchall()
+    finally:
+        con.close()
+
+
+def summarize(ktrace_db, fetch_db, write_db, key, title, commands, out_md):
+    """Turn the three rocprofv3 databases of one bench configuration into a short text summary
+    under profiles/ and the traffic entry bench.py reports.  Counters are KiB per dispatch;
+    each is scaled by what it reads for the plain 256 MiB copy in the same run."""
+    import statistics
+
+    top = _db_rows(ktrace_db, "select name, total_calls, total_duration, average, percentage "
+                              "from top_kernels")
+    fused = [r for r in top if "fused_kernel" in r[0]]
+    main_k = max(fused, key=lambda r: r[1])  # the benched instantiation (most calls)
+    durs = [r[0] for r in _db_rows(ktrace_db, "select duration from kernels where name = '%s'"
+                                   % main_k[0].replace("'", "''"))]
+
+    def counter(db, name):
+        rows = _db_rows(db, "select kernel_name, value from counters_collection "
+                            "where counter_name = '%s'" % name)
+        mine = [v for k, v in rows if k == main_k[0]]
+        copies = sorted((v for k, v in rows if k.startswith("__amd_rocclr_copyBuffer")),
+                        reverse=True)[:10]
+        return statistics.median(mine), statistics.median(copies), len(mine)
+
+    f_k, f_copy, nf = counter(fetch_db, "FETCH_SIZE")
+    w_k, w_copy, nw = counter(write_db, "WRITE_SIZE")
+    f_scale = (COPY_BYTES / 1024) / f_copy
+    w_scale = (COPY_BYTES / 1024) / w_copy
+    fetch_b = f_k * 1024 * f_scale
+    write_b = w_k * 1024 * w_scale
+    entry = {"kernel": main_k[0], "kernel_source": kernel_source_hash(),
+             "bytes_per_launch": int(round(fetch_b + write_b)), "fetch_bytes": int(round(fetch_b)),
+             "write_bytes": int(round(write_b)),
+             "calibration": {"copy_bytes": COPY_BYTES, "fetch_kib_copy": f_copy,
+                             "write_kib_copy": w_copy, "fetch_scale": round(f_scale, 5),
+                             "write_scale": round(w_scale, 5)},
+             "avg_duration_us": round(main_k[3], 3)}
+    try:
+        allt = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        allt = {}
+    allt[key] = entry
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(allt, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+
+    lines = [f"# {title}", "", "Commands (from the repository root on the GPU box):", ""]
+    lines += [f"    {c}" for c in commands]
+    lines += ["", "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
+              "| kernel | calls | total us | average us | % |", "|---|---|---|---|---|"]
+    for r in top[:8]:
+        lines.append(f"| `{r[0][:90]}` | {r[1]} | {r[2]:.1f} | {r[3]:.3f} | {r[4]:.1f} |")
+    lines += ["", f"Benched kernel `{main_k[0]}`: {len(durs)} dispatches, average "
+              f"{main_k[3]:.3f} us, median {statistics.median(durs) / 1e3:.3f} us, "
+              f"min {min(durs) / 1e3:.3f} us, max {max(durs) / 1e3:.3f} us.", "",
+              "## HBM traffic (rocprofv3 --pmc, one counter per run)", "",
+              "| counter | benched kernel, KiB/dispatch (median of %d) | 256 MiB copy, KiB | scale "
+              "| bytes/launch |" % nf, "|---|---|---|---|---|",
+              f"| FETCH_SIZE | {f_k:.2f} | {f_copy:.2f} | {f_scale:.5f} | {fetch_b:,.0f} |",
+              f"| WRITE_SIZE | {w_k:.2f} | {w_copy:.2f} | {w_scale:.5f} | {write_b:,.0f} |", "",
+              f"Measured HBM traffic per launch: {fetch_b + write_b:,.0f} bytes.", ""]
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines))
+    return entry
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -258,7 +356,25 @@ def main():
     ap.add_argument("--launch", default="")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--summarize", nargs=3, metavar=("KTRACE_DB", "FETCH_DB", "WRITE_DB"),
+                    help="write the profiles/ summary and traffic entry for this configuration "
+                         "from three rocprofv3 databases, then exit")
+    ap.add_argument("--summary-md", default="")
+    ap.add_argument("--commands", default="", help="';;'-separated commands quoted in the summary")
     args = ap.parse_args()
+
+    if args.summarize:
+        from rmsnorm_quantization_amd import synth  # noqa: F401
+
+        wl, T, H, mode, G, flags = workload_spec(args)
+        key = f"{args.workload}_T{T}_H{H}_{MODE_NAMES[mode]}_G{G}_f{flags}"
+        md = args.summary_md or os.path.join(ROOT, "profiles", f"fused_kernel_{key}.md")
+        title = (f"fused_kernel, {wl.name}: {T} tokens x hidden {H}, {MODE_NAMES[mode]}"
+                 f"{' G=%d' % G if mode == 2 else ''}")
+        e = summarize(*args.summarize, key, title, [c.strip() for c in args.commands.split(";;")
+                                                     if c.strip()], md)
+        print(json.dumps(e))
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
@@ -269,6 +385,7 @@ def main():
     wl, T, H, mode, G, flags = workload_spec(args)
     g = gpu_leg(args, wl, T, H, mode, G, flags)
     gbs = g["bytes"] / (g["ms_per_step"] * 1e-3) / 1e9
+    # the kernel's own average duration, from dispatch-stamped event pairs
     achieved = g["bytes"] / (g["avg_launch_ms"] * 1e-3) / 1e9
     key = f"{args.workload}_T{T}_H{H}_{MODE_NAMES[mode]}_G{G}_f{flags}"
     tr = load_traffic(key)
@@ -293,14 +410,14 @@ def main():
             "flags": flags, "residual": wl.residual, "eps": wl.eps,
             "io": "bf16 in; " + ("e2m1 + e4m3 block scales out" if mode == 3 else "e4m3fn out"),
             "launch": {"threads_per_row": g["launch"][0], "chunks_per_thread": g["launch"][1],
-                       "rows_per_block": g["launch"][2]},
+                       "rows_per_block": g["launch"][2], "options": g["launch"][3]},
             "rotating_sets": g["sets"], "parallelism": "single GPU",
         },
         "tokens_per_s": round(T / (g["ms_per_step"] * 1e-3), 1),
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "bytes_per_step": g["bytes"],
-        "avg_launch_us": round(g["avg_launch_ms"] * 1e3, 3),
-        "median_launch_us": round(g["median_launch_ms"] * 1e3, 3),
+        "kernel_us": {"mean": round(g["avg_launch_ms"] * 1e3, 3),
+                      "median": round(g["median_launch_ms"] * 1e3, 3)},
         "copy_kernel_GBs": round(g["copy_gbs"], 1),
         "device": g["device"],
         "roofline": {

@@ -122,15 +122,22 @@ RMSQ_API int rmsq_validate(const void* x, const void* residual, const void* weig
 
 /*
  * Launch shape of the kernel family: one row of H elements is spread over threads_per_row
- * threads (a multiple of 64, <= 1024), each holding chunks_per_thread 16-byte chunks (1, 2, 4
- * or 8) of the row in registers; rows_per_block rows share one workgroup
+ * threads (a multiple of 64, <= 1024), each holding chunks_per_thread 16-byte chunks (1 to 8)
+ * of the row in registers; rows_per_block rows share one workgroup
  * (rows_per_block * threads_per_row <= 1024).  threads_per_row * chunks_per_thread * 8 >= H.
+ * options: RMSQ_LAUNCH_* bits.
  */
+enum {
+  /* By default workgroup b takes row block b, so the workgroups in flight touch one compact
+   * window of each array (best for HBM page locality).  With this bit each of the 8 XCDs takes
+   * a contiguous range of row blocks instead (rmsq_block_to_rowblock). */
+  RMSQ_LAUNCH_XCD_RANGES = 1
+};
 typedef struct rmsq_launch {
   int32_t threads_per_row;
   int32_t chunks_per_thread;
   int32_t rows_per_block;
-  int32_t reserved; /* must be 0 */
+  int32_t options; /* RMSQ_LAUNCH_* bits; other bits must be 0 */
 } rmsq_launch;
 
 /* rmsq_fused with an explicit launch shape (for tuning sweeps); launch == NULL behaves as
@@ -140,6 +147,16 @@ RMSQ_API int rmsq_fused_with_launch(const void* x, const void* residual, const v
                            void* residual_out, int64_t tokens, int64_t hidden, int group_size,
                            unsigned flags, int64_t scale_ld, const rmsq_launch* launch,
                            void* stream);
+
+/* rmsq_fused_with_launch for measurement: the kernel is dispatched with hipExtLaunchKernel so
+ * that start_event and stop_event (hipEvent_t created by the caller, either may be NULL) are
+ * stamped by the dispatch itself at the kernel's start and end; their elapsed time is the
+ * kernel's own duration, without the queue gaps between back-to-back launches. */
+RMSQ_API int rmsq_fused_timed(const void* x, const void* residual, const void* weight, float eps,
+                              int mode, const float* scale_in, void* out_q, void* out_scales,
+                              void* residual_out, int64_t tokens, int64_t hidden, int group_size,
+                              unsigned flags, int64_t scale_ld, const rmsq_launch* launch,
+                              void* start_event, void* stop_event, void* stream);
 
 /* The launch shape rmsq_fused picks for (mode, T, H, group_size, residual?) and its grid size
  * (number of workgroups).  Host only; makes no HIP call.  Returns RMSQ_OK or RMSQ_EINVAL. */

@@ -4,7 +4,8 @@ torch supplies device memory and the stream; every step of the computation runs 
 kernels of librmsq.so.  The library is loaded from this package directory; if it is missing
 the binding raises -- there is no fallback path.
 
-Function names match the C ABI (rmsq_fused, rmsq_fused_with_launch, rmsq_validate,
+Function names match the C ABI (rmsq_fused, rmsq_fused_with_launch, rmsq_fused_timed,
+rmsq_validate,
 rmsq_query_launch, rmsq_block_to_rowblock, rmsq_convert, rmsq_status_string,
 rmsq_abi_version).  A few allocating helpers named after the fused ops of the vLLM fusion
 pages (rms_norm_static_fp8_quant, fused_add_rms_norm_static_fp8_quant,
@@ -25,6 +26,7 @@ RMSQ_OK, RMSQ_EINVAL, RMSQ_EALIGN, RMSQ_EALIAS, RMSQ_EUNSUPPORTED, RMSQ_ELAUNCH,
 RMSQ_FP8_STATIC, RMSQ_FP8_TOKEN, RMSQ_FP8_GROUP, RMSQ_FP4_BLOCK16 = 0, 1, 2, 3
 RMSQ_SCALE_COLMAJOR, RMSQ_SCALE_E8M0, RMSQ_SCALE_E8M0_U8 = 1, 2, 4
 RMSQ_CVT_E4M3, RMSQ_CVT_E2M1, RMSQ_CVT_BF16 = 0, 1, 2
+RMSQ_LAUNCH_XCD_RANGES = 1
 RMSQ_MAX_HIDDEN = 65536
 
 
@@ -36,10 +38,10 @@ class RmsqError(RuntimeError):
 
 class rmsq_launch(C.Structure):
     _fields_ = [("threads_per_row", C.c_int32), ("chunks_per_thread", C.c_int32),
-                ("rows_per_block", C.c_int32), ("reserved", C.c_int32)]
+                ("rows_per_block", C.c_int32), ("options", C.c_int32)]
 
     def as_tuple(self):
-        return (self.threads_per_row, self.chunks_per_thread, self.rows_per_block)
+        return (self.threads_per_row, self.chunks_per_thread, self.rows_per_block, self.options)
 
 
 _lib = None
@@ -60,6 +62,8 @@ def lib():
         L.rmsq_fused.restype = i32
         L.rmsq_fused_with_launch.argtypes = fused_args + [C.POINTER(rmsq_launch), p]
         L.rmsq_fused_with_launch.restype = i32
+        L.rmsq_fused_timed.argtypes = fused_args + [C.POINTER(rmsq_launch), p, p, p]
+        L.rmsq_fused_timed.restype = i32
         L.rmsq_validate.argtypes = fused_args
         L.rmsq_validate.restype = i32
         L.rmsq_query_launch.argtypes = [i32, i64, i64, i32, i32, C.POINTER(rmsq_launch),
@@ -136,6 +140,23 @@ def rmsq_fused_with_launch(x, residual, weight, eps, mode, scale_in, out_q, out_
                            scale_ld=0, launch=None, stream=None, check=True) -> int:
     return rmsq_fused(x, residual, weight, eps, mode, scale_in, out_q, out_scales, residual_out,
                       tokens, hidden, group_size, flags, scale_ld, stream, launch, check)
+
+
+def rmsq_fused_timed(x, residual, weight, eps, mode, scale_in, out_q, out_scales, residual_out,
+                     tokens=None, hidden=None, group_size=0, flags=0, scale_ld=0, launch=None,
+                     start_event=None, stop_event=None, stream=None, check=True) -> int:
+    """One launch whose start/stop events (raw hipEvent_t handles, e.g. a recorded
+    torch.cuda.Event's .cuda_event) are stamped by the dispatch itself."""
+    T = x.shape[0] if tokens is None else tokens
+    H = x.shape[-1] if hidden is None else hidden
+    st = lib().rmsq_fused_timed(_ptr(x), _ptr(residual), _ptr(weight), float(eps), int(mode),
+                                _ptr(scale_in), _ptr(out_q), _ptr(out_scales),
+                                _ptr(residual_out), int(T), int(H), int(group_size), int(flags),
+                                int(scale_ld), None if launch is None else C.byref(launch),
+                                start_event, stop_event, _stream(stream))
+    if check:
+        _check(st, "rmsq_fused_timed")
+    return st
 
 
 def rmsq_validate(x, residual, weight, eps, mode, scale_in, out_q, out_scales, residual_out,

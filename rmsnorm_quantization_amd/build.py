@@ -13,7 +13,9 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = [os.path.join(PKG, "csrc", "rmsq.hip")]
-DEPS = SRC + [os.path.join(PKG, "csrc", "rmsq_device.hpp"), os.path.join(ROOT, "include", "rmsq.h")]
+KERNEL_SOURCES = [os.path.join(PKG, "csrc", "rmsq_device.hpp"),
+                  os.path.join(PKG, "csrc", "rmsq_kernels.hpp")]
+DEPS = SRC + KERNEL_SOURCES + [os.path.join(ROOT, "include", "rmsq.h")]
 LIB = os.path.join(PKG, "librmsq.so")
 ARCH = "gfx950"
 

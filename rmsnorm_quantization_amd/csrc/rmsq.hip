@@ -1,258 +1,14 @@
-// rmsq.hip -- fused (residual add ->) RMSNorm -> FP8 / FP4 quantization for MI355X (gfx950),
-// and the C ABI declared in include/rmsq.h.
-//
-// Operation (vLLM docs "Fusion torch.compile passes", section "RMSNorm + quantization
-// (fuse_norm_quant)"; blog "[vLLM] Compilation Fusion Passes", "Pattern matching structure",
-// fused-op map, "Why this design"; PR #51925 summary, "Motivation"): per token row,
-// h = bf16(x + residual) (written back as the residual), y = h / sqrt(mean(h^2) + eps) * w,
-// then FP8 static / per-token / per-group or FP4 block-16 quantization of y.  The fusion's
-// point is that y never reaches memory: HBM sees x, residual and weight once and the codes,
-// scales and new residual once.
-//
-// Kernel shape (MI355X-first, not taken from any of the pages' kernels):
-//   * a row of H bf16 is split into 16-byte chunks of 8 elements; chunk c of a row lives on
-//     lane (c mod threads_per_row) of the row's waves, in registers, for the whole kernel, so
-//     every input byte is loaded exactly once (128-bit non-temporal loads);
-//   * sum of squares in binary64 (exact products of bf16 values), butterfly within the wave,
-//     LDS only across the waves of one row; inv_rms rounded once to f32;
-//   * per-group (64/128) and per-block (16) absmax: a group is 8 / 16 consecutive lanes (2 for
-//     an FP4 block), reduced with DPP row operations -- no LDS, no barrier;
-//   * hardware conversions: v_cvt_pk_bf16_f32, v_cvt_pk_fp8_f32 (OCP e4m3fn on gfx950),
-//     v_cvt_scalef32_pk_fp4_f32 (unit scale), v_cvt_f32_fp8;
-//   * no MFMA: there is no contraction here, the op is HBM-bandwidth bound.
-#include "rmsq_device.hpp"
+// rmsq.hip -- host side of librmsq: argument validation, launch-shape heuristics, kernel
+// dispatch and the C ABI declared in include/rmsq.h.  The kernels are in rmsq_kernels.hpp.
+#include <hip/hip_ext.h>
 
 #include <atomic>
 #include <cmath>
 #include <cstring>
 
-#include "rmsq.h"
+#include "rmsq_kernels.hpp"
 
 namespace rmsq {
-
-constexpr int kMaxWavesPerBlock = 16;
-
-struct KArgs {
-  const uint16_t* x;
-  const uint16_t* res;
-  const uint16_t* w;
-  uint16_t* res_out;
-  uint8_t* q;
-  void* scales;
-  const float* scale_in;
-  int64_t T;
-  int64_t H;
-  int64_t ld;
-  float eps;
-  uint32_t flags;
-  int32_t tpr;    // threads per row (multiple of 64)
-  int32_t rpb;    // rows per block
-  uint32_t nblk;  // workgroups in the grid
-};
-
-// One element of y = (h * inv) * w from the packed bf16 chunk dwords.
-__device__ __forceinline__ float y_of(const u32x4& h, const u32x4& w, int e, float inv) {
-  const uint32_t hd = h[e >> 1], wd = w[e >> 1];
-  const float hf = (e & 1) ? bf16_hi(hd) : bf16_lo(hd);
-  const float wf = (e & 1) ? bf16_hi(wd) : bf16_lo(wd);
-  return (hf * inv) * wf;
-}
-
-template <int MODE, bool RES, int VPT, int GS>
-__global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
-  __shared__ double s_ss[kMaxWavesPerBlock];
-  __shared__ float s_mx[kMaxWavesPerBlock];
-
-  const int tid = threadIdx.x;
-  const int tpr = a.tpr;
-  const int rib = tid / tpr;       // row within the block
-  const int lr = tid - rib * tpr;  // thread within the row
-  const int wpr = tpr >> 6;        // waves per row
-  const int64_t row = (int64_t)rowblock_of(blockIdx.x, a.nblk) * a.rpb + rib;
-  const bool row_ok = row < a.T;
-  const int64_t nch = a.H >> 3;
-  const size_t base = (size_t)(row_ok ? row : 0) * (size_t)a.H;  // element offset of the row
-
-  // ---- load: x (+ residual) and weight chunks, each byte once ----
-  u32x4 hv[VPT], wv[VPT], rv[VPT];
-  bool ok[VPT];
-#pragma unroll
-  for (int k = 0; k < VPT; ++k) {
-    const int64_t c = lr + (int64_t)k * tpr;
-    ok[k] = row_ok && c < nch;
-    hv[k] = (u32x4){0u, 0u, 0u, 0u};
-    wv[k] = (u32x4){0u, 0u, 0u, 0u};
-    rv[k] = (u32x4){0u, 0u, 0u, 0u};
-    if (ok[k]) {
-      hv[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.x + base) + c);
-      if (RES) rv[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.res + base) + c);
-      wv[k] = reinterpret_cast<const u32x4*>(a.w)[c];
-    }
-  }
-
-  // ---- residual add: h = bf16(x + r), written back as the new residual ----
-  if constexpr (RES) {
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      u32x4 h;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        h[j] = pack_bf16x2(bf16_lo(hv[k][j]) + bf16_lo(rv[k][j]),
-                           bf16_hi(hv[k][j]) + bf16_hi(rv[k][j]));
-      hv[k] = h;
-      if (ok[k]) {
-        const int64_t c = lr + (int64_t)k * tpr;
-        __builtin_nontemporal_store(h, reinterpret_cast<u32x4*>(a.res_out + base) + c);
-      }
-    }
-  }
-
-  // ---- sum of squares (binary64) -> inv_rms ----
-  double ss = 0.0;
-#pragma unroll
-  for (int k = 0; k < VPT; ++k) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const double lo = (double)bf16_lo(hv[k][j]);
-      const double hi = (double)bf16_hi(hv[k][j]);
-      ss = fma(lo, lo, ss);
-      ss = fma(hi, hi, ss);
-    }
-  }
-  ss = wave_sum(ss);
-  if (wpr > 1) {  // uniform over the block
-    if ((tid & 63) == 0) s_ss[tid >> 6] = ss;
-    __syncthreads();
-    ss = 0.0;
-    for (int i = 0; i < wpr; ++i) ss += s_ss[rib * wpr + i];
-  }
-  const float inv = (float)(1.0 / sqrt(ss / (double)a.H + (double)a.eps));
-
-  // ---- quantize ----
-  if constexpr (MODE == RMSQ_FP8_STATIC) {
-    const float r = 1.0f / a.scale_in[0];
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = y_of(hv[k], wv[k], e, inv) * r;
-      const u32x2 qc = {fp8x4(v[0], v[1], v[2], v[3]), fp8x4(v[4], v[5], v[6], v[7])};
-      if (ok[k]) {
-        const int64_t c = lr + (int64_t)k * tpr;
-        __builtin_nontemporal_store(qc, reinterpret_cast<u32x2*>(a.q + base) + c);
-      }
-    }
-  } else if constexpr (MODE == RMSQ_FP8_TOKEN) {
-    float mx = 0.0f;
-#pragma unroll
-    for (int k = 0; k < VPT; ++k)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(y_of(hv[k], wv[k], e, inv)));
-    mx = wave_max(mx);
-    if (wpr > 1) {
-      if ((tid & 63) == 0) s_mx[tid >> 6] = mx;
-      __syncthreads();
-      mx = 0.0f;
-      for (int i = 0; i < wpr; ++i) mx = fmaxf(mx, s_mx[rib * wpr + i]);
-    }
-    const float s = mx / kFp8Max;
-    if (lr == 0 && row_ok) static_cast<float*>(a.scales)[row] = s;
-    const bool zero = (s == 0.0f);
-    const float r = zero ? 0.0f : 1.0f / s;
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = y_of(hv[k], wv[k], e, inv) * r;
-      u32x2 qc = {fp8x4(v[0], v[1], v[2], v[3]), fp8x4(v[4], v[5], v[6], v[7])};
-      if (zero) qc = (u32x2){0u, 0u};
-      if (ok[k]) {
-        const int64_t c = lr + (int64_t)k * tpr;
-        __builtin_nontemporal_store(qc, reinterpret_cast<u32x2*>(a.q + base) + c);
-      }
-    }
-  } else if constexpr (MODE == RMSQ_FP8_GROUP) {
-    constexpr int L = GS / 8;  // lanes per group
-    const bool e8 = (a.flags & (RMSQ_SCALE_E8M0 | RMSQ_SCALE_E8M0_U8)) != 0;
-    const bool u8 = (a.flags & RMSQ_SCALE_E8M0_U8) != 0;
-    const bool col = (a.flags & RMSQ_SCALE_COLMAJOR) != 0;
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      const int64_t c = lr + (int64_t)k * tpr;
-      float y[8];
-      float m = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        y[e] = y_of(hv[k], wv[k], e, inv);
-        m = fmaxf(m, fabsf(y[e]));
-      }
-      m = group_max<L>(m);
-      float s = m / kFp8Max;
-      const bool zero = (s == 0.0f);
-      uint32_t byte = 0;
-      if (e8) byte = e8m0_ceil(s, &s);
-      const float r = 1.0f / s;
-      u32x2 qc = {fp8x4(y[0] * r, y[1] * r, y[2] * r, y[3] * r),
-                  fp8x4(y[4] * r, y[5] * r, y[6] * r, y[7] * r)};
-      if (zero) qc = (u32x2){0u, 0u};
-      if (ok[k]) {
-        __builtin_nontemporal_store(qc, reinterpret_cast<u32x2*>(a.q + base) + c);
-        if ((lr % L) == 0) {
-          const int64_t g = c / L;
-          const int64_t idx = col ? g * a.ld + row : row * (a.H / GS) + g;
-          if (u8) static_cast<uint8_t*>(a.scales)[idx] = (uint8_t)byte;
-          else static_cast<float*>(a.scales)[idx] = s;
-        }
-      }
-    }
-  } else {  // RMSQ_FP4_BLOCK16
-    const float gs = a.scale_in[0];
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      const int64_t c = lr + (int64_t)k * tpr;
-      float y[8];
-      float m = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        y[e] = y_of(hv[k], wv[k], e, inv);
-        m = fmaxf(m, fabsf(y[e]));
-      }
-      m = group_max<2>(m);  // a 16-element block is two neighbouring lanes
-      const uint32_t sf = fp8x1((m * gs) / 6.0f);
-      const float d = fp8_decode(sf);
-      uint32_t qc = 0u;
-      if (d > 0.0f) {
-        const float mul = gs / d;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] *= mul;
-        qc = fp4x8(y);
-      }
-      if (ok[k]) {
-        reinterpret_cast<uint32_t*>(a.q + base / 2)[c] = qc;
-        if ((c & 1) == 0) static_cast<uint8_t*>(a.scales)[base / 16 + c / 2] = (uint8_t)sf;
-      }
-    }
-  }
-}
-
-// The kernels' own converters over a flat f32 array, 8 elements per thread.
-__global__ void __launch_bounds__(256) convert_kernel(int fmt, const float* in, void* out,
-                                                      int64_t nchunks) {
-  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= nchunks) return;
-  float v[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = in[c * 8 + e];
-  if (fmt == RMSQ_CVT_E4M3) {
-    reinterpret_cast<u32x2*>(out)[c] =
-        (u32x2){fp8x4(v[0], v[1], v[2], v[3]), fp8x4(v[4], v[5], v[6], v[7])};
-  } else if (fmt == RMSQ_CVT_E2M1) {
-    reinterpret_cast<uint32_t*>(out)[c] = fp4x8(v);
-  } else {
-    reinterpret_cast<u32x4*>(out)[c] = (u32x4){pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                                               pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
-  }
-}
 
 // ------------------------------------------------------------------ kernel table
 template <int MODE, bool RES, int GS>
@@ -260,7 +16,11 @@ const void* pick_vpt(int vpt) {
   switch (vpt) {
     case 1: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 1, GS>);
     case 2: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 2, GS>);
+    case 3: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 3, GS>);
     case 4: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 4, GS>);
+    case 5: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 5, GS>);
+    case 6: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 6, GS>);
+    case 7: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 7, GS>);
     case 8: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 8, GS>);
     default: return nullptr;
   }
@@ -281,34 +41,36 @@ const void* pick_kernel(int mode, int gs, int vpt) {
 
 // ------------------------------------------------------------------ host side
 bool valid_launch(const rmsq_launch& l, int64_t H) {
-  if (l.reserved != 0) return false;
+  if ((l.options & ~RMSQ_LAUNCH_XCD_RANGES) != 0) return false;
   if (l.threads_per_row < 64 || l.threads_per_row > 1024 || (l.threads_per_row % 64) != 0)
     return false;
-  if (l.chunks_per_thread != 1 && l.chunks_per_thread != 2 && l.chunks_per_thread != 4 &&
-      l.chunks_per_thread != 8)
-    return false;
+  if (l.chunks_per_thread < 1 || l.chunks_per_thread > 8) return false;
   if (l.rows_per_block < 1 || (int64_t)l.rows_per_block * l.threads_per_row > 1024) return false;
   if ((int64_t)l.threads_per_row * l.chunks_per_thread * 8 < H) return false;
   return true;
 }
 
-// Default launch shape.  One wave per row while the row fits in 4 chunks per lane (H <= 2048);
-// beyond that two chunks per lane and as many waves as the row needs (H = 4096: 4 waves,
-// 8192: 8 waves), four chunks per lane past 16384.  Short rows are packed several to a
-// workgroup so a workgroup has at least 256 threads.
+// Default launch shape, from sweeps on MI355X: 256 threads per row with as many 16-byte chunks
+// per thread as the row needs (H = 4096: 2, 5120: 3, 7168 and 8192: 4); short rows (H <= 2048)
+// take 128 threads, rows of at most 1024 elements one wave each, four rows to a workgroup.
+// Rows longer than 256 x 8 chunks (H > 16384) widen to as many threads as 8 chunks per thread
+// need.  Workgroups take row blocks in launch order.
 rmsq_launch default_launch(int64_t H) {
-  rmsq_launch l{64, 1, 1, 0};
+  rmsq_launch l{256, 1, 1, 0};
   const int64_t nch = H / 8;
-  if (nch <= 256) {
+  if (nch <= 128) {
     l.threads_per_row = 64;
-    l.chunks_per_thread = nch <= 64 ? 1 : (nch <= 128 ? 2 : 4);
+    l.chunks_per_thread = (int32_t)((nch + 63) / 64);
+    l.rows_per_block = 4;
+  } else if (nch <= 256) {
+    l.threads_per_row = 128;
+    l.chunks_per_thread = 2;
+  } else if (nch <= 256 * 8) {
+    l.chunks_per_thread = (int32_t)((nch + 255) / 256);
   } else {
-    int vpt = nch <= 2048 ? 2 : (nch <= 4096 ? 4 : 8);
-    int64_t t = (nch + vpt - 1) / vpt;
-    l.threads_per_row = (int32_t)((t + 63) / 64 * 64);
-    l.chunks_per_thread = vpt;
+    l.chunks_per_thread = 8;
+    l.threads_per_row = (int32_t)(((nch + 7) / 8 + 63) / 64 * 64);
   }
-  l.rows_per_block = l.threads_per_row >= 256 ? 1 : 256 / l.threads_per_row;
   return l;
 }
 
@@ -432,7 +194,8 @@ int validate(const void* x, const void* res, const void* w, float eps, int mode,
 
 int fused_impl(const void* x, const void* res, const void* w, float eps, int mode,
                const float* scale_in, void* q, void* scales, void* res_out, int64_t T, int64_t H,
-               int gs, unsigned flags, int64_t ld, const rmsq_launch* launch, void* stream) {
+               int gs, unsigned flags, int64_t ld, const rmsq_launch* launch, void* stream,
+               void* start_event = nullptr, void* stop_event = nullptr) {
   int st = validate(x, res, w, eps, mode, scale_in, q, scales, res_out, T, H, gs, flags, ld);
   if (st != RMSQ_OK) return st;
   const rmsq_launch l = launch ? *launch : default_launch(H);
@@ -461,10 +224,16 @@ int fused_impl(const void* x, const void* res, const void* w, float eps, int mod
   a.tpr = l.threads_per_row;
   a.rpb = l.rows_per_block;
   a.nblk = (uint32_t)nblk;
+  a.xcd_ranges = (l.options & RMSQ_LAUNCH_XCD_RANGES) ? 1 : 0;
   void* args[] = {&a};
-  const hipError_t e =
-      hipLaunchKernel(fn, dim3((uint32_t)nblk), dim3((uint32_t)(l.threads_per_row * l.rows_per_block)),
-                      args, 0, static_cast<hipStream_t>(stream));
+  const dim3 grid((uint32_t)nblk), block((uint32_t)(l.threads_per_row * l.rows_per_block));
+  hipError_t e;
+  if (start_event || stop_event)
+    e = hipExtLaunchKernel(fn, grid, block, args, 0, static_cast<hipStream_t>(stream),
+                           static_cast<hipEvent_t>(start_event),
+                           static_cast<hipEvent_t>(stop_event), 0);
+  else
+    e = hipLaunchKernel(fn, grid, block, args, 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? RMSQ_OK : RMSQ_ELAUNCH;
 }
 
@@ -489,6 +258,16 @@ int rmsq_fused_with_launch(const void* x, const void* residual, const void* weig
                            void* stream) {
   return fused_impl(x, residual, weight, eps, mode, scale_in, out_q, out_scales, residual_out,
                     tokens, hidden, group_size, flags, scale_ld, launch, stream);
+}
+
+int rmsq_fused_timed(const void* x, const void* residual, const void* weight, float eps, int mode,
+                     const float* scale_in, void* out_q, void* out_scales, void* residual_out,
+                     int64_t tokens, int64_t hidden, int group_size, unsigned flags,
+                     int64_t scale_ld, const rmsq_launch* launch, void* start_event,
+                     void* stop_event, void* stream) {
+  return fused_impl(x, residual, weight, eps, mode, scale_in, out_q, out_scales, residual_out,
+                    tokens, hidden, group_size, flags, scale_ld, launch, stream, start_event,
+                    stop_event);
 }
 
 int rmsq_validate(const void* x, const void* residual, const void* weight, float eps, int mode,

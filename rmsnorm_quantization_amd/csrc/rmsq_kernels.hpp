@@ -1,0 +1,261 @@
+// rmsq_kernels.hpp -- the gfx950 kernels of librmsq: the fused (residual add ->) RMSNorm ->
+// FP8 / FP4 quantization kernel family and the converter diagnostic kernel.
+//
+// Operation (vLLM docs "Fusion torch.compile passes", section "RMSNorm + quantization
+// (fuse_norm_quant)"; blog "[vLLM] Compilation Fusion Passes", "Pattern matching structure",
+// fused-op map, "Why this design"; PR #51925 summary, "Motivation"): per token row,
+// h = bf16(x + residual) (written back as the residual), y = h / sqrt(mean(h^2) + eps) * w,
+// then FP8 static / per-token / per-group or FP4 block-16 quantization of y.  The fusion's
+// point is that y never reaches memory: HBM sees x, residual and weight once and the codes,
+// scales and new residual once.
+//
+// Kernel shape (MI355X-first, not taken from any of the pages' kernels):
+//   * a row of H bf16 is split into 16-byte chunks of 8 elements; chunk c of a row lives on
+//     thread (c mod threads_per_row) of the row's waves, in registers, for the whole kernel, so
+//     every input byte is loaded exactly once (128-bit non-temporal loads);
+//   * sum of squares in binary64 (exact products of bf16 values), DPP butterfly within the
+//     wave, LDS only across the waves of one row; inv_rms rounded once to f32;
+//   * per-group (64/128) and per-block (16) absmax: a group is 8 / 16 consecutive lanes (2 for
+//     an FP4 block), reduced with DPP row operations -- no LDS, no barrier;
+//   * hardware conversions: v_cvt_pk_bf16_f32, v_cvt_pk_fp8_f32 (OCP e4m3fn on gfx950),
+//     v_cvt_scalef32_pk_fp4_f32 (unit scale), v_cvt_f32_fp8;
+//   * no MFMA: there is no contraction here, the op is HBM-bandwidth bound.
+#pragma once
+
+#include "rmsq_device.hpp"
+#include "rmsq.h"
+
+namespace rmsq {
+
+constexpr int kMaxWavesPerBlock = 16;
+
+struct KArgs {
+  const uint16_t* x;
+  const uint16_t* res;
+  const uint16_t* w;
+  uint16_t* res_out;
+  uint8_t* q;
+  void* scales;
+  const float* scale_in;
+  int64_t T;
+  int64_t H;
+  int64_t ld;
+  float eps;
+  uint32_t flags;
+  int32_t tpr;    // threads per row (multiple of 64)
+  int32_t rpb;    // rows per block
+  uint32_t nblk;  // workgroups in the grid
+  int32_t xcd_ranges;  // XCD-contiguous row-block ranges instead of launch order
+};
+
+// One element of y = (h * inv) * w from the packed bf16 chunk dwords.
+__device__ __forceinline__ float y_of(const u32x4& h, const u32x4& w, int e, float inv) {
+  const uint32_t hd = h[e >> 1], wd = w[e >> 1];
+  const float hf = (e & 1) ? bf16_hi(hd) : bf16_lo(hd);
+  const float wf = (e & 1) ? bf16_hi(wd) : bf16_lo(wd);
+  return (hf * inv) * wf;
+}
+
+template <int MODE, bool RES, int VPT, int GS>
+__global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
+  __shared__ double s_ss[kMaxWavesPerBlock];
+  __shared__ float s_mx[kMaxWavesPerBlock];
+
+  const int tid = threadIdx.x;
+  const int tpr = a.tpr;
+  const int rib = tid / tpr;       // row within the block
+  const int lr = tid - rib * tpr;  // thread within the row
+  const int wpr = tpr >> 6;        // waves per row
+  const uint32_t rb = a.xcd_ranges ? rowblock_of(blockIdx.x, a.nblk) : blockIdx.x;
+  const int64_t row = (int64_t)rb * a.rpb + rib;
+  const bool row_ok = row < a.T;
+  const int64_t nch = a.H >> 3;
+  const size_t base = (size_t)(row_ok ? row : 0) * (size_t)a.H;  // element offset of the row
+
+  // The per-tensor scale is fetched first, with the row: fetched later it would cost every
+  // workgroup a second memory round trip after the reduction.
+  float scale_val = 0.0f;
+  if constexpr (MODE == RMSQ_FP8_STATIC || MODE == RMSQ_FP4_BLOCK16) scale_val = a.scale_in[0];
+
+  // ---- load: x (+ residual) and weight chunks, each byte once ----
+  u32x4 hv[VPT], wv[VPT], rv[VPT];
+  bool ok[VPT];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int64_t c = lr + (int64_t)k * tpr;
+    ok[k] = row_ok && c < nch;
+    hv[k] = (u32x4){0u, 0u, 0u, 0u};
+    wv[k] = (u32x4){0u, 0u, 0u, 0u};
+    rv[k] = (u32x4){0u, 0u, 0u, 0u};
+    if (ok[k]) {
+      hv[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.x + base) + c);
+      if (RES) rv[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.res + base) + c);
+      wv[k] = reinterpret_cast<const u32x4*>(a.w)[c];
+    }
+  }
+
+  // ---- residual add: h = bf16(x + r), written back as the new residual ----
+  if constexpr (RES) {
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      u32x4 h;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        h[j] = pack_bf16x2(bf16_lo(hv[k][j]) + bf16_lo(rv[k][j]),
+                           bf16_hi(hv[k][j]) + bf16_hi(rv[k][j]));
+      hv[k] = h;
+      if (ok[k]) {
+        const int64_t c = lr + (int64_t)k * tpr;
+        __builtin_nontemporal_store(h, reinterpret_cast<u32x4*>(a.res_out + base) + c);
+      }
+    }
+  }
+
+  // ---- sum of squares (binary64) -> inv_rms ----
+  double ss = 0.0;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const double lo = (double)bf16_lo(hv[k][j]);
+      const double hi = (double)bf16_hi(hv[k][j]);
+      ss = fma(lo, lo, ss);
+      ss = fma(hi, hi, ss);
+    }
+  }
+  ss = wave_sum(ss);
+  if (wpr > 1) {  // uniform over the block
+    if ((tid & 63) == 0) s_ss[tid >> 6] = ss;
+    __syncthreads();
+    ss = 0.0;
+    for (int i = 0; i < wpr; ++i) ss += s_ss[rib * wpr + i];
+  }
+  const float inv = (float)(1.0 / sqrt(ss / (double)a.H + (double)a.eps));
+
+  // ---- quantize ----
+  if constexpr (MODE == RMSQ_FP8_STATIC) {
+    const float r = 1.0f / scale_val;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = y_of(hv[k], wv[k], e, inv) * r;
+      const u32x2 qc = {fp8x4(v[0], v[1], v[2], v[3]), fp8x4(v[4], v[5], v[6], v[7])};
+      if (ok[k]) {
+        const int64_t c = lr + (int64_t)k * tpr;
+        __builtin_nontemporal_store(qc, reinterpret_cast<u32x2*>(a.q + base) + c);
+      }
+    }
+  } else if constexpr (MODE == RMSQ_FP8_TOKEN) {
+    float mx = 0.0f;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(y_of(hv[k], wv[k], e, inv)));
+    mx = wave_max(mx);
+    if (wpr > 1) {
+      if ((tid & 63) == 0) s_mx[tid >> 6] = mx;
+      __syncthreads();
+      mx = 0.0f;
+      for (int i = 0; i < wpr; ++i) mx = fmaxf(mx, s_mx[rib * wpr + i]);
+    }
+    const float s = mx / kFp8Max;
+    if (lr == 0 && row_ok) static_cast<float*>(a.scales)[row] = s;
+    const bool zero = (s == 0.0f);
+    const float r = zero ? 0.0f : 1.0f / s;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = y_of(hv[k], wv[k], e, inv) * r;
+      u32x2 qc = {fp8x4(v[0], v[1], v[2], v[3]), fp8x4(v[4], v[5], v[6], v[7])};
+      if (zero) qc = (u32x2){0u, 0u};
+      if (ok[k]) {
+        const int64_t c = lr + (int64_t)k * tpr;
+        __builtin_nontemporal_store(qc, reinterpret_cast<u32x2*>(a.q + base) + c);
+      }
+    }
+  } else if constexpr (MODE == RMSQ_FP8_GROUP) {
+    constexpr int L = GS / 8;  // lanes per group
+    const bool e8 = (a.flags & (RMSQ_SCALE_E8M0 | RMSQ_SCALE_E8M0_U8)) != 0;
+    const bool u8 = (a.flags & RMSQ_SCALE_E8M0_U8) != 0;
+    const bool col = (a.flags & RMSQ_SCALE_COLMAJOR) != 0;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int64_t c = lr + (int64_t)k * tpr;
+      float y[8];
+      float m = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        y[e] = y_of(hv[k], wv[k], e, inv);
+        m = fmaxf(m, fabsf(y[e]));
+      }
+      m = group_max<L>(m);
+      float s = m / kFp8Max;
+      const bool zero = (s == 0.0f);
+      uint32_t byte = 0;
+      if (e8) byte = e8m0_ceil(s, &s);
+      const float r = 1.0f / s;
+      u32x2 qc = {fp8x4(y[0] * r, y[1] * r, y[2] * r, y[3] * r),
+                  fp8x4(y[4] * r, y[5] * r, y[6] * r, y[7] * r)};
+      if (zero) qc = (u32x2){0u, 0u};
+      if (ok[k]) {
+        __builtin_nontemporal_store(qc, reinterpret_cast<u32x2*>(a.q + base) + c);
+        if ((lr % L) == 0) {
+          const int64_t g = c / L;
+          const int64_t idx = col ? g * a.ld + row : row * (a.H / GS) + g;
+          if (u8) static_cast<uint8_t*>(a.scales)[idx] = (uint8_t)byte;
+          else static_cast<float*>(a.scales)[idx] = s;
+        }
+      }
+    }
+  } else {  // RMSQ_FP4_BLOCK16
+    const float gs = scale_val;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int64_t c = lr + (int64_t)k * tpr;
+      float y[8];
+      float m = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        y[e] = y_of(hv[k], wv[k], e, inv);
+        m = fmaxf(m, fabsf(y[e]));
+      }
+      m = group_max<2>(m);  // a 16-element block is two neighbouring lanes
+      const uint32_t sf = fp8x1((m * gs) / 6.0f);
+      const float d = fp8_decode(sf);
+      uint32_t qc = 0u;
+      if (d > 0.0f) {
+        const float mul = gs / d;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] *= mul;
+        qc = fp4x8(y);
+      }
+      if (ok[k]) {
+        reinterpret_cast<uint32_t*>(a.q + base / 2)[c] = qc;
+        if ((c & 1) == 0) static_cast<uint8_t*>(a.scales)[base / 16 + c / 2] = (uint8_t)sf;
+      }
+    }
+  }
+}
+
+// The kernels' own converters over a flat f32 array, 8 elements per thread.
+__global__ void __launch_bounds__(256) convert_kernel(int fmt, const float* in, void* out,
+                                                      int64_t nchunks) {
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= nchunks) return;
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = in[c * 8 + e];
+  if (fmt == RMSQ_CVT_E4M3) {
+    reinterpret_cast<u32x2*>(out)[c] =
+        (u32x2){fp8x4(v[0], v[1], v[2], v[3]), fp8x4(v[4], v[5], v[6], v[7])};
+  } else if (fmt == RMSQ_CVT_E2M1) {
+    reinterpret_cast<uint32_t*>(out)[c] = fp4x8(v);
+  } else {
+    reinterpret_cast<u32x4*>(out)[c] = (u32x4){pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                               pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+  }
+}
+
+}  // namespace rmsq

@@ -32,7 +32,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("rmsq_fused", "rmsq_fused_with_launch", "rmsq_validate", "rmsq_query_launch",
+    for n in ("rmsq_fused", "rmsq_fused_with_launch", "rmsq_fused_timed", "rmsq_validate",
+              "rmsq_query_launch",
               "rmsq_block_to_rowblock", "rmsq_convert", "rmsq_status_string",
               "rmsq_abi_version"):
         assert n in names
@@ -124,9 +125,9 @@ def test_colmajor_scale_extent_is_checked(B):
 def test_query_launch(B):
     for h in (8, 64, 1024, 2048, 2880, 4096, 5120, 7168, 8192, 16384, 65536):
         l, grid = B.rmsq_query_launch(1, 1000, h)
-        tpr, vpt, rpb = l.as_tuple()
+        tpr, vpt, rpb, _ = l.as_tuple()
         assert tpr % 64 == 0 and 64 <= tpr <= 1024
-        assert vpt in (1, 2, 4, 8) and tpr * vpt * 8 >= h
+        assert 1 <= vpt <= 8 and tpr * vpt * 8 >= h
         assert rpb >= 1 and rpb * tpr <= 1024
         assert grid == -(-1000 // rpb)
     with pytest.raises(B.RmsqError):

@@ -96,16 +96,14 @@ def test_ragged_hidden_fp4(H):
 
 def _all_launches(H):
     for tpr in (64, 128, 192, 256, 320, 448, 512, 640, 1024):
-        for vpt in (1, 2, 4, 8):
+        for vpt in range(1, 9):
             if tpr * vpt * 8 < H:
                 continue
             for rpb in (1, 2, 4, 16):
                 if rpb * tpr > 1024:
                     continue
-                l = B.rmsq_launch()
-                l.threads_per_row, l.chunks_per_thread, l.rows_per_block, l.reserved = (
-                    tpr, vpt, rpb, 0)
-                yield l
+                for opt in (0, B.RMSQ_LAUNCH_XCD_RANGES):
+                    yield B.rmsq_launch(tpr, vpt, rpb, opt)
 
 
 @pytest.mark.parametrize("mode,G,scale", MODES)
@@ -127,7 +125,7 @@ def test_every_launch_shape_gives_identical_bytes(mode, G, scale):
 def test_invalid_launch_shape_is_rejected():
     x, r, w = _inputs(4, 1024, seed=1)
     l = B.rmsq_launch()
-    l.threads_per_row, l.chunks_per_thread, l.rows_per_block, l.reserved = 64, 1, 1, 0  # too few
+    l.threads_per_row, l.chunks_per_thread, l.rows_per_block, l.options = 64, 1, 1, 0  # too few
     q = torch.empty((4, 1024), dtype=torch.uint8, device="cuda")
     sc = torch.ones(1, device="cuda")
     st = B.rmsq_fused(GH.to_dev(x), None, GH.to_dev(w), 1e-6, B.RMSQ_FP8_STATIC, sc, q, None,
@@ -206,3 +204,28 @@ def test_errors_are_returned_not_launched():
                       check=False)
     assert st == B.RMSQ_EINVAL  # eps must be > 0
     torch.cuda.synchronize()
+
+
+def test_timed_launch_matches_and_stamps_events():
+    x, r, w = _inputs(32, 4096, seed=23)
+    xd, wd = GH.to_dev(x), GH.to_dev(w)
+    outs = []
+    for timed in (False, True):
+        rd = GH.to_dev(r).clone()
+        q = torch.empty((32, 4096), dtype=torch.uint8, device="cuda")
+        s = torch.empty((32,), dtype=torch.float32, device="cuda")
+        ro = torch.empty_like(rd)
+        if timed:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            e1.record()
+            B.rmsq_fused_timed(xd, rd, wd, 1e-6, B.RMSQ_FP8_TOKEN, None, q, s, ro,
+                               start_event=e0.cuda_event, stop_event=e1.cuda_event)
+            torch.cuda.synchronize()
+            assert e0.elapsed_time(e1) > 0
+        else:
+            B.rmsq_fused(xd, rd, wd, 1e-6, B.RMSQ_FP8_TOKEN, None, q, s, ro)
+            torch.cuda.synchronize()
+        outs.append((q.cpu(), s.cpu(), ro.cpu()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)

@@ -11,32 +11,37 @@
 namespace rmsq {
 
 // ------------------------------------------------------------------ kernel table
-template <int MODE, bool RES, int GS>
+template <int MODE, bool RES, int GS, bool EXACT>
 const void* pick_vpt(int vpt) {
   switch (vpt) {
-    case 1: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 1, GS>);
-    case 2: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 2, GS>);
-    case 3: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 3, GS>);
-    case 4: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 4, GS>);
-    case 5: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 5, GS>);
-    case 6: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 6, GS>);
-    case 7: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 7, GS>);
-    case 8: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 8, GS>);
+    case 1: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 1, GS, EXACT>);
+    case 2: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 2, GS, EXACT>);
+    case 3: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 3, GS, EXACT>);
+    case 4: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 4, GS, EXACT>);
+    case 5: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 5, GS, EXACT>);
+    case 6: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 6, GS, EXACT>);
+    case 7: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 7, GS, EXACT>);
+    case 8: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 8, GS, EXACT>);
     default: return nullptr;
   }
 }
 
-template <bool RES>
-const void* pick_kernel(int mode, int gs, int vpt) {
+template <bool RES, bool EXACT>
+const void* pick_mode(int mode, int gs, int vpt) {
   switch (mode) {
-    case RMSQ_FP8_STATIC: return pick_vpt<RMSQ_FP8_STATIC, RES, 0>(vpt);
-    case RMSQ_FP8_TOKEN: return pick_vpt<RMSQ_FP8_TOKEN, RES, 0>(vpt);
+    case RMSQ_FP8_STATIC: return pick_vpt<RMSQ_FP8_STATIC, RES, 0, EXACT>(vpt);
+    case RMSQ_FP8_TOKEN: return pick_vpt<RMSQ_FP8_TOKEN, RES, 0, EXACT>(vpt);
     case RMSQ_FP8_GROUP:
-      return gs == 64 ? pick_vpt<RMSQ_FP8_GROUP, RES, 64>(vpt)
-                      : pick_vpt<RMSQ_FP8_GROUP, RES, 128>(vpt);
-    case RMSQ_FP4_BLOCK16: return pick_vpt<RMSQ_FP4_BLOCK16, RES, 16>(vpt);
+      return gs == 64 ? pick_vpt<RMSQ_FP8_GROUP, RES, 64, EXACT>(vpt)
+                      : pick_vpt<RMSQ_FP8_GROUP, RES, 128, EXACT>(vpt);
+    case RMSQ_FP4_BLOCK16: return pick_vpt<RMSQ_FP4_BLOCK16, RES, 16, EXACT>(vpt);
     default: return nullptr;
   }
+}
+
+const void* pick_kernel(int mode, bool res, int gs, int vpt, bool exact) {
+  if (res) return exact ? pick_mode<true, true>(mode, gs, vpt) : pick_mode<true, false>(mode, gs, vpt);
+  return exact ? pick_mode<false, true>(mode, gs, vpt) : pick_mode<false, false>(mode, gs, vpt);
 }
 
 // ------------------------------------------------------------------ host side
@@ -204,8 +209,9 @@ int fused_impl(const void* x, const void* res, const void* w, float eps, int mod
   st = check_device();
   if (st != RMSQ_OK) return st;
 
-  const void* fn = res ? pick_kernel<true>(mode, gs, l.chunks_per_thread)
-                       : pick_kernel<false>(mode, gs, l.chunks_per_thread);
+  const bool exact = (int64_t)l.threads_per_row * l.chunks_per_thread * 8 == H &&
+                     (T % l.rows_per_block) == 0;
+  const void* fn = pick_kernel(mode, res != nullptr, gs, l.chunks_per_thread, exact);
   if (!fn) return RMSQ_EINVAL;
   const int64_t nblk = (T + l.rows_per_block - 1) / l.rows_per_block;
   KArgs a;

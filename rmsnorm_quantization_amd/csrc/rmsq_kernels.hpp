@@ -56,46 +56,60 @@ __device__ __forceinline__ float y_of(const u32x4& h, const u32x4& w, int e, flo
   return (hf * inv) * wf;
 }
 
-template <int MODE, bool RES, int VPT, int GS>
+// EXACT: the launch covers every chunk of every row with no remainder (threads_per_row x
+// chunks_per_thread x 8 == H and T a multiple of rows_per_block), so no load or store needs a
+// predicate; otherwise out-of-range chunks and rows are masked.
+template <int MODE, bool RES, int VPT, int GS, bool EXACT>
 __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
   __shared__ double s_ss[kMaxWavesPerBlock];
   __shared__ float s_mx[kMaxWavesPerBlock];
 
   const int tid = threadIdx.x;
   const int tpr = a.tpr;
-  const int rib = tid / tpr;       // row within the block
-  const int lr = tid - rib * tpr;  // thread within the row
-  const int wpr = tpr >> 6;        // waves per row
+  const int wpr = tpr >> 6;  // waves per row
+  // Row bookkeeping is wave-uniform (scalar registers): a row spans whole waves, so the wave
+  // index decides the row within the block, and row base addresses stay scalar.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rib = (a.rpb == 1) ? 0 : wave / wpr;  // row within the block
+  const uint32_t lr = (uint32_t)(tid - rib * tpr);  // thread within the row
   const uint32_t rb = a.xcd_ranges ? rowblock_of(blockIdx.x, a.nblk) : blockIdx.x;
   const int64_t row = (int64_t)rb * a.rpb + rib;
-  const bool row_ok = row < a.T;
-  const int64_t nch = a.H >> 3;
+  const bool row_ok = EXACT || row < a.T;
+  const int nch = (int)(a.H >> 3);
   const size_t base = (size_t)(row_ok ? row : 0) * (size_t)a.H;  // element offset of the row
+  const u32x4* xrow = reinterpret_cast<const u32x4*>(a.x + base);
+  const u32x4* rrow = reinterpret_cast<const u32x4*>(a.res + base);
+  const u32x4* wrow = reinterpret_cast<const u32x4*>(a.w);
 
   // The per-tensor scale is fetched first, with the row: fetched later it would cost every
   // workgroup a second memory round trip after the reduction.
   float scale_val = 0.0f;
   if constexpr (MODE == RMSQ_FP8_STATIC || MODE == RMSQ_FP4_BLOCK16) scale_val = a.scale_in[0];
 
-  // ---- load: x (+ residual) and weight chunks, each byte once ----
+  // ---- load: x (+ residual) first, then the weight (an L2 hit), each byte once ----
   u32x4 hv[VPT], wv[VPT], rv[VPT];
   bool ok[VPT];
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
-    const int64_t c = lr + (int64_t)k * tpr;
-    ok[k] = row_ok && c < nch;
+    const uint32_t c = lr + (uint32_t)(k * tpr);
+    ok[k] = EXACT || (row_ok && c < (uint32_t)nch);
     hv[k] = (u32x4){0u, 0u, 0u, 0u};
-    wv[k] = (u32x4){0u, 0u, 0u, 0u};
     rv[k] = (u32x4){0u, 0u, 0u, 0u};
     if (ok[k]) {
-      hv[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.x + base) + c);
-      if (RES) rv[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.res + base) + c);
-      wv[k] = reinterpret_cast<const u32x4*>(a.w)[c];
+      hv[k] = __builtin_nontemporal_load(xrow + c);
+      if (RES) rv[k] = __builtin_nontemporal_load(rrow + c);
     }
+  }
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const uint32_t c = lr + (uint32_t)(k * tpr);
+    wv[k] = (u32x4){0u, 0u, 0u, 0u};
+    if (ok[k]) wv[k] = wrow[c];
   }
 
   // ---- residual add: h = bf16(x + r), written back as the new residual ----
   if constexpr (RES) {
+    u32x4* orow = reinterpret_cast<u32x4*>(a.res_out + base);
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
       u32x4 h;
@@ -104,26 +118,23 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
         h[j] = pack_bf16x2(bf16_lo(hv[k][j]) + bf16_lo(rv[k][j]),
                            bf16_hi(hv[k][j]) + bf16_hi(rv[k][j]));
       hv[k] = h;
-      if (ok[k]) {
-        const int64_t c = lr + (int64_t)k * tpr;
-        __builtin_nontemporal_store(h, reinterpret_cast<u32x4*>(a.res_out + base) + c);
-      }
+      if (ok[k]) __builtin_nontemporal_store(h, orow + lr + (uint32_t)(k * tpr));
     }
   }
 
-  // ---- sum of squares (binary64) -> inv_rms ----
-  double ss = 0.0;
+  // ---- sum of squares (binary64; two chains, the products are exact) -> inv_rms ----
+  double ss0 = 0.0, ss1 = 0.0;
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const double lo = (double)bf16_lo(hv[k][j]);
       const double hi = (double)bf16_hi(hv[k][j]);
-      ss = fma(lo, lo, ss);
-      ss = fma(hi, hi, ss);
+      ss0 = fma(lo, lo, ss0);
+      ss1 = fma(hi, hi, ss1);
     }
   }
-  ss = wave_sum(ss);
+  double ss = wave_sum(ss0 + ss1);
   if (wpr > 1) {  // uniform over the block
     if ((tid & 63) == 0) s_ss[tid >> 6] = ss;
     __syncthreads();
@@ -142,7 +153,7 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
       for (int e = 0; e < 8; ++e) v[e] = y_of(hv[k], wv[k], e, inv) * r;
       const u32x2 qc = {fp8x4(v[0], v[1], v[2], v[3]), fp8x4(v[4], v[5], v[6], v[7])};
       if (ok[k]) {
-        const int64_t c = lr + (int64_t)k * tpr;
+        const uint32_t c = lr + (uint32_t)(k * tpr);
         __builtin_nontemporal_store(qc, reinterpret_cast<u32x2*>(a.q + base) + c);
       }
     }
@@ -171,7 +182,7 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
       u32x2 qc = {fp8x4(v[0], v[1], v[2], v[3]), fp8x4(v[4], v[5], v[6], v[7])};
       if (zero) qc = (u32x2){0u, 0u};
       if (ok[k]) {
-        const int64_t c = lr + (int64_t)k * tpr;
+        const uint32_t c = lr + (uint32_t)(k * tpr);
         __builtin_nontemporal_store(qc, reinterpret_cast<u32x2*>(a.q + base) + c);
       }
     }
@@ -182,7 +193,7 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
     const bool col = (a.flags & RMSQ_SCALE_COLMAJOR) != 0;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
-      const int64_t c = lr + (int64_t)k * tpr;
+      const uint32_t c = lr + (uint32_t)(k * tpr);
       float y[8];
       float m = 0.0f;
 #pragma unroll
@@ -213,7 +224,7 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
     const float gs = scale_val;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
-      const int64_t c = lr + (int64_t)k * tpr;
+      const uint32_t c = lr + (uint32_t)(k * tpr);
       float y[8];
       float m = 0.0f;
 #pragma unroll

@@ -48,6 +48,13 @@ def lib():
         L.orc_normalize.restype = None
         L.orc_quantize_row.argtypes = [p, i64, C.c_int, C.c_float, C.c_int, C.c_uint, p, p, p]
         L.orc_quantize_row.restype = C.c_int
+        L.orc_silu_mul.argtypes = [C.c_uint16, C.c_uint16]
+        L.orc_silu_mul.restype = C.c_float
+        L.orc_silu_mul_row.argtypes = [p, i64, p]
+        L.orc_silu_mul_row.restype = None
+        L.orc_silu_mul_quant.argtypes = [p, C.c_int, C.c_float, p, p, i64, i64, C.c_int,
+                                         C.c_uint, i64, p]
+        L.orc_silu_mul_quant.restype = C.c_int
         L.orc_fused.argtypes = [p, p, p, C.c_float, C.c_int, C.c_float, p, p, p,
                                 i64, i64, C.c_int, C.c_uint, i64, p]
         L.orc_fused.restype = C.c_int
@@ -215,3 +222,31 @@ def rms_y(x, residual, weight, eps):
         h = x[t] if residual is None else residual_add(x[t], residual[t])
         y[t] = normalize(h, w, inv_rms(h, eps))
     return y
+
+
+# ---------------------------------------------------------------- SiLU+Mul -> quant
+def silu_mul(x):
+    """[T, 2I] bf16 bits -> [T, I] f32 activation silu(gate) * up."""
+    x = _c(x, np.uint16)
+    T, I2 = x.shape
+    I = I2 // 2
+    a = np.empty((T, I), np.float32)
+    for t in range(T):
+        lib().orc_silu_mul_row(_ptr(x[t]), I, a[t].ctypes.data_as(C.c_void_p))
+    return a
+
+
+def silu_mul_quant(x, mode, scale_in=0.0, group_size=0, flags=0, scale_ld=0, want_pre=False):
+    """Run the oracle's SiLU+Mul -> quant on [T, 2I] bf16 bits."""
+    x = _c(x, np.uint16)
+    T, I2 = x.shape
+    I = I2 // 2
+    q = np.zeros((T, I // 2 if mode == FP4_BLOCK16 else I), np.uint8)
+    shp, dt = scale_shape(mode, T, I, group_size, flags, scale_ld)
+    scales = None if shp is None else np.zeros(shp, dt)
+    pre = np.zeros((T, I), np.float32) if want_pre else None
+    rc = lib().orc_silu_mul_quant(_ptr(x), int(mode), float(scale_in), _ptr(q), _ptr(scales), T,
+                                  I, int(group_size), int(flags), int(scale_ld), _ptr(pre))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (rc={rc})")
+    return {"q": q, "scales": scales, "pre": pre}

@@ -337,3 +337,64 @@ int orc_fused(const uint16_t* x, const uint16_t* residual, const uint16_t* weigh
   free(sc);
   return 0;
 }
+
+/* ------------------------------------------------------------------ SiLU+Mul -> quant */
+float orc_silu_mul(uint16_t g, uint16_t u) {
+  double gd = (double)orc_bf16_to_f32(g), ud = (double)orc_bf16_to_f32(u);
+  return (float)(gd * ud / (1.0 + exp(-gd)));
+}
+
+void orc_silu_mul_row(const uint16_t* x, int64_t I, float* a) {
+  for (int64_t i = 0; i < I; ++i) a[i] = orc_silu_mul(x[i], x[I + i]);
+}
+
+int orc_silu_mul_quant(const uint16_t* x, int mode, float scale_in, uint8_t* out_q,
+                       void* out_scales, int64_t T, int64_t I, int group_size, unsigned flags,
+                       int64_t scale_ld, float* pre_q) {
+  if (T < 0 || I <= 0 || !x || !out_q) return -1;
+  if (scale_ld == 0) scale_ld = T;
+  switch (mode) {
+    case ORC_FP8_STATIC:
+      break;
+    case ORC_FP8_TOKEN:
+      if (!out_scales) return -1;
+      break;
+    case ORC_FP8_GROUP:
+      if (!out_scales || (group_size != 64 && group_size != 128) || I % group_size) return -1;
+      if (scale_ld < T) return -1;
+      break;
+    case ORC_FP4_BLOCK16:
+      if (!out_scales || group_size != 16 || I % 16) return -1;
+      break;
+    default:
+      return -1;
+  }
+  float* a = (float*)malloc((size_t)I * sizeof(float));
+  float* sc = (float*)malloc((size_t)I * sizeof(float));
+  if (!a || !sc) {
+    free(a);
+    free(sc);
+    return -1;
+  }
+  for (int64_t t = 0; t < T; ++t) {
+    orc_silu_mul_row(x + t * 2 * I, I, a);
+    uint8_t* qrow = out_q + t * (mode == ORC_FP4_BLOCK16 ? I / 2 : I);
+    orc_quantize_row(a, I, mode, scale_in, group_size, flags, qrow, sc,
+                     pre_q ? pre_q + t * I : NULL);
+    if (mode == ORC_FP8_TOKEN) {
+      ((float*)out_scales)[t] = sc[0];
+    } else if (mode == ORC_FP8_GROUP) {
+      int64_t ng = I / group_size;
+      for (int64_t g = 0; g < ng; ++g) {
+        int64_t idx = (flags & ORC_SCALE_COLMAJOR) ? g * scale_ld + t : t * ng + g;
+        if (flags & ORC_SCALE_E8M0_U8) ((uint8_t*)out_scales)[idx] = ((uint8_t*)sc)[g];
+        else ((float*)out_scales)[idx] = sc[g];
+      }
+    } else if (mode == ORC_FP4_BLOCK16) {
+      memcpy((uint8_t*)out_scales + t * (I / 16), sc, (size_t)(I / 16));
+    }
+  }
+  free(a);
+  free(sc);
+  return 0;
+}

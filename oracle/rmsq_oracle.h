@@ -97,6 +97,20 @@ int orc_fused(const uint16_t* x, const uint16_t* residual, const uint16_t* weigh
               int64_t T, int64_t H, int group_size, unsigned flags, int64_t scale_ld,
               float* pre_q);
 
+/* ---- SiLU+Mul -> quantization (vLLM docs "Fusion torch.compile passes", section "SiLU+Mul +
+ * quantization (fuse_act_quant)": the gated up-projection activation silu_and_mul fused with the
+ * quantization that follows; FP8 static per-tensor, FP8 dynamic per-group 128/64, FP4). ----
+ * A row of x is [2I] bf16: the gate g = x[0:I], the up projection u = x[I:2I].
+ * a_i = silu(g_i) * u_i = g_i * u_i / (1 + exp(-g_i)), evaluated in binary64 and rounded once to
+ * f32; a is then quantized exactly like the normalized row of orc_fused. */
+float orc_silu_mul(uint16_t g, uint16_t u);
+void orc_silu_mul_row(const uint16_t* x, int64_t I, float* a);
+/* x [T, 2I] bf16; out_q FP8 [T, I] / FP4 [T, I/2]; out_scales laid out as in orc_fused with H = I.
+ * Returns 0, or -1 on an invalid argument. */
+int orc_silu_mul_quant(const uint16_t* x, int mode, float scale_in, uint8_t* out_q,
+                       void* out_scales, int64_t T, int64_t I, int group_size, unsigned flags,
+                       int64_t scale_ld, float* pre_q);
+
 #ifdef __cplusplus
 }
 #endif

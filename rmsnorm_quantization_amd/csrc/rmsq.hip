@@ -55,26 +55,30 @@ bool valid_launch(const rmsq_launch& l, int64_t H) {
   return true;
 }
 
-// Default launch shape, from sweeps on MI355X: 256 threads per row with as many 16-byte chunks
-// per thread as the row needs (H = 4096: 2, 5120: 3, 7168 and 8192: 4); short rows (H <= 2048)
-// take 128 threads, rows of at most 1024 elements one wave each, four rows to a workgroup.
-// Rows longer than 256 x 8 chunks (H > 16384) widen to as many threads as 8 chunks per thread
-// need.  Workgroups take row blocks in launch order.
+// Default launch shape, from sweeps on MI355X.  Rows of at most 128 chunks (H <= 1024) take one
+// wave each, four rows to a workgroup.  Longer rows take the chunks-per-thread count in 2..8
+// that leaves the fewest idle lanes with at most 1024 threads per row, fewer chunks per thread
+// on a tie: H = 2048 / 4096 / 5120 / 7168 / 8192 / 16384 give 128 / 256 / 320 / 448 / 512 /
+// 1024 threads x 2 chunks, all exact fits (no predicated loads).  Exact fits measured 2-3%
+// faster than 256 threads with idle lanes.
 rmsq_launch default_launch(int64_t H) {
-  rmsq_launch l{256, 1, 1, 0};
+  rmsq_launch l{64, 1, 1, 0};
   const int64_t nch = H / 8;
   if (nch <= 128) {
-    l.threads_per_row = 64;
     l.chunks_per_thread = (int32_t)((nch + 63) / 64);
     l.rows_per_block = 4;
-  } else if (nch <= 256) {
-    l.threads_per_row = 128;
-    l.chunks_per_thread = 2;
-  } else if (nch <= 256 * 8) {
-    l.chunks_per_thread = (int32_t)((nch + 255) / 256);
-  } else {
-    l.chunks_per_thread = 8;
-    l.threads_per_row = (int32_t)(((nch + 7) / 8 + 63) / 64 * 64);
+    return l;
+  }
+  int64_t best_waste = -1;
+  for (int vpt = 2; vpt <= 8; ++vpt) {
+    const int64_t tpr = ((nch + vpt - 1) / vpt + 63) / 64 * 64;
+    if (tpr > 1024) continue;
+    const int64_t waste = tpr * vpt - nch;
+    if (best_waste < 0 || waste < best_waste) {
+      best_waste = waste;
+      l.threads_per_row = (int32_t)tpr;
+      l.chunks_per_thread = vpt;
+    }
   }
   return l;
 }

@@ -16,7 +16,8 @@ data.  Prints ONE JSON line:
                  copy's counters) when the committed counters match the current kernel source
   cpu_baseline   the CPU oracle on a bounded sample of the same workload, one core
 
-Other workloads (--workload w0..w4) and forced launch shapes (--launch tpr,vpt,rpb) are for
+Other workloads (--workload w0..w5; w5 is SiLU+Mul -> quant with --quant
+static|token|group|fp4) and forced launch shapes (--launch tpr,vpt,rpb[,options]) are for
 exploration; only one GPU is supported (--gpus above 1 exits with a message).
 """
 import argparse
@@ -52,8 +53,12 @@ def workload_spec(args):
     wl = synth.WORKLOADS[int(args.workload[1:])]
     T = args.tokens or max(wl.tokens)
     H = args.hidden or (7168 if wl.index == 3 else wl.hidden[0])
-    mode = {0: B.RMSQ_FP8_STATIC, 1: B.RMSQ_FP8_STATIC, 2: B.RMSQ_FP8_TOKEN,
-            3: B.RMSQ_FP8_GROUP, 4: B.RMSQ_FP4_BLOCK16}[wl.index]
+    if wl.kind == "act":
+        mode = {"static": B.RMSQ_FP8_STATIC, "token": B.RMSQ_FP8_TOKEN,
+                "group": B.RMSQ_FP8_GROUP, "fp4": B.RMSQ_FP4_BLOCK16}[args.quant]
+    else:
+        mode = {0: B.RMSQ_FP8_STATIC, 1: B.RMSQ_FP8_STATIC, 2: B.RMSQ_FP8_TOKEN,
+                3: B.RMSQ_FP8_GROUP, 4: B.RMSQ_FP4_BLOCK16}[wl.index]
     G = {2: args.group, 3: 16}.get(mode, 0)
     flags = 0
     if mode == B.RMSQ_FP8_GROUP:
@@ -63,10 +68,13 @@ def workload_spec(args):
     return wl, T, H, mode, G, flags
 
 
-def algorithmic_bytes(mode, T, H, G, flags, residual):
+def algorithmic_bytes(mode, T, H, G, flags, residual, kind="norm"):
     """Bytes one launch must move: every input read once, every output written once, the
-    weight once per launch."""
-    rd = 2 * T * H + (2 * T * H if residual else 0) + 2 * H + (4 if mode in (0, 3) else 0)
+    weight once per launch.  For SiLU+Mul (kind "act") H is I and the input is [T, 2I] bf16."""
+    if kind == "act":
+        rd = 4 * T * H + (4 if mode in (0, 3) else 0)
+    else:
+        rd = 2 * T * H + (2 * T * H if residual else 0) + 2 * H + (4 if mode in (0, 3) else 0)
     wr = (2 * T * H if residual else 0) + (T * H // 2 if mode == 3 else T * H)
     if mode == 1:
         wr += 4 * T
@@ -98,9 +106,13 @@ def gpu_leg(args, wl, T, H, mode, G, flags):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    x, r, w = synth.make_inputs(wl.index, T, H)
+    act = wl.kind == "act"
+    if act:
+        x, r, w = synth.make_act_inputs(wl.index, T, H), None, torch.zeros(8, dtype=torch.bfloat16)
+    else:
+        x, r, w = synth.make_inputs(wl.index, T, H)
     residual = r is not None
-    rd, wr = algorithmic_bytes(mode, T, H, G, flags, residual)
+    rd, wr = algorithmic_bytes(mode, T, H, G, flags, residual, wl.kind)
     set_bytes = rd + wr
     nsets = max(2, math.ceil(FOOTPRINT_BYTES / set_bytes))
     xd, rdv, wd = x.to(dev), (r.to(dev) if residual else None), w.to(dev)
@@ -118,7 +130,17 @@ def gpu_leg(args, wl, T, H, mode, G, flags):
     # per-tensor input scale: the static scale from the workload's warm-up batch (max|y|/448,
     # computed on the GPU with the per-token mode), the FP4 global scale 448*6/max|y|
     scale_in = None
-    if mode == 0:
+    if act and mode in (0, 3):
+        # static scale: max|a|/448 of the warm-up batch; FP4 global scale 448*6/max|a| of the
+        # batch itself -- both from the GPU's per-token launch
+        src = synth.make_act_warmup(wl.index, H).to(dev) if mode == 0 else xd
+        q = torch.empty((src.shape[0], H), dtype=torch.uint8, device=dev)
+        st = torch.empty((src.shape[0],), dtype=torch.float32, device=dev)
+        B.rmsq_silu_mul_quant(src, B.RMSQ_FP8_TOKEN, None, q, st)
+        amax = float(st.max()) * 448.0
+        scale_in = torch.tensor([amax / 448.0 if mode == 0 else 448.0 * 6.0 / amax],
+                                dtype=torch.float32, device=dev)
+    elif mode == 0:
         if wl.static_scale is not None:
             sval = wl.static_scale
         else:
@@ -141,7 +163,14 @@ def gpu_leg(args, wl, T, H, mode, G, flags):
     if args.launch:
         vals = [int(v) for v in args.launch.split(",")]
         launch = B.rmsq_launch(*(vals + [0] * (4 - len(vals))))
-    shape = launch.as_tuple() if launch else B.rmsq_query_launch(mode, T, H, G, residual)[0].as_tuple()
+    if launch:
+        shape = launch.as_tuple()
+    elif act:
+        shape = B.rmsq_silu_mul_query_launch(mode, T, H, 16 if mode == 3 else G)[0].as_tuple()
+    else:
+        shape = B.rmsq_query_launch(mode, T, H, G, residual)[0].as_tuple()
+    if act and mode == 3:
+        G = 16
     stream = torch.cuda.current_stream()
 
     # argument tuples marshalled once, so the launch loop is one C call per step
@@ -149,15 +178,30 @@ def gpu_leg(args, wl, T, H, mode, G, flags):
 
     lib = B.lib()
     ptr = (lambda t: None if t is None else t.data_ptr())
-    argsets = [(ptr(s["x"]), ptr(s["r"]), wd.data_ptr(), float(wl.eps), mode, ptr(scale_in),
-                ptr(s["q"]), ptr(s["s"]), ptr(s["ro"]), T, H, G, flags, 0) for s in sets]
     sh = stream.cuda_stream
     lref = ctypes.byref(launch) if launch is not None else None
     status = []
+    if act:
+        argsets = [(ptr(s["x"]), mode, ptr(scale_in), ptr(s["q"]), ptr(s["s"]), T, H, G, flags, 0)
+                   for s in sets]
+
+        def launch_on(a, hs):
+            return lib.rmsq_silu_mul_quant_ex(*a, lref, None, None, hs)
+
+        def launch_timed(a, e0, e1, hs):
+            return lib.rmsq_silu_mul_quant_ex(*a, lref, e0, e1, hs)
+    else:
+        argsets = [(ptr(s["x"]), ptr(s["r"]), wd.data_ptr(), float(wl.eps), mode, ptr(scale_in),
+                    ptr(s["q"]), ptr(s["s"]), ptr(s["ro"]), T, H, G, flags, 0) for s in sets]
+
+        def launch_on(a, hs):
+            return lib.rmsq_fused_with_launch(*a, lref, hs) if lref else lib.rmsq_fused(*a, hs)
+
+        def launch_timed(a, e0, e1, hs):
+            return lib.rmsq_fused_timed(*a, lref, e0, e1, hs)
 
     def step(i):
-        a = argsets[i % nsets]
-        st = lib.rmsq_fused_with_launch(*a, lref, sh) if lref else lib.rmsq_fused(*a, sh)
+        st = launch_on(argsets[i % nsets], sh)
         if st:
             status.append(st)
 
@@ -183,8 +227,7 @@ def gpu_leg(args, wl, T, H, mode, G, flags):
         with torch.cuda.graph(g_, stream=torch.cuda.Stream()):
             hs = torch.cuda.current_stream().cuda_stream
             for i in range(args.steps):
-                a = argsets[i % nsets]
-                st = lib.rmsq_fused_with_launch(*a, lref, hs) if lref else lib.rmsq_fused(*a, hs)
+                st = launch_on(argsets[i % nsets], hs)
                 if st:
                     status.append(st)
         g_.replay()
@@ -205,8 +248,7 @@ def gpu_leg(args, wl, T, H, mode, G, flags):
         b_.record(stream)
     torch.cuda.synchronize()
     for i in range(args.steps):
-        a = argsets[i % nsets]
-        st = lib.rmsq_fused_timed(*a, lref, evs[i][0].cuda_event, evs[i][1].cuda_event, sh)
+        st = launch_timed(argsets[i % nsets], evs[i][0].cuda_event, evs[i][1].cuda_event, sh)
         if st:
             status.append(st)
     torch.cuda.synchronize()
@@ -246,6 +288,29 @@ def cpu_leg(wl, T, H, mode, G, flags, budget_s=12.0):
     import oracle as O
     from rmsnorm_quantization_amd import synth
 
+    if wl.kind == "act":
+        xb = synth.bits(synth.make_act_inputs(wl.index, T, H))
+        if mode == 0:
+            s_in = float(np.abs(O.silu_mul(synth.bits(synth.make_act_warmup(wl.index, H)))).max()
+                         / np.float32(448))
+        elif mode == 3:
+            s_in = float(np.float32(448 * 6) / np.abs(O.silu_mul(xb[:256])).max())
+        else:
+            s_in = 0.0
+        G4 = 16 if mode == 3 else G
+        rows = 0
+        t0 = time.perf_counter()
+        while rows < T and time.perf_counter() - t0 < budget_s:
+            n = min(64, T - rows)
+            O.silu_mul_quant(xb[rows:rows + n], mode, scale_in=s_in, group_size=G4,
+                             flags=flags & ~1)
+            rows += n
+        dt = time.perf_counter() - t0
+        rd, wr = algorithmic_bytes(mode, rows, H, G4, flags, False, "act")
+        return {"value": (rd + wr) / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"first {rows} of {T} rows ({rows * H} outputs), {dt:.1f} s, "
+                          f"single thread, {os.cpu_count()} host CPUs visible",
+                "tokens_per_s": rows / dt}
     x, r, w = synth.make_inputs(wl.index, T, H)
     xb, rb, wb = synth.bits(x), (synth.bits(r) if r is not None else None), synth.bits(w)
     if mode == 0:
@@ -309,8 +374,8 @@ def summarize(ktrace_db, fetch_db, write_db, key, title, commands, out_md):
 
     top = _db_rows(ktrace_db, "select name, total_calls, total_duration, average, percentage "
                               "from top_kernels")
-    fused = [r for r in top if "fused_kernel" in r[0]]
-    main_k = max(fused, key=lambda r: r[1])  # the benched instantiation (most calls)
+    mine = [r for r in top if "rmsq::" in r[0]]
+    main_k = max(mine, key=lambda r: r[1])  # the benched instantiation (most calls)
     durs = [r[0] for r in _db_rows(ktrace_db, "select duration from kernels where name = '%s'"
                                    % main_k[0].replace("'", "''"))]
 
@@ -370,7 +435,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="w1", choices=["w0", "w1", "w2", "w3", "w4"])
+    ap.add_argument("--workload", default="w1", choices=["w0", "w1", "w2", "w3", "w4", "w5"],
+                    help="w0-w4: (residual add ->) RMSNorm -> quant workloads; w5: SiLU+Mul -> "
+                         "quant (default w1: add+RMSNorm -> FP8 static, 4096 x 4096)")
+    ap.add_argument("--quant", default="static", choices=["static", "token", "group", "fp4"],
+                    help="quantization scheme of the SiLU+Mul workload (w5)")
     ap.add_argument("--tokens", type=int, default=0)
     ap.add_argument("--hidden", type=int, default=0)
     ap.add_argument("--group", type=int, default=128)
@@ -393,9 +462,10 @@ def main():
 
         wl, T, H, mode, G, flags = workload_spec(args)
         key = f"{args.workload}_T{T}_H{H}_{MODE_NAMES[mode]}_G{G}_f{flags}"
-        md = args.summary_md or os.path.join(ROOT, "profiles", f"fused_kernel_{key}.md")
-        title = (f"fused_kernel, {wl.name}: {T} tokens x hidden {H}, {MODE_NAMES[mode]}"
-                 f"{' G=%d' % G if mode == 2 else ''}")
+        family = "silu_mul_kernel" if wl.kind == "act" else "fused_kernel"
+        md = args.summary_md or os.path.join(ROOT, "profiles", f"{family}_{key}.md")
+        title = (f"{family}, {wl.name}: {T} tokens x {'intermediate' if wl.kind == 'act' else 'hidden'}"
+                 f" {H}, {MODE_NAMES[mode]}{' G=%d' % G if mode == 2 else ''}")
         e = summarize(*args.summarize, key, title, [c.strip() for c in args.commands.split(";;")
                                                      if c.strip()], md)
         print(json.dumps(e))
@@ -403,7 +473,8 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
-              f"supported (token rows shard with no exchange; see the design notes)",
+              f"supported: token rows shard across GPUs with no exchange, and one GPU's share "
+              f"is what this benchmark measures",
               file=sys.stderr)
         sys.exit(2)
 
@@ -430,8 +501,11 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": f"{wl.name}: {T} tokens x hidden {H}, "
-                        f"{'residual add, ' if wl.residual else ''}{MODE_NAMES[mode]}"
+            "workload": (f"{wl.name}: {T} tokens x intermediate {H} (input [T, 2I]), "
+                         if wl.kind == "act" else
+                         f"{wl.name}: {T} tokens x hidden {H}, "
+                         f"{'residual add, ' if wl.residual else ''}")
+                        + f"{MODE_NAMES[mode]}"
                         f"{f' G={G}' if mode == 2 else ''}{f' flags={flags}' if flags else ''}",
             "tokens": T, "hidden": H, "mode": MODE_NAMES[mode], "group_size": G,
             "flags": flags, "residual": wl.residual, "eps": wl.eps,

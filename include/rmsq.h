@@ -131,7 +131,12 @@ enum {
   /* By default workgroup b takes row block b, so the workgroups in flight touch one compact
    * window of each array (best for HBM page locality).  With this bit each of the 8 XCDs takes
    * a contiguous range of row blocks instead (rmsq_block_to_rowblock). */
-  RMSQ_LAUNCH_XCD_RANGES = 1
+  RMSQ_LAUNCH_XCD_RANGES = 1,
+  /* rmsq_silu_mul_quant only, and not with per-token scaling (which needs a whole row per
+   * workgroup): each row is cut into tiles of threads_per_row x chunks_per_thread chunks
+   * (chunks_per_thread 1, 2 or 4) and each workgroup takes one tile (rows_per_block must be 1).
+   * Results are identical to whole-row launches. */
+  RMSQ_LAUNCH_ROW_TILES = 2
 };
 typedef struct rmsq_launch {
   int32_t threads_per_row;
@@ -158,10 +163,50 @@ RMSQ_API int rmsq_fused_timed(const void* x, const void* residual, const void* w
                               unsigned flags, int64_t scale_ld, const rmsq_launch* launch,
                               void* start_event, void* stop_event, void* stream);
 
+/*
+ * rmsq_silu_mul_quant -- SiLU+Mul -> quantization in one launch (vLLM docs "Fusion
+ * torch.compile passes", section "SiLU+Mul + quantization (fuse_act_quant)": the gated
+ * up-projection activation fused with the quantization that follows, so the full-precision
+ * activation is never written).
+ *
+ *  x            [T, 2I] bf16, 16-byte aligned: row t is the gate g = x[t, 0:I] followed by the
+ *               up projection u = x[t, I:2I].  Read only.
+ *  a            = silu(g) * u = g / (1 + exp(-g)) * u, in f32 (within a few ulp of the exactly
+ *               rounded value: expf and the hardware reciprocal), never stored.
+ *  mode, scale_in, out_q, out_scales, group_size, flags, scale_ld
+ *               exactly as for rmsq_fused, with I in place of H (codes FP8 [T, I] or FP4
+ *               [T, I/2]; scales over the I values of a row).
+ *  tokens       T >= 0 (0 is a no-op); inter = I: 8 <= I <= RMSQ_MAX_HIDDEN, I % 8 == 0,
+ *               I % group_size == 0.
+ * Outputs must not overlap x, scale_in or each other.  Returns RMSQ_OK or a negative status.
+ */
+RMSQ_API int rmsq_silu_mul_quant(const void* x, int mode, const float* scale_in, void* out_q,
+                                 void* out_scales, int64_t tokens, int64_t inter, int group_size,
+                                 unsigned flags, int64_t scale_ld, void* stream);
+
+/* rmsq_silu_mul_quant with an explicit launch shape (NULL: the default, chosen from I as for
+ * rmsq_fused) and optional dispatch-stamped events (as rmsq_fused_timed; NULL: none). */
+RMSQ_API int rmsq_silu_mul_quant_ex(const void* x, int mode, const float* scale_in, void* out_q,
+                                    void* out_scales, int64_t tokens, int64_t inter,
+                                    int group_size, unsigned flags, int64_t scale_ld,
+                                    const rmsq_launch* launch, void* start_event,
+                                    void* stop_event, void* stream);
+
+/* Host-only argument check of rmsq_silu_mul_quant (no HIP call, no dereference). */
+RMSQ_API int rmsq_silu_mul_quant_validate(const void* x, int mode, const float* scale_in,
+                                          const void* out_q, const void* out_scales,
+                                          int64_t tokens, int64_t inter, int group_size,
+                                          unsigned flags, int64_t scale_ld);
+
 /* The launch shape rmsq_fused picks for (mode, T, H, group_size, residual?) and its grid size
  * (number of workgroups).  Host only; makes no HIP call.  Returns RMSQ_OK or RMSQ_EINVAL. */
 RMSQ_API int rmsq_query_launch(int mode, int64_t tokens, int64_t hidden, int group_size,
                       int has_residual, rmsq_launch* launch, int64_t* grid);
+
+/* The launch shape rmsq_silu_mul_quant picks for (mode, T, I, group_size) and its grid size.
+ * Host only; makes no HIP call.  Returns RMSQ_OK or RMSQ_EINVAL. */
+RMSQ_API int rmsq_silu_mul_query_launch(int mode, int64_t tokens, int64_t inter, int group_size,
+                                        rmsq_launch* launch, int64_t* grid);
 
 /* Which block of rows workgroup `block` of a `grid`-workgroup launch processes.  Workgroups are
  * dispatched round-robin over the MI355X's 8 accelerator dies (XCDs); this map hands each die

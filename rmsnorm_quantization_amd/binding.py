@@ -5,7 +5,8 @@ kernels of librmsq.so.  The library is loaded from this package directory; if it
 the binding raises -- there is no fallback path.
 
 Function names match the C ABI (rmsq_fused, rmsq_fused_with_launch, rmsq_fused_timed,
-rmsq_validate,
+rmsq_silu_mul_quant, rmsq_silu_mul_quant_ex, rmsq_silu_mul_quant_validate,
+rmsq_silu_mul_query_launch, rmsq_validate,
 rmsq_query_launch, rmsq_block_to_rowblock, rmsq_convert, rmsq_status_string,
 rmsq_abi_version).  A few allocating helpers named after the fused ops of the vLLM fusion
 pages (rms_norm_static_fp8_quant, fused_add_rms_norm_static_fp8_quant,
@@ -27,6 +28,7 @@ RMSQ_FP8_STATIC, RMSQ_FP8_TOKEN, RMSQ_FP8_GROUP, RMSQ_FP4_BLOCK16 = 0, 1, 2, 3
 RMSQ_SCALE_COLMAJOR, RMSQ_SCALE_E8M0, RMSQ_SCALE_E8M0_U8 = 1, 2, 4
 RMSQ_CVT_E4M3, RMSQ_CVT_E2M1, RMSQ_CVT_BF16 = 0, 1, 2
 RMSQ_LAUNCH_XCD_RANGES = 1
+RMSQ_LAUNCH_ROW_TILES = 2
 RMSQ_MAX_HIDDEN = 65536
 
 
@@ -66,9 +68,19 @@ def lib():
         L.rmsq_fused_timed.restype = i32
         L.rmsq_validate.argtypes = fused_args
         L.rmsq_validate.restype = i32
+        act_args = [p, i32, p, p, p, i64, i64, i32, u32, i64]
+        L.rmsq_silu_mul_quant.argtypes = act_args + [p]
+        L.rmsq_silu_mul_quant.restype = i32
+        L.rmsq_silu_mul_quant_ex.argtypes = act_args + [C.POINTER(rmsq_launch), p, p, p]
+        L.rmsq_silu_mul_quant_ex.restype = i32
+        L.rmsq_silu_mul_quant_validate.argtypes = act_args
+        L.rmsq_silu_mul_quant_validate.restype = i32
         L.rmsq_query_launch.argtypes = [i32, i64, i64, i32, i32, C.POINTER(rmsq_launch),
                                         C.POINTER(i64)]
         L.rmsq_query_launch.restype = i32
+        L.rmsq_silu_mul_query_launch.argtypes = [i32, i64, i64, i32, C.POINTER(rmsq_launch),
+                                                 C.POINTER(i64)]
+        L.rmsq_silu_mul_query_launch.restype = i32
         L.rmsq_block_to_rowblock.argtypes = [i64, i64]
         L.rmsq_block_to_rowblock.restype = i64
         L.rmsq_convert.argtypes = [i32, p, p, i64, p]
@@ -159,6 +171,33 @@ def rmsq_fused_timed(x, residual, weight, eps, mode, scale_in, out_q, out_scales
     return st
 
 
+def rmsq_silu_mul_quant(x, mode, scale_in, out_q, out_scales, tokens=None, inter=None,
+                        group_size=0, flags=0, scale_ld=0, stream=None, launch=None,
+                        start_event=None, stop_event=None, check=True) -> int:
+    """SiLU+Mul -> quant of x [T, 2I] (gate first).  With a launch shape or events it goes
+    through rmsq_silu_mul_quant_ex."""
+    T = x.shape[0] if tokens is None else tokens
+    I = x.shape[-1] // 2 if inter is None else inter
+    args = (_ptr(x), int(mode), _ptr(scale_in), _ptr(out_q), _ptr(out_scales), int(T), int(I),
+            int(group_size), int(flags), int(scale_ld))
+    if launch is None and start_event is None and stop_event is None:
+        st = lib().rmsq_silu_mul_quant(*args, _stream(stream))
+    else:
+        st = lib().rmsq_silu_mul_quant_ex(*args, None if launch is None else C.byref(launch),
+                                          start_event, stop_event, _stream(stream))
+    if check:
+        _check(st, "rmsq_silu_mul_quant")
+    return st
+
+
+def rmsq_silu_mul_quant_validate(x, mode, scale_in, out_q, out_scales, tokens, inter,
+                                 group_size=0, flags=0, scale_ld=0) -> int:
+    """Host-only argument check; pointers are plain integers (or None)."""
+    return lib().rmsq_silu_mul_quant_validate(x, int(mode), scale_in, out_q, out_scales,
+                                              int(tokens), int(inter), int(group_size),
+                                              int(flags), int(scale_ld))
+
+
 def rmsq_validate(x, residual, weight, eps, mode, scale_in, out_q, out_scales, residual_out,
                   tokens, hidden, group_size=0, flags=0, scale_ld=0) -> int:
     """Host-only argument check; pointers are plain integers (or None) and never dereferenced."""
@@ -173,6 +212,15 @@ def rmsq_query_launch(mode, tokens, hidden, group_size=0, has_residual=True):
     _check(lib().rmsq_query_launch(int(mode), int(tokens), int(hidden), int(group_size),
                                    int(bool(has_residual)), C.byref(l), C.byref(grid)),
            "rmsq_query_launch")
+    return l, grid.value
+
+
+def rmsq_silu_mul_query_launch(mode, tokens, inter, group_size=0):
+    l = rmsq_launch()
+    grid = C.c_int64(0)
+    _check(lib().rmsq_silu_mul_query_launch(int(mode), int(tokens), int(inter), int(group_size),
+                                            C.byref(l), C.byref(grid)),
+           "rmsq_silu_mul_query_launch")
     return l, grid.value
 
 
@@ -248,3 +296,32 @@ def fused_add_rms_norm_fp4_quant(x, residual, weight, global_scale, eps, inplace
     rmsq_fused(x, residual, weight, eps, RMSQ_FP4_BLOCK16, _scalar(global_scale, x.device), q,
                sf, rout, group_size=16)
     return q, sf, rout
+
+
+def silu_and_mul_quant(x, mode, scale=None, group_size=0, col_major=False, e8m0=False,
+                       e8m0_bytes=False, scale_ld=0):
+    """(codes, scales or None) for SiLU+Mul -> quant of x [T, 2I]: FP8 codes as
+    float8_e4m3fn [T, I], FP4 as packed uint8 [T, I/2]; scale is the static per-tensor scale
+    (FP8 static) or the global encode scale (FP4)."""
+    T, I = x.shape[0], x.shape[-1] // 2
+    flags = (RMSQ_SCALE_COLMAJOR if col_major else 0) | (RMSQ_SCALE_E8M0 if e8m0 else 0) | (
+        RMSQ_SCALE_E8M0_U8 if e8m0_bytes else 0)
+    if mode == RMSQ_FP4_BLOCK16:
+        q = torch.empty((T, I // 2), dtype=torch.uint8, device=x.device)
+        s = torch.empty((T, I // 16), dtype=torch.uint8, device=x.device)
+        group_size = 16
+    else:
+        q = torch.empty((T, I), dtype=torch.float8_e4m3fn, device=x.device)
+        if mode == RMSQ_FP8_STATIC:
+            s = None
+        elif mode == RMSQ_FP8_TOKEN:
+            s = torch.empty((T,), dtype=torch.float32, device=x.device)
+        else:
+            ng, ld = I // group_size, scale_ld or T
+            s = torch.empty((ng, ld) if col_major else (T, ng),
+                            dtype=torch.uint8 if e8m0_bytes else torch.float32, device=x.device)
+    sc = _scalar(scale, x.device) if mode in (RMSQ_FP8_STATIC, RMSQ_FP4_BLOCK16) else None
+    rmsq_silu_mul_quant(x, mode, sc, q.view(torch.uint8) if q.dtype != torch.uint8 else q, s,
+                        group_size=group_size, flags=flags,
+                        scale_ld=scale_ld if col_major else 0)
+    return q, s

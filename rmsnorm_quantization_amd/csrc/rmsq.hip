@@ -108,12 +108,11 @@ int check_device() {
   return st == 1 ? RMSQ_OK : RMSQ_EUNSUPPORTED;
 }
 
-// Validation of the scalar arguments (no pointer is touched).
-int check_scalars(int64_t T, int64_t H, float eps, int mode, int gs, unsigned flags,
-                  int64_t ld) {
-  if (T < 0 || H < 8 || H > RMSQ_MAX_HIDDEN || (H % 8) != 0) return RMSQ_EINVAL;
-  if (!(eps > 0.0f) || !std::isfinite(eps)) return RMSQ_EINVAL;
-  if (T > 0x7FFFFFFFLL) return RMSQ_EINVAL;
+// ---- validation shared by both ops: the quantization outputs ----------------------------
+// Scalar arguments of a quantization of T rows of n values (no pointer is touched).
+int check_quant_scalars(int64_t T, int64_t n, int mode, int gs, unsigned flags, int64_t ld) {
+  if (T < 0 || T > 0x7FFFFFFFLL) return RMSQ_EINVAL;
+  if (n < 8 || n > RMSQ_MAX_HIDDEN || (n % 8) != 0) return RMSQ_EINVAL;
   switch (mode) {
     case RMSQ_FP8_STATIC:
     case RMSQ_FP8_TOKEN:
@@ -123,7 +122,7 @@ int check_scalars(int64_t T, int64_t H, float eps, int mode, int gs, unsigned fl
       break;
     case RMSQ_FP8_GROUP: {
       if (gs != 64 && gs != 128) return RMSQ_EINVAL;
-      if ((H % gs) != 0) return RMSQ_EINVAL;
+      if ((n % gs) != 0) return RMSQ_EINVAL;
       const unsigned known = RMSQ_SCALE_COLMAJOR | RMSQ_SCALE_E8M0 | RMSQ_SCALE_E8M0_U8;
       if ((flags & ~known) != 0) return RMSQ_EUNSUPPORTED;
       if ((flags & RMSQ_SCALE_E8M0) && (flags & RMSQ_SCALE_E8M0_U8)) return RMSQ_EUNSUPPORTED;
@@ -135,7 +134,7 @@ int check_scalars(int64_t T, int64_t H, float eps, int mode, int gs, unsigned fl
       break;
     }
     case RMSQ_FP4_BLOCK16:
-      if (gs != 16 || (H % 16) != 0) return RMSQ_EINVAL;
+      if (gs != 16 || (n % 16) != 0) return RMSQ_EINVAL;
       if (flags != 0) return RMSQ_EUNSUPPORTED;
       if (ld != 0) return RMSQ_EINVAL;
       break;
@@ -145,60 +144,96 @@ int check_scalars(int64_t T, int64_t H, float eps, int mode, int gs, unsigned fl
   return RMSQ_OK;
 }
 
-int check_pointers(const void* x, const void* res, const void* w, int mode, const float* scale_in,
-                   const void* q, const void* scales, const void* res_out, int64_t T, int64_t H,
-                   int gs, unsigned flags, int64_t ld) {
-  if (!x || !w || !q) return RMSQ_EINVAL;
-  if ((res == nullptr) != (res_out == nullptr)) return RMSQ_EINVAL;
+// Presence, alignment and byte extents of the quantization outputs (and the per-tensor scale
+// input); outputs[0..*nout) receives the output extents, in_scale the scale_in extent.
+int check_quant_outputs(int mode, const float* scale_in, const void* q, const void* scales,
+                        int64_t T, int64_t n, int gs, unsigned flags, int64_t ld, Span* outputs,
+                        int* nout, Span* in_scale) {
+  if (!q) return RMSQ_EINVAL;
   const bool needs_scale_in = (mode == RMSQ_FP8_STATIC || mode == RMSQ_FP4_BLOCK16);
   if (needs_scale_in != (scale_in != nullptr)) return RMSQ_EINVAL;
   const bool has_scales = (mode != RMSQ_FP8_STATIC);
   if (has_scales != (scales != nullptr)) return RMSQ_EINVAL;
-
-  // alignment
-  if (!aligned(x, 16) || !aligned(w, 16)) return RMSQ_EALIGN;
-  if (res && (!aligned(res, 16) || !aligned(res_out, 16))) return RMSQ_EALIGN;
   if (!aligned(q, mode == RMSQ_FP4_BLOCK16 ? 4 : 8)) return RMSQ_EALIGN;
   if (scale_in && !aligned(scale_in, 4)) return RMSQ_EALIGN;
   const bool f32_scales = (mode == RMSQ_FP8_TOKEN) ||
                           (mode == RMSQ_FP8_GROUP && !(flags & RMSQ_SCALE_E8M0_U8));
   if (f32_scales && !aligned(scales, 4)) return RMSQ_EALIGN;
-
-  // aliasing: outputs must not overlap inputs or each other; residual_out may be residual
-  const size_t act = (size_t)T * (size_t)H * 2;
-  const size_t qbytes = mode == RMSQ_FP4_BLOCK16 ? (size_t)T * (size_t)H / 2 : (size_t)T * H;
+  const size_t qbytes = mode == RMSQ_FP4_BLOCK16 ? (size_t)T * (size_t)n / 2 : (size_t)T * n;
   size_t sbytes = 0;
   if (mode == RMSQ_FP8_TOKEN) sbytes = (size_t)T * 4;
   if (mode == RMSQ_FP8_GROUP) {
-    const size_t ng = (size_t)(H / gs), el = (flags & RMSQ_SCALE_E8M0_U8) ? 1 : 4;
+    const size_t ng = (size_t)(n / gs), el = (flags & RMSQ_SCALE_E8M0_U8) ? 1 : 4;
     sbytes = (flags & RMSQ_SCALE_COLMAJOR) ? ((ng - 1) * (size_t)(ld ? ld : T) + (size_t)T) * el
                                            : (size_t)T * ng * el;
   }
-  if (mode == RMSQ_FP4_BLOCK16) sbytes = (size_t)T * (size_t)(H / 16);
-  const Span sx = span(x, act), sw = span(w, (size_t)H * 2), sq = span(q, qbytes);
-  const Span ss = span(scales, sbytes), si = span(scale_in, scale_in ? 4 : 0);
-  Span outs[3] = {sq, ss, Span{0, 0}};
-  int nout = scales ? 2 : 1;
-  if (res_out) outs[nout++] = span(res_out, act);
+  if (mode == RMSQ_FP4_BLOCK16) sbytes = (size_t)T * (size_t)(n / 16);
+  outputs[0] = span(q, qbytes);
+  *nout = 1;
+  if (scales) outputs[(*nout)++] = span(scales, sbytes);
+  *in_scale = span(scale_in, scale_in ? 4 : 0);
+  return RMSQ_OK;
+}
+
+// Outputs must not overlap one another or any input span.
+int check_aliasing(const Span* outs, int nout, const Span* ins, int nin) {
   for (int i = 0; i < nout; ++i) {
-    if (overlap(outs[i], sx) || overlap(outs[i], sw) || overlap(outs[i], si)) return RMSQ_EALIAS;
+    for (int j = 0; j < nin; ++j)
+      if (overlap(outs[i], ins[j])) return RMSQ_EALIAS;
     for (int j = i + 1; j < nout; ++j)
       if (overlap(outs[i], outs[j])) return RMSQ_EALIAS;
-  }
-  if (res) {
-    const Span sr = span(res, act);
-    if (overlap(sq, sr) || (scales && overlap(ss, sr))) return RMSQ_EALIAS;
-    if (res_out != res && overlap(span(res_out, act), sr)) return RMSQ_EALIAS;
   }
   return RMSQ_OK;
 }
 
+int launch_kernel(const void* fn, int64_t nblk, int threads, void* argstruct, void* stream,
+                  void* start_event, void* stop_event) {
+  void* args[] = {argstruct};
+  const dim3 grid((uint32_t)nblk), block((uint32_t)threads);
+  hipError_t e;
+  if (start_event || stop_event)
+    e = hipExtLaunchKernel(fn, grid, block, args, 0, static_cast<hipStream_t>(stream),
+                           static_cast<hipEvent_t>(start_event),
+                           static_cast<hipEvent_t>(stop_event), 0);
+  else
+    e = hipLaunchKernel(fn, grid, block, args, 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RMSQ_OK : RMSQ_ELAUNCH;
+}
+
+bool exact_fit(const rmsq_launch& l, int64_t T, int64_t n) {
+  return (int64_t)l.threads_per_row * l.chunks_per_thread * 8 == n && (T % l.rows_per_block) == 0;
+}
+
+// ---- fused (residual add ->) RMSNorm -> quantization ---------------------------------------
 int validate(const void* x, const void* res, const void* w, float eps, int mode,
              const float* scale_in, const void* q, const void* scales, const void* res_out,
              int64_t T, int64_t H, int gs, unsigned flags, int64_t ld) {
-  const int st = check_scalars(T, H, eps, mode, gs, flags, ld);
-  if (st != RMSQ_OK || T == 0) return st;
-  return check_pointers(x, res, w, mode, scale_in, q, scales, res_out, T, H, gs, flags, ld);
+  int st = check_quant_scalars(T, H, mode, gs, flags, ld);
+  if (st != RMSQ_OK) return st;
+  if (!(eps > 0.0f) || !std::isfinite(eps)) return RMSQ_EINVAL;
+  if (T == 0) return RMSQ_OK;
+  if (!x || !w) return RMSQ_EINVAL;
+  if ((res == nullptr) != (res_out == nullptr)) return RMSQ_EINVAL;
+  Span outs[3], sin;
+  int nout = 0;
+  st = check_quant_outputs(mode, scale_in, q, scales, T, H, gs, flags, ld, outs, &nout, &sin);
+  if (st != RMSQ_OK) return st;
+  if (!aligned(x, 16) || !aligned(w, 16)) return RMSQ_EALIGN;
+  if (res && (!aligned(res, 16) || !aligned(res_out, 16))) return RMSQ_EALIGN;
+  const size_t act = (size_t)T * (size_t)H * 2;
+  const Span ins[3] = {span(x, act), span(w, (size_t)H * 2), sin};
+  // residual_out may be the residual itself (in-place update) but must not otherwise overlap
+  // it; it is an output like the others with respect to x, weight and scale_in
+  if (res_out) outs[nout++] = span(res_out, act);
+  st = check_aliasing(outs, nout, ins, 3);
+  if (st != RMSQ_OK) return st;
+  if (res) {
+    const Span sr = span(res, act);
+    for (int i = 0; i < nout - 1; ++i)
+      if (overlap(outs[i], sr)) return RMSQ_EALIAS;
+    if (res_out != res && overlap(span(res_out, act), sr)) return RMSQ_EALIAS;
+  }
+  return RMSQ_OK;
 }
 
 int fused_impl(const void* x, const void* res, const void* w, float eps, int mode,
@@ -212,10 +247,7 @@ int fused_impl(const void* x, const void* res, const void* w, float eps, int mod
   if (T == 0) return RMSQ_OK;
   st = check_device();
   if (st != RMSQ_OK) return st;
-
-  const bool exact = (int64_t)l.threads_per_row * l.chunks_per_thread * 8 == H &&
-                     (T % l.rows_per_block) == 0;
-  const void* fn = pick_kernel(mode, res != nullptr, gs, l.chunks_per_thread, exact);
+  const void* fn = pick_kernel(mode, res != nullptr, gs, l.chunks_per_thread, exact_fit(l, T, H));
   if (!fn) return RMSQ_EINVAL;
   const int64_t nblk = (T + l.rows_per_block - 1) / l.rows_per_block;
   KArgs a;
@@ -235,16 +267,134 @@ int fused_impl(const void* x, const void* res, const void* w, float eps, int mod
   a.rpb = l.rows_per_block;
   a.nblk = (uint32_t)nblk;
   a.xcd_ranges = (l.options & RMSQ_LAUNCH_XCD_RANGES) ? 1 : 0;
-  void* args[] = {&a};
-  const dim3 grid((uint32_t)nblk), block((uint32_t)(l.threads_per_row * l.rows_per_block));
-  hipError_t e;
-  if (start_event || stop_event)
-    e = hipExtLaunchKernel(fn, grid, block, args, 0, static_cast<hipStream_t>(stream),
-                           static_cast<hipEvent_t>(start_event),
-                           static_cast<hipEvent_t>(stop_event), 0);
-  else
-    e = hipLaunchKernel(fn, grid, block, args, 0, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? RMSQ_OK : RMSQ_ELAUNCH;
+  return launch_kernel(fn, nblk, l.threads_per_row * l.rows_per_block, &a, stream, start_event,
+                       stop_event);
+}
+
+// ---- SiLU+Mul -> quantization --------------------------------------------------------------
+template <int MODE, int GS, bool EXACT>
+const void* pick_act_vpt(int vpt) {
+  switch (vpt) {
+    case 1: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 1, GS, EXACT>);
+    case 2: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 2, GS, EXACT>);
+    case 3: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 3, GS, EXACT>);
+    case 4: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 4, GS, EXACT>);
+    case 5: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 5, GS, EXACT>);
+    case 6: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 6, GS, EXACT>);
+    case 7: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 7, GS, EXACT>);
+    case 8: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 8, GS, EXACT>);
+    default: return nullptr;
+  }
+}
+
+template <int MODE, int GS, bool EXACT>
+const void* pick_tile_vpt(int vpt) {
+  switch (vpt) {
+    case 1: return reinterpret_cast<const void*>(&silu_mul_tile_kernel<MODE, 1, GS, EXACT>);
+    case 2: return reinterpret_cast<const void*>(&silu_mul_tile_kernel<MODE, 2, GS, EXACT>);
+    case 4: return reinterpret_cast<const void*>(&silu_mul_tile_kernel<MODE, 4, GS, EXACT>);
+    default: return nullptr;
+  }
+}
+
+template <bool EXACT>
+const void* pick_tile_mode(int mode, int gs, int vpt) {
+  switch (mode) {
+    case RMSQ_FP8_STATIC: return pick_tile_vpt<RMSQ_FP8_STATIC, 0, EXACT>(vpt);
+    case RMSQ_FP8_GROUP:
+      return gs == 64 ? pick_tile_vpt<RMSQ_FP8_GROUP, 64, EXACT>(vpt)
+                      : pick_tile_vpt<RMSQ_FP8_GROUP, 128, EXACT>(vpt);
+    case RMSQ_FP4_BLOCK16: return pick_tile_vpt<RMSQ_FP4_BLOCK16, 16, EXACT>(vpt);
+    default: return nullptr;
+  }
+}
+
+template <bool EXACT>
+const void* pick_act_mode(int mode, int gs, int vpt) {
+  switch (mode) {
+    case RMSQ_FP8_STATIC: return pick_act_vpt<RMSQ_FP8_STATIC, 0, EXACT>(vpt);
+    case RMSQ_FP8_TOKEN: return pick_act_vpt<RMSQ_FP8_TOKEN, 0, EXACT>(vpt);
+    case RMSQ_FP8_GROUP:
+      return gs == 64 ? pick_act_vpt<RMSQ_FP8_GROUP, 64, EXACT>(vpt)
+                      : pick_act_vpt<RMSQ_FP8_GROUP, 128, EXACT>(vpt);
+    case RMSQ_FP4_BLOCK16: return pick_act_vpt<RMSQ_FP4_BLOCK16, 16, EXACT>(vpt);
+    default: return nullptr;
+  }
+}
+
+int validate_act(const void* x, int mode, const float* scale_in, const void* q,
+                 const void* scales, int64_t T, int64_t I, int gs, unsigned flags, int64_t ld) {
+  int st = check_quant_scalars(T, I, mode, gs, flags, ld);
+  if (st != RMSQ_OK || T == 0) return st;
+  if (!x) return RMSQ_EINVAL;
+  Span outs[2], sin;
+  int nout = 0;
+  st = check_quant_outputs(mode, scale_in, q, scales, T, I, gs, flags, ld, outs, &nout, &sin);
+  if (st != RMSQ_OK) return st;
+  if (!aligned(x, 16)) return RMSQ_EALIGN;
+  const Span ins[2] = {span(x, (size_t)T * (size_t)I * 4), sin};
+  return check_aliasing(outs, nout, ins, 2);
+}
+
+// Default SiLU+Mul launch: whole rows per workgroup, shaped as for rmsq_fused.  On MI355X at
+// I = 14336 this beat every row-tiled shape (64-1024 threads x 1-4 chunks) by 3-10%.
+rmsq_launch default_act_launch(int mode, int64_t I) {
+  (void)mode;
+  return default_launch(I);
+}
+
+bool valid_act_launch(const rmsq_launch& l, int mode, int64_t I) {
+  if (!(l.options & RMSQ_LAUNCH_ROW_TILES)) return valid_launch(l, I);
+  if (l.options != RMSQ_LAUNCH_ROW_TILES || mode == RMSQ_FP8_TOKEN) return false;
+  if (l.threads_per_row < 64 || l.threads_per_row > 1024 || (l.threads_per_row % 64) != 0)
+    return false;
+  if (l.chunks_per_thread != 1 && l.chunks_per_thread != 2 && l.chunks_per_thread != 4)
+    return false;
+  return l.rows_per_block == 1;
+}
+
+int act_impl(const void* x, int mode, const float* scale_in, void* q, void* scales, int64_t T,
+             int64_t I, int gs, unsigned flags, int64_t ld, const rmsq_launch* launch,
+             void* start_event, void* stop_event, void* stream) {
+  int st = validate_act(x, mode, scale_in, q, scales, T, I, gs, flags, ld);
+  if (st != RMSQ_OK) return st;
+  const rmsq_launch l = launch ? *launch : default_act_launch(mode, I);
+  if (!valid_act_launch(l, mode, I)) return RMSQ_EINVAL;
+  if (T == 0) return RMSQ_OK;
+  st = check_device();
+  if (st != RMSQ_OK) return st;
+  const bool tiled = (l.options & RMSQ_LAUNCH_ROW_TILES) != 0;
+  const int64_t tile = (int64_t)l.threads_per_row * l.chunks_per_thread;
+  const int64_t tiles = (I / 8 + tile - 1) / tile;
+  const void* fn;
+  int64_t nblk;
+  if (tiled) {
+    if (T * tiles > 0x7FFFFFFFLL) return RMSQ_EINVAL;
+    fn = ((I / 8) % tile == 0) ? pick_tile_mode<true>(mode, gs, l.chunks_per_thread)
+                               : pick_tile_mode<false>(mode, gs, l.chunks_per_thread);
+    nblk = T * tiles;
+  } else {
+    fn = exact_fit(l, T, I) ? pick_act_mode<true>(mode, gs, l.chunks_per_thread)
+                            : pick_act_mode<false>(mode, gs, l.chunks_per_thread);
+    nblk = (T + l.rows_per_block - 1) / l.rows_per_block;
+  }
+  if (!fn) return RMSQ_EINVAL;
+  AArgs a;
+  a.x = static_cast<const uint16_t*>(x);
+  a.q = static_cast<uint8_t*>(q);
+  a.scales = scales;
+  a.scale_in = scale_in;
+  a.T = T;
+  a.I = I;
+  a.ld = (flags & RMSQ_SCALE_COLMAJOR) ? (ld ? ld : T) : 0;
+  a.flags = flags;
+  a.tpr = l.threads_per_row;
+  a.rpb = l.rows_per_block;
+  a.nblk = (uint32_t)nblk;
+  a.xcd_ranges = (l.options & RMSQ_LAUNCH_XCD_RANGES) ? 1 : 0;
+  a.tiles = (uint32_t)tiles;
+  return launch_kernel(fn, nblk, l.threads_per_row * l.rows_per_block, &a, stream, start_event,
+                       stop_event);
 }
 
 }  // namespace rmsq
@@ -288,15 +438,55 @@ int rmsq_validate(const void* x, const void* residual, const void* weight, float
                   tokens, hidden, group_size, flags, scale_ld);
 }
 
+int rmsq_silu_mul_quant(const void* x, int mode, const float* scale_in, void* out_q,
+                        void* out_scales, int64_t tokens, int64_t inter, int group_size,
+                        unsigned flags, int64_t scale_ld, void* stream) {
+  return act_impl(x, mode, scale_in, out_q, out_scales, tokens, inter, group_size, flags,
+                  scale_ld, nullptr, nullptr, nullptr, stream);
+}
+
+int rmsq_silu_mul_quant_ex(const void* x, int mode, const float* scale_in, void* out_q,
+                           void* out_scales, int64_t tokens, int64_t inter, int group_size,
+                           unsigned flags, int64_t scale_ld, const rmsq_launch* launch,
+                           void* start_event, void* stop_event, void* stream) {
+  return act_impl(x, mode, scale_in, out_q, out_scales, tokens, inter, group_size, flags,
+                  scale_ld, launch, start_event, stop_event, stream);
+}
+
+int rmsq_silu_mul_quant_validate(const void* x, int mode, const float* scale_in,
+                                 const void* out_q, const void* out_scales, int64_t tokens,
+                                 int64_t inter, int group_size, unsigned flags,
+                                 int64_t scale_ld) {
+  return validate_act(x, mode, scale_in, out_q, out_scales, tokens, inter, group_size, flags,
+                      scale_ld);
+}
+
 int rmsq_query_launch(int mode, int64_t tokens, int64_t hidden, int group_size,
                       int has_residual, rmsq_launch* launch, int64_t* grid) {
   (void)has_residual;
   if (!launch) return RMSQ_EINVAL;
   const unsigned flags = 0;
-  const int st = check_scalars(tokens, hidden, 1e-6f, mode, group_size, flags, 0);
+  const int st = check_quant_scalars(tokens, hidden, mode, group_size, flags, 0);
   if (st != RMSQ_OK) return st;
   *launch = default_launch(hidden);
   if (grid) *grid = (tokens + launch->rows_per_block - 1) / launch->rows_per_block;
+  return RMSQ_OK;
+}
+
+int rmsq_silu_mul_query_launch(int mode, int64_t tokens, int64_t inter, int group_size,
+                               rmsq_launch* launch, int64_t* grid) {
+  if (!launch) return RMSQ_EINVAL;
+  const int st = check_quant_scalars(tokens, inter, mode, group_size, 0, 0);
+  if (st != RMSQ_OK) return st;
+  *launch = default_act_launch(mode, inter);
+  if (grid) {
+    if (launch->options & RMSQ_LAUNCH_ROW_TILES) {
+      const int64_t tile = (int64_t)launch->threads_per_row * launch->chunks_per_thread;
+      *grid = tokens * ((inter / 8 + tile - 1) / tile);
+    } else {
+      *grid = (tokens + launch->rows_per_block - 1) / launch->rows_per_block;
+    }
+  }
   return RMSQ_OK;
 }
 

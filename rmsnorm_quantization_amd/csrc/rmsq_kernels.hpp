@@ -56,6 +56,137 @@ __device__ __forceinline__ float y_of(const u32x4& h, const u32x4& w, int e, flo
   return (hf * inv) * wf;
 }
 
+// Where and how one row's quantized values go.
+struct RowOut {
+  uint8_t* q;       // codes: FP8 [T, n] bytes, FP4 [T, n/2] bytes
+  void* scales;     // per-token [T] f32, per-group [T, n/G] or [n/G, ld], FP4 [T, n/16] bytes
+  int64_t row;      // token index
+  bool row_ok;      // row < T
+  size_t obase;     // row * n: the row's element offset in the outputs
+  int64_t n;        // values per row
+  int64_t ld;       // column-major scale leading dimension
+  uint32_t flags;   // RMSQ_SCALE_*
+  uint32_t lr;      // thread within the row
+  int tpr, wpr, rib, tid;
+};
+
+// Quantize and store one row held as VPT 8-element chunks per thread; Y(k, e) is the f32 value of
+// element e of the thread's chunk k (chunk index lr + k * tpr).  One of the four schemes
+// (vLLM docs "Fusion torch.compile passes": FP8 static per-tensor, dynamic per-token, dynamic
+// per-token-group 128/64; PR #51925 summary: FP4 with block scales and a global scale):
+//   static     q = e4m3(y * (1/scale))
+//   per-token  s = absmax(row)/448, q = e4m3(y * (1/s)); s == 0 gives 0 codes
+//   per-group  s = absmax(group)/448 (E8M0: rounded up to a power of two), same rule
+//   FP4        sf = e4m3(absmax(block16) * gs / 6), q = e2m1(y * (gs / decode(sf)))
+template <int MODE, int VPT, int GS, class YF>
+__device__ __forceinline__ void quantize_store(const YF& Y, const bool (&ok)[VPT], const RowOut& o,
+                                               float scale_val, float* s_mx) {
+  if constexpr (MODE == RMSQ_FP8_STATIC) {
+    const float r = 1.0f / scale_val;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = Y(k, e) * r;
+      const u32x2 qc = {fp8x4(v[0], v[1], v[2], v[3]), fp8x4(v[4], v[5], v[6], v[7])};
+      if (ok[k]) {
+        const uint32_t c = o.lr + (uint32_t)(k * o.tpr);
+        __builtin_nontemporal_store(qc, reinterpret_cast<u32x2*>(o.q + o.obase) + c);
+      }
+    }
+  } else if constexpr (MODE == RMSQ_FP8_TOKEN) {
+    float mx = 0.0f;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(Y(k, e)));
+    mx = wave_max(mx);
+    if (o.wpr > 1) {  // uniform over the block
+      if ((o.tid & 63) == 0) s_mx[o.tid >> 6] = mx;
+      __syncthreads();
+      mx = 0.0f;
+      for (int i = 0; i < o.wpr; ++i) mx = fmaxf(mx, s_mx[o.rib * o.wpr + i]);
+    }
+    const float s = mx / kFp8Max;
+    if (o.lr == 0 && o.row_ok) static_cast<float*>(o.scales)[o.row] = s;
+    const bool zero = (s == 0.0f);
+    const float r = zero ? 0.0f : 1.0f / s;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = Y(k, e) * r;
+      u32x2 qc = {fp8x4(v[0], v[1], v[2], v[3]), fp8x4(v[4], v[5], v[6], v[7])};
+      if (zero) qc = (u32x2){0u, 0u};
+      if (ok[k]) {
+        const uint32_t c = o.lr + (uint32_t)(k * o.tpr);
+        __builtin_nontemporal_store(qc, reinterpret_cast<u32x2*>(o.q + o.obase) + c);
+      }
+    }
+  } else if constexpr (MODE == RMSQ_FP8_GROUP) {
+    constexpr int L = GS / 8;  // lanes per group
+    const bool e8 = (o.flags & (RMSQ_SCALE_E8M0 | RMSQ_SCALE_E8M0_U8)) != 0;
+    const bool u8 = (o.flags & RMSQ_SCALE_E8M0_U8) != 0;
+    const bool col = (o.flags & RMSQ_SCALE_COLMAJOR) != 0;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const uint32_t c = o.lr + (uint32_t)(k * o.tpr);
+      float y[8];
+      float m = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        y[e] = Y(k, e);
+        m = fmaxf(m, fabsf(y[e]));
+      }
+      m = group_max<L>(m);
+      float s = m / kFp8Max;
+      const bool zero = (s == 0.0f);
+      uint32_t byte = 0;
+      if (e8) byte = e8m0_ceil(s, &s);
+      const float r = 1.0f / s;
+      u32x2 qc = {fp8x4(y[0] * r, y[1] * r, y[2] * r, y[3] * r),
+                  fp8x4(y[4] * r, y[5] * r, y[6] * r, y[7] * r)};
+      if (zero) qc = (u32x2){0u, 0u};
+      if (ok[k]) {
+        __builtin_nontemporal_store(qc, reinterpret_cast<u32x2*>(o.q + o.obase) + c);
+        if ((o.lr % L) == 0) {
+          const int64_t g = c / L;
+          const int64_t idx = col ? g * o.ld + o.row : o.row * (o.n / GS) + g;
+          if (u8) static_cast<uint8_t*>(o.scales)[idx] = (uint8_t)byte;
+          else static_cast<float*>(o.scales)[idx] = s;
+        }
+      }
+    }
+  } else {  // RMSQ_FP4_BLOCK16
+    const float gs = scale_val;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const uint32_t c = o.lr + (uint32_t)(k * o.tpr);
+      float y[8];
+      float m = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        y[e] = Y(k, e);
+        m = fmaxf(m, fabsf(y[e]));
+      }
+      m = group_max<2>(m);  // a 16-element block is two neighbouring lanes
+      const uint32_t sf = fp8x1((m * gs) / 6.0f);
+      const float d = fp8_decode(sf);
+      uint32_t qc = 0u;
+      if (d > 0.0f) {
+        const float mul = gs / d;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] *= mul;
+        qc = fp4x8(y);
+      }
+      if (ok[k]) {
+        reinterpret_cast<uint32_t*>(o.q + o.obase / 2)[c] = qc;
+        if ((c & 1) == 0) static_cast<uint8_t*>(o.scales)[o.obase / 16 + c / 2] = (uint8_t)sf;
+      }
+    }
+  }
+}
+
 // EXACT: the launch covers every chunk of every row with no remainder (threads_per_row x
 // chunks_per_thread x 8 == H and T a multiple of rows_per_block), so no load or store needs a
 // predicate; otherwise out-of-range chunks and rows are masked.
@@ -144,110 +275,189 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
   const float inv = (float)(1.0 / sqrt(ss / (double)a.H + (double)a.eps));
 
   // ---- quantize ----
-  if constexpr (MODE == RMSQ_FP8_STATIC) {
-    const float r = 1.0f / scale_val;
+  RowOut o;
+  o.q = a.q;
+  o.scales = a.scales;
+  o.row = row;
+  o.row_ok = row_ok;
+  o.obase = base;
+  o.n = a.H;
+  o.ld = a.ld;
+  o.flags = a.flags;
+  o.lr = lr;
+  o.tpr = tpr;
+  o.wpr = wpr;
+  o.rib = rib;
+  o.tid = tid;
+  quantize_store<MODE, VPT, GS>(
+      [&](int k, int e) { return y_of(hv[k], wv[k], e, inv); }, ok, o, scale_val, s_mx);
+}
+
+// ------------------------------------------------------------------ SiLU+Mul -> quantization
+// vLLM docs "Fusion torch.compile passes", section "SiLU+Mul + quantization (fuse_act_quant)":
+// the gated up-projection activation silu_and_mul fused with the quantization that follows, so
+// the f32 activation never reaches memory.  Row t of x is [2I] bf16: gate g = x[t, 0:I], up
+// u = x[t, I:2I]; a = silu(g) * u = g / (1 + exp(-g)) * u in f32, then quantize_store.
+struct AArgs {
+  const uint16_t* x;
+  uint8_t* q;
+  void* scales;
+  const float* scale_in;
+  int64_t T;
+  int64_t I;
+  int64_t ld;
+  uint32_t flags;
+  int32_t tpr;
+  int32_t rpb;
+  uint32_t nblk;
+  int32_t xcd_ranges;
+  uint32_t tiles;  // row-tiled launch: tiles per row
+};
+
+// exp(x) for x <= 0 in f32, within ~2 ulp: 2^(x log2 e) on the hardware exp2 (v_exp_f32), with
+// the rounding error of the product x * log2(e) -- recovered exactly by an FMA, plus the part of
+// log2(e) that f32 cannot hold -- applied as the first-order factor 1 + r ln 2.  For x <= 0 the
+// result lies in [0, 1], so no overflow handling is needed; below about -103 it is 0.
+__device__ __forceinline__ float exp_nonpositive(float x) {
+  constexpr float kLog2e = 1.44269502162933349609375f;    // log2(e) rounded to f32
+  constexpr float kLog2eLo = 1.925963033500011e-08f;      // log2(e) - kLog2e
+  constexpr float kLn2 = 0.693147180559945309f;
+  const float p = x * kLog2e;
+  const float r = fmaf(x, kLog2eLo, fmaf(x, kLog2e, -p));
+  const float e0 = __builtin_amdgcn_exp2f(p);
+  return fmaf(e0, r * kLn2, e0);
+}
+
+// silu(g) * u in f32, within a few ulp of the exactly rounded value: with e = exp(-|g|),
+// silu(g) = g / (1 + e) for g >= 0 and g * e / (1 + e) for g < 0 (nothing overflows; very
+// negative gates give the tiny activations they should), the reciprocal on the hardware
+// v_rcp_f32 (1 ulp).
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float e = exp_nonpositive(-fabsf(g));
+  const float num = g >= 0.0f ? g : g * e;
+  return (num * __builtin_amdgcn_rcpf(1.0f + e)) * u;
+}
+
+template <int MODE, int VPT, int GS, bool EXACT>
+__global__ void __launch_bounds__(1024) silu_mul_kernel(AArgs a) {
+  __shared__ float s_mx[kMaxWavesPerBlock];
+
+  const int tid = threadIdx.x;
+  const int tpr = a.tpr;
+  const int wpr = tpr >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rib = (a.rpb == 1) ? 0 : wave / wpr;
+  const uint32_t lr = (uint32_t)(tid - rib * tpr);
+  const uint32_t rb = a.xcd_ranges ? rowblock_of(blockIdx.x, a.nblk) : blockIdx.x;
+  const int64_t row = (int64_t)rb * a.rpb + rib;
+  const bool row_ok = EXACT || row < a.T;
+  const int nch = (int)(a.I >> 3);
+  const size_t obase = (size_t)(row_ok ? row : 0) * (size_t)a.I;
+  const u32x4* grow = reinterpret_cast<const u32x4*>(a.x + 2 * obase);
+  const u32x4* urow = reinterpret_cast<const u32x4*>(a.x + 2 * obase + a.I);
+
+  float scale_val = 0.0f;
+  if constexpr (MODE == RMSQ_FP8_STATIC || MODE == RMSQ_FP4_BLOCK16) scale_val = a.scale_in[0];
+
+  u32x4 gv[VPT], uv[VPT];
+  bool ok[VPT];
 #pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = y_of(hv[k], wv[k], e, inv) * r;
-      const u32x2 qc = {fp8x4(v[0], v[1], v[2], v[3]), fp8x4(v[4], v[5], v[6], v[7])};
-      if (ok[k]) {
-        const uint32_t c = lr + (uint32_t)(k * tpr);
-        __builtin_nontemporal_store(qc, reinterpret_cast<u32x2*>(a.q + base) + c);
-      }
-    }
-  } else if constexpr (MODE == RMSQ_FP8_TOKEN) {
-    float mx = 0.0f;
-#pragma unroll
-    for (int k = 0; k < VPT; ++k)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(y_of(hv[k], wv[k], e, inv)));
-    mx = wave_max(mx);
-    if (wpr > 1) {
-      if ((tid & 63) == 0) s_mx[tid >> 6] = mx;
-      __syncthreads();
-      mx = 0.0f;
-      for (int i = 0; i < wpr; ++i) mx = fmaxf(mx, s_mx[rib * wpr + i]);
-    }
-    const float s = mx / kFp8Max;
-    if (lr == 0 && row_ok) static_cast<float*>(a.scales)[row] = s;
-    const bool zero = (s == 0.0f);
-    const float r = zero ? 0.0f : 1.0f / s;
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = y_of(hv[k], wv[k], e, inv) * r;
-      u32x2 qc = {fp8x4(v[0], v[1], v[2], v[3]), fp8x4(v[4], v[5], v[6], v[7])};
-      if (zero) qc = (u32x2){0u, 0u};
-      if (ok[k]) {
-        const uint32_t c = lr + (uint32_t)(k * tpr);
-        __builtin_nontemporal_store(qc, reinterpret_cast<u32x2*>(a.q + base) + c);
-      }
-    }
-  } else if constexpr (MODE == RMSQ_FP8_GROUP) {
-    constexpr int L = GS / 8;  // lanes per group
-    const bool e8 = (a.flags & (RMSQ_SCALE_E8M0 | RMSQ_SCALE_E8M0_U8)) != 0;
-    const bool u8 = (a.flags & RMSQ_SCALE_E8M0_U8) != 0;
-    const bool col = (a.flags & RMSQ_SCALE_COLMAJOR) != 0;
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      const uint32_t c = lr + (uint32_t)(k * tpr);
-      float y[8];
-      float m = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        y[e] = y_of(hv[k], wv[k], e, inv);
-        m = fmaxf(m, fabsf(y[e]));
-      }
-      m = group_max<L>(m);
-      float s = m / kFp8Max;
-      const bool zero = (s == 0.0f);
-      uint32_t byte = 0;
-      if (e8) byte = e8m0_ceil(s, &s);
-      const float r = 1.0f / s;
-      u32x2 qc = {fp8x4(y[0] * r, y[1] * r, y[2] * r, y[3] * r),
-                  fp8x4(y[4] * r, y[5] * r, y[6] * r, y[7] * r)};
-      if (zero) qc = (u32x2){0u, 0u};
-      if (ok[k]) {
-        __builtin_nontemporal_store(qc, reinterpret_cast<u32x2*>(a.q + base) + c);
-        if ((lr % L) == 0) {
-          const int64_t g = c / L;
-          const int64_t idx = col ? g * a.ld + row : row * (a.H / GS) + g;
-          if (u8) static_cast<uint8_t*>(a.scales)[idx] = (uint8_t)byte;
-          else static_cast<float*>(a.scales)[idx] = s;
-        }
-      }
-    }
-  } else {  // RMSQ_FP4_BLOCK16
-    const float gs = scale_val;
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      const uint32_t c = lr + (uint32_t)(k * tpr);
-      float y[8];
-      float m = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        y[e] = y_of(hv[k], wv[k], e, inv);
-        m = fmaxf(m, fabsf(y[e]));
-      }
-      m = group_max<2>(m);  // a 16-element block is two neighbouring lanes
-      const uint32_t sf = fp8x1((m * gs) / 6.0f);
-      const float d = fp8_decode(sf);
-      uint32_t qc = 0u;
-      if (d > 0.0f) {
-        const float mul = gs / d;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] *= mul;
-        qc = fp4x8(y);
-      }
-      if (ok[k]) {
-        reinterpret_cast<uint32_t*>(a.q + base / 2)[c] = qc;
-        if ((c & 1) == 0) static_cast<uint8_t*>(a.scales)[base / 16 + c / 2] = (uint8_t)sf;
-      }
+  for (int k = 0; k < VPT; ++k) {
+    const uint32_t c = lr + (uint32_t)(k * tpr);
+    ok[k] = EXACT || (row_ok && c < (uint32_t)nch);
+    gv[k] = (u32x4){0u, 0u, 0u, 0u};
+    uv[k] = (u32x4){0u, 0u, 0u, 0u};
+    if (ok[k]) {
+      gv[k] = __builtin_nontemporal_load(grow + c);
+      uv[k] = __builtin_nontemporal_load(urow + c);
     }
   }
+  float act[VPT][8];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      act[k][2 * j] = silu_mul(bf16_lo(gv[k][j]), bf16_lo(uv[k][j]));
+      act[k][2 * j + 1] = silu_mul(bf16_hi(gv[k][j]), bf16_hi(uv[k][j]));
+    }
+
+  RowOut o;
+  o.q = a.q;
+  o.scales = a.scales;
+  o.row = row;
+  o.row_ok = row_ok;
+  o.obase = obase;
+  o.n = a.I;
+  o.ld = a.ld;
+  o.flags = a.flags;
+  o.lr = lr;
+  o.tpr = tpr;
+  o.wpr = wpr;
+  o.rib = rib;
+  o.tid = tid;
+  quantize_store<MODE, VPT, GS>([&](int k, int e) { return act[k][e]; }, ok, o, scale_val, s_mx);
+}
+
+// Row-tiled SiLU+Mul -> quantization for the schemes that need no row-wide reduction (static,
+// per-group, FP4): workgroup b takes tile (b mod tiles) of row (b / tiles), a tile being
+// threads x VPT chunks, so consecutive workgroups cover consecutive stretches of a row and a
+// long row does not become one very wide workgroup.  Tiles hold whole groups (threads is a
+// multiple of 64, a group at most 16 chunks).
+template <int MODE, int VPT, int GS, bool EXACT>
+__global__ void __launch_bounds__(1024) silu_mul_tile_kernel(AArgs a) {
+  static_assert(MODE != RMSQ_FP8_TOKEN, "per-token scaling needs whole rows");
+  const int tid = threadIdx.x;
+  const int tpr = a.tpr;  // threads per tile
+  const uint32_t row32 = blockIdx.x / a.tiles;
+  const uint32_t tile = blockIdx.x - row32 * a.tiles;
+  const int64_t row = row32;
+  const int nch = (int)(a.I >> 3);
+  const uint32_t lr = tile * (uint32_t)(tpr * VPT) + (uint32_t)tid;  // first chunk of this thread
+  const size_t obase = (size_t)row * (size_t)a.I;
+  const u32x4* grow = reinterpret_cast<const u32x4*>(a.x + 2 * obase);
+  const u32x4* urow = reinterpret_cast<const u32x4*>(a.x + 2 * obase + a.I);
+
+  float scale_val = 0.0f;
+  if constexpr (MODE == RMSQ_FP8_STATIC || MODE == RMSQ_FP4_BLOCK16) scale_val = a.scale_in[0];
+
+  u32x4 gv[VPT], uv[VPT];
+  bool ok[VPT];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const uint32_t c = lr + (uint32_t)(k * tpr);
+    ok[k] = EXACT || c < (uint32_t)nch;
+    gv[k] = (u32x4){0u, 0u, 0u, 0u};
+    uv[k] = (u32x4){0u, 0u, 0u, 0u};
+    if (ok[k]) {
+      gv[k] = __builtin_nontemporal_load(grow + c);
+      uv[k] = __builtin_nontemporal_load(urow + c);
+    }
+  }
+  float act[VPT][8];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      act[k][2 * j] = silu_mul(bf16_lo(gv[k][j]), bf16_lo(uv[k][j]));
+      act[k][2 * j + 1] = silu_mul(bf16_hi(gv[k][j]), bf16_hi(uv[k][j]));
+    }
+
+  RowOut o;
+  o.q = a.q;
+  o.scales = a.scales;
+  o.row = row;
+  o.row_ok = true;
+  o.obase = obase;
+  o.n = a.I;
+  o.ld = a.ld;
+  o.flags = a.flags;
+  o.lr = lr;
+  o.tpr = tpr;
+  o.wpr = 1;
+  o.rib = 0;
+  o.tid = tid;
+  quantize_store<MODE, VPT, GS>([&](int k, int e) { return act[k][e]; }, ok, o, scale_val,
+                                nullptr);
 }
 
 // The kernels' own converters over a flat f32 array, 8 elements per thread.

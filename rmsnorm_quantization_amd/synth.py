@@ -2,8 +2,9 @@
 
 Both the GPU path and the CPU oracle are fed from here.  Values are drawn in float32 from a
 seeded torch CPU generator and cast to bf16 by torch; nothing in this module normalizes,
-scales or quantizes.  Five workloads are defined, matching the shapes and distributions of the
-fused RMSNorm + quantization workloads this library is measured on:
+scales or quantizes.  Six workloads are defined, matching the shapes and distributions of the
+fused RMSNorm + quantization (0-4) and SiLU+Mul + quantization (5) workloads this library is
+measured on:
 
   0  RMSNorm -> FP8 static        T=16,  H=4096, x~N(0,1), w~U(0.5,1.5), eps 1e-5, scale 0.05
   1  add+RMSNorm -> FP8 static    T in {1,64,512,4096}, H=4096, x,r~N(0,1), eps 1e-5,
@@ -14,6 +15,11 @@ fused RMSNorm + quantization workloads this library is measured on:
                                   row/col-major, f32/E8M0 scales, eps 1e-6
   4  add+RMSNorm -> FP4 block-16  T in {1,32,256,4096}, H=2048, eps 1e-6, global scale
                                   448*6/max|y| of the same batch
+
+  5  SiLU+Mul -> quant            T in {1,256,4096}, I=14336 (the intermediate size of the
+                                  Llama-3.1-8B model the pages use in their examples);
+                                  x = [gate | up] ~N(0,1), [T, 2I]; static scale from a fixed
+                                  512 x 2I warm-up batch, FP4 global scale 448*6/max|a|
 
 Seeds: 1000*workload + tensor id (x=1, residual=2, weight=3, outlier channels=4,
 warm-up x=5, warm-up residual=6).  Unless stated otherwise, weight ~ U(0.5, 1.5) and the
@@ -39,6 +45,7 @@ class Workload:
     static_scale: Optional[float] = None   # fixed per-tensor scale, if the workload fixes one
     warmup_shape: Optional[Tuple[int, int]] = None  # batch the static scale is derived from
     group_sizes: Tuple[int, ...] = field(default_factory=tuple)
+    kind: str = "norm"   # "norm": (residual add ->) RMSNorm -> quant; "act": SiLU+Mul -> quant
 
 
 WORKLOADS = {
@@ -50,6 +57,8 @@ WORKLOADS = {
     3: Workload(3, "add_rmsnorm_fp8_per_group", (1, 128, 1024, 16384), (5120, 7168), 1e-6, True,
                 group_sizes=(128, 64)),
     4: Workload(4, "add_rmsnorm_fp4_block16", (1, 32, 256, 4096), (2048,), 1e-6, True),
+    5: Workload(5, "silu_mul_quant", (1, 256, 4096), (14336,), 0.0, False,
+                warmup_shape=(512, 14336), group_sizes=(128, 64), kind="act"),
 }
 
 X, RESIDUAL, WEIGHT, OUTLIERS, WARM_X, WARM_R = 1, 2, 3, 4, 5, 6
@@ -104,6 +113,19 @@ def make_warmup(workload: int, H: Optional[int] = None):
     x = make_x(wl, T, H, tensor=WARM_X)
     r = normal_bf16((T, H), wl.index, WARM_R) if wl.residual else None
     return x, r
+
+
+def make_act_inputs(workload: int, T: int, I: Optional[int] = None, tensor: int = X):
+    """x = [gate | up] as one [T, 2I] CPU bf16 tensor for a SiLU+Mul workload."""
+    wl = WORKLOADS[workload]
+    I = I if I is not None else wl.hidden[0]
+    return normal_bf16((T, 2 * I), wl.index, tensor)
+
+
+def make_act_warmup(workload: int, I: Optional[int] = None):
+    wl = WORKLOADS[workload]
+    T, Iw = wl.warmup_shape
+    return make_act_inputs(workload, T, I if I is not None else Iw, tensor=WARM_X)
 
 
 def bits(t: torch.Tensor) -> np.ndarray:

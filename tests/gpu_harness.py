@@ -126,3 +126,36 @@ def oracle_on_rows(mode, xb, rb, wb, eps, rows, scale_in=0.0, group_size=0, flag
     rs = None if rb is None else (rb if rows is None else rb[rows])
     return O.fused(xs, rs, wb, eps, mode, scale_in=scale_in, group_size=group_size,
                    flags=flags, want_pre=True)
+
+
+def run_act(mode, x, scale_in=None, group_size=0, flags=0, scale_ld=0, launch=None, rows=None):
+    """SiLU+Mul -> quant on device x [T, 2I], outputs guarded like run()."""
+    T, I = x.shape[0], x.shape[1] // 2
+    qb = T * I // 2 if mode == O.FP4_BLOCK16 else T * I
+    gq = Guarded(qb)
+    sb, sshape, sdt = scale_bytes(mode, T, I, group_size, flags, scale_ld)
+    gs = Guarded(sb) if sshape is not None else None
+    sc = None
+    if scale_in is not None:
+        sc = torch.tensor([float(np.float32(scale_in))], dtype=torch.float32, device="cuda")
+    sview = None
+    if gs is not None:
+        sview = gs.data if sdt == np.uint8 else gs.data.view(torch.float32)
+    B.rmsq_silu_mul_quant(x, mode, sc, gq.data, sview, group_size=group_size, flags=flags,
+                          scale_ld=scale_ld, launch=launch)
+    torch.cuda.synchronize()
+    gq.check("out_q")
+    if gs is not None:
+        gs.check("out_scales")
+    qcols = I // 2 if mode == O.FP4_BLOCK16 else I
+    q = gq.data.view(T, qcols)
+    sel = None if rows is None else torch.as_tensor(np.asarray(rows), device="cuda")
+    out = {"q": (q if sel is None else q[sel]).cpu().numpy(), "residual_out": None}
+    if gs is not None:
+        s = sview.view(*sshape)
+        if sel is not None:
+            s = s[:, sel] if (mode == O.FP8_GROUP and flags & O.SCALE_COLMAJOR) else s[sel]
+        out["scales"] = s.cpu().numpy()
+    else:
+        out["scales"] = None
+    return out

@@ -5,17 +5,22 @@ The bar, per output:
   codes          equal, or the adjacent magnitude with the same sign (+0 and -0 count as
                  equal); a mismatch is only accepted where the oracle's pre-rounding value lies
                  within 1e-5 (relative) of the rounding midpoint between the two codes, and
-                 mismatches may total at most 0.01% of the elements.  Elements of a group whose
-                 scale differs are judged by the dequantized rule instead.
+                 mismatches may total at most 0.01% of the elements.  This applies to every
+                 element except those of a group whose E8M0 scale flipped by a factor 2 (or an
+                 FP4 block whose e4m3 scale moved one code): those are judged by the dequantized
+                 rule only.
   f32 scales     within 1e-6 relative.  E8M0 scales: equal, or a x2 flip where the unrounded
                  scale is within 1e-6 of a power of two.  FP4 e4m3 block scales: equal or +-1
                  code, counted as mismatches.
-  dequantized    FP8: per row (per group in group mode) max |dq_gpu - dq_ref| <=
-                 1e-2 * max |dq_ref|.  FP4: per element within one e2m1 step * d / gs.
+  dequantized    FP8: per row, ||dq_gpu - dq_ref||_2 <= 1e-2 * ||dq_ref||_2 (a relative error
+                 of the dequantized row; a per-element bound cannot hold, since an allowed
+                 one-code tie flip near 448 is a ~7% change of that element).  FP4: per element
+                 within one e2m1 step * d / gs.
 Why ties can differ at all: the GPU sums squares in a different order than the oracle, so
-inv_rms may differ in its last bit, and a value sitting on a rounding midpoint can then land
-on either neighbour.  In practice the binary64 sums agree after rounding to f32 and the
-counts below come out zero; the rule is what is asserted.
+inv_rms may differ in its last bit (and SiLU uses expf, a few ulp from the exactly rounded
+activation), and a value sitting on a rounding midpoint can then land on either neighbour.
+For the norm path the binary64 sums agree after rounding to f32 and the counts come out zero;
+the rule is what is asserted.
 """
 from dataclasses import dataclass, field
 
@@ -151,21 +156,21 @@ def compare(mode, gpu, ref, *, T, H, group_size=0, flags=0, scale_in=0.0, rows=N
                     assert np.all(ratio == 2.0), "E8M0 scale differs by more than a factor 2"
                     p2 = np.ldexp(1.0, np.round(np.log2(raw[diff])).astype(np.int64))
                     assert np.all(np.abs(raw[diff] - p2) <= SCALE_REL * p2), "E8M0 flip off a power of two"
+                    excluded = np.repeat(diff, G, axis=1)
             else:
                 rel = np.abs(s_g - s_r) / np.maximum(np.abs(s_r), 1e-38)
                 diff = rel > 0
                 assert np.all(rel <= SCALE_REL), f"scale off by {rel.max():.3g} relative"
             rep.scale_mismatch = int(diff.sum())
-            excluded = np.repeat(diff, G, axis=1) if diff.shape[1] * G == H else excluded
         _codes_ok(qg, qr, pre, "e4m3", excluded, rep)
-        # rule 4: dequantized, per row (static/token) or per group
-        dqg = e4_table()[qg].reshape(T, H // G, G) * s_g[:, :, None]
-        dqr = e4_table()[qr].reshape(T, H // G, G) * s_r[:, :, None]
-        err = np.abs(dqg - dqr).max(axis=2)
-        ref_max = np.abs(dqr).max(axis=2)
-        ok = err <= DEQ_REL * ref_max
-        assert np.all(ok | (ref_max == 0) & (err == 0)), "dequantized output off by > 1e-2 relative"
-        rel = err / np.maximum(ref_max, 1e-38)
+        # rule 4: relative L2 error of each dequantized row
+        dqg = (e4_table()[qg].reshape(T, H // G, G) * s_g[:, :, None]).reshape(T, H)
+        dqr = (e4_table()[qr].reshape(T, H // G, G) * s_r[:, :, None]).reshape(T, H)
+        err = np.sqrt(((dqg - dqr) ** 2).sum(axis=1))
+        ref_norm = np.sqrt((dqr ** 2).sum(axis=1))
+        assert np.all((err <= DEQ_REL * ref_norm) | ((ref_norm == 0) & (err == 0))), \
+            "dequantized row off by > 1e-2 relative"
+        rel = err / np.maximum(ref_norm, 1e-38)
         rep.max_dequant_rel = float(rel.max()) if rel.size else 0.0
 
     assert rep.code_mismatch <= MAX_MISMATCH_FRAC * rep.elements, \

@@ -33,6 +33,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("rmsq_fused", "rmsq_fused_with_launch", "rmsq_fused_timed", "rmsq_validate",
+              "rmsq_silu_mul_quant", "rmsq_silu_mul_quant_ex", "rmsq_silu_mul_quant_validate",
+              "rmsq_silu_mul_query_launch",
               "rmsq_query_launch",
               "rmsq_block_to_rowblock", "rmsq_convert", "rmsq_status_string",
               "rmsq_abi_version"):
@@ -152,3 +154,49 @@ def test_convert_argument_checks(B):
     assert L.rmsq_convert(0, X, Q, 0, None) == B.RMSQ_OK
     assert L.rmsq_convert(0, X + 4, Q, 8, None) == B.RMSQ_EALIGN
     assert L.rmsq_convert(0, X, X + 16, 8, None) == B.RMSQ_EALIAS
+
+
+# ------------------------------------------------------------------ SiLU+Mul -> quant checks
+def VA(B, x=X, mode=1, sc=None, q=Q, s=S, t=T, i=H, g=0, f=0, ld=0):
+    return B.rmsq_silu_mul_quant_validate(x, mode, sc, q, s, t, i, g, f, ld)
+
+
+def test_act_valid_calls(B):
+    assert VA(B) == B.RMSQ_OK
+    assert VA(B, mode=0, sc=SC, s=None) == B.RMSQ_OK
+    assert VA(B, mode=2, g=64, f=B.RMSQ_SCALE_COLMAJOR | B.RMSQ_SCALE_E8M0_U8, ld=9) == B.RMSQ_OK
+    assert VA(B, mode=3, g=16, sc=SC) == B.RMSQ_OK
+    assert VA(B, t=0, x=None, q=None) == B.RMSQ_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(t=-1), "EINVAL"), (dict(i=12), "EINVAL"), (dict(i=0), "EINVAL"),
+    (dict(i=65536 + 8), "EINVAL"), (dict(mode=5), "EINVAL"), (dict(x=None), "EINVAL"),
+    (dict(q=None), "EINVAL"), (dict(s=None), "EINVAL"), (dict(sc=SC), "EINVAL"),
+    (dict(mode=2, g=128, i=192), "EINVAL"), (dict(mode=3, g=16), "EINVAL"),
+    (dict(f=1), "EUNSUPPORTED"), (dict(mode=2, g=64, f=6), "EUNSUPPORTED"),
+    (dict(x=X + 8), "EALIGN"), (dict(q=Q + 4), "EALIGN"), (dict(s=S + 1), "EALIGN"),
+    # x spans T * 2I bf16 = 4 * T * I bytes
+    (dict(q=X + 4 * T * H - 16), "EALIAS"), (dict(s=X + 16), "EALIAS"), (dict(s=Q + 8), "EALIAS"),
+    (dict(mode=0, s=None, sc=Q), "EALIAS"),
+])
+def test_act_bad_arguments(B, kw, status):
+    code = getattr(B, "RMSQ_" + status)
+    assert VA(B, **kw) == code
+    assert B.lib().rmsq_silu_mul_quant(kw.get("x", X), kw.get("mode", 1), kw.get("sc", None),
+                                       kw.get("q", Q), kw.get("s", S), kw.get("t", T),
+                                       kw.get("i", H), kw.get("g", 0), kw.get("f", 0),
+                                       kw.get("ld", 0), None) == code
+
+
+def test_act_x_extent_is_two_rows_wide(B):
+    assert VA(B, q=X + 4 * T * H) == B.RMSQ_OK   # just past x [T, 2I] bf16
+
+
+def test_act_query_launch(B):
+    l, grid = B.rmsq_silu_mul_query_launch(B.RMSQ_FP8_TOKEN, 100, 14336)
+    assert l.options == 0 and l.threads_per_row * l.chunks_per_thread * 8 >= 14336
+    for mode, G in ((B.RMSQ_FP8_STATIC, 0), (B.RMSQ_FP8_GROUP, 128), (B.RMSQ_FP4_BLOCK16, 16)):
+        l, grid = B.rmsq_silu_mul_query_launch(mode, 100, 14336, G)
+        assert l.as_tuple() == B.rmsq_query_launch(mode, 100, 14336, G)[0].as_tuple()
+        assert grid == -(-100 // l.rows_per_block)

@@ -55,6 +55,8 @@ def lib():
         L.orc_silu_mul_quant.argtypes = [p, C.c_int, C.c_float, p, p, i64, i64, C.c_int,
                                          C.c_uint, i64, p]
         L.orc_silu_mul_quant.restype = C.c_int
+        L.orc_rms_norm_pad.argtypes = [p, p, p, C.c_float, p, p, i64, i64, i64]
+        L.orc_rms_norm_pad.restype = C.c_int
         L.orc_fused.argtypes = [p, p, p, C.c_float, C.c_int, C.c_float, p, p, p,
                                 i64, i64, C.c_int, C.c_uint, i64, p]
         L.orc_fused.restype = C.c_int
@@ -250,3 +252,19 @@ def silu_mul_quant(x, mode, scale_in=0.0, group_size=0, flags=0, scale_ld=0, wan
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (rc={rc})")
     return {"q": q, "scales": scales, "pre": pre}
+
+
+# ---------------------------------------------------------------- RMSNorm -> padded bf16
+def rms_norm_pad(x, residual, weight, eps, out_ld):
+    """[T, H] bf16 bits -> (out [T, out_ld] bf16 bits, residual_out or None)."""
+    x = _c(x, np.uint16)
+    T, H = x.shape
+    r = None if residual is None else _c(residual, np.uint16)
+    w = _c(weight, np.uint16)
+    out = np.full((T, out_ld), 0xFFFF, np.uint16)
+    rout = None if r is None else np.zeros_like(r)
+    rc = lib().orc_rms_norm_pad(_ptr(x), _ptr(r), _ptr(w), float(eps), _ptr(out), _ptr(rout), T,
+                                H, int(out_ld))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (rc={rc})")
+    return out, rout

@@ -338,6 +338,35 @@ int orc_fused(const uint16_t* x, const uint16_t* residual, const uint16_t* weigh
   return 0;
 }
 
+/* ------------------------------------------------------------------ RMSNorm -> padded bf16 */
+int orc_rms_norm_pad(const uint16_t* x, const uint16_t* residual, const uint16_t* weight,
+                     float eps, uint16_t* out, uint16_t* residual_out, int64_t T, int64_t H,
+                     int64_t out_ld) {
+  if (T < 0 || H <= 0 || out_ld < H || !x || !weight || !out) return -1;
+  if ((residual == NULL) != (residual_out == NULL)) return -1;
+  if (!(eps >= 0.0f) || isinf(eps)) return -1;
+  uint16_t* h = (uint16_t*)malloc((size_t)H * sizeof(uint16_t));
+  float* y = (float*)malloc((size_t)H * sizeof(float));
+  if (!h || !y) {
+    free(h);
+    free(y);
+    return -1;
+  }
+  for (int64_t t = 0; t < T; ++t) {
+    if (residual) {
+      orc_residual_add(x + t * H, residual + t * H, h, H);
+      memcpy(residual_out + t * H, h, (size_t)H * sizeof(uint16_t));
+    } else {
+      memcpy(h, x + t * H, (size_t)H * sizeof(uint16_t));
+    }
+    orc_normalize(h, weight, orc_inv_rms(h, H, eps), y, H);
+    for (int64_t i = 0; i < out_ld; ++i) out[t * out_ld + i] = i < H ? orc_f32_to_bf16(y[i]) : 0;
+  }
+  free(h);
+  free(y);
+  return 0;
+}
+
 /* ------------------------------------------------------------------ SiLU+Mul -> quant */
 float orc_silu_mul(uint16_t g, uint16_t u) {
   double gd = (double)orc_bf16_to_f32(g), ud = (double)orc_bf16_to_f32(u);

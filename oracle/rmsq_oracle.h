@@ -97,6 +97,15 @@ int orc_fused(const uint16_t* x, const uint16_t* residual, const uint16_t* weigh
               int64_t T, int64_t H, int group_size, unsigned flags, int64_t scale_ld,
               float* pre_q);
 
+/* ---- residual add + RMSNorm -> padded bf16 output (vLLM docs "Fusion torch.compile passes",
+ * section "RMSNorm + padding (fuse_act_padding)": the residual add and RMSNorm fused with the
+ * padding of the hidden dimension to the multiple a downstream GEMM needs; hidden size 2880).
+ * out [T, out_ld] bf16: out[t, i] = bf16(y_i) for i < H (y as in orc_fused), 0 for H <= i <
+ * out_ld.  residual_out as in orc_fused.  Returns 0, or -1 on an invalid argument. */
+int orc_rms_norm_pad(const uint16_t* x, const uint16_t* residual, const uint16_t* weight,
+                     float eps, uint16_t* out, uint16_t* residual_out, int64_t T, int64_t H,
+                     int64_t out_ld);
+
 /* ---- SiLU+Mul -> quantization (vLLM docs "Fusion torch.compile passes", section "SiLU+Mul +
  * quantization (fuse_act_quant)": the gated up-projection activation silu_and_mul fused with the
  * quantization that follows; FP8 static per-tensor, FP8 dynamic per-group 128/64, FP4). ----

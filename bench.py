@@ -34,7 +34,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 FOOTPRINT_BYTES = 1536 << 20   # rotating buffer sets: at least 6x the 256 MB MALL
-MODE_NAMES = {0: "fp8_static", 1: "fp8_per_token", 2: "fp8_per_group", 3: "fp4_block16"}
+MODE_NAMES = {0: "fp8_static", 1: "fp8_per_token", 2: "fp8_per_group", 3: "fp4_block16",
+              4: "bf16_padded"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -53,7 +54,9 @@ def workload_spec(args):
     wl = synth.WORKLOADS[int(args.workload[1:])]
     T = args.tokens or max(wl.tokens)
     H = args.hidden or (7168 if wl.index == 3 else wl.hidden[0])
-    if wl.kind == "act":
+    if wl.kind == "pad":
+        mode = 4  # not a quantization scheme: the normalized row as padded bf16
+    elif wl.kind == "act":
         mode = {"static": B.RMSQ_FP8_STATIC, "token": B.RMSQ_FP8_TOKEN,
                 "group": B.RMSQ_FP8_GROUP, "fp4": B.RMSQ_FP4_BLOCK16}[args.quant]
     else:
@@ -71,6 +74,8 @@ def workload_spec(args):
 def algorithmic_bytes(mode, T, H, G, flags, residual, kind="norm"):
     """Bytes one launch must move: every input read once, every output written once, the
     weight once per launch.  For SiLU+Mul (kind "act") H is I and the input is [T, 2I] bf16."""
+    if kind == "pad":  # H here is the padded row length of the bf16 output; see gpu_leg
+        raise ValueError("use pad_bytes")
     if kind == "act":
         rd = 4 * T * H + (4 if mode in (0, 3) else 0)
     else:
@@ -82,6 +87,14 @@ def algorithmic_bytes(mode, T, H, G, flags, residual, kind="norm"):
         wr += T * (H // G) * (1 if flags & 4 else 4)
     elif mode == 3:
         wr += T * (H // 16)
+    return rd, wr
+
+
+def pad_bytes(T, H, ld, residual=True):
+    """Residual add + RMSNorm -> padded bf16: read x (and the residual) and the weight once,
+    write the new residual and the padded output rows."""
+    rd = 2 * T * H + (2 * T * H if residual else 0) + 2 * H
+    wr = (2 * T * H if residual else 0) + 2 * T * ld
     return rd, wr
 
 
@@ -107,22 +120,28 @@ def gpu_leg(args, wl, T, H, mode, G, flags):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     act = wl.kind == "act"
+    pad = wl.kind == "pad"
+    ld = -(-H // wl.pad_multiple) * wl.pad_multiple if pad else 0
     if act:
         x, r, w = synth.make_act_inputs(wl.index, T, H), None, torch.zeros(8, dtype=torch.bfloat16)
     else:
         x, r, w = synth.make_inputs(wl.index, T, H)
     residual = r is not None
-    rd, wr = algorithmic_bytes(mode, T, H, G, flags, residual, wl.kind)
+    if pad:
+        rd, wr = pad_bytes(T, H, ld, residual)
+    else:
+        rd, wr = algorithmic_bytes(mode, T, H, G, flags, residual, wl.kind)
     set_bytes = rd + wr
     nsets = max(2, math.ceil(FOOTPRINT_BYTES / set_bytes))
     xd, rdv, wd = x.to(dev), (r.to(dev) if residual else None), w.to(dev)
-    sshape, sdt = scale_layout(mode, T, H, G, flags)
+    sshape, sdt = scale_layout(mode, T, H, G, flags) if not pad else (None, None)
     qcols = H // 2 if mode == 3 else H
     sets = []
     for _ in range(nsets):
         s = {"x": xd.clone(), "r": rdv.clone() if residual else None,
              "ro": torch.empty_like(xd) if residual else None,
-             "q": torch.empty((T, qcols), dtype=torch.uint8, device=dev),
+             "q": (torch.empty((T, ld), dtype=torch.bfloat16, device=dev) if pad else
+                   torch.empty((T, qcols), dtype=torch.uint8, device=dev)),
              "s": torch.empty(sshape, dtype=sdt, device=dev) if sshape else None}
         sets.append(s)
     wd = wd.contiguous()
@@ -130,7 +149,9 @@ def gpu_leg(args, wl, T, H, mode, G, flags):
     # per-tensor input scale: the static scale from the workload's warm-up batch (max|y|/448,
     # computed on the GPU with the per-token mode), the FP4 global scale 448*6/max|y|
     scale_in = None
-    if act and mode in (0, 3):
+    if pad:
+        pass
+    elif act and mode in (0, 3):
         # static scale: max|a|/448 of the warm-up batch; FP4 global scale 448*6/max|a| of the
         # batch itself -- both from the GPU's per-token launch
         src = synth.make_act_warmup(wl.index, H).to(dev) if mode == 0 else xd
@@ -165,6 +186,8 @@ def gpu_leg(args, wl, T, H, mode, G, flags):
         launch = B.rmsq_launch(*(vals + [0] * (4 - len(vals))))
     if launch:
         shape = launch.as_tuple()
+    elif pad:
+        shape = B.rmsq_query_launch(0, T, ld, 0, residual)[0].as_tuple()
     elif act:
         shape = B.rmsq_silu_mul_query_launch(mode, T, H, 16 if mode == 3 else G)[0].as_tuple()
     else:
@@ -181,7 +204,16 @@ def gpu_leg(args, wl, T, H, mode, G, flags):
     sh = stream.cuda_stream
     lref = ctypes.byref(launch) if launch is not None else None
     status = []
-    if act:
+    if pad:
+        argsets = [(ptr(s["x"]), ptr(s["r"]), wd.data_ptr(), float(wl.eps), ptr(s["q"]),
+                    ptr(s["ro"]), T, H, ld) for s in sets]
+
+        def launch_on(a, hs):
+            return lib.rmsq_rms_norm_pad_ex(*a, lref, None, None, hs)
+
+        def launch_timed(a, e0, e1, hs):
+            return lib.rmsq_rms_norm_pad_ex(*a, lref, e0, e1, hs)
+    elif act:
         argsets = [(ptr(s["x"]), mode, ptr(scale_in), ptr(s["q"]), ptr(s["s"]), T, H, G, flags, 0)
                    for s in sets]
 
@@ -311,6 +343,21 @@ def cpu_leg(wl, T, H, mode, G, flags, budget_s=12.0):
                 "sample": f"first {rows} of {T} rows ({rows * H} outputs), {dt:.1f} s, "
                           f"single thread, {os.cpu_count()} host CPUs visible",
                 "tokens_per_s": rows / dt}
+    if wl.kind == "pad":
+        ld = -(-H // wl.pad_multiple) * wl.pad_multiple
+        x, r, w = synth.make_inputs(wl.index, T, H)
+        xb, rb, wb = synth.bits(x), synth.bits(r), synth.bits(w)
+        rows = 0
+        t0 = time.perf_counter()
+        while rows < T and time.perf_counter() - t0 < budget_s:
+            n = min(64, T - rows)
+            O.rms_norm_pad(xb[rows:rows + n], rb[rows:rows + n], wb, wl.eps, ld)
+            rows += n
+        dt = time.perf_counter() - t0
+        rd, wr = pad_bytes(rows, H, ld)
+        return {"value": (rd + wr) / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"first {rows} of {T} rows, {dt:.1f} s, single thread, "
+                          f"{os.cpu_count()} host CPUs visible", "tokens_per_s": rows / dt}
     x, r, w = synth.make_inputs(wl.index, T, H)
     xb, rb, wb = synth.bits(x), (synth.bits(r) if r is not None else None), synth.bits(w)
     if mode == 0:
@@ -435,9 +482,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="w1", choices=["w0", "w1", "w2", "w3", "w4", "w5"],
+    ap.add_argument("--workload", default="w1", choices=["w0", "w1", "w2", "w3", "w4", "w5", "w6"],
                     help="w0-w4: (residual add ->) RMSNorm -> quant workloads; w5: SiLU+Mul -> "
-                         "quant (default w1: add+RMSNorm -> FP8 static, 4096 x 4096)")
+                         "quant; w6: add+RMSNorm -> padded bf16 (default w1: add+RMSNorm -> FP8 "
+                         "static, 4096 x 4096)")
     ap.add_argument("--quant", default="static", choices=["static", "token", "group", "fp4"],
                     help="quantization scheme of the SiLU+Mul workload (w5)")
     ap.add_argument("--tokens", type=int, default=0)
@@ -509,7 +557,9 @@ def main():
                         f"{f' G={G}' if mode == 2 else ''}{f' flags={flags}' if flags else ''}",
             "tokens": T, "hidden": H, "mode": MODE_NAMES[mode], "group_size": G,
             "flags": flags, "residual": wl.residual, "eps": wl.eps,
-            "io": "bf16 in; " + ("e2m1 + e4m3 block scales out" if mode == 3 else "e4m3fn out"),
+            "io": "bf16 in; " + {3: "e2m1 + e4m3 block scales out",
+                                 4: f"bf16 out, rows padded to a multiple of {wl.pad_multiple}"
+                                 }.get(mode, "e4m3fn out"),
             "launch": {"threads_per_row": g["launch"][0], "chunks_per_thread": g["launch"][1],
                        "rows_per_block": g["launch"][2], "options": g["launch"][3]},
             "rotating_sets": g["sets"], "parallelism": "single GPU",

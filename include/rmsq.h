@@ -164,6 +164,36 @@ RMSQ_API int rmsq_fused_timed(const void* x, const void* residual, const void* w
                               void* start_event, void* stop_event, void* stream);
 
 /*
+ * rmsq_rms_norm_pad -- (residual add ->) RMSNorm -> bf16 output in a padded row layout, in one
+ * launch (vLLM docs "Fusion torch.compile passes", section "RMSNorm + padding
+ * (fuse_act_padding)": the residual add and RMSNorm fused with padding the hidden dimension --
+ * 2880 for the model named there -- to the multiple a downstream GEMM needs).
+ *
+ *  x, residual, weight, eps, residual_out, tokens, hidden
+ *               exactly as for rmsq_fused (residual NULL: plain RMSNorm).
+ *  out          [T, out_ld] bf16, 16-byte aligned: out[t, i] = bf16(y_i) (round to nearest
+ *               even) for i < H and 0 for H <= i < out_ld.  Must not overlap any input or
+ *               residual_out.
+ *  out_ld       the padded row length: H <= out_ld <= RMSQ_MAX_HIDDEN, out_ld % 8 == 0.
+ * Returns RMSQ_OK or a negative status.
+ */
+RMSQ_API int rmsq_rms_norm_pad(const void* x, const void* residual, const void* weight,
+                               float eps, void* out, void* residual_out, int64_t tokens,
+                               int64_t hidden, int64_t out_ld, void* stream);
+
+/* rmsq_rms_norm_pad with an explicit launch shape (NULL: the default for a row of out_ld
+ * elements; a shape must cover out_ld) and optional dispatch-stamped events. */
+RMSQ_API int rmsq_rms_norm_pad_ex(const void* x, const void* residual, const void* weight,
+                                  float eps, void* out, void* residual_out, int64_t tokens,
+                                  int64_t hidden, int64_t out_ld, const rmsq_launch* launch,
+                                  void* start_event, void* stop_event, void* stream);
+
+/* Host-only argument check of rmsq_rms_norm_pad (no HIP call, no dereference). */
+RMSQ_API int rmsq_rms_norm_pad_validate(const void* x, const void* residual, const void* weight,
+                                        float eps, const void* out, const void* residual_out,
+                                        int64_t tokens, int64_t hidden, int64_t out_ld);
+
+/*
  * rmsq_silu_mul_quant -- SiLU+Mul -> quantization in one launch (vLLM docs "Fusion
  * torch.compile passes", section "SiLU+Mul + quantization (fuse_act_quant)": the gated
  * up-projection activation fused with the quantization that follows, so the full-precision

@@ -6,7 +6,8 @@ the binding raises -- there is no fallback path.
 
 Function names match the C ABI (rmsq_fused, rmsq_fused_with_launch, rmsq_fused_timed,
 rmsq_silu_mul_quant, rmsq_silu_mul_quant_ex, rmsq_silu_mul_quant_validate,
-rmsq_silu_mul_query_launch, rmsq_validate,
+rmsq_silu_mul_query_launch, rmsq_rms_norm_pad, rmsq_rms_norm_pad_ex, rmsq_rms_norm_pad_validate,
+rmsq_validate,
 rmsq_query_launch, rmsq_block_to_rowblock, rmsq_convert, rmsq_status_string,
 rmsq_abi_version).  A few allocating helpers named after the fused ops of the vLLM fusion
 pages (rms_norm_static_fp8_quant, fused_add_rms_norm_static_fp8_quant,
@@ -68,6 +69,13 @@ def lib():
         L.rmsq_fused_timed.restype = i32
         L.rmsq_validate.argtypes = fused_args
         L.rmsq_validate.restype = i32
+        pad_args = [p, p, p, f32, p, p, i64, i64, i64]
+        L.rmsq_rms_norm_pad.argtypes = pad_args + [p]
+        L.rmsq_rms_norm_pad.restype = i32
+        L.rmsq_rms_norm_pad_ex.argtypes = pad_args + [C.POINTER(rmsq_launch), p, p, p]
+        L.rmsq_rms_norm_pad_ex.restype = i32
+        L.rmsq_rms_norm_pad_validate.argtypes = pad_args
+        L.rmsq_rms_norm_pad_validate.restype = i32
         act_args = [p, i32, p, p, p, i64, i64, i32, u32, i64]
         L.rmsq_silu_mul_quant.argtypes = act_args + [p]
         L.rmsq_silu_mul_quant.restype = i32
@@ -169,6 +177,32 @@ def rmsq_fused_timed(x, residual, weight, eps, mode, scale_in, out_q, out_scales
     if check:
         _check(st, "rmsq_fused_timed")
     return st
+
+
+def rmsq_rms_norm_pad(x, residual, weight, eps, out, residual_out, tokens=None, hidden=None,
+                      out_ld=None, stream=None, launch=None, start_event=None, stop_event=None,
+                      check=True) -> int:
+    """(Residual add ->) RMSNorm -> bf16 out [T, out_ld] with zero padding columns."""
+    T = x.shape[0] if tokens is None else tokens
+    H = x.shape[-1] if hidden is None else hidden
+    ld = out.shape[-1] if out_ld is None else out_ld
+    args = (_ptr(x), _ptr(residual), _ptr(weight), float(eps), _ptr(out), _ptr(residual_out),
+            int(T), int(H), int(ld))
+    if launch is None and start_event is None and stop_event is None:
+        st = lib().rmsq_rms_norm_pad(*args, _stream(stream))
+    else:
+        st = lib().rmsq_rms_norm_pad_ex(*args, None if launch is None else C.byref(launch),
+                                        start_event, stop_event, _stream(stream))
+    if check:
+        _check(st, "rmsq_rms_norm_pad")
+    return st
+
+
+def rmsq_rms_norm_pad_validate(x, residual, weight, eps, out, residual_out, tokens, hidden,
+                               out_ld) -> int:
+    """Host-only argument check; pointers are plain integers (or None)."""
+    return lib().rmsq_rms_norm_pad_validate(x, residual, weight, float(eps), out, residual_out,
+                                            int(tokens), int(hidden), int(out_ld))
 
 
 def rmsq_silu_mul_quant(x, mode, scale_in, out_q, out_scales, tokens=None, inter=None,
@@ -325,3 +359,14 @@ def silu_and_mul_quant(x, mode, scale=None, group_size=0, col_major=False, e8m0=
                         group_size=group_size, flags=flags,
                         scale_ld=scale_ld if col_major else 0)
     return q, s
+
+
+def fused_add_rms_norm_pad(x, residual, weight, eps, multiple=256, inplace=True):
+    """(out [T, H padded up to `multiple`] bf16 with zero padding, residual_out): residual add
+    + RMSNorm with the hidden dimension padded for a downstream GEMM."""
+    T, H = x.shape
+    ld = -(-H // multiple) * multiple
+    out = torch.empty((T, ld), dtype=torch.bfloat16, device=x.device)
+    rout = None if residual is None else (residual if inplace else torch.empty_like(residual))
+    rmsq_rms_norm_pad(x, residual, weight, eps, out, rout)
+    return out, rout

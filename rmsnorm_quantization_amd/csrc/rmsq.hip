@@ -271,6 +271,68 @@ int fused_impl(const void* x, const void* res, const void* w, float eps, int mod
                        stop_event);
 }
 
+// ---- residual add + RMSNorm -> padded bf16 --------------------------------------------------
+int validate_pad(const void* x, const void* res, const void* w, float eps, const void* out,
+                 const void* res_out, int64_t T, int64_t H, int64_t out_ld) {
+  if (T < 0 || T > 0x7FFFFFFFLL) return RMSQ_EINVAL;
+  if (H < 8 || H > RMSQ_MAX_HIDDEN || (H % 8) != 0) return RMSQ_EINVAL;
+  if (out_ld < H || out_ld > RMSQ_MAX_HIDDEN || (out_ld % 8) != 0) return RMSQ_EINVAL;
+  if (!(eps > 0.0f) || !std::isfinite(eps)) return RMSQ_EINVAL;
+  if (T == 0) return RMSQ_OK;
+  if (!x || !w || !out) return RMSQ_EINVAL;
+  if ((res == nullptr) != (res_out == nullptr)) return RMSQ_EINVAL;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(out, 16)) return RMSQ_EALIGN;
+  if (res && (!aligned(res, 16) || !aligned(res_out, 16))) return RMSQ_EALIGN;
+  const size_t act = (size_t)T * (size_t)H * 2;
+  Span outs[2] = {span(out, (size_t)T * (size_t)out_ld * 2), Span{0, 0}};
+  int nout = 1;
+  if (res_out) outs[nout++] = span(res_out, act);
+  const Span ins[2] = {span(x, act), span(w, (size_t)H * 2)};
+  int st = check_aliasing(outs, nout, ins, 2);
+  if (st != RMSQ_OK) return st;
+  if (res) {
+    const Span sr = span(res, act);
+    if (overlap(outs[0], sr)) return RMSQ_EALIAS;
+    if (res_out != res && overlap(span(res_out, act), sr)) return RMSQ_EALIAS;
+  }
+  return RMSQ_OK;
+}
+
+int pad_impl(const void* x, const void* res, const void* w, float eps, void* out, void* res_out,
+             int64_t T, int64_t H, int64_t out_ld, const rmsq_launch* launch, void* start_event,
+             void* stop_event, void* stream) {
+  int st = validate_pad(x, res, w, eps, out, res_out, T, H, out_ld);
+  if (st != RMSQ_OK) return st;
+  const rmsq_launch l = launch ? *launch : default_launch(out_ld);
+  if (!valid_launch(l, out_ld)) return RMSQ_EINVAL;  // the launch covers the padded row
+  if (T == 0) return RMSQ_OK;
+  st = check_device();
+  if (st != RMSQ_OK) return st;
+  const void* fn = res ? pick_vpt<kModeBf16Pad, true, 0, false>(l.chunks_per_thread)
+                       : pick_vpt<kModeBf16Pad, false, 0, false>(l.chunks_per_thread);
+  if (!fn) return RMSQ_EINVAL;
+  const int64_t nblk = (T + l.rows_per_block - 1) / l.rows_per_block;
+  KArgs a;
+  a.x = static_cast<const uint16_t*>(x);
+  a.res = static_cast<const uint16_t*>(res);
+  a.w = static_cast<const uint16_t*>(w);
+  a.res_out = static_cast<uint16_t*>(res_out);
+  a.q = static_cast<uint8_t*>(out);
+  a.scales = nullptr;
+  a.scale_in = nullptr;
+  a.T = T;
+  a.H = H;
+  a.ld = out_ld;
+  a.eps = eps;
+  a.flags = 0;
+  a.tpr = l.threads_per_row;
+  a.rpb = l.rows_per_block;
+  a.nblk = (uint32_t)nblk;
+  a.xcd_ranges = (l.options & RMSQ_LAUNCH_XCD_RANGES) ? 1 : 0;
+  return launch_kernel(fn, nblk, l.threads_per_row * l.rows_per_block, &a, stream, start_event,
+                       stop_event);
+}
+
 // ---- SiLU+Mul -> quantization --------------------------------------------------------------
 template <int MODE, int GS, bool EXACT>
 const void* pick_act_vpt(int vpt) {
@@ -436,6 +498,27 @@ int rmsq_validate(const void* x, const void* residual, const void* weight, float
                   unsigned flags, int64_t scale_ld) {
   return validate(x, residual, weight, eps, mode, scale_in, out_q, out_scales, residual_out,
                   tokens, hidden, group_size, flags, scale_ld);
+}
+
+int rmsq_rms_norm_pad(const void* x, const void* residual, const void* weight, float eps,
+                      void* out, void* residual_out, int64_t tokens, int64_t hidden,
+                      int64_t out_ld, void* stream) {
+  return pad_impl(x, residual, weight, eps, out, residual_out, tokens, hidden, out_ld, nullptr,
+                  nullptr, nullptr, stream);
+}
+
+int rmsq_rms_norm_pad_ex(const void* x, const void* residual, const void* weight, float eps,
+                         void* out, void* residual_out, int64_t tokens, int64_t hidden,
+                         int64_t out_ld, const rmsq_launch* launch, void* start_event,
+                         void* stop_event, void* stream) {
+  return pad_impl(x, residual, weight, eps, out, residual_out, tokens, hidden, out_ld, launch,
+                  start_event, stop_event, stream);
+}
+
+int rmsq_rms_norm_pad_validate(const void* x, const void* residual, const void* weight, float eps,
+                               const void* out, const void* residual_out, int64_t tokens,
+                               int64_t hidden, int64_t out_ld) {
+  return validate_pad(x, residual, weight, eps, out, residual_out, tokens, hidden, out_ld);
 }
 
 int rmsq_silu_mul_quant(const void* x, int mode, const float* scale_in, void* out_q,

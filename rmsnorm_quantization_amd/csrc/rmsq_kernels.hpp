@@ -28,6 +28,9 @@
 namespace rmsq {
 
 constexpr int kMaxWavesPerBlock = 16;
+// Internal mode of fused_kernel: the normalized row rounded to bf16 and written with a padded
+// row stride (ld), the padding columns zero.  Not a quantization scheme, so not in rmsq_mode.
+constexpr int kModeBf16Pad = 4;
 
 struct KArgs {
   const uint16_t* x;
@@ -157,6 +160,21 @@ __device__ __forceinline__ void quantize_store(const YF& Y, const bool (&ok)[VPT
         }
       }
     }
+  } else if constexpr (MODE == kModeBf16Pad) {
+    // bf16 row of n values at a stride of ld elements; chunks n/8 .. ld/8-1 are zero padding.
+    // The launch covers ld/8 chunks per row (ok[] marks the chunks below n).
+    const uint32_t nchp = (uint32_t)(o.ld >> 3);
+    u32x4* orow = reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(o.q) + o.obase);
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const uint32_t c = o.lr + (uint32_t)(k * o.tpr);
+      u32x4 v = (u32x4){0u, 0u, 0u, 0u};
+      if (ok[k]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = pack_bf16x2(Y(k, 2 * j), Y(k, 2 * j + 1));
+      }
+      if (o.row_ok && c < nchp) __builtin_nontemporal_store(v, orow + c);
+    }
   } else {  // RMSQ_FP4_BLOCK16
     const float gs = scale_val;
 #pragma unroll
@@ -280,7 +298,7 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
   o.scales = a.scales;
   o.row = row;
   o.row_ok = row_ok;
-  o.obase = base;
+  o.obase = (MODE == kModeBf16Pad) ? (size_t)(row_ok ? row : 0) * (size_t)a.ld : base;
   o.n = a.H;
   o.ld = a.ld;
   o.flags = a.flags;

@@ -2,9 +2,9 @@
 
 Both the GPU path and the CPU oracle are fed from here.  Values are drawn in float32 from a
 seeded torch CPU generator and cast to bf16 by torch; nothing in this module normalizes,
-scales or quantizes.  Six workloads are defined, matching the shapes and distributions of the
-fused RMSNorm + quantization (0-4) and SiLU+Mul + quantization (5) workloads this library is
-measured on:
+scales or quantizes.  Seven workloads are defined, matching the shapes and distributions of
+the fused RMSNorm + quantization (0-4), SiLU+Mul + quantization (5) and RMSNorm + padding (6)
+workloads this library is measured on:
 
   0  RMSNorm -> FP8 static        T=16,  H=4096, x~N(0,1), w~U(0.5,1.5), eps 1e-5, scale 0.05
   1  add+RMSNorm -> FP8 static    T in {1,64,512,4096}, H=4096, x,r~N(0,1), eps 1e-5,
@@ -20,6 +20,10 @@ measured on:
                                   Llama-3.1-8B model the pages use in their examples);
                                   x = [gate | up] ~N(0,1), [T, 2I]; static scale from a fixed
                                   512 x 2I warm-up batch, FP4 global scale 448*6/max|a|
+
+  6  add+RMSNorm -> padded bf16    T in {1,256,4096}, H=2880 (the hidden size the pages name for
+                                  this fusion) padded to a multiple of 256 (3072), x,r~N(0,1),
+                                  eps 1e-5
 
 Seeds: 1000*workload + tensor id (x=1, residual=2, weight=3, outlier channels=4,
 warm-up x=5, warm-up residual=6).  Unless stated otherwise, weight ~ U(0.5, 1.5) and the
@@ -45,7 +49,9 @@ class Workload:
     static_scale: Optional[float] = None   # fixed per-tensor scale, if the workload fixes one
     warmup_shape: Optional[Tuple[int, int]] = None  # batch the static scale is derived from
     group_sizes: Tuple[int, ...] = field(default_factory=tuple)
-    kind: str = "norm"   # "norm": (residual add ->) RMSNorm -> quant; "act": SiLU+Mul -> quant
+    kind: str = "norm"   # "norm": (residual add ->) RMSNorm -> quant; "act": SiLU+Mul -> quant;
+    #                      "pad": (residual add ->) RMSNorm -> padded bf16
+    pad_multiple: int = 0
 
 
 WORKLOADS = {
@@ -59,6 +65,8 @@ WORKLOADS = {
     4: Workload(4, "add_rmsnorm_fp4_block16", (1, 32, 256, 4096), (2048,), 1e-6, True),
     5: Workload(5, "silu_mul_quant", (1, 256, 4096), (14336,), 0.0, False,
                 warmup_shape=(512, 14336), group_sizes=(128, 64), kind="act"),
+    6: Workload(6, "add_rmsnorm_pad", (1, 256, 4096), (2880,), 1e-5, True, kind="pad",
+                pad_multiple=256),
 }
 
 X, RESIDUAL, WEIGHT, OUTLIERS, WARM_X, WARM_R = 1, 2, 3, 4, 5, 6

@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("rmsq_fused", "rmsq_fused_with_launch", "rmsq_fused_timed", "rmsq_validate",
               "rmsq_silu_mul_quant", "rmsq_silu_mul_quant_ex", "rmsq_silu_mul_quant_validate",
-              "rmsq_silu_mul_query_launch",
+              "rmsq_silu_mul_query_launch", "rmsq_rms_norm_pad", "rmsq_rms_norm_pad_ex",
+              "rmsq_rms_norm_pad_validate",
               "rmsq_query_launch",
               "rmsq_block_to_rowblock", "rmsq_convert", "rmsq_status_string",
               "rmsq_abi_version"):
@@ -200,3 +201,35 @@ def test_act_query_launch(B):
         l, grid = B.rmsq_silu_mul_query_launch(mode, 100, 14336, G)
         assert l.as_tuple() == B.rmsq_query_launch(mode, 100, 14336, G)[0].as_tuple()
         assert grid == -(-100 // l.rows_per_block)
+
+
+# ------------------------------------------------------------------ RMSNorm -> padded bf16
+def VP(B, x=X, r=R, w=W, eps=1e-6, out=Q, ro=RO, t=T, h=H, ld=H + 64):
+    return B.rmsq_rms_norm_pad_validate(x, r, w, eps, out, ro, t, h, ld)
+
+
+def test_pad_valid_calls(B):
+    assert VP(B) == B.RMSQ_OK
+    assert VP(B, ld=H) == B.RMSQ_OK
+    assert VP(B, r=None, ro=None) == B.RMSQ_OK
+    assert VP(B, ro=R) == B.RMSQ_OK
+    assert VP(B, t=0, x=None, out=None) == B.RMSQ_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ld=H - 8), "EINVAL"), (dict(ld=H + 4), "EINVAL"), (dict(ld=65536 + 8), "EINVAL"),
+    (dict(h=12), "EINVAL"), (dict(eps=0.0), "EINVAL"), (dict(t=-1), "EINVAL"),
+    (dict(out=None), "EINVAL"), (dict(ro=None), "EINVAL"), (dict(x=None), "EINVAL"),
+    (dict(out=Q + 8), "EALIGN"), (dict(x=X + 2), "EALIGN"), (dict(ro=RO + 4), "EALIGN"),
+    (dict(out=X), "EALIAS"), (dict(out=W), "EALIAS"), (dict(out=R), "EALIAS"),
+    (dict(ro=Q), "EALIAS"), (dict(ro=X + 16), "EALIAS"), (dict(ro=R + 16), "EALIAS"),
+    # out spans T * ld * 2 bytes
+    (dict(ro=Q + T * (H + 64) * 2 - 16), "EALIAS"),
+])
+def test_pad_bad_arguments(B, kw, status):
+    code = getattr(B, "RMSQ_" + status)
+    assert VP(B, **kw) == code
+    assert B.lib().rmsq_rms_norm_pad(kw.get("x", X), kw.get("r", R), kw.get("w", W),
+                                     kw.get("eps", 1e-6), kw.get("out", Q), kw.get("ro", RO),
+                                     kw.get("t", T), kw.get("h", H), kw.get("ld", H + 64),
+                                     None) == code

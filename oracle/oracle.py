@@ -57,6 +57,10 @@ def lib():
         L.orc_silu_mul_quant.restype = C.c_int
         L.orc_rms_norm_pad.argtypes = [p, p, p, C.c_float, p, p, i64, i64, i64]
         L.orc_rms_norm_pad.restype = C.c_int
+        L.orc_rope_cache.argtypes = [p, i64, i64, C.c_double]
+        L.orc_rope_cache.restype = None
+        L.orc_qk_norm_rope.argtypes = [p, p, p, p, p, C.c_float, i64, i64, i64, i64, i64, C.c_int]
+        L.orc_qk_norm_rope.restype = C.c_int
         L.orc_fused.argtypes = [p, p, p, C.c_float, C.c_int, C.c_float, p, p, p,
                                 i64, i64, C.c_int, C.c_uint, i64, p]
         L.orc_fused.restype = C.c_int
@@ -268,3 +272,26 @@ def rms_norm_pad(x, residual, weight, eps, out_ld):
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (rc={rc})")
     return out, rout
+
+
+# ---------------------------------------------------------------- QK-norm + RoPE
+def rope_cache(max_pos, D, base=1_000_000.0):
+    """[max_pos, D] f32: cos | sin of p * base^(-2i/D)."""
+    cache = np.empty((max_pos, D), np.float32)
+    lib().orc_rope_cache(_ptr(cache), int(max_pos), int(D), float(base))
+    return cache
+
+
+def qk_norm_rope(qkv, qw, kw, cache, pos, eps, Hq, Hkv, D, neox=True):
+    """Returns a new [T, (Hq+2Hkv)*D] bf16-bit array (the input is not modified)."""
+    out = np.array(qkv, np.uint16, copy=True, order="C")
+    T = out.shape[0]
+    qw = _c(qw, np.uint16)
+    kw = _c(kw, np.uint16)
+    cache = _c(cache, np.float32)
+    pos = _c(pos, np.int64)
+    rc = lib().orc_qk_norm_rope(_ptr(out), _ptr(qw), _ptr(kw), _ptr(cache), _ptr(pos), float(eps),
+                                T, int(Hq), int(Hkv), int(D), cache.shape[0], int(bool(neox)))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (rc={rc})")
+    return out

@@ -367,6 +367,54 @@ int orc_rms_norm_pad(const uint16_t* x, const uint16_t* residual, const uint16_t
   return 0;
 }
 
+/* ------------------------------------------------------------------ QK-norm + RoPE */
+void orc_rope_cache(float* cache, int64_t max_pos, int64_t D, double base) {
+  for (int64_t p = 0; p < max_pos; ++p)
+    for (int64_t i = 0; i < D / 2; ++i) {
+      double theta = (double)p * pow(base, -2.0 * (double)i / (double)D);
+      cache[p * D + i] = (float)cos(theta);
+      cache[p * D + D / 2 + i] = (float)sin(theta);
+    }
+}
+
+static void rotate_pair(float a, float b, float c, float s, float* out_a, float* out_b) {
+  float ac = a * c, bs = b * s, bc = b * c, as = a * s;
+  *out_a = ac - bs;
+  *out_b = bc + as;
+}
+
+int orc_qk_norm_rope(uint16_t* qkv, const uint16_t* qw, const uint16_t* kw, const float* cache,
+                     const int64_t* pos, float eps, int64_t T, int64_t Hq, int64_t Hkv,
+                     int64_t D, int64_t max_pos, int neox) {
+  if (T < 0 || Hq < 0 || Hkv < 0 || D < 2 || (D % 2) || !qkv || !qw || !kw || !cache || !pos)
+    return -1;
+  if (!(eps >= 0.0f) || isinf(eps)) return -1;
+  float* y = (float*)malloc((size_t)D * sizeof(float));
+  float* o = (float*)malloc((size_t)D * sizeof(float));
+  if (!y || !o) {
+    free(y);
+    free(o);
+    return -1;
+  }
+  const int64_t width = (Hq + 2 * Hkv) * D;
+  for (int64_t t = 0; t < T; ++t) {
+    if (pos[t] < 0 || pos[t] >= max_pos) continue;
+    const float* cs = cache + pos[t] * D;
+    for (int64_t hd = 0; hd < Hq + Hkv; ++hd) {
+      uint16_t* head = qkv + t * width + hd * D;
+      orc_normalize(head, hd < Hq ? qw : kw, orc_inv_rms(head, D, eps), y, D);
+      for (int64_t i = 0; i < D / 2; ++i) {
+        int64_t ia = neox ? i : 2 * i, ib = neox ? i + D / 2 : 2 * i + 1;
+        rotate_pair(y[ia], y[ib], cs[i], cs[D / 2 + i], &o[ia], &o[ib]);
+      }
+      for (int64_t i = 0; i < D; ++i) head[i] = orc_f32_to_bf16(o[i]);
+    }
+  }
+  free(y);
+  free(o);
+  return 0;
+}
+
 /* ------------------------------------------------------------------ SiLU+Mul -> quant */
 float orc_silu_mul(uint16_t g, uint16_t u) {
   double gd = (double)orc_bf16_to_f32(g), ud = (double)orc_bf16_to_f32(u);

@@ -106,6 +106,24 @@ int orc_rms_norm_pad(const uint16_t* x, const uint16_t* residual, const uint16_t
                      float eps, uint16_t* out, uint16_t* residual_out, int64_t T, int64_t H,
                      int64_t out_ld);
 
+/* ---- QK-norm + RoPE (vLLM docs "Fusion torch.compile passes", section "QK Norm + RoPE":
+ * for models with per-head Q/K normalization, the per-head RMSNorm of q and k fused with the
+ * rotary embedding that follows, on the packed qkv tensor). ----
+ * cache [max_pos, D] f32: cache[p, i] = cos(p * base^(-2i/D)), cache[p, D/2 + i] = sin(...),
+ * i < D/2, evaluated in binary64 and rounded once to f32. */
+void orc_rope_cache(float* cache, int64_t max_pos, int64_t D, double base);
+/* qkv [T, (Hq + 2 Hkv) * D] bf16, rewritten in place: for each q head (weight qw [D]) and each
+ * k head (weight kw [D]) of token t with 0 <= pos[t] < max_pos:
+ *   y = rmsnorm(head) exactly as orc_normalize after orc_inv_rms over the D values,
+ *   NeoX (neox != 0): pairs (i, i + D/2); GPT-J: pairs (2i, 2i + 1); with c, s the cache's
+ *   cos and sin of the pair's frequency i at position pos[t]:
+ *     out_a = a*c - b*s,  out_b = b*c + a*s   (each product rounded to f32, then the sum)
+ *   written back rounded to bf16.  v heads and out-of-range tokens are left unchanged.
+ * Returns 0, or -1 on an invalid argument (D even, D >= 2). */
+int orc_qk_norm_rope(uint16_t* qkv, const uint16_t* qw, const uint16_t* kw, const float* cache,
+                     const int64_t* pos, float eps, int64_t T, int64_t Hq, int64_t Hkv,
+                     int64_t D, int64_t max_pos, int neox);
+
 /* ---- SiLU+Mul -> quantization (vLLM docs "Fusion torch.compile passes", section "SiLU+Mul +
  * quantization (fuse_act_quant)": the gated up-projection activation silu_and_mul fused with the
  * quantization that follows; FP8 static per-tensor, FP8 dynamic per-group 128/64, FP4). ----

@@ -16,9 +16,11 @@ data.  Prints ONE JSON line:
                  copy's counters) when the committed counters match the current kernel source
   cpu_baseline   the CPU oracle on a bounded sample of the same workload, one core
 
-Other workloads (--workload w0..w5; w5 is SiLU+Mul -> quant with --quant
-static|token|group|fp4) and forced launch shapes (--launch tpr,vpt,rpb[,options]) are for
-exploration; only one GPU is supported (--gpus above 1 exits with a message).
+Other workloads (--workload w0..w7; w5 is SiLU+Mul -> quant with --quant
+static|token|group|fp4, w6 add+RMSNorm -> padded bf16, w7 QK-norm + RoPE) and forced launch
+shapes (--launch tpr,vpt,rpb[,options]; for w7 --launch heads_per_block,heads_per_lane) are
+for exploration;
+only one GPU is supported (--gpus above 1 exits with a message).
 """
 import argparse
 import hashlib
@@ -35,7 +37,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 FOOTPRINT_BYTES = 1536 << 20   # rotating buffer sets: at least 6x the 256 MB MALL
 MODE_NAMES = {0: "fp8_static", 1: "fp8_per_token", 2: "fp8_per_group", 3: "fp4_block16",
-              4: "bf16_padded"}
+              4: "bf16_padded", 5: "bf16_qk_norm_rope"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -54,7 +56,9 @@ def workload_spec(args):
     wl = synth.WORKLOADS[int(args.workload[1:])]
     T = args.tokens or max(wl.tokens)
     H = args.hidden or (7168 if wl.index == 3 else wl.hidden[0])
-    if wl.kind == "pad":
+    if wl.kind == "rope":
+        mode = 5  # not a quantization scheme: normalized and rotated heads, bf16 in place
+    elif wl.kind == "pad":
         mode = 4  # not a quantization scheme: the normalized row as padded bf16
     elif wl.kind == "act":
         mode = {"static": B.RMSQ_FP8_STATIC, "token": B.RMSQ_FP8_TOKEN,
@@ -96,6 +100,121 @@ def pad_bytes(T, H, ld, residual=True):
     rd = 2 * T * H + (2 * T * H if residual else 0) + 2 * H
     wr = (2 * T * H if residual else 0) + 2 * T * ld
     return rd, wr
+
+
+def rope_bytes(T, hq, hkv, D):
+    """QK-norm + RoPE: read and rewrite the q and k heads once, read both weights once per
+    launch, each token's position and its cos/sin cache row (D f32) once."""
+    qk = 2 * T * (hq + hkv) * D
+    return qk + 2 * 2 * D + 8 * T + 4 * D * T, qk
+
+
+def rope_cache(max_pos, D, base):
+    """The caller-built [max_pos, D] f32 cos | sin table (binary64, rounded once)."""
+    import torch
+
+    inv = base ** (-2.0 * torch.arange(D // 2, dtype=torch.float64) / D)
+    th = torch.arange(max_pos, dtype=torch.float64)[:, None] * inv[None, :]
+    return torch.cat([th.cos(), th.sin()], dim=1).float()
+
+
+def rope_leg(args, wl, T, D):
+    """GPU timing of QK-norm + RoPE, structured like gpu_leg."""
+    import ctypes
+
+    import torch
+
+    from rmsnorm_quantization_amd import binding as B
+    from rmsnorm_quantization_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    hq, hkv = wl.heads
+    qkv, qw, kw, pos = synth.make_rope_inputs(wl.index, T)
+    cache = rope_cache(wl.max_position, D, wl.rope_base).to(dev)
+    rd, wr = rope_bytes(T, hq, hkv, D)
+    qkv_bytes = qkv.numel() * 2
+    nsets = max(2, math.ceil(FOOTPRINT_BYTES / qkv_bytes))
+    qkv_d = qkv.to(dev)
+    sets = [qkv_d.clone() for _ in range(nsets)]
+    qw_d, kw_d, pos_d = qw.to(dev), kw.to(dev), pos.to(dev)
+    if args.launch:
+        hpb, hpl = (int(v) for v in args.launch.split(","))
+    else:
+        hpb, hpl, _ = B.rmsq_qk_norm_rope_query_launch(T, hq, hkv, D)
+    lib = B.lib()
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    status = []
+    argsets = [(q.data_ptr(), qw_d.data_ptr(), kw_d.data_ptr(), cache.data_ptr(),
+                pos_d.data_ptr(), float(wl.eps), T, hq, hkv, D, wl.max_position, 1, hpb, hpl)
+               for q in sets]
+
+    def launch(a, e0, e1, hs):
+        st = lib.rmsq_qk_norm_rope_ex(*a, e0, e1, hs)
+        if st:
+            status.append(st)
+
+    for i in range(args.warmup):
+        launch(argsets[i % nsets], None, None, sh)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        launch(argsets[i % nsets], None, None, sh)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    ms_per_step_graph = None
+    if args.graph:
+        g_ = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_, stream=torch.cuda.Stream()):
+            hs = torch.cuda.current_stream().cuda_stream
+            for i in range(args.steps):
+                launch(argsets[i % nsets], None, None, hs)
+        g_.replay()
+        torch.cuda.synchronize()
+        t0.record(stream)
+        g_.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms_per_step_graph = t0.elapsed_time(t1) / args.steps
+        del g_
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a_, b_ in evs:
+        a_.record(stream)
+        b_.record(stream)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        launch(argsets[i % nsets], evs[i][0].cuda_event, evs[i][1].cuda_event, sh)
+    torch.cuda.synchronize()
+    if status:
+        raise RuntimeError(f"rmsq_qk_norm_rope failed: {B.rmsq_status_string(status[0])}")
+    per = sorted(a.elapsed_time(b) for a, b in evs)
+    copy_gbs = copy_ceiling(dev, stream)
+    return {"ms_per_step": ms_per_step, "ms_per_step_graph": ms_per_step_graph,
+            "avg_launch_ms": sum(per) / len(per), "median_launch_ms": per[len(per) // 2],
+            "bytes": rd + wr, "read": rd, "write": wr, "sets": nsets, "launch": (hpb, hpl),
+            "copy_gbs": copy_gbs, "device": torch.cuda.get_device_name(dev)}
+
+
+def copy_ceiling(dev, stream):
+    """GB/s of a plain 256 MiB device copy (practical HBM ceiling, for context)."""
+    import torch
+
+    copy_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    copy_dst = torch.empty_like(copy_src)
+    for _ in range(3):
+        copy_dst.copy_(copy_src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    c0.record(stream)
+    for _ in range(10):
+        copy_dst.copy_(copy_src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    return 2 * copy_src.numel() * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
 
 
 def scale_layout(mode, T, H, G, flags):
@@ -290,19 +409,8 @@ def gpu_leg(args, wl, T, H, mode, G, flags):
     avg_launch_ms = sum(per) / len(per)
     med_launch_ms = per[len(per) // 2]
 
-    # a plain device copy of the same footprint, for context (practical HBM ceiling)
-    copy_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
-    copy_dst = torch.empty_like(copy_src)
-    for _ in range(3):
-        copy_dst.copy_(copy_src)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    c0.record(stream)
-    for _ in range(10):
-        copy_dst.copy_(copy_src)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbs = 2 * copy_src.numel() * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    # a plain device copy, for context (practical HBM ceiling)
+    copy_gbs = copy_ceiling(dev, stream)
 
     return {"ms_per_step": ms_per_step, "ms_per_step_graph": ms_per_step_graph,
             "avg_launch_ms": avg_launch_ms,
@@ -320,6 +428,23 @@ def cpu_leg(wl, T, H, mode, G, flags, budget_s=12.0):
     import oracle as O
     from rmsnorm_quantization_amd import synth
 
+    if wl.kind == "rope":
+        hq, hkv = wl.heads
+        qkv, qw, kw, pos = synth.make_rope_inputs(wl.index, T)
+        xb, qwb, kwb, posn = synth.bits(qkv), synth.bits(qw), synth.bits(kw), pos.numpy()
+        cache = O.rope_cache(wl.max_position, H, wl.rope_base)
+        rows = 0
+        t0 = time.perf_counter()
+        while rows < T and time.perf_counter() - t0 < budget_s:
+            n = min(64, T - rows)
+            O.qk_norm_rope(xb[rows:rows + n], qwb, kwb, cache, posn[rows:rows + n], wl.eps, hq,
+                           hkv, H)
+            rows += n
+        dt = time.perf_counter() - t0
+        rd, wr = rope_bytes(rows, hq, hkv, H)
+        return {"value": (rd + wr) / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"first {rows} of {T} tokens, {dt:.1f} s, single thread, "
+                          f"{os.cpu_count()} host CPUs visible", "tokens_per_s": rows / dt}
     if wl.kind == "act":
         xb = synth.bits(synth.make_act_inputs(wl.index, T, H))
         if mode == 0:
@@ -482,9 +607,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="w1", choices=["w0", "w1", "w2", "w3", "w4", "w5", "w6"],
+    ap.add_argument("--workload", default="w1", choices=["w0", "w1", "w2", "w3", "w4", "w5", "w6", "w7"],
                     help="w0-w4: (residual add ->) RMSNorm -> quant workloads; w5: SiLU+Mul -> "
-                         "quant; w6: add+RMSNorm -> padded bf16 (default w1: add+RMSNorm -> FP8 "
+                         "quant; w6: add+RMSNorm -> padded bf16; w7: QK-norm + RoPE (default w1: "
+                         "add+RMSNorm -> FP8 "
                          "static, 4096 x 4096)")
     ap.add_argument("--quant", default="static", choices=["static", "token", "group", "fp4"],
                     help="quantization scheme of the SiLU+Mul workload (w5)")
@@ -510,10 +636,16 @@ def main():
 
         wl, T, H, mode, G, flags = workload_spec(args)
         key = f"{args.workload}_T{T}_H{H}_{MODE_NAMES[mode]}_G{G}_f{flags}"
-        family = "silu_mul_kernel" if wl.kind == "act" else "fused_kernel"
+        family = {"act": "silu_mul_kernel", "rope": "qk_norm_rope_kernel"}.get(wl.kind,
+                                                                             "fused_kernel")
         md = args.summary_md or os.path.join(ROOT, "profiles", f"{family}_{key}.md")
-        title = (f"{family}, {wl.name}: {T} tokens x {'intermediate' if wl.kind == 'act' else 'hidden'}"
-                 f" {H}, {MODE_NAMES[mode]}{' G=%d' % G if mode == 2 else ''}")
+        if wl.kind == "rope":
+            title = (f"{family}, {wl.name}: {T} tokens x {wl.heads[0]} q + {wl.heads[1]} k heads "
+                     f"of {H} (qkv in place)")
+        else:
+            title = (f"{family}, {wl.name}: {T} tokens x "
+                     f"{'intermediate' if wl.kind == 'act' else 'hidden'}"
+                     f" {H}, {MODE_NAMES[mode]}{' G=%d' % G if mode == 2 else ''}")
         e = summarize(*args.summarize, key, title, [c.strip() for c in args.commands.split(";;")
                                                      if c.strip()], md)
         print(json.dumps(e))
@@ -527,7 +659,8 @@ def main():
         sys.exit(2)
 
     wl, T, H, mode, G, flags = workload_spec(args)
-    g = gpu_leg(args, wl, T, H, mode, G, flags)
+    rope = wl.kind == "rope"
+    g = rope_leg(args, wl, T, H) if rope else gpu_leg(args, wl, T, H, mode, G, flags)
     eager_gbs = g["bytes"] / (g["ms_per_step"] * 1e-3) / 1e9
     step_ms = g["ms_per_step_graph"] if g["ms_per_step_graph"] else g["ms_per_step"]
     gbs = g["bytes"] / (step_ms * 1e-3) / 1e9
@@ -549,7 +682,11 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": (f"{wl.name}: {T} tokens x intermediate {H} (input [T, 2I]), "
+            "workload": (f"{wl.name}: {T} tokens x ({wl.heads[0]} q + {wl.heads[1]} k + "
+                         f"{wl.heads[1]} v heads) x head size {H}, positions in "
+                         f"[0, {wl.max_position}), NeoX rotation, "
+                         if rope else
+                         f"{wl.name}: {T} tokens x intermediate {H} (input [T, 2I]), "
                          if wl.kind == "act" else
                          f"{wl.name}: {T} tokens x hidden {H}, "
                          f"{'residual add, ' if wl.residual else ''}")
@@ -558,10 +695,13 @@ def main():
             "tokens": T, "hidden": H, "mode": MODE_NAMES[mode], "group_size": G,
             "flags": flags, "residual": wl.residual, "eps": wl.eps,
             "io": "bf16 in; " + {3: "e2m1 + e4m3 block scales out",
-                                 4: f"bf16 out, rows padded to a multiple of {wl.pad_multiple}"
+                                 4: f"bf16 out, rows padded to a multiple of {wl.pad_multiple}",
+                                 5: "q and k heads rewritten in place (bf16), f32 cos/sin cache"
                                  }.get(mode, "e4m3fn out"),
-            "launch": {"threads_per_row": g["launch"][0], "chunks_per_thread": g["launch"][1],
-                       "rows_per_block": g["launch"][2], "options": g["launch"][3]},
+            "launch": ({"heads_per_block": g["launch"][0], "heads_per_lane": g["launch"][1]}
+                       if rope else
+                       {"threads_per_row": g["launch"][0], "chunks_per_thread": g["launch"][1],
+                        "rows_per_block": g["launch"][2], "options": g["launch"][3]}),
             "rotating_sets": g["sets"], "parallelism": "single GPU",
         },
         "tokens_per_s": round(T / (step_ms * 1e-3), 1),

@@ -228,6 +228,63 @@ RMSQ_API int rmsq_silu_mul_quant_validate(const void* x, int mode, const float* 
                                           int64_t tokens, int64_t inter, int group_size,
                                           unsigned flags, int64_t scale_ld);
 
+/*
+ * rmsq_qk_norm_rope -- per-head RMSNorm of the q and k heads followed by the rotary position
+ * embedding, in place, in one launch (vLLM docs "Fusion torch.compile passes", section "QK Norm
+ * + RoPE": for models that normalize Q and K per head, the split of the packed qkv tensor, the
+ * two RMSNorms and the rotary embedding become one kernel).
+ *
+ *  qkv          [T, (Hq + 2 Hkv) * D] bf16, 16-byte aligned, row t = Hq q heads, Hkv k heads,
+ *               Hkv v heads of D elements each.  Rewritten in place: every q head h becomes
+ *               rope(rmsnorm(h) * q_weight), every k head rope(rmsnorm(h) * k_weight), rounded
+ *               once to bf16 (nearest even) from f32; v heads are not touched.
+ *  rmsnorm      y_i = (h_i * inv) * w_i in f32, inv = 1/sqrt(sum h_i^2 / D + eps) from a
+ *               binary64 sum, rounded to f32 (as rmsq_fused, over one head of D elements).
+ *  q_weight, k_weight
+ *               [D] bf16, 16-byte aligned, read only.
+ *  cos_sin_cache
+ *               [max_position, D] f32, 16-byte aligned: row p = cos(p * f_i) for i < D/2, then
+ *               sin(p * f_i); the caller builds it (any base).  Read only.
+ *  positions    [T] int64, 8-byte aligned: token t uses cache row positions[t].  A token whose
+ *               position lies outside [0, max_position) is left entirely unchanged.
+ *  is_neox      nonzero: element i pairs with i + D/2 (half split); zero: 2i pairs with 2i + 1
+ *               (interleaved).  Pair (a, b) with frequency j becomes (a c - b s, b c + a s),
+ *               each product rounded to f32 before the sum.
+ *  tokens       T >= 0 (0 is a no-op); num_q_heads Hq >= 1, num_kv_heads Hkv >= 1,
+ *               (Hq + 2 Hkv) * D <= 2^20; head_dim D in {64, 128, 256}; max_position >= 1.
+ * qkv must not overlap the other arguments.  Returns RMSQ_OK or a negative status.
+ */
+RMSQ_API int rmsq_qk_norm_rope(void* qkv, const void* q_weight, const void* k_weight,
+                               const float* cos_sin_cache, const int64_t* positions, float eps,
+                               int64_t tokens, int num_q_heads, int num_kv_heads, int head_dim,
+                               int64_t max_position, int is_neox, void* stream);
+
+/* rmsq_qk_norm_rope with an explicit launch shape and optional dispatch-stamped events (as
+ * rmsq_fused_timed; NULL: none).  A head is held by D/16 lanes (16 elements each); a lane group
+ * serves heads_per_lane heads (1 to 6) and a workgroup heads_per_block heads of one token, a
+ * multiple of heads_per_lane, with (heads_per_block / heads_per_lane) * D/16 <= 1024 threads.
+ * Both 0: the default shape. */
+RMSQ_API int rmsq_qk_norm_rope_ex(void* qkv, const void* q_weight, const void* k_weight,
+                                  const float* cos_sin_cache, const int64_t* positions,
+                                  float eps, int64_t tokens, int num_q_heads, int num_kv_heads,
+                                  int head_dim, int64_t max_position, int is_neox,
+                                  int heads_per_block, int heads_per_lane, void* start_event,
+                                  void* stop_event, void* stream);
+
+/* Host-only argument check of rmsq_qk_norm_rope (no HIP call, no dereference). */
+RMSQ_API int rmsq_qk_norm_rope_validate(const void* qkv, const void* q_weight,
+                                        const void* k_weight, const float* cos_sin_cache,
+                                        const int64_t* positions, float eps, int64_t tokens,
+                                        int num_q_heads, int num_kv_heads, int head_dim,
+                                        int64_t max_position);
+
+/* The default launch shape of rmsq_qk_norm_rope (heads per workgroup, heads per lane group) and
+ * its grid size (tokens times the workgroups per token).  Host only; makes no HIP call.
+ * Returns RMSQ_OK or RMSQ_EINVAL. */
+RMSQ_API int rmsq_qk_norm_rope_query_launch(int64_t tokens, int num_q_heads, int num_kv_heads,
+                                            int head_dim, int* heads_per_block,
+                                            int* heads_per_lane, int64_t* grid);
+
 /* The launch shape rmsq_fused picks for (mode, T, H, group_size, residual?) and its grid size
  * (number of workgroups).  Host only; makes no HIP call.  Returns RMSQ_OK or RMSQ_EINVAL. */
 RMSQ_API int rmsq_query_launch(int mode, int64_t tokens, int64_t hidden, int group_size,

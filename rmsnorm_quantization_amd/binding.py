@@ -7,7 +7,8 @@ the binding raises -- there is no fallback path.
 Function names match the C ABI (rmsq_fused, rmsq_fused_with_launch, rmsq_fused_timed,
 rmsq_silu_mul_quant, rmsq_silu_mul_quant_ex, rmsq_silu_mul_quant_validate,
 rmsq_silu_mul_query_launch, rmsq_rms_norm_pad, rmsq_rms_norm_pad_ex, rmsq_rms_norm_pad_validate,
-rmsq_validate,
+rmsq_qk_norm_rope, rmsq_qk_norm_rope_ex, rmsq_qk_norm_rope_validate,
+rmsq_qk_norm_rope_query_launch, rmsq_validate,
 rmsq_query_launch, rmsq_block_to_rowblock, rmsq_convert, rmsq_status_string,
 rmsq_abi_version).  A few allocating helpers named after the fused ops of the vLLM fusion
 pages (rms_norm_static_fp8_quant, fused_add_rms_norm_static_fp8_quant,
@@ -83,6 +84,16 @@ def lib():
         L.rmsq_silu_mul_quant_ex.restype = i32
         L.rmsq_silu_mul_quant_validate.argtypes = act_args
         L.rmsq_silu_mul_quant_validate.restype = i32
+        rope_args = [p, p, p, p, p, f32, i64, i32, i32, i32, i64]
+        L.rmsq_qk_norm_rope.argtypes = rope_args + [i32, p]
+        L.rmsq_qk_norm_rope.restype = i32
+        L.rmsq_qk_norm_rope_ex.argtypes = rope_args + [i32, i32, i32, p, p, p]
+        L.rmsq_qk_norm_rope_ex.restype = i32
+        L.rmsq_qk_norm_rope_validate.argtypes = rope_args
+        L.rmsq_qk_norm_rope_validate.restype = i32
+        L.rmsq_qk_norm_rope_query_launch.argtypes = [i64, i32, i32, i32, C.POINTER(i32),
+                                                     C.POINTER(i32), C.POINTER(i64)]
+        L.rmsq_qk_norm_rope_query_launch.restype = i32
         L.rmsq_query_launch.argtypes = [i32, i64, i64, i32, i32, C.POINTER(rmsq_launch),
                                         C.POINTER(i64)]
         L.rmsq_query_launch.restype = i32
@@ -232,6 +243,50 @@ def rmsq_silu_mul_quant_validate(x, mode, scale_in, out_q, out_scales, tokens, i
                                               int(flags), int(scale_ld))
 
 
+def rmsq_qk_norm_rope(qkv, q_weight, k_weight, cos_sin_cache, positions, eps, num_q_heads,
+                      num_kv_heads, head_dim, is_neox=True, tokens=None, max_position=None,
+                      stream=None, heads_per_block=0, heads_per_lane=0, start_event=None,
+                      stop_event=None, check=True) -> int:
+    """In-place per-head RMSNorm + rotary embedding of the q and k heads of qkv
+    [T, (Hq + 2 Hkv) * D]; cos_sin_cache [max_position, D] f32, positions [T] int64.  With a
+    launch shape (heads per workgroup and per lane group) or events it goes through
+    rmsq_qk_norm_rope_ex."""
+    T = qkv.shape[0] if tokens is None else tokens
+    mp = cos_sin_cache.shape[0] if max_position is None else max_position
+    args = (_ptr(qkv), _ptr(q_weight), _ptr(k_weight), _ptr(cos_sin_cache), _ptr(positions),
+            float(eps), int(T), int(num_q_heads), int(num_kv_heads), int(head_dim), int(mp))
+    if heads_per_block == 0 and heads_per_lane == 0 and start_event is None and \
+            stop_event is None:
+        st = lib().rmsq_qk_norm_rope(*args, int(bool(is_neox)), _stream(stream))
+    else:
+        st = lib().rmsq_qk_norm_rope_ex(*args, int(bool(is_neox)), int(heads_per_block),
+                                        int(heads_per_lane), start_event, stop_event,
+                                        _stream(stream))
+    if check:
+        _check(st, "rmsq_qk_norm_rope")
+    return st
+
+
+def rmsq_qk_norm_rope_validate(qkv, q_weight, k_weight, cos_sin_cache, positions, eps, tokens,
+                               num_q_heads, num_kv_heads, head_dim, max_position) -> int:
+    """Host-only argument check; pointers are plain integers (or None)."""
+    return lib().rmsq_qk_norm_rope_validate(qkv, q_weight, k_weight, cos_sin_cache, positions,
+                                            float(eps), int(tokens), int(num_q_heads),
+                                            int(num_kv_heads), int(head_dim), int(max_position))
+
+
+def rmsq_qk_norm_rope_query_launch(tokens, num_q_heads, num_kv_heads, head_dim):
+    """(heads per workgroup, heads per lane group, grid size) of the default launch."""
+    hpb = C.c_int(0)
+    hpl = C.c_int(0)
+    grid = C.c_int64(0)
+    _check(lib().rmsq_qk_norm_rope_query_launch(int(tokens), int(num_q_heads), int(num_kv_heads),
+                                                int(head_dim), C.byref(hpb), C.byref(hpl),
+                                                C.byref(grid)),
+           "rmsq_qk_norm_rope_query_launch")
+    return hpb.value, hpl.value, grid.value
+
+
 def rmsq_validate(x, residual, weight, eps, mode, scale_in, out_q, out_scales, residual_out,
                   tokens, hidden, group_size=0, flags=0, scale_ld=0) -> int:
     """Host-only argument check; pointers are plain integers (or None) and never dereferenced."""
@@ -370,3 +425,12 @@ def fused_add_rms_norm_pad(x, residual, weight, eps, multiple=256, inplace=True)
     rout = None if residual is None else (residual if inplace else torch.empty_like(residual))
     rmsq_rms_norm_pad(x, residual, weight, eps, out, rout)
     return out, rout
+
+
+def qk_norm_rope(qkv, positions, q_weight, k_weight, cos_sin_cache, eps, num_q_heads,
+                 num_kv_heads, is_neox=True):
+    """The fused QK-norm + RoPE op on qkv [T, (Hq + 2 Hkv) * D] bf16, in place; returns qkv."""
+    D = q_weight.shape[0]
+    rmsq_qk_norm_rope(qkv, q_weight, k_weight, cos_sin_cache, positions, eps, num_q_heads,
+                      num_kv_heads, D, is_neox)
+    return qkv

@@ -4,6 +4,7 @@
 
 #include <atomic>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 
 #include "rmsq_kernels.hpp"
@@ -188,6 +189,8 @@ int check_aliasing(const Span* outs, int nout, const Span* ins, int nin) {
 
 int launch_kernel(const void* fn, int64_t nblk, int threads, void* argstruct, void* stream,
                   void* start_event, void* stop_event) {
+  // the dispatch packet's grid is counted in work-items, a 32-bit quantity
+  if (nblk <= 0 || nblk * (int64_t)threads > 0xFFFFFFFFLL) return RMSQ_EINVAL;
   void* args[] = {argstruct};
   const dim3 grid((uint32_t)nblk), block((uint32_t)threads);
   hipError_t e;
@@ -459,6 +462,132 @@ int act_impl(const void* x, int mode, const float* scale_in, void* q, void* scal
                        stop_event);
 }
 
+// ---- QK-norm + RoPE ------------------------------------------------------------------------
+constexpr int64_t kMaxQkvWidth = 1 << 20;  // elements of one token's qkv row
+
+template <int D, bool NEOX>
+const void* pick_rope_hpl(int hpl) {
+  switch (hpl) {
+    case 1: return reinterpret_cast<const void*>(&qk_norm_rope_kernel<D, NEOX, 1>);
+    case 2: return reinterpret_cast<const void*>(&qk_norm_rope_kernel<D, NEOX, 2>);
+    case 3: return reinterpret_cast<const void*>(&qk_norm_rope_kernel<D, NEOX, 3>);
+    case 4: return reinterpret_cast<const void*>(&qk_norm_rope_kernel<D, NEOX, 4>);
+    case 5: return reinterpret_cast<const void*>(&qk_norm_rope_kernel<D, NEOX, 5>);
+    case 6: return reinterpret_cast<const void*>(&qk_norm_rope_kernel<D, NEOX, 6>);
+    default: return nullptr;
+  }
+}
+
+const void* pick_rope(int D, bool neox, int hpl) {
+  switch (D) {
+    case 64: return neox ? pick_rope_hpl<64, true>(hpl) : pick_rope_hpl<64, false>(hpl);
+    case 128: return neox ? pick_rope_hpl<128, true>(hpl) : pick_rope_hpl<128, false>(hpl);
+    case 256: return neox ? pick_rope_hpl<256, true>(hpl) : pick_rope_hpl<256, false>(hpl);
+    default: return nullptr;
+  }
+}
+
+bool valid_rope_hpl(int hpl) { return hpl >= 1 && hpl <= 6; }
+
+int validate_rope(const void* qkv, const void* qw, const void* kw, const float* cache,
+                  const int64_t* pos, float eps, int64_t T, int hq, int hkv, int D,
+                  int64_t max_pos) {
+  if (T < 0 || T > 0x7FFFFFFFLL) return RMSQ_EINVAL;
+  if (D != 64 && D != 128 && D != 256) return RMSQ_EINVAL;
+  if (hq < 1 || hkv < 1 || (int64_t)(hq + 2LL * hkv) * D > kMaxQkvWidth) return RMSQ_EINVAL;
+  if (max_pos < 1) return RMSQ_EINVAL;
+  if (!(eps > 0.0f) || !std::isfinite(eps)) return RMSQ_EINVAL;
+  if (T == 0) return RMSQ_OK;
+  if (!qkv || !qw || !kw || !cache || !pos) return RMSQ_EINVAL;
+  if (!aligned(qkv, 16) || !aligned(qw, 16) || !aligned(kw, 16) || !aligned(cache, 16) ||
+      !aligned(pos, 8))
+    return RMSQ_EALIGN;
+  const Span out = span(qkv, (size_t)T * (size_t)(hq + 2 * hkv) * (size_t)D * 2);
+  const Span ins[4] = {span(qw, (size_t)D * 2), span(kw, (size_t)D * 2),
+                       span(cache, (size_t)max_pos * (size_t)D * 4), span(pos, (size_t)T * 8)};
+  return check_aliasing(&out, 1, ins, 4);
+}
+
+// Default shape: heads per lane group (hpl) and heads per workgroup (hpb, a multiple of hpl).
+// Keys, in order: the fewest wasted lanes per token (idle heads and partly filled waves); then
+// enough waves to occupy the chip (kMinRopeWaves: four per SIMD), and among the shapes that
+// have them the most heads per lane (more loads in flight per lane), among the others the most
+// waves (the batch is small and latency decides); then the workgroup closest to 256 threads.
+constexpr int64_t kMinRopeWaves = 4096;
+
+void default_rope_shape(int64_t T, int nh, int D, int* hpl_out, int* hpb_out) {
+  const int L = D / 16;
+  int best_hpl = 1, best_hpb = nh;
+  bool have = false;
+  int64_t best[4] = {0, 0, 0, 0};
+  for (int hpl : {1, 2, 3, 4, 5, 6}) {
+    if (hpl > nh) continue;
+    for (int g = 1; g * L <= 1024; ++g) {
+      const int hpb = g * hpl;
+      if (hpb - hpl >= nh) break;  // a lane group with no head at all
+      const int64_t nhb = (nh + hpb - 1) / hpb;
+      const int64_t wpb = (g * L + 63) / 64;  // waves per workgroup
+      // lane-head slots of one token's workgroups minus the ones its heads fill
+      const int64_t waste = nhb * wpb * 64 * hpl - (int64_t)nh * L;
+      const int64_t waves = T * nhb * wpb;
+      const bool reach = waves >= kMinRopeWaves;
+      const int64_t key[4] = {waste, reach ? 0 : 1, reach ? -hpl : -waves,
+                              std::llabs((int64_t)g * L - 256)};
+      bool better = !have;
+      for (int q = 0; q < 4 && !better; ++q) {
+        if (key[q] != best[q]) {
+          better = key[q] < best[q];
+          break;
+        }
+      }
+      if (better) {
+        have = true;
+        best_hpl = hpl;
+        best_hpb = hpb;
+        for (int q = 0; q < 4; ++q) best[q] = key[q];
+      }
+    }
+  }
+  *hpl_out = best_hpl;
+  *hpb_out = best_hpb;
+}
+
+int rope_impl(void* qkv, const void* qw, const void* kw, const float* cache, const int64_t* pos,
+              float eps, int64_t T, int hq, int hkv, int D, int64_t max_pos, int neox,
+              int heads_per_block, int heads_per_lane, void* start_event, void* stop_event,
+              void* stream) {
+  int st = validate_rope(qkv, qw, kw, cache, pos, eps, T, hq, hkv, D, max_pos);
+  if (st != RMSQ_OK) return st;
+  const int nh = hq + hkv;
+  int hpl = heads_per_lane, hpb = heads_per_block;
+  if (hpl < 0 || hpb < 0 || (hpl == 0) != (hpb == 0)) return RMSQ_EINVAL;
+  if (hpl == 0) default_rope_shape(T, nh, D, &hpl, &hpb);
+  if (!valid_rope_hpl(hpl) || hpb % hpl != 0 || (int64_t)(hpb / hpl) * (D / 16) > 1024)
+    return RMSQ_EINVAL;
+  if (T == 0) return RMSQ_OK;
+  st = check_device();
+  if (st != RMSQ_OK) return st;
+  const void* fn = pick_rope(D, neox != 0, hpl);
+  if (!fn) return RMSQ_EINVAL;
+  const int64_t nhb = (nh + hpb - 1) / hpb;
+  RArgs a;
+  a.qkv = static_cast<uint16_t*>(qkv);
+  a.qw = static_cast<const uint16_t*>(qw);
+  a.kw = static_cast<const uint16_t*>(kw);
+  a.cache = cache;
+  a.pos = pos;
+  a.T = T;
+  a.max_pos = max_pos;
+  a.eps = eps;
+  a.hq = hq;
+  a.nh = nh;
+  a.width = (hq + 2 * hkv) * D;
+  a.hpb = hpb;
+  a.groups = hpb / hpl;
+  a.nhb = (uint32_t)nhb;
+  return launch_kernel(fn, T * nhb, (hpb / hpl) * (D / 16), &a, stream, start_event, stop_event);
+}
+
 }  // namespace rmsq
 
 using namespace rmsq;
@@ -570,6 +699,46 @@ int rmsq_silu_mul_query_launch(int mode, int64_t tokens, int64_t inter, int grou
       *grid = (tokens + launch->rows_per_block - 1) / launch->rows_per_block;
     }
   }
+  return RMSQ_OK;
+}
+
+int rmsq_qk_norm_rope(void* qkv, const void* q_weight, const void* k_weight,
+                      const float* cos_sin_cache, const int64_t* positions, float eps,
+                      int64_t tokens, int num_q_heads, int num_kv_heads, int head_dim,
+                      int64_t max_position, int is_neox, void* stream) {
+  return rope_impl(qkv, q_weight, k_weight, cos_sin_cache, positions, eps, tokens, num_q_heads,
+                   num_kv_heads, head_dim, max_position, is_neox, 0, 0, nullptr, nullptr, stream);
+}
+
+int rmsq_qk_norm_rope_ex(void* qkv, const void* q_weight, const void* k_weight,
+                         const float* cos_sin_cache, const int64_t* positions, float eps,
+                         int64_t tokens, int num_q_heads, int num_kv_heads, int head_dim,
+                         int64_t max_position, int is_neox, int heads_per_block,
+                         int heads_per_lane, void* start_event, void* stop_event, void* stream) {
+  return rope_impl(qkv, q_weight, k_weight, cos_sin_cache, positions, eps, tokens, num_q_heads,
+                   num_kv_heads, head_dim, max_position, is_neox, heads_per_block,
+                   heads_per_lane, start_event, stop_event, stream);
+}
+
+int rmsq_qk_norm_rope_validate(const void* qkv, const void* q_weight, const void* k_weight,
+                               const float* cos_sin_cache, const int64_t* positions, float eps,
+                               int64_t tokens, int num_q_heads, int num_kv_heads, int head_dim,
+                               int64_t max_position) {
+  return validate_rope(qkv, q_weight, k_weight, cos_sin_cache, positions, eps, tokens,
+                       num_q_heads, num_kv_heads, head_dim, max_position);
+}
+
+int rmsq_qk_norm_rope_query_launch(int64_t tokens, int num_q_heads, int num_kv_heads,
+                                   int head_dim, int* heads_per_block, int* heads_per_lane,
+                                   int64_t* grid) {
+  if (tokens < 0 || num_q_heads < 1 || num_kv_heads < 1) return RMSQ_EINVAL;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return RMSQ_EINVAL;
+  const int nh = num_q_heads + num_kv_heads;
+  int hpl = 1, hpb = 1;
+  rmsq::default_rope_shape(tokens, nh, head_dim, &hpl, &hpb);
+  if (heads_per_block) *heads_per_block = hpb;
+  if (heads_per_lane) *heads_per_lane = hpl;
+  if (grid) *grid = tokens * ((nh + hpb - 1) / hpb);
   return RMSQ_OK;
 }
 

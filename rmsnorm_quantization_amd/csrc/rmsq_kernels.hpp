@@ -478,6 +478,159 @@ __global__ void __launch_bounds__(1024) silu_mul_tile_kernel(AArgs a) {
                                 nullptr);
 }
 
+// ------------------------------------------------------------------ QK-norm + RoPE
+// vLLM docs "Fusion torch.compile passes", section "QK Norm + RoPE": for models with per-head
+// Q/K normalization, each q and k head of the packed qkv tensor is RMS-normalized (q and k with
+// their own weights) and rotated by the rotary embedding, in place, in one pass.
+//
+// Layout on the lanes: a head of D elements is held by L = D/16 consecutive lanes; lane c holds
+// the two 8-element chunks c and c + L, i.e. elements 8c..8c+7 of the first half of the head and
+// the same offsets of the second half.  Every NeoX pair (i, i + D/2) and every interleaved pair
+// (2i, 2i+1) is then inside one lane, so the rotation needs no cross-lane traffic; only the sum
+// of squares is reduced over the L lanes.  A workgroup serves hpb heads of one token with
+// hpb / HPT lane groups; group g takes heads g, g + groups, ... (HPT of them), so each load
+// instruction of a wave reads whole 128-byte lines and every lane has 2*HPT chunks in flight.
+struct RArgs {
+  uint16_t* qkv;           // [T, (Hq + 2 Hkv) * D] bf16, q and k heads rewritten in place
+  const uint16_t* qw;      // [D]
+  const uint16_t* kw;      // [D]
+  const float* cache;      // [max_pos, D]: cos | sin
+  const int64_t* pos;      // [T]
+  int64_t T;
+  int64_t max_pos;
+  float eps;
+  int32_t hq;              // q heads
+  int32_t nh;              // q + k heads (the ones rewritten)
+  int32_t width;           // (Hq + 2 Hkv) * D
+  int32_t hpb;             // heads per workgroup
+  int32_t groups;          // lane groups per workgroup (hpb / HPT)
+  uint32_t nhb;            // workgroups per token
+};
+
+template <int L>
+__device__ __forceinline__ double group_sum(double v) {
+  // Sum over aligned groups of L lanes (2 to 16, within one DPP row); every lane of a group
+  // gets the sum.  Must run with all lanes of the group active.
+  v += dpp<0xB1>(v);                   // lane ^ 1
+  if (L >= 4) v += dpp<0x4E>(v);       // lane ^ 2
+  if (L >= 8) v += dpp<0x141>(v);      // the other quad of the 8
+  if (L >= 16) v += dpp<0x140>(v);     // the other half of the 16
+  return v;
+}
+
+template <int D, bool NEOX, int HPT>
+__global__ void __launch_bounds__(1024) qk_norm_rope_kernel(RArgs a) {
+  constexpr int L = D / 16;   // lanes per head
+  constexpr int CH = D / 8;   // 16-byte chunks per head
+  const uint32_t t = blockIdx.x / a.nhb;
+  const uint32_t hb = blockIdx.x - t * a.nhb;
+  const int64_t p = a.pos[t];
+  if (p < 0 || p >= a.max_pos) return;  // out-of-range position: the token is left unchanged
+  const int tid = threadIdx.x;
+  const int c = tid % L;
+  const int h0 = (int)hb * a.hpb + tid / L;
+  u32x4* row = reinterpret_cast<u32x4*>(a.qkv + (size_t)t * (size_t)a.width);
+
+  // every load first: the heads' chunks, both weights, this lane's cos/sin
+  u32x4 xv[HPT][2];
+#pragma unroll
+  for (int k = 0; k < HPT; ++k) {
+    const int h = h0 + k * a.groups;
+    xv[k][0] = xv[k][1] = (u32x4){0u, 0u, 0u, 0u};
+    if (h < a.nh) {
+      xv[k][0] = __builtin_nontemporal_load(row + h * CH + c);
+      xv[k][1] = __builtin_nontemporal_load(row + h * CH + c + L);
+    }
+  }
+  const u32x4* qw = reinterpret_cast<const u32x4*>(a.qw);
+  const u32x4* kw = reinterpret_cast<const u32x4*>(a.kw);
+  const u32x4 wq0 = qw[c], wq1 = qw[c + L], wk0 = kw[c], wk1 = kw[c + L];
+  const float* cs = a.cache + (size_t)p * D;
+  float cv[16], sv[16];
+  if constexpr (NEOX) {
+    // elements 8c+e and D/2+8c+e form pair j = 8c+e
+    const f32x4* cp = reinterpret_cast<const f32x4*>(cs + 8 * c);
+    const f32x4* sp = reinterpret_cast<const f32x4*>(cs + D / 2 + 8 * c);
+    const f32x4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      cv[e] = c0[e]; cv[4 + e] = c1[e];
+      sv[e] = s0[e]; sv[4 + e] = s1[e];
+    }
+  } else {
+    // chunk c holds pairs j = 4c..4c+3, chunk c+L pairs j = D/4+4c..D/4+4c+3
+    const f32x4 c0 = *reinterpret_cast<const f32x4*>(cs + 4 * c);
+    const f32x4 c1 = *reinterpret_cast<const f32x4*>(cs + D / 4 + 4 * c);
+    const f32x4 s0 = *reinterpret_cast<const f32x4*>(cs + D / 2 + 4 * c);
+    const f32x4 s1 = *reinterpret_cast<const f32x4*>(cs + D / 2 + D / 4 + 4 * c);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      cv[m] = c0[m]; cv[4 + m] = c1[m];
+      sv[m] = s0[m]; sv[4 + m] = s1[m];
+    }
+  }
+
+#pragma unroll
+  for (int k = 0; k < HPT; ++k) {
+    const int h = h0 + k * a.groups;
+    double ss0 = 0.0, ss1 = 0.0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const double lo = (double)bf16_lo(xv[k][hh][j]), hi = (double)bf16_hi(xv[k][hh][j]);
+        ss0 = fma(lo, lo, ss0);
+        ss1 = fma(hi, hi, ss1);
+      }
+    }
+    const double ss = group_sum<L>(ss0 + ss1);
+    const float inv = (float)(1.0 / sqrt(ss / (double)D + (double)a.eps));
+    const bool isq = h < a.hq;
+    const u32x4 w0 = isq ? wq0 : wk0, w1 = isq ? wq1 : wk1;
+    float y0[8], y1[8], o0[8], o1[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      y0[e] = y_of(xv[k][0], w0, e, inv);
+      y1[e] = y_of(xv[k][1], w1, e, inv);
+    }
+    if constexpr (NEOX) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float ac = y0[e] * cv[e], bs = y1[e] * sv[e];
+        const float bc = y1[e] * cv[e], as = y0[e] * sv[e];
+        o0[e] = ac - bs;
+        o1[e] = bc + as;
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        {
+          const float ac = y0[2 * m] * cv[m], bs = y0[2 * m + 1] * sv[m];
+          const float bc = y0[2 * m + 1] * cv[m], as = y0[2 * m] * sv[m];
+          o0[2 * m] = ac - bs;
+          o0[2 * m + 1] = bc + as;
+        }
+        {
+          const float ac = y1[2 * m] * cv[4 + m], bs = y1[2 * m + 1] * sv[4 + m];
+          const float bc = y1[2 * m + 1] * cv[4 + m], as = y1[2 * m] * sv[4 + m];
+          o1[2 * m] = ac - bs;
+          o1[2 * m + 1] = bc + as;
+        }
+      }
+    }
+    if (h < a.nh) {
+      __builtin_nontemporal_store(
+          (u32x4){pack_bf16x2(o0[0], o0[1]), pack_bf16x2(o0[2], o0[3]),
+                  pack_bf16x2(o0[4], o0[5]), pack_bf16x2(o0[6], o0[7])},
+          row + h * CH + c);
+      __builtin_nontemporal_store(
+          (u32x4){pack_bf16x2(o1[0], o1[1]), pack_bf16x2(o1[2], o1[3]),
+                  pack_bf16x2(o1[4], o1[5]), pack_bf16x2(o1[6], o1[7])},
+          row + h * CH + c + L);
+    }
+  }
+}
+
 // The kernels' own converters over a flat f32 array, 8 elements per thread.
 __global__ void __launch_bounds__(256) convert_kernel(int fmt, const float* in, void* out,
                                                       int64_t nchunks) {

@@ -3,8 +3,8 @@
 Both the GPU path and the CPU oracle are fed from here.  Values are drawn in float32 from a
 seeded torch CPU generator and cast to bf16 by torch; nothing in this module normalizes,
 scales or quantizes.  Seven workloads are defined, matching the shapes and distributions of
-the fused RMSNorm + quantization (0-4), SiLU+Mul + quantization (5) and RMSNorm + padding (6)
-workloads this library is measured on:
+the fused RMSNorm + quantization (0-4), SiLU+Mul + quantization (5), RMSNorm + padding (6) and
+QK-norm + RoPE (7) workloads this library is measured on:
 
   0  RMSNorm -> FP8 static        T=16,  H=4096, x~N(0,1), w~U(0.5,1.5), eps 1e-5, scale 0.05
   1  add+RMSNorm -> FP8 static    T in {1,64,512,4096}, H=4096, x,r~N(0,1), eps 1e-5,
@@ -25,8 +25,15 @@ workloads this library is measured on:
                                   this fusion) padded to a multiple of 256 (3072), x,r~N(0,1),
                                   eps 1e-5
 
+  7  QK-norm + RoPE                T in {1,256,4096}, qkv [T, (32 + 2*8) * 128] ~N(0,1) (the head
+                                  layout of Qwen3-8B, a model of the family the pages name for
+                                  this fusion: 32 q heads, 8 kv heads, head size 128), q/k weights
+                                  ~U(0.5,1.5), positions ~ uniform integers in [0, 32768) (a
+                                  batch of independent sequences), NeoX pairing, eps 1e-6; the
+                                  cos/sin cache (base 1e6, 32768 positions) is built by the caller
+
 Seeds: 1000*workload + tensor id (x=1, residual=2, weight=3, outlier channels=4,
-warm-up x=5, warm-up residual=6).  Unless stated otherwise, weight ~ U(0.5, 1.5) and the
+warm-up x=5, warm-up residual=6, k weight=7, positions=8).  Unless stated otherwise, weight ~ U(0.5, 1.5) and the
 residual ~ N(0,1) without outliers.
 """
 from dataclasses import dataclass, field
@@ -50,8 +57,11 @@ class Workload:
     warmup_shape: Optional[Tuple[int, int]] = None  # batch the static scale is derived from
     group_sizes: Tuple[int, ...] = field(default_factory=tuple)
     kind: str = "norm"   # "norm": (residual add ->) RMSNorm -> quant; "act": SiLU+Mul -> quant;
-    #                      "pad": (residual add ->) RMSNorm -> padded bf16
+    #                      "pad": (residual add ->) RMSNorm -> padded bf16; "rope": QK-norm + RoPE
     pad_multiple: int = 0
+    heads: Tuple[int, int] = (0, 0)   # (q heads, kv heads) of a "rope" workload; hidden = head size
+    max_position: int = 0
+    rope_base: float = 0.0
 
 
 WORKLOADS = {
@@ -67,9 +77,11 @@ WORKLOADS = {
                 warmup_shape=(512, 14336), group_sizes=(128, 64), kind="act"),
     6: Workload(6, "add_rmsnorm_pad", (1, 256, 4096), (2880,), 1e-5, True, kind="pad",
                 pad_multiple=256),
+    7: Workload(7, "qk_norm_rope", (1, 256, 4096), (128,), 1e-6, False, kind="rope",
+                heads=(32, 8), max_position=32768, rope_base=1e6),
 }
 
-X, RESIDUAL, WEIGHT, OUTLIERS, WARM_X, WARM_R = 1, 2, 3, 4, 5, 6
+X, RESIDUAL, WEIGHT, OUTLIERS, WARM_X, WARM_R, K_WEIGHT, POSITIONS = 1, 2, 3, 4, 5, 6, 7, 8
 
 
 def _gen(workload: int, tensor: int) -> torch.Generator:
@@ -134,6 +146,22 @@ def make_act_warmup(workload: int, I: Optional[int] = None):
     wl = WORKLOADS[workload]
     T, Iw = wl.warmup_shape
     return make_act_inputs(workload, T, I if I is not None else Iw, tensor=WARM_X)
+
+
+def make_rope_inputs(workload: int, T: int, hq: Optional[int] = None, hkv: Optional[int] = None,
+                     D: Optional[int] = None, max_position: Optional[int] = None):
+    """(qkv [T, (hq + 2 hkv) * D], q weight [D], k weight [D]) as CPU bf16 tensors and positions
+    [T] int64 for a QK-norm + RoPE workload."""
+    wl = WORKLOADS[workload]
+    hq = hq if hq is not None else wl.heads[0]
+    hkv = hkv if hkv is not None else wl.heads[1]
+    D = D if D is not None else wl.hidden[0]
+    mp = max_position if max_position is not None else wl.max_position
+    qkv = normal_bf16((T, (hq + 2 * hkv) * D), wl.index, X)
+    qw = uniform_bf16((D,), 0.5, 1.5, wl.index, WEIGHT)
+    kw = uniform_bf16((D,), 0.5, 1.5, wl.index, K_WEIGHT)
+    pos = torch.randint(0, mp, (T,), generator=_gen(wl.index, POSITIONS), dtype=torch.int64)
+    return qkv, qw, kw, pos
 
 
 def bits(t: torch.Tensor) -> np.ndarray:

@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
     for n in ("rmsq_fused", "rmsq_fused_with_launch", "rmsq_fused_timed", "rmsq_validate",
               "rmsq_silu_mul_quant", "rmsq_silu_mul_quant_ex", "rmsq_silu_mul_quant_validate",
               "rmsq_silu_mul_query_launch", "rmsq_rms_norm_pad", "rmsq_rms_norm_pad_ex",
-              "rmsq_rms_norm_pad_validate",
+              "rmsq_rms_norm_pad_validate", "rmsq_qk_norm_rope", "rmsq_qk_norm_rope_ex",
+              "rmsq_qk_norm_rope_validate", "rmsq_qk_norm_rope_query_launch",
               "rmsq_query_launch",
               "rmsq_block_to_rowblock", "rmsq_convert", "rmsq_status_string",
               "rmsq_abi_version"):
@@ -233,3 +234,78 @@ def test_pad_bad_arguments(B, kw, status):
                                      kw.get("eps", 1e-6), kw.get("out", Q), kw.get("ro", RO),
                                      kw.get("t", T), kw.get("h", H), kw.get("ld", H + 64),
                                      None) == code
+
+
+# ------------------------------------------------------------------ QK-norm + RoPE
+HQ, HKV, D, MP = 4, 2, 128, 64
+QKV, QW, KW, CS, POS = X, W, R, S, SC
+
+
+def VR(B, qkv=QKV, qw=QW, kw=KW, cs=CS, pos=POS, eps=1e-6, t=T, hq=HQ, hkv=HKV, d=D, mp=MP):
+    return B.rmsq_qk_norm_rope_validate(qkv, qw, kw, cs, pos, eps, t, hq, hkv, d, mp)
+
+
+def test_rope_valid_calls(B):
+    assert VR(B) == B.RMSQ_OK
+    for d in (64, 256):
+        assert VR(B, d=d) == B.RMSQ_OK
+    assert VR(B, qw=KW) == B.RMSQ_OK                     # q and k may share one weight
+    assert VR(B, t=0, qkv=None, pos=None) == B.RMSQ_OK
+    assert VR(B, hq=64, hkv=8, d=128) == B.RMSQ_OK
+    # qkv spans T * (Hq + 2 Hkv) * D * 2 bytes: a neighbour just past it is fine
+    assert VR(B, pos=QKV + T * (HQ + 2 * HKV) * D * 2) == B.RMSQ_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), "EINVAL"), (dict(d=32), "EINVAL"), (dict(d=512), "EINVAL"),
+    (dict(hq=0), "EINVAL"), (dict(hkv=0), "EINVAL"), (dict(hq=4096, d=256), "EINVAL"),
+    (dict(mp=0), "EINVAL"), (dict(eps=0.0), "EINVAL"), (dict(eps=float("nan")), "EINVAL"),
+    (dict(t=-1), "EINVAL"), (dict(t=1 << 31), "EINVAL"),
+    (dict(qkv=None), "EINVAL"), (dict(qw=None), "EINVAL"), (dict(kw=None), "EINVAL"),
+    (dict(cs=None), "EINVAL"), (dict(pos=None), "EINVAL"),
+    (dict(qkv=QKV + 8), "EALIGN"), (dict(qw=QW + 2), "EALIGN"), (dict(cs=CS + 4), "EALIGN"),
+    (dict(pos=POS + 4), "EALIGN"),
+    (dict(qw=QKV), "EALIAS"), (dict(cs=QKV + 16), "EALIAS"), (dict(pos=QKV + 256), "EALIAS"),
+    (dict(pos=QKV + T * (HQ + 2 * HKV) * D * 2 - 8), "EALIAS"),
+    (dict(kw=QKV - 16), "EALIAS"),
+])
+def test_rope_bad_arguments(B, kw, status):
+    code = getattr(B, "RMSQ_" + status)
+    assert VR(B, **kw) == code
+    a = dict(qkv=QKV, qw=QW, kw=KW, cs=CS, pos=POS, eps=1e-6, t=T, hq=HQ, hkv=HKV, d=D, mp=MP)
+    a.update(kw)
+    assert B.lib().rmsq_qk_norm_rope(a["qkv"], a["qw"], a["kw"], a["cs"], a["pos"], a["eps"],
+                                     a["t"], a["hq"], a["hkv"], a["d"], a["mp"], 1, None) == code
+
+
+def test_rope_launch_shape_is_checked(B):
+    """Bad explicit shapes are rejected before any device call."""
+    def ex(hpb, hpl):
+        return B.lib().rmsq_qk_norm_rope_ex(QKV, QW, KW, CS, POS, 1e-6, T, HQ, HKV, D, MP, 1,
+                                            hpb, hpl, None, None, None)
+    L = D // 16
+    for hpb, hpl in ((1024 // L + 1, 1), (6, 4), (-1, 1), (4, -1), (0, 2), (2, 0), (7, 7),
+                     (16, 8), (2 * (1024 // L + 1), 2)):
+        assert ex(hpb, hpl) == B.RMSQ_EINVAL, (hpb, hpl)
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (64, 8, 128), (16, 8, 64), (8, 1, 256),
+                                      (40, 8, 128), (1, 1, 128), (28, 4, 128), (12, 4, 64)])
+def test_rope_query_launch(B, hq, hkv, d):
+    hpb, hpl, grid = B.rmsq_qk_norm_rope_query_launch(1000, hq, hkv, d)
+    nh, L = hq + hkv, d // 16
+    groups = hpb // hpl
+    assert 1 <= hpl <= 6 and hpb % hpl == 0 and groups * L <= 1024
+    assert (groups * L) % 64 == 0 or hpb >= nh   # whole waves unless one workgroup per token
+    assert hpb - hpl < nh                          # every lane group has a head
+    assert grid == 1000 * -(-nh // hpb)
+    with pytest.raises(B.RmsqError):
+        B.rmsq_qk_norm_rope_query_launch(1000, hq, hkv, 96)
+
+
+def test_rope_default_shape_follows_the_batch(B):
+    """Small batches get one head per lane (more, shorter waves); large ones several heads per
+    lane (more loads in flight) -- for the 32 q + 8 kv heads of size 128 layout."""
+    assert B.rmsq_qk_norm_rope_query_launch(1, 32, 8, 128)[:2] == (40, 1)
+    assert B.rmsq_qk_norm_rope_query_launch(256, 32, 8, 128)[:2] == (40, 1)
+    assert B.rmsq_qk_norm_rope_query_launch(4096, 32, 8, 128)[:2] == (40, 5)

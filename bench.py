@@ -262,6 +262,8 @@ def gpu_leg(args, wl, T, H, mode, G, flags):
              "q": (torch.empty((T, ld), dtype=torch.bfloat16, device=dev) if pad else
                    torch.empty((T, qcols), dtype=torch.uint8, device=dev)),
              "s": torch.empty(sshape, dtype=sdt, device=dev) if sshape else None}
+        if residual and args.inplace:
+            s["ro"] = s["r"]  # the residual is updated in place, as the fused-add op does
         sets.append(s)
     wd = wd.contiguous()
 
@@ -306,7 +308,7 @@ def gpu_leg(args, wl, T, H, mode, G, flags):
     if launch:
         shape = launch.as_tuple()
     elif pad:
-        shape = B.rmsq_query_launch(0, T, ld, 0, residual)[0].as_tuple()
+        shape = B.rmsq_rms_norm_pad_query_launch(T, H, ld)[0].as_tuple()
     elif act:
         shape = B.rmsq_silu_mul_query_launch(mode, T, H, 16 if mode == 3 else G)[0].as_tuple()
     else:
@@ -620,6 +622,8 @@ def main():
     ap.add_argument("--flags", default="")
     ap.add_argument("--launch", default="")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--inplace", action="store_true",
+                    help="write the updated residual over the residual input")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="time eager back-to-back launches only (default: also a HIP-graph "
                          "replay of the same K launches, which is what value reports)")

@@ -181,8 +181,9 @@ RMSQ_API int rmsq_rms_norm_pad(const void* x, const void* residual, const void* 
                                float eps, void* out, void* residual_out, int64_t tokens,
                                int64_t hidden, int64_t out_ld, void* stream);
 
-/* rmsq_rms_norm_pad with an explicit launch shape (NULL: the default for a row of out_ld
- * elements; a shape must cover out_ld) and optional dispatch-stamped events. */
+/* rmsq_rms_norm_pad with an explicit launch shape (NULL: the default, see
+ * rmsq_rms_norm_pad_query_launch; a shape must cover out_ld) and optional dispatch-stamped
+ * events. */
 RMSQ_API int rmsq_rms_norm_pad_ex(const void* x, const void* residual, const void* weight,
                                   float eps, void* out, void* residual_out, int64_t tokens,
                                   int64_t hidden, int64_t out_ld, const rmsq_launch* launch,
@@ -289,6 +290,11 @@ RMSQ_API int rmsq_qk_norm_rope_query_launch(int64_t tokens, int num_q_heads, int
  * (number of workgroups).  Host only; makes no HIP call.  Returns RMSQ_OK or RMSQ_EINVAL. */
 RMSQ_API int rmsq_query_launch(int mode, int64_t tokens, int64_t hidden, int group_size,
                       int has_residual, rmsq_launch* launch, int64_t* grid);
+
+/* The launch shape rmsq_rms_norm_pad picks for (T, H, out_ld) and its grid size.  Host only;
+ * makes no HIP call.  Returns RMSQ_OK or RMSQ_EINVAL. */
+RMSQ_API int rmsq_rms_norm_pad_query_launch(int64_t tokens, int64_t hidden, int64_t out_ld,
+                                            rmsq_launch* launch, int64_t* grid);
 
 /* The launch shape rmsq_silu_mul_quant picks for (mode, T, I, group_size) and its grid size.
  * Host only; makes no HIP call.  Returns RMSQ_OK or RMSQ_EINVAL. */

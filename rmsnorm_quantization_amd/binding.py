@@ -7,6 +7,7 @@ the binding raises -- there is no fallback path.
 Function names match the C ABI (rmsq_fused, rmsq_fused_with_launch, rmsq_fused_timed,
 rmsq_silu_mul_quant, rmsq_silu_mul_quant_ex, rmsq_silu_mul_quant_validate,
 rmsq_silu_mul_query_launch, rmsq_rms_norm_pad, rmsq_rms_norm_pad_ex, rmsq_rms_norm_pad_validate,
+rmsq_rms_norm_pad_query_launch,
 rmsq_qk_norm_rope, rmsq_qk_norm_rope_ex, rmsq_qk_norm_rope_validate,
 rmsq_qk_norm_rope_query_launch, rmsq_validate,
 rmsq_query_launch, rmsq_block_to_rowblock, rmsq_convert, rmsq_status_string,
@@ -97,6 +98,9 @@ def lib():
         L.rmsq_query_launch.argtypes = [i32, i64, i64, i32, i32, C.POINTER(rmsq_launch),
                                         C.POINTER(i64)]
         L.rmsq_query_launch.restype = i32
+        L.rmsq_rms_norm_pad_query_launch.argtypes = [i64, i64, i64, C.POINTER(rmsq_launch),
+                                                     C.POINTER(i64)]
+        L.rmsq_rms_norm_pad_query_launch.restype = i32
         L.rmsq_silu_mul_query_launch.argtypes = [i32, i64, i64, i32, C.POINTER(rmsq_launch),
                                                  C.POINTER(i64)]
         L.rmsq_silu_mul_query_launch.restype = i32
@@ -301,6 +305,14 @@ def rmsq_query_launch(mode, tokens, hidden, group_size=0, has_residual=True):
     _check(lib().rmsq_query_launch(int(mode), int(tokens), int(hidden), int(group_size),
                                    int(bool(has_residual)), C.byref(l), C.byref(grid)),
            "rmsq_query_launch")
+    return l, grid.value
+
+
+def rmsq_rms_norm_pad_query_launch(tokens, hidden, out_ld):
+    l = rmsq_launch()
+    grid = C.c_int64(0)
+    _check(lib().rmsq_rms_norm_pad_query_launch(int(tokens), int(hidden), int(out_ld), C.byref(l),
+                                                C.byref(grid)), "rmsq_rms_norm_pad_query_launch")
     return l, grid.value
 
 

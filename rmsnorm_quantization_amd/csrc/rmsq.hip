@@ -301,12 +301,22 @@ int validate_pad(const void* x, const void* res, const void* w, float eps, const
   return RMSQ_OK;
 }
 
+// Default shape of the padded-output launch: one wave per row with up to 8 chunks per lane when
+// the padded row fits (ld <= 4096: 64 threads x ceil(ld/512) chunks), else the quantizing
+// kernel's rule.  Measured on MI355X for 2880 -> 3072 (4096 rows): 17.1 us against 18.3 us
+// for 192 threads x 2 chunks; equal at 4000 -> 4096; better at 2000 -> 2048.
+rmsq_launch default_pad_launch(int64_t ld) {
+  const int64_t nch = ld / 8;
+  if (nch > 128 && nch <= 512) return rmsq_launch{64, (int32_t)((nch + 63) / 64), 1, 0};
+  return default_launch(ld);
+}
+
 int pad_impl(const void* x, const void* res, const void* w, float eps, void* out, void* res_out,
              int64_t T, int64_t H, int64_t out_ld, const rmsq_launch* launch, void* start_event,
              void* stop_event, void* stream) {
   int st = validate_pad(x, res, w, eps, out, res_out, T, H, out_ld);
   if (st != RMSQ_OK) return st;
-  const rmsq_launch l = launch ? *launch : default_launch(out_ld);
+  const rmsq_launch l = launch ? *launch : default_pad_launch(out_ld);
   if (!valid_launch(l, out_ld)) return RMSQ_EINVAL;  // the launch covers the padded row
   if (T == 0) return RMSQ_OK;
   st = check_device();
@@ -509,47 +519,77 @@ int validate_rope(const void* qkv, const void* qw, const void* kw, const float* 
 }
 
 // Default shape: heads per lane group (hpl) and heads per workgroup (hpb, a multiple of hpl).
-// Keys, in order: the fewest wasted lanes per token (idle heads and partly filled waves); then
-// enough waves to occupy the chip (kMinRopeWaves: four per SIMD), and among the shapes that
-// have them the most heads per lane (more loads in flight per lane), among the others the most
-// waves (the batch is small and latency decides); then the workgroup closest to 256 threads.
-constexpr int64_t kMinRopeWaves = 4096;
+//
+// A shape is judged by the lane-head slots it wastes per token (idle heads, partly filled
+// waves) and by how many "rounds" its grid takes: waves / (what the chip holds at once, from
+// the kernel's register use).  Measured on MI355X (40 heads of 128, T = 256 ... 16384):
+//  * while one head per lane still fits in one round, it wins (more, shorter waves: T <= 1024);
+//  * else the most heads per lane that still fits in one round (T = 2048, 4096: 5 per lane,
+//    one 64-thread workgroup per token, 15.9 us at 4096 against 17.2-18.4 for the others);
+//  * past one round, 2 heads per lane in single-wave workgroups (T = 8192: 29.2 us against
+//    31.7 for 5 per lane; T = 16384: 55.4 against 60.5).
+// Waves per SIMD by heads per lane (VGPRs 57 / 76 / 86 / 96 / 104 / 116 of 512), the same for
+// every head size since a lane always holds 16 elements of a head.
+constexpr int kRopeWavesPerSimd[7] = {0, 8, 6, 5, 5, 4, 4};
+constexpr int64_t kSimds = 256 * 4;  // MI355X: 256 CUs x 4 SIMDs
 
 void default_rope_shape(int64_t T, int nh, int D, int* hpl_out, int* hpb_out) {
   const int L = D / 16;
-  int best_hpl = 1, best_hpb = nh;
-  bool have = false;
-  int64_t best[4] = {0, 0, 0, 0};
-  for (int hpl : {1, 2, 3, 4, 5, 6}) {
+  struct Cand {
+    int hpl, hpb;
+    int64_t waste, wpb, dist;
+    bool fits;
+  };
+  Cand cs[6 * 1024];
+  int n = 0;
+  int64_t least = -1;
+  for (int hpl = 1; hpl <= 6; ++hpl) {
     if (hpl > nh) continue;
     for (int g = 1; g * L <= 1024; ++g) {
       const int hpb = g * hpl;
-      if (hpb - hpl >= nh) break;  // a lane group with no head at all
+      if (hpb - hpl >= nh) break;                        // a lane group with no head at all
+      if ((g * L) % 64 != 0 && hpb < nh) continue;       // whole waves, or all of a token's heads
+      Cand c;
+      c.hpl = hpl;
+      c.hpb = hpb;
       const int64_t nhb = (nh + hpb - 1) / hpb;
-      const int64_t wpb = (g * L + 63) / 64;  // waves per workgroup
+      c.wpb = ((int64_t)g * L + 63) / 64;
       // lane-head slots of one token's workgroups minus the ones its heads fill
-      const int64_t waste = nhb * wpb * 64 * hpl - (int64_t)nh * L;
-      const int64_t waves = T * nhb * wpb;
-      const bool reach = waves >= kMinRopeWaves;
-      const int64_t key[4] = {waste, reach ? 0 : 1, reach ? -hpl : -waves,
-                              std::llabs((int64_t)g * L - 256)};
-      bool better = !have;
-      for (int q = 0; q < 4 && !better; ++q) {
-        if (key[q] != best[q]) {
-          better = key[q] < best[q];
-          break;
-        }
-      }
-      if (better) {
-        have = true;
-        best_hpl = hpl;
-        best_hpb = hpb;
-        for (int q = 0; q < 4; ++q) best[q] = key[q];
-      }
+      c.waste = nhb * c.wpb * 64 * hpl - (int64_t)nh * L;
+      c.dist = std::llabs((int64_t)g * L - 256);
+      c.fits = T * nhb * c.wpb <= kSimds * kRopeWavesPerSimd[hpl];
+      cs[n++] = c;
+      if (least < 0 || c.waste < least) least = c.waste;
     }
   }
-  *hpl_out = best_hpl;
-  *hpb_out = best_hpb;
+  // the pick: (a) one head per lane if it fits in one round; (b) else the most heads per lane
+  // that fits in one round; both among the shapes of least waste, closest to 256 threads;
+  // (c) else two heads per lane, least waste among those, then single-wave workgroups
+  int best = -1;
+  auto take = [&](int k, bool by_wpb) {
+    if (best < 0) { best = k; return; }
+    const Cand &c = cs[k], &b = cs[best];
+    if (c.waste != b.waste) { if (c.waste < b.waste) best = k; return; }
+    if (by_wpb && c.wpb != b.wpb) { if (c.wpb < b.wpb) best = k; return; }
+    if (c.dist < b.dist) best = k;
+  };
+  for (int k = 0; k < n; ++k)
+    if (cs[k].hpl == 1 && cs[k].waste == least && cs[k].fits) take(k, false);
+  if (best < 0) {
+    int top = 0;
+    for (int k = 0; k < n; ++k)
+      if (cs[k].waste == least && cs[k].fits && cs[k].hpl > top) top = cs[k].hpl;
+    for (int k = 0; k < n; ++k)
+      if (top && cs[k].hpl == top && cs[k].waste == least && cs[k].fits) take(k, false);
+  }
+  if (best < 0)
+    for (int k = 0; k < n; ++k)
+      if (cs[k].hpl == 2) take(k, true);
+  if (best < 0)  // a single head: one head per lane
+    for (int k = 0; k < n; ++k)
+      if (cs[k].hpl == 1) take(k, false);
+  *hpl_out = cs[best].hpl;
+  *hpb_out = cs[best].hpb;
 }
 
 int rope_impl(void* qkv, const void* qw, const void* kw, const float* cache, const int64_t* pos,
@@ -682,6 +722,17 @@ int rmsq_query_launch(int mode, int64_t tokens, int64_t hidden, int group_size,
   if (st != RMSQ_OK) return st;
   *launch = default_launch(hidden);
   if (grid) *grid = (tokens + launch->rows_per_block - 1) / launch->rows_per_block;
+  return RMSQ_OK;
+}
+
+int rmsq_rms_norm_pad_query_launch(int64_t tokens, int64_t hidden, int64_t out_ld,
+                                   rmsq_launch* launch, int64_t* grid) {
+  if (tokens < 0 || hidden < 8 || (hidden % 8) != 0 || out_ld < hidden ||
+      out_ld > RMSQ_MAX_HIDDEN || (out_ld % 8) != 0)
+    return RMSQ_EINVAL;
+  const rmsq_launch l = rmsq::default_pad_launch(out_ld);
+  if (launch) *launch = l;
+  if (grid) *grid = (tokens + l.rows_per_block - 1) / l.rows_per_block;
   return RMSQ_OK;
 }
 

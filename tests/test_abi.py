@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
     for n in ("rmsq_fused", "rmsq_fused_with_launch", "rmsq_fused_timed", "rmsq_validate",
               "rmsq_silu_mul_quant", "rmsq_silu_mul_quant_ex", "rmsq_silu_mul_quant_validate",
               "rmsq_silu_mul_query_launch", "rmsq_rms_norm_pad", "rmsq_rms_norm_pad_ex",
-              "rmsq_rms_norm_pad_validate", "rmsq_qk_norm_rope", "rmsq_qk_norm_rope_ex",
+              "rmsq_rms_norm_pad_validate", "rmsq_rms_norm_pad_query_launch",
+              "rmsq_qk_norm_rope", "rmsq_qk_norm_rope_ex",
               "rmsq_qk_norm_rope_validate", "rmsq_qk_norm_rope_query_launch",
               "rmsq_query_launch",
               "rmsq_block_to_rowblock", "rmsq_convert", "rmsq_status_string",
@@ -209,6 +210,18 @@ def VP(B, x=X, r=R, w=W, eps=1e-6, out=Q, ro=RO, t=T, h=H, ld=H + 64):
     return B.rmsq_rms_norm_pad_validate(x, r, w, eps, out, ro, t, h, ld)
 
 
+def test_pad_query_launch(B):
+    l, grid = B.rmsq_rms_norm_pad_query_launch(4096, 2880, 3072)
+    assert l.as_tuple() == (64, 6, 1, 0) and grid == 4096   # one wave per padded row
+    l, grid = B.rmsq_rms_norm_pad_query_launch(100, 8192, 8192)
+    assert l.as_tuple() == B.rmsq_query_launch(0, 100, 8192, 0)[0].as_tuple()
+    l, _ = B.rmsq_rms_norm_pad_query_launch(8, 520, 1024)
+    assert l.threads_per_row * l.chunks_per_thread * 8 >= 1024
+    for bad in ((4, 2880, 2872), (4, 12, 16), (-1, 64, 64), (4, 64, 65536 + 8)):
+        with pytest.raises(B.RmsqError):
+            B.rmsq_rms_norm_pad_query_launch(*bad)
+
+
 def test_pad_valid_calls(B):
     assert VP(B) == B.RMSQ_OK
     assert VP(B, ld=H) == B.RMSQ_OK
@@ -304,8 +317,10 @@ def test_rope_query_launch(B, hq, hkv, d):
 
 
 def test_rope_default_shape_follows_the_batch(B):
-    """Small batches get one head per lane (more, shorter waves); large ones several heads per
-    lane (more loads in flight) -- for the 32 q + 8 kv heads of size 128 layout."""
+    """Small batches get one head per lane (more, shorter waves), batches that fill the chip
+    once the most heads per lane that fit, larger ones two heads per lane in single-wave
+    workgroups -- for the 32 q + 8 kv heads of size 128 layout."""
     assert B.rmsq_qk_norm_rope_query_launch(1, 32, 8, 128)[:2] == (40, 1)
     assert B.rmsq_qk_norm_rope_query_launch(256, 32, 8, 128)[:2] == (40, 1)
     assert B.rmsq_qk_norm_rope_query_launch(4096, 32, 8, 128)[:2] == (40, 5)
+    assert B.rmsq_qk_norm_rope_query_launch(16384, 32, 8, 128)[:2] == (16, 2)

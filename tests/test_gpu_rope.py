@@ -82,6 +82,14 @@ def test_workload_shapes(T, neox):
     assert not np.array_equal(got, x)
 
 
+def test_largest_batch_default_shape():
+    """16384 tokens: the default shape switches to 2 heads per lane (multi-round grid)."""
+    x, qw, kw, pos = wl_inputs(16384, max_pos=32768)
+    print("rope workload T=16384", flush=True)
+    got, ref = run_rope(x, qw, kw, pos, 32, 8, 128, True, max_pos=32768)
+    assert_same(got, ref, "T=16384")
+
+
 @pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("neox", [True, False])
 @pytest.mark.parametrize("hq,hkv", [(1, 1), (4, 2), (12, 4), (64, 8)])
@@ -93,7 +101,7 @@ def test_head_sizes_and_counts(D, neox, hq, hkv):
     assert_same(got, ref, f"D={D} hq={hq} hkv={hkv}")
 
 
-@pytest.mark.parametrize("hpb,hpl", [(1, 1), (2, 1), (7, 1), (64, 1), (8, 2), (30, 3), (16, 4),
+@pytest.mark.parametrize("hpb,hpl", [(1, 1), (2, 1), (7, 1), (64, 1), (8, 2), (16, 2), (30, 3), (16, 4),
                                      (40, 4), (40, 5), (36, 6), (48, 6), (6, 6), (20, 5)])
 def test_launch_shapes(hpb, hpl):
     """Every launch shape gives the same bits: partial waves ((hpb / hpl) * 8 lanes not a

@@ -44,7 +44,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 def kernel_source_hash():
     h = hashlib.sha256()
     for p in ("rmsnorm_quantization_amd/csrc/rmsq_kernels.hpp",
-              "rmsnorm_quantization_amd/csrc/rmsq_device.hpp", "rmsnorm_quantization_amd/build.py"):
+              "rmsnorm_quantization_amd/csrc/rmsq_device.hpp",
+              "rmsnorm_quantization_amd/csrc/rmsq.hip", "rmsnorm_quantization_amd/build.py"):
         h.update(open(os.path.join(ROOT, p), "rb").read())
     return h.hexdigest()[:16]
 

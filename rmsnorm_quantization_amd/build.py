@@ -1,4 +1,5 @@
-"""Build librmsq.so (the HIP kernels + C ABI) in-tree for gfx950 with hipcc.
+"""Build librmsq.so (the HIP kernels + C ABI) in-tree for gfx950 with hipcc, and beside it
+librmsq_probe.so (the memory-only reference kernel of include/rmsq_probe.h, for measurement).
 
 Flags that matter for results:
   -ffp-contract=off                          no FMA contraction of the binary32 steps
@@ -17,6 +18,9 @@ KERNEL_SOURCES = [os.path.join(PKG, "csrc", "rmsq_device.hpp"),
                   os.path.join(PKG, "csrc", "rmsq_kernels.hpp")]
 DEPS = SRC + KERNEL_SOURCES + [os.path.join(ROOT, "include", "rmsq.h")]
 LIB = os.path.join(PKG, "librmsq.so")
+PROBE_SRC = [os.path.join(PKG, "csrc", "rmsq_probe.hip")]
+PROBE_DEPS = PROBE_SRC + [os.path.join(ROOT, "include", "rmsq_probe.h")]
+PROBE_LIB = os.path.join(PKG, "librmsq_probe.so")
 ARCH = "gfx950"
 
 
@@ -27,13 +31,13 @@ def hipcc():
     return "hipcc"
 
 
-def command(out=LIB, extra=()):
+def command(out=LIB, extra=(), src=None):
     return [
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-fvisibility=hidden", "-Wall", "-I", os.path.join(ROOT, "include"),
-        *extra, *SRC, "-o", out,
+        *extra, *(SRC if src is None else src), "-o", out,
     ]
 
 
@@ -49,6 +53,25 @@ def build_library(verbose: bool = False) -> str:
     return LIB
 
 
+def build_probe_library(verbose: bool = False) -> str:
+    cmd = command(PROBE_LIB + ".tmp", src=PROBE_SRC)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed to build librmsq_probe.so")
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
+    return PROBE_LIB
+
+
+def probe_is_stale() -> bool:
+    if not os.path.exists(PROBE_LIB):
+        return True
+    t = os.path.getmtime(PROBE_LIB)
+    return any(os.path.getmtime(p) > t for p in PROBE_DEPS)
+
+
 def is_stale() -> bool:
     if not os.path.exists(LIB):
         return True
@@ -58,3 +81,4 @@ def is_stale() -> bool:
 
 if __name__ == "__main__":
     print(build_library(verbose=True))
+    print(build_probe_library(verbose=True))

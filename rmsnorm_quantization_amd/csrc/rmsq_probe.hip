@@ -1,0 +1,101 @@
+// rmsq_probe.hip -- the memory-only reference kernel declared in include/rmsq_probe.h.  It
+// mirrors the fused kernel's row and chunk mapping (one workgroup per row, chunk c on thread
+// c mod threads_per_row, 16-byte non-temporal loads and stores) so that the two differ only in
+// the arithmetic.
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "rmsq_probe.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct ProbeArgs {
+  const u32x4* in0;
+  const u32x4* in1;
+  u32x4* out0;
+  uint8_t* out1;
+  int64_t nch;  // 16-byte chunks per row
+  int32_t tpr;
+};
+
+template <int VPT, int OUT1>
+__global__ void __launch_bounds__(1024) stream_probe_kernel(ProbeArgs a) {
+  const size_t base = (size_t)blockIdx.x * (size_t)a.nch;
+  const uint32_t lr = threadIdx.x;
+  u32x4 v[VPT];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const size_t c = base + lr + (size_t)k * a.tpr;
+    v[k] = __builtin_nontemporal_load(a.in0 + c);
+    if (a.in1) v[k] ^= __builtin_nontemporal_load(a.in1 + c);
+  }
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const size_t c = base + lr + (size_t)k * a.tpr;
+    if (a.out0) __builtin_nontemporal_store(v[k], a.out0 + c);
+    if constexpr (OUT1 == 8) {
+      if (a.out1)
+        __builtin_nontemporal_store((u32x2){v[k][0] ^ v[k][2], v[k][1] ^ v[k][3]},
+                                    reinterpret_cast<u32x2*>(a.out1) + c);
+    } else if constexpr (OUT1 == 4) {
+      if (a.out1)
+        __builtin_nontemporal_store(v[k][0] ^ v[k][1] ^ v[k][2] ^ v[k][3],
+                                    reinterpret_cast<uint32_t*>(a.out1) + c);
+    }
+  }
+}
+
+template <int OUT1>
+const void* pick(int vpt) {
+  switch (vpt) {
+    case 1: return reinterpret_cast<const void*>(&stream_probe_kernel<1, OUT1>);
+    case 2: return reinterpret_cast<const void*>(&stream_probe_kernel<2, OUT1>);
+    case 3: return reinterpret_cast<const void*>(&stream_probe_kernel<3, OUT1>);
+    case 4: return reinterpret_cast<const void*>(&stream_probe_kernel<4, OUT1>);
+    case 5: return reinterpret_cast<const void*>(&stream_probe_kernel<5, OUT1>);
+    case 6: return reinterpret_cast<const void*>(&stream_probe_kernel<6, OUT1>);
+    case 7: return reinterpret_cast<const void*>(&stream_probe_kernel<7, OUT1>);
+    case 8: return reinterpret_cast<const void*>(&stream_probe_kernel<8, OUT1>);
+    default: return nullptr;
+  }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace
+
+extern "C" int rmsq_probe_stream(const void* in0, const void* in1, void* out0, void* out1,
+                                 int64_t rows, int64_t hidden, int out1_bytes_per_chunk,
+                                 int threads_per_row, int chunks_per_thread, void* start_event,
+                                 void* stop_event, void* stream) {
+  if (rows < 0 || rows > 0x7FFFFFFFLL || hidden < 8 || hidden % 8 != 0) return -1;
+  if (threads_per_row < 64 || threads_per_row > 1024 || threads_per_row % 64 != 0) return -1;
+  if (chunks_per_thread < 1 || chunks_per_thread > 8) return -1;
+  if ((int64_t)threads_per_row * chunks_per_thread * 8 != hidden) return -1;
+  if (out1_bytes_per_chunk != 0 && out1_bytes_per_chunk != 4 && out1_bytes_per_chunk != 8)
+    return -1;
+  if (rows == 0) return 0;
+  if (!in0) return -1;
+  if (!aligned16(in0) || !aligned16(in1) || !aligned16(out0) || !aligned16(out1)) return -2;
+  const void* fn = out1_bytes_per_chunk == 8   ? pick<8>(chunks_per_thread)
+                   : out1_bytes_per_chunk == 4 ? pick<4>(chunks_per_thread)
+                                               : pick<0>(chunks_per_thread);
+  ProbeArgs a;
+  a.in0 = static_cast<const u32x4*>(in0);
+  a.in1 = static_cast<const u32x4*>(in1);
+  a.out0 = static_cast<u32x4*>(out0);
+  a.out1 = out1_bytes_per_chunk ? static_cast<uint8_t*>(out1) : nullptr;
+  a.nch = hidden / 8;
+  a.tpr = threads_per_row;
+  void* args[] = {&a};
+  const hipError_t e = hipExtLaunchKernel(
+      fn, dim3((uint32_t)rows), dim3((uint32_t)threads_per_row), args, 0,
+      static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(start_event),
+      static_cast<hipEvent_t>(stop_event), 0);
+  return e == hipSuccess ? 0 : -5;
+}

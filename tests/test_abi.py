@@ -324,3 +324,32 @@ def test_rope_default_shape_follows_the_batch(B):
     assert B.rmsq_qk_norm_rope_query_launch(256, 32, 8, 128)[:2] == (40, 1)
     assert B.rmsq_qk_norm_rope_query_launch(4096, 32, 8, 128)[:2] == (40, 5)
     assert B.rmsq_qk_norm_rope_query_launch(16384, 32, 8, 128)[:2] == (16, 2)
+
+
+# ------------------------------------------------------------------ measurement probe library
+def test_probe_library_exports_and_checks_arguments():
+    """librmsq_probe.so (include/rmsq_probe.h) exports exactly its entry point and rejects bad
+    shapes on the host before any device call."""
+    import ctypes
+
+    from rmsnorm_quantization_amd import build
+
+    if build.probe_is_stale():
+        build.build_probe_library()
+    out = subprocess.run(["nm", "-D", "--defined-only", build.PROBE_LIB], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
+    assert {e for e in exported if "rmsq" in e} == {"rmsq_probe_stream"}
+    L = ctypes.CDLL(build.PROBE_LIB)
+    p = ctypes.c_void_p
+    L.rmsq_probe_stream.argtypes = [p, p, p, p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_int, p, p, p]
+
+    def call(rows=4, hidden=4096, out1=8, tpr=256, vpt=2, a=X, b=R, c=RO, d=Q):
+        return L.rmsq_probe_stream(a, b, c, d, rows, hidden, out1, tpr, vpt, None, None, None)
+
+    assert call(rows=0) == 0
+    for kw in (dict(hidden=4000), dict(tpr=96), dict(tpr=2048, vpt=1, hidden=16384),
+               dict(vpt=9), dict(tpr=256, vpt=3), dict(out1=2), dict(rows=-1), dict(a=None)):
+        assert call(**kw) == -1, kw
+    assert call(a=X + 8) == -2 and call(d=Q + 4) == -2

@@ -467,10 +467,23 @@ def probe_leg(args, sets, T, H, mode, shape, stream, evs):
     return {"kernel_us": sum(per) / len(per) * 1e3, "bytes": nbytes}
 
 
+def host_threads():
+    """Threads the CPU leg may use: the CPUs this process may run on, at most 16 (one GPU's
+    share of a host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def cpu_leg(wl, T, H, mode, G, flags, budget_s=12.0):
-    """The oracle as it stands (single thread) on whole rows of the same workload, processed
-    in chunks until about budget_s seconds of CPU work; returns GB/s with the same
-    algorithmic byte count per row."""
+    """The oracle as it stands on whole rows of the same workload: first one thread, in chunks
+    of 64 rows until about budget_s seconds of CPU work (or the whole batch); then the same rows
+    split over host_threads() threads (the oracle is C called through ctypes, which releases the
+    GIL).  GB/s with the same algorithmic byte count per row as the GPU leg."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
 
     import oracle as O
@@ -481,19 +494,14 @@ def cpu_leg(wl, T, H, mode, G, flags, budget_s=12.0):
         qkv, qw, kw, pos = synth.make_rope_inputs(wl.index, T)
         xb, qwb, kwb, posn = synth.bits(qkv), synth.bits(qw), synth.bits(kw), pos.numpy()
         cache = O.rope_cache(wl.max_position, H, wl.rope_base)
-        rows = 0
-        t0 = time.perf_counter()
-        while rows < T and time.perf_counter() - t0 < budget_s:
-            n = min(64, T - rows)
-            O.qk_norm_rope(xb[rows:rows + n], qwb, kwb, cache, posn[rows:rows + n], wl.eps, hq,
-                           hkv, H)
-            rows += n
-        dt = time.perf_counter() - t0
-        rd, wr = rope_bytes(rows, hq, hkv, H)
-        return {"value": (rd + wr) / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-                "sample": f"first {rows} of {T} tokens, {dt:.1f} s, single thread, "
-                          f"{os.cpu_count()} host CPUs visible", "tokens_per_s": rows / dt}
-    if wl.kind == "act":
+
+        def run_rows(lo, hi):
+            O.qk_norm_rope(xb[lo:hi], qwb, kwb, cache, posn[lo:hi], wl.eps, hq, hkv, H)
+
+        def nbytes(rows):
+            return sum(rope_bytes(rows, hq, hkv, H))
+        unit = "tokens"
+    elif wl.kind == "act":
         xb = synth.bits(synth.make_act_inputs(wl.index, T, H))
         if mode == 0:
             s_in = float(np.abs(O.silu_mul(synth.bits(synth.make_act_warmup(wl.index, H)))).max()
@@ -503,62 +511,70 @@ def cpu_leg(wl, T, H, mode, G, flags, budget_s=12.0):
         else:
             s_in = 0.0
         G4 = 16 if mode == 3 else G
-        rows = 0
-        t0 = time.perf_counter()
-        while rows < T and time.perf_counter() - t0 < budget_s:
-            n = min(64, T - rows)
-            O.silu_mul_quant(xb[rows:rows + n], mode, scale_in=s_in, group_size=G4,
-                             flags=flags & ~1)
-            rows += n
-        dt = time.perf_counter() - t0
-        rd, wr = algorithmic_bytes(mode, rows, H, G4, flags, False, "act")
-        return {"value": (rd + wr) / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-                "sample": f"first {rows} of {T} rows ({rows * H} outputs), {dt:.1f} s, "
-                          f"single thread, {os.cpu_count()} host CPUs visible",
-                "tokens_per_s": rows / dt}
-    if wl.kind == "pad":
+
+        def run_rows(lo, hi):
+            O.silu_mul_quant(xb[lo:hi], mode, scale_in=s_in, group_size=G4, flags=flags & ~1)
+
+        def nbytes(rows):
+            return sum(algorithmic_bytes(mode, rows, H, G4, flags, False, "act"))
+        unit = "rows"
+    elif wl.kind == "pad":
         ld = -(-H // wl.pad_multiple) * wl.pad_multiple
         x, r, w = synth.make_inputs(wl.index, T, H)
         xb, rb, wb = synth.bits(x), synth.bits(r), synth.bits(w)
-        rows = 0
-        t0 = time.perf_counter()
-        while rows < T and time.perf_counter() - t0 < budget_s:
-            n = min(64, T - rows)
-            O.rms_norm_pad(xb[rows:rows + n], rb[rows:rows + n], wb, wl.eps, ld)
-            rows += n
-        dt = time.perf_counter() - t0
-        rd, wr = pad_bytes(rows, H, ld)
-        return {"value": (rd + wr) / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-                "sample": f"first {rows} of {T} rows, {dt:.1f} s, single thread, "
-                          f"{os.cpu_count()} host CPUs visible", "tokens_per_s": rows / dt}
-    x, r, w = synth.make_inputs(wl.index, T, H)
-    xb, rb, wb = synth.bits(x), (synth.bits(r) if r is not None else None), synth.bits(w)
-    if mode == 0:
-        if wl.static_scale is not None:
-            s_in = wl.static_scale
-        else:
-            xw, rw = synth.make_warmup(wl.index, H)
-            y = O.rms_y(synth.bits(xw), synth.bits(rw), wb, wl.eps)
-            s_in = float(np.abs(y).max() / np.float32(448))
-    elif mode == 3:
-        s_in = float(np.float32(448 * 6) / np.abs(O.rms_y(xb[:256], None if rb is None else rb[:256],
-                                                        wb, wl.eps)).max())
+
+        def run_rows(lo, hi):
+            O.rms_norm_pad(xb[lo:hi], rb[lo:hi], wb, wl.eps, ld)
+
+        def nbytes(rows):
+            return sum(pad_bytes(rows, H, ld))
+        unit = "rows"
     else:
-        s_in = 0.0
-    chunk = max(1, min(T, 64))
+        x, r, w = synth.make_inputs(wl.index, T, H)
+        xb, rb, wb = synth.bits(x), (synth.bits(r) if r is not None else None), synth.bits(w)
+        if mode == 0:
+            if wl.static_scale is not None:
+                s_in = wl.static_scale
+            else:
+                xw, rw = synth.make_warmup(wl.index, H)
+                y = O.rms_y(synth.bits(xw), synth.bits(rw), wb, wl.eps)
+                s_in = float(np.abs(y).max() / np.float32(448))
+        elif mode == 3:
+            s_in = float(np.float32(448 * 6) / np.abs(
+                O.rms_y(xb[:256], None if rb is None else rb[:256], wb, wl.eps)).max())
+        else:
+            s_in = 0.0
+
+        def run_rows(lo, hi):
+            O.fused(xb[lo:hi], None if rb is None else rb[lo:hi], wb, wl.eps, mode,
+                    scale_in=s_in, group_size=G, flags=flags & ~1)
+
+        def nbytes(rows):
+            return sum(algorithmic_bytes(mode, rows, H, G, flags, rb is not None))
+        unit = "rows"
+
+    chunk = 64
     rows = 0
     t0 = time.perf_counter()
     while rows < T and time.perf_counter() - t0 < budget_s:
         n = min(chunk, T - rows)
-        O.fused(xb[rows:rows + n], None if rb is None else rb[rows:rows + n], wb, wl.eps, mode,
-                scale_in=s_in, group_size=G, flags=flags & ~1)
+        run_rows(rows, rows + n)
         rows += n
-    dt = time.perf_counter() - t0
-    rd, wr = algorithmic_bytes(mode, rows, H, G, flags, rb is not None)
-    return {"value": (rd + wr) / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {rows} of {T} rows ({rows * H} elements), {dt:.1f} s, "
-                      f"single thread, {os.cpu_count()} host CPUs visible",
-            "tokens_per_s": rows / dt}
+    dt1 = time.perf_counter() - t0
+    nthr = min(host_threads(), rows)
+    step = -(-rows // (4 * nthr))  # four spans per thread
+    spans = [(lo, min(lo + step, rows)) for lo in range(0, rows, step)]
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=nthr) as ex:
+        list(ex.map(lambda sp: run_rows(*sp), spans))
+    dtn = time.perf_counter() - t0
+    b = nbytes(rows)
+    return {"value": b / dtn / 1e9, "unit": "GB/s", "cores": nthr, "kind": "oracle",
+            "sample": f"first {rows} of {T} {unit}: {dt1:.1f} s on one thread, {dtn:.2f} s on "
+                      f"{nthr} threads ({os.cpu_count()} host CPUs visible)",
+            "tokens_per_s": rows / dtn,
+            "single_thread": {"value": b / dt1 / 1e9, "unit": "GB/s", "cores": 1,
+                              "tokens_per_s": rows / dt1}}
 
 
 def load_traffic(key):

@@ -64,6 +64,9 @@ def lib():
         L.orc_fused.argtypes = [p, p, p, C.c_float, C.c_int, C.c_float, p, p, p,
                                 i64, i64, C.c_int, C.c_uint, i64, p]
         L.orc_fused.restype = C.c_int
+        L.rmsq_ref_fused.argtypes = [p, p, p, C.c_float, C.c_int, p, p, p, p, i64, i64,
+                                     C.c_int, C.c_uint, i64]
+        L.rmsq_ref_fused.restype = C.c_int
         _lib = L
     return _lib
 

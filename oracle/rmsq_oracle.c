@@ -339,6 +339,17 @@ int orc_fused(const uint16_t* x, const uint16_t* residual, const uint16_t* weigh
 }
 
 /* ------------------------------------------------------------------ RMSNorm -> padded bf16 */
+int rmsq_ref_fused(const void* x, const void* residual, const void* weight, float eps, int mode,
+                   const float* scale_in, void* out_q, void* out_scales, void* residual_out,
+                   int64_t tokens, int64_t hidden, int group_size, unsigned flags,
+                   int64_t scale_ld) {
+  const int needs_scale = mode == ORC_FP8_STATIC || mode == ORC_FP4_BLOCK16;
+  if (needs_scale && !scale_in) return -1;
+  return orc_fused((const uint16_t*)x, (const uint16_t*)residual, (const uint16_t*)weight, eps,
+                   mode, needs_scale ? *scale_in : 0.0f, (uint8_t*)out_q, out_scales,
+                   (uint16_t*)residual_out, tokens, hidden, group_size, flags, scale_ld, NULL);
+}
+
 int orc_rms_norm_pad(const uint16_t* x, const uint16_t* residual, const uint16_t* weight,
                      float eps, uint16_t* out, uint16_t* residual_out, int64_t T, int64_t H,
                      int64_t out_ld) {

@@ -97,6 +97,16 @@ int orc_fused(const uint16_t* x, const uint16_t* residual, const uint16_t* weigh
               int64_t T, int64_t H, int group_size, unsigned flags, int64_t scale_ld,
               float* pre_q);
 
+/* The whole operation with the argument list of the GPU library's fused entry point, on host
+ * buffers and without a stream: the oracle's counterpart of that call, so that a caller can run
+ * both sides of a parity check with one set of arguments.  scale_in points at one f32 (FP8
+ * static dequant scale, FP4 global scale) or is NULL for the dynamic modes.  Same behaviour and
+ * return value as orc_fused (no pre_q output). */
+int rmsq_ref_fused(const void* x, const void* residual, const void* weight, float eps, int mode,
+                   const float* scale_in, void* out_q, void* out_scales, void* residual_out,
+                   int64_t tokens, int64_t hidden, int group_size, unsigned flags,
+                   int64_t scale_ld);
+
 /* ---- residual add + RMSNorm -> padded bf16 output (vLLM docs "Fusion torch.compile passes",
  * section "RMSNorm + padding (fuse_act_padding)": the residual add and RMSNorm fused with the
  * padding of the hidden dimension to the multiple a downstream GEMM needs; hidden size 2880).

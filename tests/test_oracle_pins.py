@@ -299,3 +299,32 @@ def test_empty_and_invalid(orc):
         orc.fused(np.zeros((2, 64), np.uint16), None, w, 1e-6, orc.FP8_GROUP, group_size=32)
     with pytest.raises(ValueError):
         orc.fused(np.zeros((2, 64), np.uint16), None, w, 1e-6, 7)
+
+
+def test_ref_fused_entry_matches_orc_fused(orc):
+    """rmsq_ref_fused (the GPU entry point's argument list on host buffers) is orc_fused."""
+    import ctypes
+
+    rng = np.random.default_rng(11)
+    T, H = 5, 256
+    x = bf16_bits(rng.standard_normal((T, H)))
+    r = bf16_bits(rng.standard_normal((T, H)))
+    w = bf16_bits(rng.uniform(0.5, 1.5, H))
+    L = orc.lib()
+    for mode, G, sc in ((orc.FP8_STATIC, 0, 0.02), (orc.FP8_TOKEN, 0, None),
+                        (orc.FP8_GROUP, 64, None), (orc.FP4_BLOCK16, 16, 400.0)):
+        ref = orc.fused(x, r, w, 1e-6, mode, scale_in=sc or 0.0, group_size=G)
+        q = np.zeros_like(ref["q"])
+        s = None if ref["scales"] is None else np.zeros_like(ref["scales"])
+        ro = np.zeros_like(r)
+        s_in = None if sc is None else np.array([sc], np.float32)
+        ptr = (lambda a: None if a is None else a.ctypes.data)
+        rc = L.rmsq_ref_fused(ptr(x), ptr(r), ptr(w), 1e-6, mode, ptr(s_in), ptr(q), ptr(s),
+                              ptr(ro), T, H, G, 0, 0)
+        assert rc == 0
+        assert np.array_equal(q, ref["q"]) and np.array_equal(ro, ref["residual_out"])
+        if s is not None:
+            assert np.array_equal(s, ref["scales"])
+    # a static mode without its scale is refused
+    assert L.rmsq_ref_fused(x.ctypes.data, None, w.ctypes.data, 1e-6, orc.FP8_STATIC, None,
+                            q.ctypes.data, None, None, T, H, 0, 0, 0) == -1

@@ -196,13 +196,57 @@ def rope_leg(args, wl, T, D):
     copy_gbs = copy_ceiling(dev, stream)
     return {"ms_per_step": ms_per_step, "ms_per_step_graph": ms_per_step_graph,
             "avg_launch_ms": sum(per) / len(per), "median_launch_ms": per[len(per) // 2],
+            "p10_launch_ms": per[len(per) // 10], "p90_launch_ms": per[(9 * len(per)) // 10],
             "bytes": rd + wr, "read": rd, "write": wr, "sets": nsets, "launch": (hpb, hpl),
             "copy_gbs": copy_gbs, "device": torch.cuda.get_device_name(dev)}
 
 
+def _probe_lib():
+    import ctypes
+
+    from rmsnorm_quantization_amd import build as hb
+
+    if not os.path.exists(hb.PROBE_LIB):
+        hb.build_probe_library()
+    L = ctypes.CDLL(hb.PROBE_LIB)
+    p = ctypes.c_void_p
+    L.rmsq_probe_stream.argtypes = [p, p, p, p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_int, p, p, p]
+    L.rmsq_probe_stream.restype = ctypes.c_int
+    return L
+
+
 def copy_ceiling(dev, stream):
-    """GB/s of a plain 256 MiB device copy (practical HBM ceiling, for context)."""
+    """The practical HBM ceiling for streaming: GB/s of a plain 128-bit copy kernel (the probe
+    library with one input and one output) over two 256 MiB buffer pairs, 20 launches each
+    stamped by its own dispatch; and, for context, torch's own device copy."""
     import torch
+
+    L = _probe_lib()
+    H = 4096
+    rows = (256 << 20) // (2 * H)
+    pairs = [(torch.empty((rows, H), dtype=torch.bfloat16, device=dev),
+              torch.empty((rows, H), dtype=torch.bfloat16, device=dev)) for _ in range(2)]
+    sh = stream.cuda_stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(20)]
+    for a_, b_ in evs:
+        a_.record(stream)
+        b_.record(stream)
+    for i in range(4):
+        src, dst = pairs[i % 2]
+        L.rmsq_probe_stream(src.data_ptr(), None, dst.data_ptr(), None, rows, H, 0, 256, 2,
+                            None, None, sh)
+    torch.cuda.synchronize()
+    for i, (a_, b_) in enumerate(evs):
+        src, dst = pairs[i % 2]
+        st = L.rmsq_probe_stream(src.data_ptr(), None, dst.data_ptr(), None, rows, H, 0, 256, 2,
+                                 a_.cuda_event, b_.cuda_event, sh)
+        if st:
+            raise RuntimeError(f"rmsq_probe_stream (copy) failed ({st})")
+    torch.cuda.synchronize()
+    per = sorted(a_.elapsed_time(b_) for a_, b_ in evs)
+    probe_copy = 2 * rows * H * 2 / (per[len(per) // 2] * 1e-3) / 1e9
 
     copy_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
     copy_dst = torch.empty_like(copy_src)
@@ -215,7 +259,8 @@ def copy_ceiling(dev, stream):
         copy_dst.copy_(copy_src)
     c1.record(stream)
     torch.cuda.synchronize()
-    return 2 * copy_src.numel() * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    torch_copy = 2 * copy_src.numel() * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    return {"copy_GBs": probe_copy, "torch_copy_GBs": torch_copy}
 
 
 def scale_layout(mode, T, H, G, flags):
@@ -423,7 +468,8 @@ def gpu_leg(args, wl, T, H, mode, G, flags):
 
     return {"ms_per_step": ms_per_step, "ms_per_step_graph": ms_per_step_graph,
             "avg_launch_ms": avg_launch_ms,
-            "median_launch_ms": med_launch_ms, "bytes": rd + wr, "read": rd, "write": wr,
+            "median_launch_ms": med_launch_ms, "p10_launch_ms": per[len(per) // 10],
+            "p90_launch_ms": per[(9 * len(per)) // 10], "bytes": rd + wr, "read": rd, "write": wr,
             "sets": nsets, "launch": shape, "copy_gbs": copy_gbs, "ceiling": ceiling,
             "device": torch.cuda.get_device_name(dev)}
 
@@ -432,17 +478,7 @@ def probe_leg(args, sets, T, H, mode, shape, stream, evs):
     """Time librmsq_probe.so's memory-only kernel over the same buffer sets: it reads x and the
     residual and writes the new residual and codes-sized output in the fused kernel's layout,
     with no arithmetic.  Returns its mean dispatch-stamped duration and bytes."""
-    import ctypes
-
-    from rmsnorm_quantization_amd import build as hb
-
-    if not os.path.exists(hb.PROBE_LIB):
-        hb.build_probe_library()
-    L = ctypes.CDLL(hb.PROBE_LIB)
-    p = ctypes.c_void_p
-    L.rmsq_probe_stream.argtypes = [p, p, p, p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
-                                    ctypes.c_int, ctypes.c_int, p, p, p]
-    L.rmsq_probe_stream.restype = ctypes.c_int
+    L = _probe_lib()
     out1 = 4 if mode == 3 else 8
     ptr = (lambda t: None if t is None else t.data_ptr())
     sh = stream.cuda_stream
@@ -465,6 +501,17 @@ def probe_leg(args, sets, T, H, mode, shape, stream, evs):
     nbytes = T * (2 * H + (2 * H if sets[0]["r"] is not None else 0)
                   + (2 * H if sets[0]["ro"] is not None else 0) + H * out1 // 8)
     return {"kernel_us": sum(per) / len(per) * 1e3, "bytes": nbytes}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
 
 
 def host_threads():
@@ -564,14 +611,18 @@ def cpu_leg(wl, T, H, mode, G, flags, budget_s=12.0):
     nthr = min(host_threads(), rows)
     step = -(-rows // (4 * nthr))  # four spans per thread
     spans = [(lo, min(lo + step, rows)) for lo in range(0, rows, step)]
-    t0 = time.perf_counter()
+    times = []
     with ThreadPoolExecutor(max_workers=nthr) as ex:
-        list(ex.map(lambda sp: run_rows(*sp), spans))
-    dtn = time.perf_counter() - t0
+        for _ in range(3):  # median of three threaded passes
+            t0 = time.perf_counter()
+            list(ex.map(lambda sp: run_rows(*sp), spans))
+            times.append(time.perf_counter() - t0)
+    dtn = sorted(times)[1]
     b = nbytes(rows)
     return {"value": b / dtn / 1e9, "unit": "GB/s", "cores": nthr, "kind": "oracle",
             "sample": f"first {rows} of {T} {unit}: {dt1:.1f} s on one thread, {dtn:.2f} s on "
-                      f"{nthr} threads ({os.cpu_count()} host CPUs visible)",
+                      f"{nthr} threads (median of 3; {os.cpu_count()} host CPUs visible, "
+                      f"{cpu_model()})",
             "tokens_per_s": rows / dtn,
             "single_thread": {"value": b / dt1 / 1e9, "unit": "GB/s", "cores": 1,
                               "tokens_per_s": rows / dt1}}
@@ -771,18 +822,27 @@ def main():
             "rotating_sets": g["sets"], "parallelism": "single GPU",
         },
         "tokens_per_s": round(T / (step_ms * 1e-3), 1),
+        "latency_us_per_launch": round(step_ms * 1e3, 3),
         "timing": ("one HIP graph of K launches" if g["ms_per_step_graph"]
                    else "K eager back-to-back launches"),
         "eager": {"ms_per_step": round(g["ms_per_step"], 5), "GBs": round(eager_gbs, 1)},
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "bytes_per_step": g["bytes"],
         "kernel_us": {"mean": round(g["avg_launch_ms"] * 1e3, 3),
-                      "median": round(g["median_launch_ms"] * 1e3, 3)},
-        "copy_kernel_GBs": round(g["copy_gbs"], 1),
+                      "median": round(g["median_launch_ms"] * 1e3, 3),
+                      "p10": round(g["p10_launch_ms"] * 1e3, 3),
+                      "p90": round(g["p90_launch_ms"] * 1e3, 3)},
+        "copy_ceiling": {
+            "kernel": "128-bit copy over 2 x 256 MiB (librmsq_probe.so), median of 20",
+            "GBs": round(g["copy_gbs"]["copy_GBs"], 1),
+            "frac_of_peak": round(g["copy_gbs"]["copy_GBs"] / HBM_PEAK_GBS, 4),
+            "torch_copy_GBs": round(g["copy_gbs"]["torch_copy_GBs"], 1),
+            "eighty_pct_of_peak_reachable": g["copy_gbs"]["copy_GBs"] >= 0.8 * HBM_PEAK_GBS},
         "device": g["device"],
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "frac_of_copy_ceiling": round(achieved / g["copy_gbs"]["copy_GBs"], 4),
             "traffic": None if tr is None else tr["bytes_per_launch"],
         },
         "cpu_baseline": None,

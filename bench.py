@@ -42,11 +42,16 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_hash():
+    """Identity of what the HBM counters were taken on: the kernel and launch-heuristic sources
+    of librmsq and its hipcc command line (flags only, paths stripped)."""
+    from rmsnorm_quantization_amd import build as hb
+
     h = hashlib.sha256()
     for p in ("rmsnorm_quantization_amd/csrc/rmsq_kernels.hpp",
               "rmsnorm_quantization_amd/csrc/rmsq_device.hpp",
-              "rmsnorm_quantization_amd/csrc/rmsq.hip", "rmsnorm_quantization_amd/build.py"):
+              "rmsnorm_quantization_amd/csrc/rmsq.hip"):
         h.update(open(os.path.join(ROOT, p), "rb").read())
+    h.update(" ".join(a for a in hb.command("lib.so")[1:] if not a.startswith("/")).encode())
     return h.hexdigest()[:16]
 
 

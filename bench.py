@@ -658,7 +658,7 @@ def _db_rows(db, sql):
         con.close()
 
 
-def summarize(ktrace_db, fetch_db, write_db, key, title, commands, out_md):
+def summarize(ktrace_db, fetch_db, write_db, key, title, commands, out_md, util=()):
     """Turn the three rocprofv3 databases of one bench configuration into a short text summary
     under profiles/ and the traffic entry bench.py reports.  Counters are KiB per dispatch;
     each is scaled by what it reads for the plain 256 MiB copy in the same run."""
@@ -717,6 +717,17 @@ def summarize(ktrace_db, fetch_db, write_db, key, title, commands, out_md):
               f"| FETCH_SIZE | {f_k:.2f} | {f_copy:.2f} | {f_scale:.5f} | {fetch_b:,.0f} |",
               f"| WRITE_SIZE | {w_k:.2f} | {w_copy:.2f} | {w_scale:.5f} | {write_b:,.0f} |", "",
               f"Measured HBM traffic per launch: {fetch_b + write_b:,.0f} bytes.", ""]
+    if util:
+        lines += ["## Utilization (rocprofv3 derived metrics, one per run)", "",
+                  "| metric | benched kernel, median over dispatches | dispatches |", "|---|---|---|"]
+        for name, db in util:
+            rows = _db_rows(db, "select kernel_name, value from counters_collection "
+                                "where counter_name = '%s'" % name)
+            vals = [v for k, v in rows if k == main_k[0]]
+            lines.append(f"| {name} | {statistics.median(vals):.2f} | {len(vals)} |")
+        lines += ["", "VALUBusy: % of GPU time the vector ALUs issue; MemUnitStalled: % of GPU time "
+                  "the texture/memory unit stalls on data; OccupancyPercent: resident waves as % "
+                  "of the maximum.", ""]
     with open(out_md, "w") as fh:
         fh.write("\n".join(lines))
     return entry
@@ -750,6 +761,8 @@ def main():
                     help="write the profiles/ summary and traffic entry for this configuration "
                          "from three rocprofv3 databases, then exit")
     ap.add_argument("--summary-md", default="")
+    ap.add_argument("--util", nargs="*", default=[], metavar="METRIC=DB",
+                    help="with --summarize: rocprofv3 databases of derived-metric runs to add")
     ap.add_argument("--commands", default="", help="';;'-separated commands quoted in the summary")
     args = ap.parse_args()
 
@@ -768,8 +781,9 @@ def main():
             title = (f"{family}, {wl.name}: {T} tokens x "
                      f"{'intermediate' if wl.kind == 'act' else 'hidden'}"
                      f" {H}, {MODE_NAMES[mode]}{' G=%d' % G if mode == 2 else ''}")
+        util = [tuple(u.split("=", 1)) for u in args.util]
         e = summarize(*args.summarize, key, title, [c.strip() for c in args.commands.split(";;")
-                                                     if c.strip()], md)
+                                                     if c.strip()], md, util)
         print(json.dumps(e))
         return
 

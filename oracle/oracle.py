@@ -12,6 +12,7 @@ from .build import ensure_built
 
 FP8_STATIC, FP8_TOKEN, FP8_GROUP, FP4_BLOCK16 = 0, 1, 2, 3
 SCALE_COLMAJOR, SCALE_E8M0, SCALE_E8M0_U8 = 1, 2, 4
+INPUT_F16 = 1 << 8  # x, residual, weight and residual_out are IEEE binary16 patterns
 
 _lib = None
 
@@ -40,6 +41,18 @@ def lib():
                      "orc_e8m0_ceil_exp_n"):
             getattr(L, name).argtypes = [p, p, i64]
             getattr(L, name).restype = None
+        L.orc_f16_to_f32.argtypes = [C.c_uint16]
+        L.orc_f16_to_f32.restype = C.c_float
+        L.orc_f32_to_f16.argtypes = [C.c_float]
+        L.orc_f32_to_f16.restype = C.c_uint16
+        L.orc_f32_to_f16_n.argtypes = [p, p, i64]
+        L.orc_f32_to_f16_n.restype = None
+        L.orc_residual_add_dt.argtypes = [p, p, p, i64, C.c_int]
+        L.orc_residual_add_dt.restype = None
+        L.orc_inv_rms_dt.argtypes = [p, i64, C.c_float, C.c_int]
+        L.orc_inv_rms_dt.restype = C.c_float
+        L.orc_normalize_dt.argtypes = [p, p, C.c_float, p, i64, C.c_int]
+        L.orc_normalize_dt.restype = None
         L.orc_residual_add.argtypes = [p, p, p, i64]
         L.orc_residual_add.restype = None
         L.orc_inv_rms.argtypes = [p, i64, C.c_float]
@@ -89,6 +102,21 @@ def f32_to_bf16(v):
     v = _c(v, np.float32)
     out = np.empty(v.shape, np.uint16)
     lib().orc_f32_to_bf16_n(_ptr(v), _ptr(out), v.size)
+    return out
+
+
+def f16_to_f32(bits):
+    """binary16 bit patterns -> f32 values, decoded by the oracle."""
+    bits = _c(bits, np.uint16)
+    flat = bits.reshape(-1)
+    out = np.array([lib().orc_f16_to_f32(int(b)) for b in flat], np.float32)
+    return out.reshape(bits.shape)
+
+
+def f32_to_f16(v):
+    v = _c(v, np.float32)
+    out = np.empty(v.shape, np.uint16)
+    lib().orc_f32_to_f16_n(_ptr(v), _ptr(out), v.size)
     return out
 
 
@@ -221,15 +249,26 @@ def quantize_row(y, mode, scale_in=0.0, group_size=0, flags=0):
     return q, (None if mode == FP8_STATIC else sc), pre
 
 
-def rms_y(x, residual, weight, eps):
-    """The normalized f32 rows y (before quantization), built from the oracle's steps."""
+def rms_y(x, residual, weight, eps, f16=False):
+    """The normalized f32 rows y (before quantization), built from the oracle's steps; f16: the
+    16-bit inputs are IEEE binary16 rather than bf16."""
     x = _c(x, np.uint16)
     w = _c(weight, np.uint16)
     T, H = x.shape
+    dt = int(bool(f16))
     y = np.empty((T, H), np.float32)
+    h = np.empty(H, np.uint16)
     for t in range(T):
-        h = x[t] if residual is None else residual_add(x[t], residual[t])
-        y[t] = normalize(h, w, inv_rms(h, eps))
+        if residual is None:
+            h[:] = x[t]
+        else:
+            r = _c(residual[t], np.uint16)
+            xt = _c(x[t], np.uint16)
+            lib().orc_residual_add_dt(_ptr(xt), _ptr(r), _ptr(h), H, dt)
+        inv = lib().orc_inv_rms_dt(_ptr(h), H, float(eps), dt)
+        yt = np.empty(H, np.float32)
+        lib().orc_normalize_dt(_ptr(h), _ptr(w), float(inv), _ptr(yt), H, dt)
+        y[t] = yt
     return y
 
 

@@ -66,6 +66,51 @@ uint16_t orc_f32_to_bf16(float v) {
   return (uint16_t)(sign | pick);
 }
 
+/* ------------------------------------------------------------------ IEEE binary16 */
+/* 1 sign bit, 5 exponent bits (bias 15), 10 mantissa bits; exponent field 0 is subnormal
+ * (m * 2^-24); exponent field 31 is infinity (m = 0) or NaN.  Largest finite 65504. */
+float orc_f16_to_f32(uint16_t b) {
+  int s = (b >> 15) & 1, e = (b >> 10) & 0x1F, m = b & 0x3FF;
+  double mag;
+  if (e == 0x1F) return m ? NAN : (s ? -INFINITY : INFINITY);
+  if (e == 0) mag = ldexp((double)m, -24);
+  else mag = ldexp(1.0 + m / 1024.0, e - 15);
+  return (float)(s ? -mag : mag);
+}
+
+/* Value of a binary16 magnitude code for rounding-distance purposes: infinity (0x7C00) counts
+ * as 2^16, one step beyond the largest finite value (IEEE overflow rule). */
+static double f16_distance_value(uint16_t code) {
+  if (code >= 0x7C00u) return 65536.0;
+  return (double)orc_f16_to_f32(code);
+}
+
+/* Nearest binary16 by comparing the two neighbours of |v|, found by bisection over the
+ * magnitude codes (finite codes are ordered like their values); ties go to the even code. */
+uint16_t orc_f32_to_f16(float v) {
+  uint16_t sign = signbit(v) ? 0x8000u : 0x0000u;
+  if (isnan(v)) return (uint16_t)(sign | 0x7E00u);
+  double a = fabs((double)v);
+  if (a >= 65536.0) return (uint16_t)(sign | 0x7C00u);
+  uint16_t lo = 0, hi = 0x7C00u; /* decode(lo) <= a < value(hi) */
+  while (hi - lo > 1) {
+    uint16_t mid = (uint16_t)((lo + hi) / 2);
+    if (f16_distance_value(mid) <= a) lo = mid;
+    else hi = mid;
+  }
+  if (f16_distance_value(lo) == a) return (uint16_t)(sign | lo);
+  double dlo = a - f16_distance_value(lo), dhi = f16_distance_value(hi) - a;
+  uint16_t pick;
+  if (dlo < dhi) pick = lo;
+  else if (dhi < dlo) pick = hi;
+  else pick = (lo & 1u) ? hi : lo;
+  return (uint16_t)(sign | pick);
+}
+
+void orc_f32_to_f16_n(const float* v, uint16_t* b, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) b[i] = orc_f32_to_f16(v[i]);
+}
+
 /* ------------------------------------------------------------------ e4m3fn (OCP FP8) */
 /* 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits; exponent field 0 is subnormal
  * (m * 2^-9); S.1111.111 is NaN; there is no infinity.  Largest finite magnitude 448. */
@@ -147,27 +192,41 @@ void orc_e8m0_ceil_exp_n(const float* s, int32_t* k, int64_t n) {
 }
 
 /* ------------------------------------------------------------------ row steps */
-void orc_residual_add(const uint16_t* x, const uint16_t* r, uint16_t* h, int64_t n) {
+static float in16_to_f32(uint16_t b, int f16) { return f16 ? orc_f16_to_f32(b) : orc_bf16_to_f32(b); }
+static uint16_t f32_to_in16(float v, int f16) { return f16 ? orc_f32_to_f16(v) : orc_f32_to_bf16(v); }
+
+void orc_residual_add_dt(const uint16_t* x, const uint16_t* r, uint16_t* h, int64_t n, int f16) {
   for (int64_t i = 0; i < n; ++i) {
-    float sum = orc_bf16_to_f32(x[i]) + orc_bf16_to_f32(r[i]);
-    h[i] = orc_f32_to_bf16(sum);
+    float sum = in16_to_f32(x[i], f16) + in16_to_f32(r[i], f16);
+    h[i] = f32_to_in16(sum, f16);
   }
 }
 
-float orc_inv_rms(const uint16_t* h, int64_t n, float eps) {
+void orc_residual_add(const uint16_t* x, const uint16_t* r, uint16_t* h, int64_t n) {
+  orc_residual_add_dt(x, r, h, n, 0);
+}
+
+float orc_inv_rms_dt(const uint16_t* h, int64_t n, float eps, int f16) {
   double ss = 0.0;
   for (int64_t i = 0; i < n; ++i) {
-    double v = (double)orc_bf16_to_f32(h[i]);
+    double v = (double)in16_to_f32(h[i], f16);
     ss += v * v;
   }
   return (float)(1.0 / sqrt(ss / (double)n + (double)eps));
 }
 
-void orc_normalize(const uint16_t* h, const uint16_t* w, float inv, float* y, int64_t n) {
+float orc_inv_rms(const uint16_t* h, int64_t n, float eps) { return orc_inv_rms_dt(h, n, eps, 0); }
+
+void orc_normalize_dt(const uint16_t* h, const uint16_t* w, float inv, float* y, int64_t n,
+                      int f16) {
   for (int64_t i = 0; i < n; ++i) {
-    float t = orc_bf16_to_f32(h[i]) * inv;
-    y[i] = t * orc_bf16_to_f32(w[i]);
+    float t = in16_to_f32(h[i], f16) * inv;
+    y[i] = t * in16_to_f32(w[i], f16);
   }
+}
+
+void orc_normalize(const uint16_t* h, const uint16_t* w, float inv, float* y, int64_t n) {
+  orc_normalize_dt(h, w, inv, y, n, 0);
 }
 
 static float absmax(const float* y, int64_t n) {
@@ -306,17 +365,19 @@ int orc_fused(const uint16_t* x, const uint16_t* residual, const uint16_t* weigh
     return -1;
   }
 
+  const int f16 = (flags & ORC_INPUT_F16) != 0;
   for (int64_t t = 0; t < T; ++t) {
     if (residual) {
-      orc_residual_add(x + t * H, residual + t * H, h, H);
+      orc_residual_add_dt(x + t * H, residual + t * H, h, H, f16);
       memcpy(residual_out + t * H, h, (size_t)H * sizeof(uint16_t));
     } else {
       memcpy(h, x + t * H, (size_t)H * sizeof(uint16_t));
     }
-    float inv = orc_inv_rms(h, H, eps);
-    orc_normalize(h, weight, inv, y, H);
+    float inv = orc_inv_rms_dt(h, H, eps, f16);
+    orc_normalize_dt(h, weight, inv, y, H, f16);
     uint8_t* qrow = out_q + t * (mode == ORC_FP4_BLOCK16 ? H / 2 : H);
-    orc_quantize_row(y, H, mode, scale_in, group_size, flags, qrow, sc, pre_q ? pre_q + t * H : NULL);
+    orc_quantize_row(y, H, mode, scale_in, group_size, flags & ~(unsigned)ORC_INPUT_F16, qrow, sc,
+                     pre_q ? pre_q + t * H : NULL);
 
     /* place this row's scales */
     if (mode == ORC_FP8_TOKEN) {

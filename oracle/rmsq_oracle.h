@@ -47,12 +47,16 @@ enum {
 enum {
   ORC_SCALE_COLMAJOR = 1u << 0, /* scales stored [H/G][scale_ld], element (t,g) at g*ld + t   */
   ORC_SCALE_E8M0 = 1u << 1,     /* scale rounded up to a power of two, stored as f32           */
-  ORC_SCALE_E8M0_U8 = 1u << 2   /* scale rounded up to a power of two, stored as its E8M0 byte */
+  ORC_SCALE_E8M0_U8 = 1u << 2,  /* scale rounded up to a power of two, stored as its E8M0 byte */
+  ORC_INPUT_F16 = 1u << 8       /* x, residual, weight, residual_out are IEEE binary16, not bf16 */
 };
 
 /* ---- formats (decoded from bit fields; encoders are nearest-value searches) ---- */
 float orc_bf16_to_f32(uint16_t b);
 uint16_t orc_f32_to_bf16(float v);  /* round to nearest, ties to even significand */
+float orc_f16_to_f32(uint16_t b);    /* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 mantissa */
+uint16_t orc_f32_to_f16(float v);    /* nearest binary16, ties to even, overflow to infinity */
+void orc_f32_to_f16_n(const float* v, uint16_t* b, int64_t n);
 float orc_e4m3_decode(uint8_t c);   /* OCP e4m3fn; 0x7F/0xFF decode to NaN */
 uint8_t orc_e4m3_encode(float v);   /* nearest, ties -> even code, saturate at 448, NaN -> 0x7F */
 float orc_e2m1_decode(uint8_t c);   /* low 4 bits used */
@@ -68,6 +72,11 @@ void orc_e8m0_ceil_exp_n(const float* s, int32_t* k, int64_t n);
 /* ---- steps of one row ---- */
 /* h = bf16(f32(x) + f32(r)) elementwise; residual_out takes h. */
 void orc_residual_add(const uint16_t* x, const uint16_t* r, uint16_t* h, int64_t n);
+/* The same three row steps for either 16-bit input type: f16 = 0 bf16, 1 IEEE binary16. */
+void orc_residual_add_dt(const uint16_t* x, const uint16_t* r, uint16_t* h, int64_t n, int f16);
+float orc_inv_rms_dt(const uint16_t* h, int64_t n, float eps, int f16);
+void orc_normalize_dt(const uint16_t* h, const uint16_t* w, float inv, float* y, int64_t n,
+                      int f16);
 /* inv = 1 / sqrt(mean(h^2) + eps), sum in index order in binary64, result rounded to f32. */
 float orc_inv_rms(const uint16_t* h, int64_t n, float eps);
 /* y_i = (h_i * inv) * w_i, two binary32 products in that order. */

@@ -75,15 +75,21 @@ enum {
   RMSQ_SCALE_E8M0_U8 = 1u << 2   /* same rounding, stored as the E8M0 byte (exponent + 127)  */
 };
 
+/* ---- activation type flag, any mode of rmsq_fused (docs "Fusion torch.compile passes" and the
+ *      blog's type check: x and the weight share the model's activation dtype) ---- */
+enum {
+  RMSQ_INPUT_F16 = 1u << 8 /* x, residual, weight, residual_out are IEEE binary16, not bf16 */
+};
+
 /*
  * rmsq_fused -- one launch of the fused kernel family.
  *
- *  x            [T,H] bf16, row stride H, 16-byte aligned.  Read only; must not overlap any
- *               output.
- *  residual     [T,H] bf16, 16-byte aligned, or NULL for plain RMSNorm (vLLM rms_norm ->
+ *  x            [T,H] bf16 (binary16 with RMSQ_INPUT_F16), row stride H, 16-byte aligned.
+ *               Read only; must not overlap any output.
+ *  residual     [T,H] same type, 16-byte aligned, or NULL for plain RMSNorm (vLLM rms_norm ->
  *               quant); non-NULL selects the fused-add form (fused_add_rms_norm -> quant).
- *  weight       [H] bf16, 16-byte aligned (same dtype as x: the blog's "Type check" rejects
- *               mixed input/weight dtypes; bf16 is the one dtype supported).
+ *  weight       [H] same type as x, 16-byte aligned (the blog's "Type check" rejects mixed
+ *               input/weight dtypes: bf16, or binary16 for all three with RMSQ_INPUT_F16).
  *  eps          finite, > 0 (the pages' patterns use 1e-5 and 1e-6).
  *  mode         rmsq_mode.
  *  scale_in     device f32, 4-byte aligned: FP8_STATIC the per-tensor dequant scale (positive,
@@ -95,13 +101,15 @@ enum {
  *               row-major, or [H/G, scale_ld] f32 with RMSQ_SCALE_COLMAJOR, or bytes with
  *               RMSQ_SCALE_E8M0_U8.  FP4_BLOCK16: [T,H/16] e4m3 bytes, row-major.  f32 scales
  *               need 4-byte alignment.  Column-major padding (columns T..ld-1) is not written.
- *  residual_out [T,H] bf16, 16-byte aligned; receives h.  Must be non-NULL iff residual is;
+ *  residual_out [T,H] same type as x, 16-byte aligned; receives h = x + residual rounded to
+ *               that type (nearest even; binary16 overflows to infinity).  Non-NULL iff residual is;
  *               may equal residual exactly (in-place update, as vLLM's fused_add_rms_norm
  *               does), must not otherwise overlap anything.
  *  tokens       T >= 0; T == 0 is a successful no-op (pointers are then not checked).
  *  hidden       H: 8 <= H <= RMSQ_MAX_HIDDEN, H % 8 == 0, and H % group_size == 0.
  *  group_size   FP8_GROUP: 64 or 128.  FP4_BLOCK16: 16.  Otherwise 0.
- *  flags        RMSQ_SCALE_* for FP8_GROUP (E8M0 and E8M0_U8 are exclusive); 0 otherwise.
+ *  flags        RMSQ_SCALE_* for FP8_GROUP (E8M0 and E8M0_U8 are exclusive), plus
+ *               RMSQ_INPUT_F16 in any mode; 0 otherwise.
  *  scale_ld     FP8_GROUP with RMSQ_SCALE_COLMAJOR: leading dimension >= T (0 means T).
  *               Otherwise 0.
  *  stream       hipStream_t to enqueue on.

@@ -29,6 +29,7 @@ RMSQ_OK, RMSQ_EINVAL, RMSQ_EALIGN, RMSQ_EALIAS, RMSQ_EUNSUPPORTED, RMSQ_ELAUNCH,
     0, -1, -2, -3, -4, -5, -6)
 RMSQ_FP8_STATIC, RMSQ_FP8_TOKEN, RMSQ_FP8_GROUP, RMSQ_FP4_BLOCK16 = 0, 1, 2, 3
 RMSQ_SCALE_COLMAJOR, RMSQ_SCALE_E8M0, RMSQ_SCALE_E8M0_U8 = 1, 2, 4
+RMSQ_INPUT_F16 = 1 << 8
 RMSQ_CVT_E4M3, RMSQ_CVT_E2M1, RMSQ_CVT_BF16 = 0, 1, 2
 RMSQ_LAUNCH_XCD_RANGES = 1
 RMSQ_LAUNCH_ROW_TILES = 2
@@ -338,6 +339,17 @@ def rmsq_convert(fmt, inp, out, n=None, stream=None, check=True) -> int:
 
 
 # ---------------------------------------------------------------- allocating helpers
+def _act_flag(x, weight, residual=None) -> int:
+    """RMSQ_INPUT_F16 for float16 activations, 0 for bfloat16; x, the weight and the residual
+    must share the dtype (the pages' type check), anything else is refused."""
+    if x.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError(f"rmsq: activations must be bfloat16 or float16, not {x.dtype}")
+    for t in (weight, residual):
+        if t is not None and t.dtype != x.dtype:
+            raise TypeError(f"rmsq: x is {x.dtype} but another input is {t.dtype}")
+    return RMSQ_INPUT_F16 if x.dtype == torch.float16 else 0
+
+
 def _scalar(v, dev) -> torch.Tensor:
     if isinstance(v, torch.Tensor):
         return v.to(device=dev, dtype=torch.float32).reshape(1).contiguous()
@@ -350,7 +362,7 @@ def rms_norm_static_fp8_quant(x, weight, scale, eps, residual=None, inplace=True
     q = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
     rout = None if residual is None else (residual if inplace else torch.empty_like(residual))
     rmsq_fused(x, residual, weight, eps, RMSQ_FP8_STATIC, _scalar(scale, x.device),
-               q.view(torch.uint8), None, rout)
+               q.view(torch.uint8), None, rout, flags=_act_flag(x, weight, residual))
     return q, rout
 
 
@@ -365,7 +377,8 @@ def rms_norm_dynamic_per_token_quant(x, weight, eps, residual=None, inplace=True
     q = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
     s = torch.empty((T,), dtype=torch.float32, device=x.device)
     rout = None if residual is None else (residual if inplace else torch.empty_like(residual))
-    rmsq_fused(x, residual, weight, eps, RMSQ_FP8_TOKEN, None, q.view(torch.uint8), s, rout)
+    rmsq_fused(x, residual, weight, eps, RMSQ_FP8_TOKEN, None, q.view(torch.uint8), s, rout,
+               flags=_act_flag(x, weight, residual))
     return q, s, rout
 
 
@@ -376,7 +389,7 @@ def rms_norm_per_block_quant(x, weight, eps, group_size=128, residual=None, inpl
     T, H = x.shape
     ng = H // group_size
     flags = (RMSQ_SCALE_COLMAJOR if col_major else 0) | (RMSQ_SCALE_E8M0 if e8m0 else 0) | (
-        RMSQ_SCALE_E8M0_U8 if e8m0_bytes else 0)
+        RMSQ_SCALE_E8M0_U8 if e8m0_bytes else 0) | _act_flag(x, weight, residual)
     ld = scale_ld or T
     shape = (ng, ld) if col_major else (T, ng)
     s = torch.empty(shape, dtype=torch.uint8 if e8m0_bytes else torch.float32, device=x.device)
@@ -395,7 +408,7 @@ def fused_add_rms_norm_fp4_quant(x, residual, weight, global_scale, eps, inplace
     sf = torch.empty((T, H // 16), dtype=torch.uint8, device=x.device)
     rout = residual if inplace else torch.empty_like(residual)
     rmsq_fused(x, residual, weight, eps, RMSQ_FP4_BLOCK16, _scalar(global_scale, x.device), q,
-               sf, rout, group_size=16)
+               sf, rout, group_size=16, flags=_act_flag(x, weight, residual))
     return q, sf, rout
 
 

@@ -12,37 +12,46 @@
 namespace rmsq {
 
 // ------------------------------------------------------------------ kernel table
-template <int MODE, bool RES, int GS, bool EXACT>
+template <int MODE, bool RES, int GS, bool EXACT, int DT = 0>
 const void* pick_vpt(int vpt) {
   switch (vpt) {
-    case 1: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 1, GS, EXACT>);
-    case 2: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 2, GS, EXACT>);
-    case 3: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 3, GS, EXACT>);
-    case 4: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 4, GS, EXACT>);
-    case 5: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 5, GS, EXACT>);
-    case 6: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 6, GS, EXACT>);
-    case 7: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 7, GS, EXACT>);
-    case 8: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 8, GS, EXACT>);
+    case 1: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 1, GS, EXACT, DT>);
+    case 2: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 2, GS, EXACT, DT>);
+    case 3: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 3, GS, EXACT, DT>);
+    case 4: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 4, GS, EXACT, DT>);
+    case 5: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 5, GS, EXACT, DT>);
+    case 6: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 6, GS, EXACT, DT>);
+    case 7: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 7, GS, EXACT, DT>);
+    case 8: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 8, GS, EXACT, DT>);
     default: return nullptr;
   }
 }
 
-template <bool RES, bool EXACT>
+template <bool RES, bool EXACT, int DT>
 const void* pick_mode(int mode, int gs, int vpt) {
   switch (mode) {
-    case RMSQ_FP8_STATIC: return pick_vpt<RMSQ_FP8_STATIC, RES, 0, EXACT>(vpt);
-    case RMSQ_FP8_TOKEN: return pick_vpt<RMSQ_FP8_TOKEN, RES, 0, EXACT>(vpt);
+    case RMSQ_FP8_STATIC: return pick_vpt<RMSQ_FP8_STATIC, RES, 0, EXACT, DT>(vpt);
+    case RMSQ_FP8_TOKEN: return pick_vpt<RMSQ_FP8_TOKEN, RES, 0, EXACT, DT>(vpt);
     case RMSQ_FP8_GROUP:
-      return gs == 64 ? pick_vpt<RMSQ_FP8_GROUP, RES, 64, EXACT>(vpt)
-                      : pick_vpt<RMSQ_FP8_GROUP, RES, 128, EXACT>(vpt);
-    case RMSQ_FP4_BLOCK16: return pick_vpt<RMSQ_FP4_BLOCK16, RES, 16, EXACT>(vpt);
+      return gs == 64 ? pick_vpt<RMSQ_FP8_GROUP, RES, 64, EXACT, DT>(vpt)
+                      : pick_vpt<RMSQ_FP8_GROUP, RES, 128, EXACT, DT>(vpt);
+    case RMSQ_FP4_BLOCK16: return pick_vpt<RMSQ_FP4_BLOCK16, RES, 16, EXACT, DT>(vpt);
     default: return nullptr;
   }
 }
 
-const void* pick_kernel(int mode, bool res, int gs, int vpt, bool exact) {
-  if (res) return exact ? pick_mode<true, true>(mode, gs, vpt) : pick_mode<true, false>(mode, gs, vpt);
-  return exact ? pick_mode<false, true>(mode, gs, vpt) : pick_mode<false, false>(mode, gs, vpt);
+template <int DT>
+const void* pick_kernel_dt(int mode, bool res, int gs, int vpt, bool exact) {
+  if (res)
+    return exact ? pick_mode<true, true, DT>(mode, gs, vpt)
+                 : pick_mode<true, false, DT>(mode, gs, vpt);
+  return exact ? pick_mode<false, true, DT>(mode, gs, vpt)
+               : pick_mode<false, false, DT>(mode, gs, vpt);
+}
+
+const void* pick_kernel(int mode, bool res, int gs, int vpt, bool exact, bool f16) {
+  return f16 ? pick_kernel_dt<1>(mode, res, gs, vpt, exact)
+             : pick_kernel_dt<0>(mode, res, gs, vpt, exact);
 }
 
 // ------------------------------------------------------------------ host side
@@ -211,6 +220,7 @@ bool exact_fit(const rmsq_launch& l, int64_t T, int64_t n) {
 int validate(const void* x, const void* res, const void* w, float eps, int mode,
              const float* scale_in, const void* q, const void* scales, const void* res_out,
              int64_t T, int64_t H, int gs, unsigned flags, int64_t ld) {
+  flags &= ~(unsigned)RMSQ_INPUT_F16;  // the activation type; the rest describes the scales
   int st = check_quant_scalars(T, H, mode, gs, flags, ld);
   if (st != RMSQ_OK) return st;
   if (!(eps > 0.0f) || !std::isfinite(eps)) return RMSQ_EINVAL;
@@ -250,7 +260,8 @@ int fused_impl(const void* x, const void* res, const void* w, float eps, int mod
   if (T == 0) return RMSQ_OK;
   st = check_device();
   if (st != RMSQ_OK) return st;
-  const void* fn = pick_kernel(mode, res != nullptr, gs, l.chunks_per_thread, exact_fit(l, T, H));
+  const void* fn = pick_kernel(mode, res != nullptr, gs, l.chunks_per_thread, exact_fit(l, T, H),
+                               (flags & RMSQ_INPUT_F16) != 0);
   if (!fn) return RMSQ_EINVAL;
   const int64_t nblk = (T + l.rows_per_block - 1) / l.rows_per_block;
   KArgs a;

@@ -34,6 +34,39 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// ---- IEEE binary16 ----------------------------------------------------------------------
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float f16_lo(uint32_t d) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(d & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t d) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(d >> 16));
+}
+
+// Round two f32 to binary16 (nearest even, overflow to infinity), a in the low half.
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  f16x2 r = __builtin_convertvector((f32x2){a, b}, f16x2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// The 16-bit activation type of a launch: DT 0 = bf16, 1 = IEEE binary16.
+template <int DT>
+__device__ __forceinline__ float in_lo(uint32_t d) {
+  if constexpr (DT == 1) return f16_lo(d);
+  else return bf16_lo(d);
+}
+template <int DT>
+__device__ __forceinline__ float in_hi(uint32_t d) {
+  if constexpr (DT == 1) return f16_hi(d);
+  else return bf16_hi(d);
+}
+template <int DT>
+__device__ __forceinline__ uint32_t pack_in(float a, float b) {
+  if constexpr (DT == 1) return pack_f16x2(a, b);
+  else return pack_bf16x2(a, b);
+}
+
 // ---- FP8 e4m3fn --------------------------------------------------------------------------
 __device__ __forceinline__ float clamp_sym(float v, float m) {
   return __builtin_amdgcn_fmed3f(v, -m, m);

@@ -51,11 +51,12 @@ struct KArgs {
   int32_t xcd_ranges;  // XCD-contiguous row-block ranges instead of launch order
 };
 
-// One element of y = (h * inv) * w from the packed bf16 chunk dwords.
+// One element of y = (h * inv) * w from the packed 16-bit chunk dwords (DT: 0 bf16, 1 binary16).
+template <int DT = 0>
 __device__ __forceinline__ float y_of(const u32x4& h, const u32x4& w, int e, float inv) {
   const uint32_t hd = h[e >> 1], wd = w[e >> 1];
-  const float hf = (e & 1) ? bf16_hi(hd) : bf16_lo(hd);
-  const float wf = (e & 1) ? bf16_hi(wd) : bf16_lo(wd);
+  const float hf = (e & 1) ? in_hi<DT>(hd) : in_lo<DT>(hd);
+  const float wf = (e & 1) ? in_hi<DT>(wd) : in_lo<DT>(wd);
   return (hf * inv) * wf;
 }
 
@@ -208,7 +209,9 @@ __device__ __forceinline__ void quantize_store(const YF& Y, const bool (&ok)[VPT
 // EXACT: the launch covers every chunk of every row with no remainder (threads_per_row x
 // chunks_per_thread x 8 == H and T a multiple of rows_per_block), so no load or store needs a
 // predicate; otherwise out-of-range chunks and rows are masked.
-template <int MODE, bool RES, int VPT, int GS, bool EXACT>
+// DT: the activation type of x, the residual, the weight and the new residual (0 bf16,
+// 1 IEEE binary16); everything after the residual sum is f32 either way.
+template <int MODE, bool RES, int VPT, int GS, bool EXACT, int DT>
 __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
   __shared__ double s_ss[kMaxWavesPerBlock];
   __shared__ float s_mx[kMaxWavesPerBlock];
@@ -256,7 +259,7 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
     if (ok[k]) wv[k] = wrow[c];
   }
 
-  // ---- residual add: h = bf16(x + r), written back as the new residual ----
+  // ---- residual add: h = round16(x + r), written back as the new residual ----
   if constexpr (RES) {
     u32x4* orow = reinterpret_cast<u32x4*>(a.res_out + base);
 #pragma unroll
@@ -264,8 +267,8 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
       u32x4 h;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        h[j] = pack_bf16x2(bf16_lo(hv[k][j]) + bf16_lo(rv[k][j]),
-                           bf16_hi(hv[k][j]) + bf16_hi(rv[k][j]));
+        h[j] = pack_in<DT>(in_lo<DT>(hv[k][j]) + in_lo<DT>(rv[k][j]),
+                           in_hi<DT>(hv[k][j]) + in_hi<DT>(rv[k][j]));
       hv[k] = h;
       if (ok[k]) __builtin_nontemporal_store(h, orow + lr + (uint32_t)(k * tpr));
     }
@@ -277,8 +280,8 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
   for (int k = 0; k < VPT; ++k) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const double lo = (double)bf16_lo(hv[k][j]);
-      const double hi = (double)bf16_hi(hv[k][j]);
+      const double lo = (double)in_lo<DT>(hv[k][j]);
+      const double hi = (double)in_hi<DT>(hv[k][j]);
       ss0 = fma(lo, lo, ss0);
       ss1 = fma(hi, hi, ss1);
     }
@@ -308,7 +311,7 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
   o.rib = rib;
   o.tid = tid;
   quantize_store<MODE, VPT, GS>(
-      [&](int k, int e) { return y_of(hv[k], wv[k], e, inv); }, ok, o, scale_val, s_mx);
+      [&](int k, int e) { return y_of<DT>(hv[k], wv[k], e, inv); }, ok, o, scale_val, s_mx);
 }
 
 // ------------------------------------------------------------------ SiLU+Mul -> quantization

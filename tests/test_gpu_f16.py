@@ -1,0 +1,136 @@
+"""GPU parity of the fused op on IEEE binary16 activations (RMSQ_INPUT_F16) against the oracle.
+
+Same comparison rule as the bf16 path (tests/parity.py): the new residual bit-exact, codes equal
+or one step apart only at rounding midpoints, scales within 1e-6.  Shapes span several tiles and
+ragged rows; values include binary16 subnormals and sums that overflow binary16.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from rmsnorm_quantization_amd import binding as B
+from tests import gpu_harness as GH
+from tests.parity import compare
+
+pytestmark = pytest.mark.gpu
+F16 = O.INPUT_F16
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    GH.require_gpu()
+
+
+def _inputs(T, H, seed, scale=1.0, residual=True):
+    g = torch.Generator().manual_seed(seed)
+    x = (torch.randn((T, H), generator=g) * scale).to(torch.float16)
+    r = (torch.randn((T, H), generator=g) * scale).to(torch.float16) if residual else None
+    w = (torch.rand((H,), generator=g) + 0.5).to(torch.float16)
+    return x, r, w
+
+
+def _bits(t):
+    return None if t is None else t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def _check(mode, x, r, w, eps=1e-6, G=0, flags=0, launch=None, scale=None):
+    T, H = x.shape
+    xb, rb, wb = _bits(x), _bits(r), _bits(w)
+    flags |= F16
+    if scale is None:
+        y = O.rms_y(xb, rb, wb, eps, f16=True)
+        amax = float(np.abs(y).max()) or 1.0
+        scale = {O.FP8_STATIC: float(np.float32(amax / 448)),
+                 O.FP4_BLOCK16: float(np.float32(448 * 6 / amax))}.get(mode, 0.0)
+    print(f"[f16] mode={mode} T={T} H={H} G={G} flags={flags} launch="
+          f"{None if launch is None else launch.as_tuple()}", flush=True)
+    gpu = GH.run(mode, GH.to_dev(x), GH.to_dev(r), GH.to_dev(w), eps,
+                 scale_in=scale if mode in (O.FP8_STATIC, O.FP4_BLOCK16) else None,
+                 group_size=G, flags=flags, launch=launch)
+    ref = O.fused(xb, rb, wb, eps, mode, scale_in=scale, group_size=G, flags=flags,
+                  want_pre=True)
+    raw = None
+    if mode == O.FP8_GROUP and flags & (O.SCALE_E8M0 | O.SCALE_E8M0_U8):
+        raw = O.fused(xb, rb, wb, eps, mode, group_size=G,
+                      flags=flags & (O.SCALE_COLMAJOR | F16))["scales"]
+    return compare(mode, gpu, ref, T=T, H=H, group_size=G, flags=flags, scale_in=scale,
+                   raw_group_scales=raw)
+
+
+MODES = [(O.FP8_STATIC, 0, 0), (O.FP8_TOKEN, 0, 0), (O.FP8_GROUP, 128, 0),
+         (O.FP8_GROUP, 64, O.SCALE_COLMAJOR), (O.FP8_GROUP, 128, O.SCALE_E8M0),
+         (O.FP8_GROUP, 128, O.SCALE_E8M0_U8 | O.SCALE_COLMAJOR), (O.FP4_BLOCK16, 16, 0)]
+
+
+@pytest.mark.parametrize("mode,G,flags", MODES)
+@pytest.mark.parametrize("T,H", [(1, 4096), (37, 2048), (512, 4096), (64, 5120)])
+def test_modes_and_shapes(mode, G, flags, T, H):
+    x, r, w = _inputs(T, H, T * 7 + H)
+    _check(mode, x, r, w, G=G, flags=flags)
+
+
+@pytest.mark.parametrize("mode,G,flags", MODES[:2] + MODES[-1:])
+def test_plain_norm(mode, G, flags):
+    x, _, w = _inputs(19, 4096, 5, residual=False)
+    _check(mode, x, None, w, G=G, flags=flags)
+
+
+@pytest.mark.parametrize("launch", [(64, 8, 1), (128, 4, 2), (192, 3, 1), (1024, 1, 1)])
+def test_launch_shapes(launch):
+    x, r, w = _inputs(21, 4096, 6)
+    _check(O.FP8_TOKEN, x, r, w, launch=B.rmsq_launch(*launch, 0))
+
+
+def test_subnormal_and_large_values():
+    """binary16 subnormals (below 6.1e-5) in x and the residual, and values near the top of the
+    range whose sums stay finite."""
+    x, r, w = _inputs(16, 2048, 7, scale=1e-5)
+    _check(O.FP8_TOKEN, x, r, w)
+    _check(O.FP4_BLOCK16, x, r, w, G=16)
+    x, r, w = _inputs(16, 2048, 8, scale=8000.0)
+    _check(O.FP8_TOKEN, x, r, w)
+
+
+def test_residual_overflow_to_infinity():
+    """Sums beyond the binary16 range become +-infinity in the new residual on both sides (the
+    codes of such rows are outside the contract and not compared)."""
+    T, H = 4, 256
+    x = torch.full((T, H), 40000.0).to(torch.float16)
+    x[:, ::2] = -40000.0
+    r = x.clone()
+    w = torch.ones(H).to(torch.float16)
+    gpu = GH.run(O.FP8_TOKEN, GH.to_dev(x), GH.to_dev(r), GH.to_dev(w), 1e-6, flags=F16)
+    ref = O.fused(_bits(x), _bits(r), _bits(w), 1e-6, O.FP8_TOKEN, flags=F16)
+    assert np.array_equal(gpu["residual_out"], ref["residual_out"])
+    assert np.all((ref["residual_out"] & 0x7FFF) == 0x7C00)
+
+
+def test_flag_selects_the_type():
+    """The same 16-bit patterns read as bf16 and as binary16 give different codes."""
+    x, r, w = _inputs(8, 1024, 9)
+    a = GH.run(O.FP8_TOKEN, GH.to_dev(x), GH.to_dev(r), GH.to_dev(w), 1e-6, flags=F16)
+    b = GH.run(O.FP8_TOKEN, GH.to_dev(x), GH.to_dev(r), GH.to_dev(w), 1e-6, flags=0)
+    assert not np.array_equal(a["q"], b["q"])
+
+
+def test_flag_rejected_by_other_entry_points():
+    x = torch.zeros((4, 2 * 256), dtype=torch.float16, device="cuda")
+    q = torch.empty((4, 256), dtype=torch.uint8, device="cuda")
+    st = B.rmsq_silu_mul_quant(x, B.RMSQ_FP8_TOKEN, None, q,
+                               torch.empty(4, dtype=torch.float32, device="cuda"),
+                               flags=B.RMSQ_INPUT_F16, check=False)
+    assert st == B.RMSQ_EUNSUPPORTED
+
+
+def test_helpers_follow_the_tensor_dtype():
+    """The allocating helpers pass RMSQ_INPUT_F16 for float16 tensors and refuse mixed dtypes."""
+    x, r, w = _inputs(8, 1024, 10)
+    xd, rd, wd = GH.to_dev(x), GH.to_dev(r), GH.to_dev(w)
+    q, s, rout = B.rms_norm_dynamic_per_token_quant(xd, wd, 1e-6, residual=rd.clone())
+    torch.cuda.synchronize()
+    ref = O.fused(_bits(x), _bits(r), _bits(w), 1e-6, O.FP8_TOKEN, flags=F16)
+    assert np.array_equal(q.view(torch.uint8).cpu().numpy(), ref["q"])
+    assert np.array_equal(_bits(rout.cpu()), ref["residual_out"])
+    with pytest.raises(TypeError):
+        B.rms_norm_dynamic_per_token_quant(xd, wd.to(torch.bfloat16), 1e-6)

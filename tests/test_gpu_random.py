@@ -56,9 +56,14 @@ def _fused_case(seed):
     r = rng.standard_normal((T, H)) * sigma if residual else None
     w = rng.uniform(-1.5, 1.5, H) if rng.random() < 0.3 else rng.uniform(0.5, 1.5, H)
     eps = float(rng.choice([1e-6, 1e-5]))
-    xb, wb = synth.bits(_bf16(x)), synth.bits(_bf16(w))
-    rb = None if r is None else synth.bits(_bf16(r))
-    y = O.rms_y(xb, rb, wb, eps)
+    f16 = bool(rng.random() < 0.3)  # IEEE binary16 activations instead of bf16
+    to16 = ((lambda a: np.asarray(a, np.float32).astype(np.float16).view(np.uint16)) if f16
+            else (lambda a: synth.bits(_bf16(a))))
+    xb, wb = to16(x), to16(w)
+    rb = None if r is None else to16(r)
+    if f16:
+        flags |= O.INPUT_F16
+    y = O.rms_y(xb, rb, wb, eps, f16=f16)
     amax = float(np.abs(y).max()) or 1.0
     scale = 0.0
     if mode == O.FP8_STATIC:
@@ -86,7 +91,8 @@ def test_random_fused(seed):
     raw = None
     if c["mode"] == O.FP8_GROUP and c["flags"] & (O.SCALE_E8M0 | O.SCALE_E8M0_U8):
         raw = O.fused(c["xb"], c["rb"], c["wb"], c["eps"], c["mode"], group_size=c["G"],
-                      flags=c["flags"] & O.SCALE_COLMAJOR, scale_ld=c["ld"])["scales"]
+                      flags=c["flags"] & (O.SCALE_COLMAJOR | O.INPUT_F16),
+                      scale_ld=c["ld"])["scales"]
     if c["flags"] & O.SCALE_COLMAJOR and c["ld"] > c["T"]:
         # columns past T are padding the library never writes: compare the written part only
         gpu["scales"] = gpu["scales"][:, :c["T"]]

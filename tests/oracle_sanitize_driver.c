@@ -45,6 +45,13 @@ static uint16_t* bf16_array(int64_t n, float scale) {
   return a;
 }
 
+static uint16_t* in16_array(int64_t n, float scale, int f16) {
+  if (!f16) return bf16_array(n, scale);
+  uint16_t* a = (uint16_t*)xalloc((size_t)n * sizeof(uint16_t));
+  for (int64_t i = 0; i < n; ++i) a[i] = orc_f32_to_f16(next_normalish(scale));
+  return a;
+}
+
 static int failures = 0;
 #define EXPECT(cond, ...)                  \
   do {                                     \
@@ -70,6 +77,8 @@ static void formats(void) {
     (void)orc_f32_to_bf16(f);
     if (f >= 0.0f) (void)orc_e8m0_ceil_exp(f);
     (void)orc_bf16_to_f32((uint16_t)bits);
+    (void)orc_f32_to_f16(f);
+    (void)orc_f16_to_f32((uint16_t)bits);
   }
   for (int64_t n = 0; n < 40; n += 7) {
     float* v = (float*)xalloc((size_t)n * 4);
@@ -104,10 +113,14 @@ static size_t scale_bytes(int mode, int64_t T, int64_t H, int G, unsigned flags,
 
 static void fused_case(int mode, int residual, int64_t T, int64_t H, int G, unsigned flags) {
   const int64_t ld = (flags & ORC_SCALE_COLMAJOR) ? T + 3 : 0;
-  uint16_t* x = bf16_array(T * H, 2.0f);
-  uint16_t* r = residual ? bf16_array(T * H, 2.0f) : NULL;
-  uint16_t* w = bf16_array(H, 0.5f);
-  for (int64_t i = 0; i < H; ++i) w[i] = orc_f32_to_bf16(1.0f + orc_bf16_to_f32(w[i]));
+  const int f16 = (flags & ORC_INPUT_F16) != 0;
+  uint16_t* x = in16_array(T * H, 2.0f, f16);
+  uint16_t* r = residual ? in16_array(T * H, 2.0f, f16) : NULL;
+  uint16_t* w = in16_array(H, 0.5f, 0);
+  for (int64_t i = 0; i < H; ++i) {
+    const float wi = 1.0f + orc_bf16_to_f32(w[i]);
+    w[i] = f16 ? orc_f32_to_f16(wi) : orc_f32_to_bf16(wi);
+  }
   const size_t qb = mode == ORC_FP4_BLOCK16 ? (size_t)(T * H / 2) : (size_t)(T * H);
   uint8_t* q = (uint8_t*)xalloc(qb);
   const size_t sb = scale_bytes(mode, T, H, G, flags, ld);
@@ -122,16 +135,17 @@ static void fused_case(int mode, int residual, int64_t T, int64_t H, int G, unsi
   if (T > 0 && rc == 0) {
     float* y = (float*)xalloc((size_t)H * 4);
     uint16_t* h = (uint16_t*)xalloc((size_t)H * 2);
-    if (r) orc_residual_add(x, r, h, H);
+    if (r) orc_residual_add_dt(x, r, h, H, f16);
     else memcpy(h, x, (size_t)H * 2);
-    orc_normalize(h, w, orc_inv_rms(h, H, 1e-6f), y, H);
+    orc_normalize_dt(h, w, orc_inv_rms_dt(h, H, 1e-6f, f16), y, H, f16);
     uint8_t* q1 = (uint8_t*)xalloc(mode == ORC_FP4_BLOCK16 ? (size_t)H / 2 : (size_t)H);
     const size_t rsb = mode == ORC_FP8_TOKEN ? 4
                        : mode == ORC_FP8_GROUP ? (size_t)(H / G) * ((flags & ORC_SCALE_E8M0_U8) ? 1 : 4)
                        : mode == ORC_FP4_BLOCK16 ? (size_t)H / 16 : 0;
     void* s1 = rsb ? xalloc(rsb) : NULL;
     float* p1 = (float*)xalloc((size_t)H * 4);
-    EXPECT(orc_quantize_row(y, H, mode, sc, G, flags & ~(unsigned)ORC_SCALE_COLMAJOR, q1, s1,
+    EXPECT(orc_quantize_row(y, H, mode, sc, G,
+                            flags & ~(unsigned)(ORC_SCALE_COLMAJOR | ORC_INPUT_F16), q1, s1,
                             p1) == 0, "orc_quantize_row");
     EXPECT(memcmp(q1, q, mode == ORC_FP4_BLOCK16 ? (size_t)H / 2 : (size_t)H) == 0,
            "row 0 codes differ from orc_fused");
@@ -159,7 +173,9 @@ static void fused_all(void) {
         const int64_t T = Ts[ti], H = Hs[hi];
         fused_case(ORC_FP8_STATIC, res, T, H, 0, 0);
         fused_case(ORC_FP8_TOKEN, res, T, H, 0, 0);
+        fused_case(ORC_FP8_TOKEN, res, T, H, 0, ORC_INPUT_F16);
         fused_case(ORC_FP4_BLOCK16, res, T, H, 16, 0);
+        fused_case(ORC_FP4_BLOCK16, res, T, H, 16, ORC_INPUT_F16);
         for (int G = 64; G <= 128; G *= 2) {
           if (H % G) continue;
           const unsigned fl[] = {0, ORC_SCALE_COLMAJOR, ORC_SCALE_E8M0,

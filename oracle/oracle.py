@@ -63,6 +63,8 @@ def lib():
         L.orc_quantize_row.restype = C.c_int
         L.orc_silu_mul.argtypes = [C.c_uint16, C.c_uint16]
         L.orc_silu_mul.restype = C.c_float
+        L.orc_silu_mul_row_dt.argtypes = [p, i64, p, C.c_int]
+        L.orc_silu_mul_row_dt.restype = None
         L.orc_silu_mul_row.argtypes = [p, i64, p]
         L.orc_silu_mul_row.restype = None
         L.orc_silu_mul_quant.argtypes = [p, C.c_int, C.c_float, p, p, i64, i64, C.c_int,
@@ -273,14 +275,15 @@ def rms_y(x, residual, weight, eps, f16=False):
 
 
 # ---------------------------------------------------------------- SiLU+Mul -> quant
-def silu_mul(x):
-    """[T, 2I] bf16 bits -> [T, I] f32 activation silu(gate) * up."""
+def silu_mul(x, f16=False):
+    """[T, 2I] bf16 bits (IEEE binary16 with f16) -> [T, I] f32 activation silu(gate) * up."""
     x = _c(x, np.uint16)
     T, I2 = x.shape
     I = I2 // 2
     a = np.empty((T, I), np.float32)
     for t in range(T):
-        lib().orc_silu_mul_row(_ptr(x[t]), I, a[t].ctypes.data_as(C.c_void_p))
+        lib().orc_silu_mul_row_dt(_ptr(x[t]), I, a[t].ctypes.data_as(C.c_void_p),
+                                  int(bool(f16)))
     return a
 
 

@@ -488,14 +488,18 @@ int orc_qk_norm_rope(uint16_t* qkv, const uint16_t* qw, const uint16_t* kw, cons
 }
 
 /* ------------------------------------------------------------------ SiLU+Mul -> quant */
+static float silu_mul_values(double gd, double ud) { return (float)(gd * ud / (1.0 + exp(-gd))); }
+
 float orc_silu_mul(uint16_t g, uint16_t u) {
-  double gd = (double)orc_bf16_to_f32(g), ud = (double)orc_bf16_to_f32(u);
-  return (float)(gd * ud / (1.0 + exp(-gd)));
+  return silu_mul_values((double)orc_bf16_to_f32(g), (double)orc_bf16_to_f32(u));
 }
 
-void orc_silu_mul_row(const uint16_t* x, int64_t I, float* a) {
-  for (int64_t i = 0; i < I; ++i) a[i] = orc_silu_mul(x[i], x[I + i]);
+void orc_silu_mul_row_dt(const uint16_t* x, int64_t I, float* a, int f16) {
+  for (int64_t i = 0; i < I; ++i)
+    a[i] = silu_mul_values((double)in16_to_f32(x[i], f16), (double)in16_to_f32(x[I + i], f16));
 }
+
+void orc_silu_mul_row(const uint16_t* x, int64_t I, float* a) { orc_silu_mul_row_dt(x, I, a, 0); }
 
 int orc_silu_mul_quant(const uint16_t* x, int mode, float scale_in, uint8_t* out_q,
                        void* out_scales, int64_t T, int64_t I, int group_size, unsigned flags,
@@ -525,10 +529,11 @@ int orc_silu_mul_quant(const uint16_t* x, int mode, float scale_in, uint8_t* out
     free(sc);
     return -1;
   }
+  const int f16 = (flags & ORC_INPUT_F16) != 0;
   for (int64_t t = 0; t < T; ++t) {
-    orc_silu_mul_row(x + t * 2 * I, I, a);
+    orc_silu_mul_row_dt(x + t * 2 * I, I, a, f16);
     uint8_t* qrow = out_q + t * (mode == ORC_FP4_BLOCK16 ? I / 2 : I);
-    orc_quantize_row(a, I, mode, scale_in, group_size, flags, qrow, sc,
+    orc_quantize_row(a, I, mode, scale_in, group_size, flags & ~(unsigned)ORC_INPUT_F16, qrow, sc,
                      pre_q ? pre_q + t * I : NULL);
     if (mode == ORC_FP8_TOKEN) {
       ((float*)out_scales)[t] = sc[0];

@@ -151,8 +151,10 @@ int orc_qk_norm_rope(uint16_t* qkv, const uint16_t* qw, const uint16_t* kw, cons
  * f32; a is then quantized exactly like the normalized row of orc_fused. */
 float orc_silu_mul(uint16_t g, uint16_t u);
 void orc_silu_mul_row(const uint16_t* x, int64_t I, float* a);
-/* x [T, 2I] bf16; out_q FP8 [T, I] / FP4 [T, I/2]; out_scales laid out as in orc_fused with H = I.
- * Returns 0, or -1 on an invalid argument. */
+/* The same for either 16-bit input type (f16 = 1: IEEE binary16). */
+void orc_silu_mul_row_dt(const uint16_t* x, int64_t I, float* a, int f16);
+/* x [T, 2I] bf16 (IEEE binary16 with ORC_INPUT_F16 in flags); out_q FP8 [T, I] / FP4 [T, I/2];
+ * out_scales laid out as in orc_fused with H = I.  Returns 0, or -1 on an invalid argument. */
 int orc_silu_mul_quant(const uint16_t* x, int mode, float scale_in, uint8_t* out_q,
                        void* out_scales, int64_t T, int64_t I, int group_size, unsigned flags,
                        int64_t scale_ld, float* pre_q);

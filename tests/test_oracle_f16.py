@@ -102,3 +102,20 @@ def test_plain_norm_ignores_missing_residual(orc, flags):
     z = np.zeros_like(x)  # +0 in both formats
     b = orc.fused(x, z, w, 1e-6, orc.FP8_TOKEN, flags=flags)
     assert np.array_equal(a["q"], b["q"]) and np.array_equal(b["residual_out"], x)
+
+
+def test_silu_mul_on_binary16(orc):
+    """SiLU+Mul on binary16 gate/up: torch's silu in float64 on the decoded values, rounded once
+    to f32 (within the last bit of exp), and the quantizers compose as for bf16."""
+    rng = np.random.default_rng(20)
+    x = f16_bits(rng.standard_normal((4, 2 * 512)) * 4.0)
+    a = orc.silu_mul(x, f16=True)
+    xt = torch.from_numpy(x.view(np.float16).astype(np.float64))
+    ref = (torch.nn.functional.silu(xt[:, :512]) * xt[:, 512:]).float().numpy()
+    ulp = np.abs(a.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+    assert ulp.max() <= 1
+    tk = orc.silu_mul_quant(x, orc.FP8_TOKEN, flags=orc.INPUT_F16)
+    s = np.abs(a).max(axis=1) / np.float32(448)
+    assert np.array_equal(tk["scales"], s)
+    assert np.array_equal(tk["q"], torch_e4m3(a * (np.float32(1) / s)[:, None]))
+    assert not np.array_equal(orc.silu_mul(x), a)  # read as bf16 it is another activation

@@ -75,8 +75,9 @@ enum {
   RMSQ_SCALE_E8M0_U8 = 1u << 2   /* same rounding, stored as the E8M0 byte (exponent + 127)  */
 };
 
-/* ---- activation type flag, any mode of rmsq_fused (docs "Fusion torch.compile passes" and the
- *      blog's type check: x and the weight share the model's activation dtype) ---- */
+/* ---- activation type flag, any mode of rmsq_fused and rmsq_silu_mul_quant (docs "Fusion
+ *      torch.compile passes" and the blog's type check: x and the weight share the model's
+ *      activation dtype) ---- */
 enum {
   RMSQ_INPUT_F16 = 1u << 8 /* x, residual, weight, residual_out are IEEE binary16, not bf16 */
 };
@@ -208,8 +209,9 @@ RMSQ_API int rmsq_rms_norm_pad_validate(const void* x, const void* residual, con
  * up-projection activation fused with the quantization that follows, so the full-precision
  * activation is never written).
  *
- *  x            [T, 2I] bf16, 16-byte aligned: row t is the gate g = x[t, 0:I] followed by the
- *               up projection u = x[t, I:2I].  Read only.
+ *  x            [T, 2I] bf16 (IEEE binary16 with RMSQ_INPUT_F16 in flags), 16-byte aligned: row
+ *               t is the gate g = x[t, 0:I] followed by the up projection u = x[t, I:2I].  Read
+ *               only.
  *  a            = silu(g) * u = g / (1 + exp(-g)) * u, in f32 (within a few ulp of the exactly
  *               rounded value: expf and the hardware reciprocal), never stored.
  *  mode, scale_in, out_q, out_scales, group_size, flags, scale_ld

@@ -419,7 +419,7 @@ def silu_and_mul_quant(x, mode, scale=None, group_size=0, col_major=False, e8m0=
     (FP8 static) or the global encode scale (FP4)."""
     T, I = x.shape[0], x.shape[-1] // 2
     flags = (RMSQ_SCALE_COLMAJOR if col_major else 0) | (RMSQ_SCALE_E8M0 if e8m0 else 0) | (
-        RMSQ_SCALE_E8M0_U8 if e8m0_bytes else 0)
+        RMSQ_SCALE_E8M0_U8 if e8m0_bytes else 0) | _act_flag(x, x)
     if mode == RMSQ_FP4_BLOCK16:
         q = torch.empty((T, I // 2), dtype=torch.uint8, device=x.device)
         s = torch.empty((T, I // 16), dtype=torch.uint8, device=x.device)

@@ -358,58 +358,70 @@ int pad_impl(const void* x, const void* res, const void* w, float eps, void* out
 }
 
 // ---- SiLU+Mul -> quantization --------------------------------------------------------------
-template <int MODE, int GS, bool EXACT>
+template <int MODE, int GS, bool EXACT, int DT>
 const void* pick_act_vpt(int vpt) {
   switch (vpt) {
-    case 1: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 1, GS, EXACT>);
-    case 2: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 2, GS, EXACT>);
-    case 3: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 3, GS, EXACT>);
-    case 4: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 4, GS, EXACT>);
-    case 5: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 5, GS, EXACT>);
-    case 6: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 6, GS, EXACT>);
-    case 7: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 7, GS, EXACT>);
-    case 8: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 8, GS, EXACT>);
+    case 1: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 1, GS, EXACT, DT>);
+    case 2: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 2, GS, EXACT, DT>);
+    case 3: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 3, GS, EXACT, DT>);
+    case 4: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 4, GS, EXACT, DT>);
+    case 5: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 5, GS, EXACT, DT>);
+    case 6: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 6, GS, EXACT, DT>);
+    case 7: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 7, GS, EXACT, DT>);
+    case 8: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 8, GS, EXACT, DT>);
     default: return nullptr;
   }
 }
 
-template <int MODE, int GS, bool EXACT>
+template <int MODE, int GS, bool EXACT, int DT>
 const void* pick_tile_vpt(int vpt) {
   switch (vpt) {
-    case 1: return reinterpret_cast<const void*>(&silu_mul_tile_kernel<MODE, 1, GS, EXACT>);
-    case 2: return reinterpret_cast<const void*>(&silu_mul_tile_kernel<MODE, 2, GS, EXACT>);
-    case 4: return reinterpret_cast<const void*>(&silu_mul_tile_kernel<MODE, 4, GS, EXACT>);
+    case 1: return reinterpret_cast<const void*>(&silu_mul_tile_kernel<MODE, 1, GS, EXACT, DT>);
+    case 2: return reinterpret_cast<const void*>(&silu_mul_tile_kernel<MODE, 2, GS, EXACT, DT>);
+    case 4: return reinterpret_cast<const void*>(&silu_mul_tile_kernel<MODE, 4, GS, EXACT, DT>);
     default: return nullptr;
   }
 }
 
-template <bool EXACT>
+template <bool EXACT, int DT>
 const void* pick_tile_mode(int mode, int gs, int vpt) {
   switch (mode) {
-    case RMSQ_FP8_STATIC: return pick_tile_vpt<RMSQ_FP8_STATIC, 0, EXACT>(vpt);
+    case RMSQ_FP8_STATIC: return pick_tile_vpt<RMSQ_FP8_STATIC, 0, EXACT, DT>(vpt);
     case RMSQ_FP8_GROUP:
-      return gs == 64 ? pick_tile_vpt<RMSQ_FP8_GROUP, 64, EXACT>(vpt)
-                      : pick_tile_vpt<RMSQ_FP8_GROUP, 128, EXACT>(vpt);
-    case RMSQ_FP4_BLOCK16: return pick_tile_vpt<RMSQ_FP4_BLOCK16, 16, EXACT>(vpt);
+      return gs == 64 ? pick_tile_vpt<RMSQ_FP8_GROUP, 64, EXACT, DT>(vpt)
+                      : pick_tile_vpt<RMSQ_FP8_GROUP, 128, EXACT, DT>(vpt);
+    case RMSQ_FP4_BLOCK16: return pick_tile_vpt<RMSQ_FP4_BLOCK16, 16, EXACT, DT>(vpt);
     default: return nullptr;
   }
 }
 
-template <bool EXACT>
+template <bool EXACT, int DT>
 const void* pick_act_mode(int mode, int gs, int vpt) {
   switch (mode) {
-    case RMSQ_FP8_STATIC: return pick_act_vpt<RMSQ_FP8_STATIC, 0, EXACT>(vpt);
-    case RMSQ_FP8_TOKEN: return pick_act_vpt<RMSQ_FP8_TOKEN, 0, EXACT>(vpt);
+    case RMSQ_FP8_STATIC: return pick_act_vpt<RMSQ_FP8_STATIC, 0, EXACT, DT>(vpt);
+    case RMSQ_FP8_TOKEN: return pick_act_vpt<RMSQ_FP8_TOKEN, 0, EXACT, DT>(vpt);
     case RMSQ_FP8_GROUP:
-      return gs == 64 ? pick_act_vpt<RMSQ_FP8_GROUP, 64, EXACT>(vpt)
-                      : pick_act_vpt<RMSQ_FP8_GROUP, 128, EXACT>(vpt);
-    case RMSQ_FP4_BLOCK16: return pick_act_vpt<RMSQ_FP4_BLOCK16, 16, EXACT>(vpt);
+      return gs == 64 ? pick_act_vpt<RMSQ_FP8_GROUP, 64, EXACT, DT>(vpt)
+                      : pick_act_vpt<RMSQ_FP8_GROUP, 128, EXACT, DT>(vpt);
+    case RMSQ_FP4_BLOCK16: return pick_act_vpt<RMSQ_FP4_BLOCK16, 16, EXACT, DT>(vpt);
     default: return nullptr;
   }
+}
+
+const void* pick_act(bool tiled, bool exact, bool f16, int mode, int gs, int vpt) {
+  if (tiled) {
+    if (f16) return exact ? pick_tile_mode<true, 1>(mode, gs, vpt)
+                          : pick_tile_mode<false, 1>(mode, gs, vpt);
+    return exact ? pick_tile_mode<true, 0>(mode, gs, vpt) : pick_tile_mode<false, 0>(mode, gs, vpt);
+  }
+  if (f16) return exact ? pick_act_mode<true, 1>(mode, gs, vpt)
+                        : pick_act_mode<false, 1>(mode, gs, vpt);
+  return exact ? pick_act_mode<true, 0>(mode, gs, vpt) : pick_act_mode<false, 0>(mode, gs, vpt);
 }
 
 int validate_act(const void* x, int mode, const float* scale_in, const void* q,
                  const void* scales, int64_t T, int64_t I, int gs, unsigned flags, int64_t ld) {
+  flags &= ~(unsigned)RMSQ_INPUT_F16;  // the activation type; the rest describes the scales
   int st = check_quant_scalars(T, I, mode, gs, flags, ld);
   if (st != RMSQ_OK || T == 0) return st;
   if (!x) return RMSQ_EINVAL;
@@ -454,14 +466,13 @@ int act_impl(const void* x, int mode, const float* scale_in, void* q, void* scal
   const int64_t tiles = (I / 8 + tile - 1) / tile;
   const void* fn;
   int64_t nblk;
+  const bool f16 = (flags & RMSQ_INPUT_F16) != 0;
   if (tiled) {
     if (T * tiles > 0x7FFFFFFFLL) return RMSQ_EINVAL;
-    fn = ((I / 8) % tile == 0) ? pick_tile_mode<true>(mode, gs, l.chunks_per_thread)
-                               : pick_tile_mode<false>(mode, gs, l.chunks_per_thread);
+    fn = pick_act(true, (I / 8) % tile == 0, f16, mode, gs, l.chunks_per_thread);
     nblk = T * tiles;
   } else {
-    fn = exact_fit(l, T, I) ? pick_act_mode<true>(mode, gs, l.chunks_per_thread)
-                            : pick_act_mode<false>(mode, gs, l.chunks_per_thread);
+    fn = pick_act(false, exact_fit(l, T, I), f16, mode, gs, l.chunks_per_thread);
     nblk = (T + l.rows_per_block - 1) / l.rows_per_block;
   }
   if (!fn) return RMSQ_EINVAL;

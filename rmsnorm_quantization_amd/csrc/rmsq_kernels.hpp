@@ -317,8 +317,9 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
 // ------------------------------------------------------------------ SiLU+Mul -> quantization
 // vLLM docs "Fusion torch.compile passes", section "SiLU+Mul + quantization (fuse_act_quant)":
 // the gated up-projection activation silu_and_mul fused with the quantization that follows, so
-// the f32 activation never reaches memory.  Row t of x is [2I] bf16: gate g = x[t, 0:I], up
-// u = x[t, I:2I]; a = silu(g) * u = g / (1 + exp(-g)) * u in f32, then quantize_store.
+// the f32 activation never reaches memory.  Row t of x is [2I] 16-bit values (DT 0 bf16, 1 IEEE
+// binary16): gate g = x[t, 0:I], up u = x[t, I:2I]; a = silu(g) * u = g / (1 + exp(-g)) * u in
+// f32, then quantize_store.
 struct AArgs {
   const uint16_t* x;
   uint8_t* q;
@@ -359,7 +360,7 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return (num * __builtin_amdgcn_rcpf(1.0f + e)) * u;
 }
 
-template <int MODE, int VPT, int GS, bool EXACT>
+template <int MODE, int VPT, int GS, bool EXACT, int DT>
 __global__ void __launch_bounds__(1024) silu_mul_kernel(AArgs a) {
   __shared__ float s_mx[kMaxWavesPerBlock];
 
@@ -398,8 +399,8 @@ __global__ void __launch_bounds__(1024) silu_mul_kernel(AArgs a) {
   for (int k = 0; k < VPT; ++k)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      act[k][2 * j] = silu_mul(bf16_lo(gv[k][j]), bf16_lo(uv[k][j]));
-      act[k][2 * j + 1] = silu_mul(bf16_hi(gv[k][j]), bf16_hi(uv[k][j]));
+      act[k][2 * j] = silu_mul(in_lo<DT>(gv[k][j]), in_lo<DT>(uv[k][j]));
+      act[k][2 * j + 1] = silu_mul(in_hi<DT>(gv[k][j]), in_hi<DT>(uv[k][j]));
     }
 
   RowOut o;
@@ -424,7 +425,7 @@ __global__ void __launch_bounds__(1024) silu_mul_kernel(AArgs a) {
 // threads x VPT chunks, so consecutive workgroups cover consecutive stretches of a row and a
 // long row does not become one very wide workgroup.  Tiles hold whole groups (threads is a
 // multiple of 64, a group at most 16 chunks).
-template <int MODE, int VPT, int GS, bool EXACT>
+template <int MODE, int VPT, int GS, bool EXACT, int DT>
 __global__ void __launch_bounds__(1024) silu_mul_tile_kernel(AArgs a) {
   static_assert(MODE != RMSQ_FP8_TOKEN, "per-token scaling needs whole rows");
   const int tid = threadIdx.x;
@@ -459,8 +460,8 @@ __global__ void __launch_bounds__(1024) silu_mul_tile_kernel(AArgs a) {
   for (int k = 0; k < VPT; ++k)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      act[k][2 * j] = silu_mul(bf16_lo(gv[k][j]), bf16_lo(uv[k][j]));
-      act[k][2 * j + 1] = silu_mul(bf16_hi(gv[k][j]), bf16_hi(uv[k][j]));
+      act[k][2 * j] = silu_mul(in_lo<DT>(gv[k][j]), in_lo<DT>(uv[k][j]));
+      act[k][2 * j + 1] = silu_mul(in_hi<DT>(gv[k][j]), in_hi<DT>(uv[k][j]));
     }
 
   RowOut o;

@@ -355,11 +355,13 @@ def test_probe_library_exports_and_checks_arguments():
     assert call(a=X + 8) == -2 and call(d=Q + 4) == -2
 
 
-def test_input_f16_flag_is_accepted_by_the_fused_op_only(B):
+def test_input_f16_flag_is_accepted_by_the_quantizing_ops(B):
     F = B.RMSQ_INPUT_F16
     assert V(B, mode=B.RMSQ_FP8_TOKEN, f=F) == B.RMSQ_OK
     assert V(B, mode=B.RMSQ_FP8_STATIC, sc=SC, s=None, f=F) == B.RMSQ_OK
     assert V(B, mode=B.RMSQ_FP8_GROUP, g=128, f=F | B.RMSQ_SCALE_COLMAJOR) == B.RMSQ_OK
     assert V(B, mode=B.RMSQ_FP4_BLOCK16, sc=SC, g=16, f=F) == B.RMSQ_OK
     assert V(B, mode=B.RMSQ_FP8_TOKEN, f=F | (1 << 9)) == B.RMSQ_EUNSUPPORTED
-    assert VA(B, f=F) == B.RMSQ_EUNSUPPORTED
+    assert VA(B, f=F) == B.RMSQ_OK
+    assert VA(B, mode=B.RMSQ_FP8_GROUP, g=128, f=F | B.RMSQ_SCALE_E8M0) == B.RMSQ_OK
+    assert VA(B, f=F | (1 << 9)) == B.RMSQ_EUNSUPPORTED

@@ -114,13 +114,40 @@ def test_flag_selects_the_type():
     assert not np.array_equal(a["q"], b["q"])
 
 
-def test_flag_rejected_by_other_entry_points():
-    x = torch.zeros((4, 2 * 256), dtype=torch.float16, device="cuda")
-    q = torch.empty((4, 256), dtype=torch.uint8, device="cuda")
-    st = B.rmsq_silu_mul_quant(x, B.RMSQ_FP8_TOKEN, None, q,
-                               torch.empty(4, dtype=torch.float32, device="cuda"),
-                               flags=B.RMSQ_INPUT_F16, check=False)
-    assert st == B.RMSQ_EUNSUPPORTED
+@pytest.mark.parametrize("mode,G,flags", [(O.FP8_STATIC, 0, 0), (O.FP8_TOKEN, 0, 0),
+                                           (O.FP8_GROUP, 128, O.SCALE_COLMAJOR),
+                                           (O.FP8_GROUP, 64, O.SCALE_E8M0),
+                                           (O.FP4_BLOCK16, 16, 0)])
+@pytest.mark.parametrize("T,I", [(1, 14336), (33, 2048)])
+def test_silu_mul_quant(mode, G, flags, T, I):
+    """SiLU+Mul -> quant on binary16 gate/up (the activation is within a few ulp of the
+    oracle's, so codes may differ at rounding midpoints, as for bf16)."""
+    g = torch.Generator().manual_seed(T + I + mode)
+    x = (torch.randn((T, 2 * I), generator=g) * 3.0).to(torch.float16)
+    xb = _bits(x)
+    flags |= F16
+    a = O.silu_mul(xb, f16=True)
+    amax = float(np.abs(a).max())
+    scale = {O.FP8_STATIC: float(np.float32(amax / 448)),
+             O.FP4_BLOCK16: float(np.float32(448 * 6 / amax))}.get(mode, 0.0)
+    print(f"[f16] silu mode={mode} T={T} I={I} G={G} flags={flags}", flush=True)
+    gpu = GH.run_act(mode, GH.to_dev(x),
+                     scale_in=scale if mode in (O.FP8_STATIC, O.FP4_BLOCK16) else None,
+                     group_size=G, flags=flags)
+    ref = O.silu_mul_quant(xb, mode, scale_in=scale, group_size=G, flags=flags, want_pre=True)
+    raw = None
+    if mode == O.FP8_GROUP and flags & O.SCALE_E8M0:
+        raw = O.silu_mul_quant(xb, mode, group_size=G,
+                               flags=flags & (O.SCALE_COLMAJOR | F16))["scales"]
+    compare(mode, gpu, ref, T=T, H=I, group_size=G, flags=flags, scale_in=scale,
+            raw_group_scales=raw)
+
+
+def test_silu_flag_selects_the_type():
+    x = (torch.randn((4, 2 * 1024)) * 2.0).to(torch.float16)
+    a = GH.run_act(O.FP8_TOKEN, GH.to_dev(x), flags=F16)
+    b = GH.run_act(O.FP8_TOKEN, GH.to_dev(x), flags=0)
+    assert not np.array_equal(a["q"], b["q"])
 
 
 def test_helpers_follow_the_tensor_dtype():

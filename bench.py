@@ -42,15 +42,13 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_hash():
-    """Identity of what the HBM counters were taken on: the kernel and launch-heuristic sources
-    of librmsq and its hipcc command line (flags only, paths stripped)."""
+    """Identity of what the HBM counters were taken on: every source unit and kernel header of
+    librmsq (kernels, instantiation tables, launch heuristics) and its hipcc flags."""
     from rmsnorm_quantization_amd import build as hb
 
     h = hashlib.sha256()
-    for p in ("rmsnorm_quantization_amd/csrc/rmsq_kernels.hpp",
-              "rmsnorm_quantization_amd/csrc/rmsq_device.hpp",
-              "rmsnorm_quantization_amd/csrc/rmsq.hip"):
-        h.update(open(os.path.join(ROOT, p), "rb").read())
+    for p in sorted(hb.SRC + hb.KERNEL_SOURCES):
+        h.update(open(p, "rb").read())
     h.update(" ".join(a for a in hb.command("lib.so")[1:] if not a.startswith("/")).encode())
     return h.hexdigest()[:16]
 

@@ -13,9 +13,14 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = [os.path.join(PKG, "csrc", "rmsq.hip")]
+# translation units of librmsq, compiled in parallel and linked into one shared library: the
+# host side, and the kernel instantiation tables (rmsq_kernel_table.hpp)
+SRC = [os.path.join(PKG, "csrc", f) for f in ("rmsq.hip", "table_fused_bf16.hip",
+                                              "table_fused_f16.hip", "table_act.hip",
+                                              "table_misc.hip")]
 KERNEL_SOURCES = [os.path.join(PKG, "csrc", "rmsq_device.hpp"),
-                  os.path.join(PKG, "csrc", "rmsq_kernels.hpp")]
+                  os.path.join(PKG, "csrc", "rmsq_kernels.hpp"),
+                  os.path.join(PKG, "csrc", "rmsq_kernel_table.hpp")]
 DEPS = SRC + KERNEL_SOURCES + [os.path.join(ROOT, "include", "rmsq.h")]
 LIB = os.path.join(PKG, "librmsq.so")
 PROBE_SRC = [os.path.join(PKG, "csrc", "rmsq_probe.hip")]
@@ -32,6 +37,7 @@ def hipcc():
 
 
 def command(out=LIB, extra=(), src=None):
+    """The hipcc command line that builds `out` from `src` (default: every unit of librmsq)."""
     return [
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
@@ -41,14 +47,33 @@ def command(out=LIB, extra=(), src=None):
     ]
 
 
-def build_library(verbose: bool = False) -> str:
-    cmd = command(LIB + ".tmp")
+def _run(cmd, verbose, what):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed to build librmsq.so")
+        raise RuntimeError(f"hipcc failed to build {what}")
+
+
+def build_library(verbose: bool = False) -> str:
+    """Compile every unit to an object in parallel (same flags as command()), then link."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+
+    with tempfile.TemporaryDirectory(prefix="rmsq_build_") as tmp:
+        objs = [os.path.join(tmp, os.path.basename(src) + ".o") for src in SRC]
+        jobs = []
+        for src, obj in zip(SRC, objs):
+            cmd = command(obj, src=[src])
+            cmd.remove("-shared")
+            cmd.insert(1, "-c")
+            jobs.append((cmd, os.path.basename(src)))
+        workers = max(1, min(len(jobs), os.cpu_count() or 1))
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(lambda j: _run(j[0], verbose, j[1]), jobs))
+        link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", LIB + ".tmp"]
+        _run(link, verbose, "librmsq.so (link)")
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

@@ -1,5 +1,7 @@
 // rmsq.hip -- host side of librmsq: argument validation, launch-shape heuristics, kernel
-// dispatch and the C ABI declared in include/rmsq.h.  The kernels are in rmsq_kernels.hpp.
+// dispatch and the C ABI declared in include/rmsq.h.  The kernels are in rmsq_kernels.hpp; their
+// instantiations live in the table_*.hip units (compiled in parallel), reached through
+// rmsq_kernel_table.hpp.
 #include <hip/hip_ext.h>
 
 #include <atomic>
@@ -7,52 +9,9 @@
 #include <cstdlib>
 #include <cstring>
 
-#include "rmsq_kernels.hpp"
+#include "rmsq_kernel_table.hpp"
 
 namespace rmsq {
-
-// ------------------------------------------------------------------ kernel table
-template <int MODE, bool RES, int GS, bool EXACT, int DT = 0>
-const void* pick_vpt(int vpt) {
-  switch (vpt) {
-    case 1: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 1, GS, EXACT, DT>);
-    case 2: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 2, GS, EXACT, DT>);
-    case 3: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 3, GS, EXACT, DT>);
-    case 4: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 4, GS, EXACT, DT>);
-    case 5: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 5, GS, EXACT, DT>);
-    case 6: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 6, GS, EXACT, DT>);
-    case 7: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 7, GS, EXACT, DT>);
-    case 8: return reinterpret_cast<const void*>(&fused_kernel<MODE, RES, 8, GS, EXACT, DT>);
-    default: return nullptr;
-  }
-}
-
-template <bool RES, bool EXACT, int DT>
-const void* pick_mode(int mode, int gs, int vpt) {
-  switch (mode) {
-    case RMSQ_FP8_STATIC: return pick_vpt<RMSQ_FP8_STATIC, RES, 0, EXACT, DT>(vpt);
-    case RMSQ_FP8_TOKEN: return pick_vpt<RMSQ_FP8_TOKEN, RES, 0, EXACT, DT>(vpt);
-    case RMSQ_FP8_GROUP:
-      return gs == 64 ? pick_vpt<RMSQ_FP8_GROUP, RES, 64, EXACT, DT>(vpt)
-                      : pick_vpt<RMSQ_FP8_GROUP, RES, 128, EXACT, DT>(vpt);
-    case RMSQ_FP4_BLOCK16: return pick_vpt<RMSQ_FP4_BLOCK16, RES, 16, EXACT, DT>(vpt);
-    default: return nullptr;
-  }
-}
-
-template <int DT>
-const void* pick_kernel_dt(int mode, bool res, int gs, int vpt, bool exact) {
-  if (res)
-    return exact ? pick_mode<true, true, DT>(mode, gs, vpt)
-                 : pick_mode<true, false, DT>(mode, gs, vpt);
-  return exact ? pick_mode<false, true, DT>(mode, gs, vpt)
-               : pick_mode<false, false, DT>(mode, gs, vpt);
-}
-
-const void* pick_kernel(int mode, bool res, int gs, int vpt, bool exact, bool f16) {
-  return f16 ? pick_kernel_dt<1>(mode, res, gs, vpt, exact)
-             : pick_kernel_dt<0>(mode, res, gs, vpt, exact);
-}
 
 // ------------------------------------------------------------------ host side
 bool valid_launch(const rmsq_launch& l, int64_t H) {
@@ -260,8 +219,10 @@ int fused_impl(const void* x, const void* res, const void* w, float eps, int mod
   if (T == 0) return RMSQ_OK;
   st = check_device();
   if (st != RMSQ_OK) return st;
-  const void* fn = pick_kernel(mode, res != nullptr, gs, l.chunks_per_thread, exact_fit(l, T, H),
-                               (flags & RMSQ_INPUT_F16) != 0);
+  const bool exact = exact_fit(l, T, H);
+  const void* fn = (flags & RMSQ_INPUT_F16)
+                       ? fused_kernel_f16(mode, res != nullptr, gs, l.chunks_per_thread, exact)
+                       : fused_kernel_bf16(mode, res != nullptr, gs, l.chunks_per_thread, exact);
   if (!fn) return RMSQ_EINVAL;
   const int64_t nblk = (T + l.rows_per_block - 1) / l.rows_per_block;
   KArgs a;
@@ -332,8 +293,7 @@ int pad_impl(const void* x, const void* res, const void* w, float eps, void* out
   if (T == 0) return RMSQ_OK;
   st = check_device();
   if (st != RMSQ_OK) return st;
-  const void* fn = res ? pick_vpt<kModeBf16Pad, true, 0, false>(l.chunks_per_thread)
-                       : pick_vpt<kModeBf16Pad, false, 0, false>(l.chunks_per_thread);
+  const void* fn = pad_kernel(res != nullptr, l.chunks_per_thread);
   if (!fn) return RMSQ_EINVAL;
   const int64_t nblk = (T + l.rows_per_block - 1) / l.rows_per_block;
   KArgs a;
@@ -358,67 +318,6 @@ int pad_impl(const void* x, const void* res, const void* w, float eps, void* out
 }
 
 // ---- SiLU+Mul -> quantization --------------------------------------------------------------
-template <int MODE, int GS, bool EXACT, int DT>
-const void* pick_act_vpt(int vpt) {
-  switch (vpt) {
-    case 1: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 1, GS, EXACT, DT>);
-    case 2: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 2, GS, EXACT, DT>);
-    case 3: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 3, GS, EXACT, DT>);
-    case 4: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 4, GS, EXACT, DT>);
-    case 5: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 5, GS, EXACT, DT>);
-    case 6: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 6, GS, EXACT, DT>);
-    case 7: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 7, GS, EXACT, DT>);
-    case 8: return reinterpret_cast<const void*>(&silu_mul_kernel<MODE, 8, GS, EXACT, DT>);
-    default: return nullptr;
-  }
-}
-
-template <int MODE, int GS, bool EXACT, int DT>
-const void* pick_tile_vpt(int vpt) {
-  switch (vpt) {
-    case 1: return reinterpret_cast<const void*>(&silu_mul_tile_kernel<MODE, 1, GS, EXACT, DT>);
-    case 2: return reinterpret_cast<const void*>(&silu_mul_tile_kernel<MODE, 2, GS, EXACT, DT>);
-    case 4: return reinterpret_cast<const void*>(&silu_mul_tile_kernel<MODE, 4, GS, EXACT, DT>);
-    default: return nullptr;
-  }
-}
-
-template <bool EXACT, int DT>
-const void* pick_tile_mode(int mode, int gs, int vpt) {
-  switch (mode) {
-    case RMSQ_FP8_STATIC: return pick_tile_vpt<RMSQ_FP8_STATIC, 0, EXACT, DT>(vpt);
-    case RMSQ_FP8_GROUP:
-      return gs == 64 ? pick_tile_vpt<RMSQ_FP8_GROUP, 64, EXACT, DT>(vpt)
-                      : pick_tile_vpt<RMSQ_FP8_GROUP, 128, EXACT, DT>(vpt);
-    case RMSQ_FP4_BLOCK16: return pick_tile_vpt<RMSQ_FP4_BLOCK16, 16, EXACT, DT>(vpt);
-    default: return nullptr;
-  }
-}
-
-template <bool EXACT, int DT>
-const void* pick_act_mode(int mode, int gs, int vpt) {
-  switch (mode) {
-    case RMSQ_FP8_STATIC: return pick_act_vpt<RMSQ_FP8_STATIC, 0, EXACT, DT>(vpt);
-    case RMSQ_FP8_TOKEN: return pick_act_vpt<RMSQ_FP8_TOKEN, 0, EXACT, DT>(vpt);
-    case RMSQ_FP8_GROUP:
-      return gs == 64 ? pick_act_vpt<RMSQ_FP8_GROUP, 64, EXACT, DT>(vpt)
-                      : pick_act_vpt<RMSQ_FP8_GROUP, 128, EXACT, DT>(vpt);
-    case RMSQ_FP4_BLOCK16: return pick_act_vpt<RMSQ_FP4_BLOCK16, 16, EXACT, DT>(vpt);
-    default: return nullptr;
-  }
-}
-
-const void* pick_act(bool tiled, bool exact, bool f16, int mode, int gs, int vpt) {
-  if (tiled) {
-    if (f16) return exact ? pick_tile_mode<true, 1>(mode, gs, vpt)
-                          : pick_tile_mode<false, 1>(mode, gs, vpt);
-    return exact ? pick_tile_mode<true, 0>(mode, gs, vpt) : pick_tile_mode<false, 0>(mode, gs, vpt);
-  }
-  if (f16) return exact ? pick_act_mode<true, 1>(mode, gs, vpt)
-                        : pick_act_mode<false, 1>(mode, gs, vpt);
-  return exact ? pick_act_mode<true, 0>(mode, gs, vpt) : pick_act_mode<false, 0>(mode, gs, vpt);
-}
-
 int validate_act(const void* x, int mode, const float* scale_in, const void* q,
                  const void* scales, int64_t T, int64_t I, int gs, unsigned flags, int64_t ld) {
   flags &= ~(unsigned)RMSQ_INPUT_F16;  // the activation type; the rest describes the scales
@@ -469,10 +368,12 @@ int act_impl(const void* x, int mode, const float* scale_in, void* q, void* scal
   const bool f16 = (flags & RMSQ_INPUT_F16) != 0;
   if (tiled) {
     if (T * tiles > 0x7FFFFFFFLL) return RMSQ_EINVAL;
-    fn = pick_act(true, (I / 8) % tile == 0, f16, mode, gs, l.chunks_per_thread);
+    fn = f16 ? act_kernel_f16(true, (I / 8) % tile == 0, mode, gs, l.chunks_per_thread)
+             : act_kernel_bf16(true, (I / 8) % tile == 0, mode, gs, l.chunks_per_thread);
     nblk = T * tiles;
   } else {
-    fn = pick_act(false, exact_fit(l, T, I), f16, mode, gs, l.chunks_per_thread);
+    fn = f16 ? act_kernel_f16(false, exact_fit(l, T, I), mode, gs, l.chunks_per_thread)
+             : act_kernel_bf16(false, exact_fit(l, T, I), mode, gs, l.chunks_per_thread);
     nblk = (T + l.rows_per_block - 1) / l.rows_per_block;
   }
   if (!fn) return RMSQ_EINVAL;
@@ -496,28 +397,6 @@ int act_impl(const void* x, int mode, const float* scale_in, void* q, void* scal
 
 // ---- QK-norm + RoPE ------------------------------------------------------------------------
 constexpr int64_t kMaxQkvWidth = 1 << 20;  // elements of one token's qkv row
-
-template <int D, bool NEOX>
-const void* pick_rope_hpl(int hpl) {
-  switch (hpl) {
-    case 1: return reinterpret_cast<const void*>(&qk_norm_rope_kernel<D, NEOX, 1>);
-    case 2: return reinterpret_cast<const void*>(&qk_norm_rope_kernel<D, NEOX, 2>);
-    case 3: return reinterpret_cast<const void*>(&qk_norm_rope_kernel<D, NEOX, 3>);
-    case 4: return reinterpret_cast<const void*>(&qk_norm_rope_kernel<D, NEOX, 4>);
-    case 5: return reinterpret_cast<const void*>(&qk_norm_rope_kernel<D, NEOX, 5>);
-    case 6: return reinterpret_cast<const void*>(&qk_norm_rope_kernel<D, NEOX, 6>);
-    default: return nullptr;
-  }
-}
-
-const void* pick_rope(int D, bool neox, int hpl) {
-  switch (D) {
-    case 64: return neox ? pick_rope_hpl<64, true>(hpl) : pick_rope_hpl<64, false>(hpl);
-    case 128: return neox ? pick_rope_hpl<128, true>(hpl) : pick_rope_hpl<128, false>(hpl);
-    case 256: return neox ? pick_rope_hpl<256, true>(hpl) : pick_rope_hpl<256, false>(hpl);
-    default: return nullptr;
-  }
-}
 
 bool valid_rope_hpl(int hpl) { return hpl >= 1 && hpl <= 6; }
 
@@ -629,7 +508,7 @@ int rope_impl(void* qkv, const void* qw, const void* kw, const float* cache, con
   if (T == 0) return RMSQ_OK;
   st = check_device();
   if (st != RMSQ_OK) return st;
-  const void* fn = pick_rope(D, neox != 0, hpl);
+  const void* fn = rope_kernel(D, neox != 0, hpl);
   if (!fn) return RMSQ_EINVAL;
   const int64_t nhb = (nh + hpb - 1) / hpb;
   RArgs a;
@@ -836,7 +715,7 @@ int rmsq_convert(int format, const float* in, void* out, int64_t n, void* stream
   if (blocks > 0x7FFFFFFFLL) return RMSQ_EINVAL;
   int fmt = format;
   void* args[] = {&fmt, &in, &out, const_cast<int64_t*>(&nch)};
-  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&convert_kernel),
+  const hipError_t e = hipLaunchKernel(convert_kernel_ptr(),
                                        dim3((uint32_t)blocks), dim3(256), args, 0,
                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? RMSQ_OK : RMSQ_ELAUNCH;

@@ -70,11 +70,12 @@ def lib():
         L.orc_silu_mul_quant.argtypes = [p, C.c_int, C.c_float, p, p, i64, i64, C.c_int,
                                          C.c_uint, i64, p]
         L.orc_silu_mul_quant.restype = C.c_int
-        L.orc_rms_norm_pad.argtypes = [p, p, p, C.c_float, p, p, i64, i64, i64]
+        L.orc_rms_norm_pad.argtypes = [p, p, p, C.c_float, p, p, i64, i64, i64, C.c_uint]
         L.orc_rms_norm_pad.restype = C.c_int
         L.orc_rope_cache.argtypes = [p, i64, i64, C.c_double]
         L.orc_rope_cache.restype = None
-        L.orc_qk_norm_rope.argtypes = [p, p, p, p, p, C.c_float, i64, i64, i64, i64, i64, C.c_int]
+        L.orc_qk_norm_rope.argtypes = [p, p, p, p, p, C.c_float, i64, i64, i64, i64, i64, C.c_int,
+                                       C.c_uint]
         L.orc_qk_norm_rope.restype = C.c_int
         L.orc_fused.argtypes = [p, p, p, C.c_float, C.c_int, C.c_float, p, p, p,
                                 i64, i64, C.c_int, C.c_uint, i64, p]
@@ -304,8 +305,9 @@ def silu_mul_quant(x, mode, scale_in=0.0, group_size=0, flags=0, scale_ld=0, wan
 
 
 # ---------------------------------------------------------------- RMSNorm -> padded bf16
-def rms_norm_pad(x, residual, weight, eps, out_ld):
-    """[T, H] bf16 bits -> (out [T, out_ld] bf16 bits, residual_out or None)."""
+def rms_norm_pad(x, residual, weight, eps, out_ld, flags=0):
+    """[T, H] bf16 bits -> (out [T, out_ld] bf16 bits, residual_out or None); with
+    flags=INPUT_F16 every 16-bit array is IEEE binary16."""
     x = _c(x, np.uint16)
     T, H = x.shape
     r = None if residual is None else _c(residual, np.uint16)
@@ -313,7 +315,7 @@ def rms_norm_pad(x, residual, weight, eps, out_ld):
     out = np.full((T, out_ld), 0xFFFF, np.uint16)
     rout = None if r is None else np.zeros_like(r)
     rc = lib().orc_rms_norm_pad(_ptr(x), _ptr(r), _ptr(w), float(eps), _ptr(out), _ptr(rout), T,
-                                H, int(out_ld))
+                                H, int(out_ld), int(flags))
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (rc={rc})")
     return out, rout
@@ -327,8 +329,9 @@ def rope_cache(max_pos, D, base=1_000_000.0):
     return cache
 
 
-def qk_norm_rope(qkv, qw, kw, cache, pos, eps, Hq, Hkv, D, neox=True):
-    """Returns a new [T, (Hq+2Hkv)*D] bf16-bit array (the input is not modified)."""
+def qk_norm_rope(qkv, qw, kw, cache, pos, eps, Hq, Hkv, D, neox=True, flags=0):
+    """Returns a new [T, (Hq+2Hkv)*D] bf16-bit array (the input is not modified); with
+    flags=INPUT_F16, qkv, qw, kw and the result are IEEE binary16."""
     out = np.array(qkv, np.uint16, copy=True, order="C")
     T = out.shape[0]
     qw = _c(qw, np.uint16)
@@ -336,7 +339,8 @@ def qk_norm_rope(qkv, qw, kw, cache, pos, eps, Hq, Hkv, D, neox=True):
     cache = _c(cache, np.float32)
     pos = _c(pos, np.int64)
     rc = lib().orc_qk_norm_rope(_ptr(out), _ptr(qw), _ptr(kw), _ptr(cache), _ptr(pos), float(eps),
-                                T, int(Hq), int(Hkv), int(D), cache.shape[0], int(bool(neox)))
+                                T, int(Hq), int(Hkv), int(D), cache.shape[0], int(bool(neox)),
+                                int(flags))
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (rc={rc})")
     return out

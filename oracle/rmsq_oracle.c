@@ -413,8 +413,10 @@ int rmsq_ref_fused(const void* x, const void* residual, const void* weight, floa
 
 int orc_rms_norm_pad(const uint16_t* x, const uint16_t* residual, const uint16_t* weight,
                      float eps, uint16_t* out, uint16_t* residual_out, int64_t T, int64_t H,
-                     int64_t out_ld) {
+                     int64_t out_ld, unsigned flags) {
   if (T < 0 || H <= 0 || out_ld < H || !x || !weight || !out) return -1;
+  if (flags & ~(unsigned)ORC_INPUT_F16) return -1;
+  const int f16 = (flags & ORC_INPUT_F16) != 0;
   if ((residual == NULL) != (residual_out == NULL)) return -1;
   if (!(eps >= 0.0f) || isinf(eps)) return -1;
   uint16_t* h = (uint16_t*)malloc((size_t)H * sizeof(uint16_t));
@@ -426,13 +428,13 @@ int orc_rms_norm_pad(const uint16_t* x, const uint16_t* residual, const uint16_t
   }
   for (int64_t t = 0; t < T; ++t) {
     if (residual) {
-      orc_residual_add(x + t * H, residual + t * H, h, H);
+      orc_residual_add_dt(x + t * H, residual + t * H, h, H, f16);
       memcpy(residual_out + t * H, h, (size_t)H * sizeof(uint16_t));
     } else {
       memcpy(h, x + t * H, (size_t)H * sizeof(uint16_t));
     }
-    orc_normalize(h, weight, orc_inv_rms(h, H, eps), y, H);
-    for (int64_t i = 0; i < out_ld; ++i) out[t * out_ld + i] = i < H ? orc_f32_to_bf16(y[i]) : 0;
+    orc_normalize_dt(h, weight, orc_inv_rms_dt(h, H, eps, f16), y, H, f16);
+    for (int64_t i = 0; i < out_ld; ++i) out[t * out_ld + i] = i < H ? f32_to_in16(y[i], f16) : 0;
   }
   free(h);
   free(y);
@@ -457,9 +459,11 @@ static void rotate_pair(float a, float b, float c, float s, float* out_a, float*
 
 int orc_qk_norm_rope(uint16_t* qkv, const uint16_t* qw, const uint16_t* kw, const float* cache,
                      const int64_t* pos, float eps, int64_t T, int64_t Hq, int64_t Hkv,
-                     int64_t D, int64_t max_pos, int neox) {
+                     int64_t D, int64_t max_pos, int neox, unsigned flags) {
   if (T < 0 || Hq < 0 || Hkv < 0 || D < 2 || (D % 2) || !qkv || !qw || !kw || !cache || !pos)
     return -1;
+  if (flags & ~(unsigned)ORC_INPUT_F16) return -1;
+  const int f16 = (flags & ORC_INPUT_F16) != 0;
   if (!(eps >= 0.0f) || isinf(eps)) return -1;
   float* y = (float*)malloc((size_t)D * sizeof(float));
   float* o = (float*)malloc((size_t)D * sizeof(float));
@@ -474,12 +478,12 @@ int orc_qk_norm_rope(uint16_t* qkv, const uint16_t* qw, const uint16_t* kw, cons
     const float* cs = cache + pos[t] * D;
     for (int64_t hd = 0; hd < Hq + Hkv; ++hd) {
       uint16_t* head = qkv + t * width + hd * D;
-      orc_normalize(head, hd < Hq ? qw : kw, orc_inv_rms(head, D, eps), y, D);
+      orc_normalize_dt(head, hd < Hq ? qw : kw, orc_inv_rms_dt(head, D, eps, f16), y, D, f16);
       for (int64_t i = 0; i < D / 2; ++i) {
         int64_t ia = neox ? i : 2 * i, ib = neox ? i + D / 2 : 2 * i + 1;
         rotate_pair(y[ia], y[ib], cs[i], cs[D / 2 + i], &o[ia], &o[ib]);
       }
-      for (int64_t i = 0; i < D; ++i) head[i] = orc_f32_to_bf16(o[i]);
+      for (int64_t i = 0; i < D; ++i) head[i] = f32_to_in16(o[i], f16);
     }
   }
   free(y);

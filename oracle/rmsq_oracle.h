@@ -116,14 +116,16 @@ int rmsq_ref_fused(const void* x, const void* residual, const void* weight, floa
                    int64_t tokens, int64_t hidden, int group_size, unsigned flags,
                    int64_t scale_ld);
 
-/* ---- residual add + RMSNorm -> padded bf16 output (vLLM docs "Fusion torch.compile passes",
+/* ---- residual add + RMSNorm -> padded 16-bit output (vLLM docs "Fusion torch.compile passes",
  * section "RMSNorm + padding (fuse_act_padding)": the residual add and RMSNorm fused with the
  * padding of the hidden dimension to the multiple a downstream GEMM needs; hidden size 2880).
- * out [T, out_ld] bf16: out[t, i] = bf16(y_i) for i < H (y as in orc_fused), 0 for H <= i <
- * out_ld.  residual_out as in orc_fused.  Returns 0, or -1 on an invalid argument. */
+ * out [T, out_ld]: out[t, i] = y_i rounded to the input type (nearest even) for i < H (y as in
+ * orc_fused), 0 for H <= i < out_ld.  residual_out as in orc_fused.  flags: 0 (bf16) or
+ * ORC_INPUT_F16 (x, residual, weight, residual_out and out IEEE binary16; binary16 rounding
+ * overflows to infinity).  Returns 0, or -1 on an invalid argument. */
 int orc_rms_norm_pad(const uint16_t* x, const uint16_t* residual, const uint16_t* weight,
                      float eps, uint16_t* out, uint16_t* residual_out, int64_t T, int64_t H,
-                     int64_t out_ld);
+                     int64_t out_ld, unsigned flags);
 
 /* ---- QK-norm + RoPE (vLLM docs "Fusion torch.compile passes", section "QK Norm + RoPE":
  * for models with per-head Q/K normalization, the per-head RMSNorm of q and k fused with the
@@ -138,10 +140,12 @@ void orc_rope_cache(float* cache, int64_t max_pos, int64_t D, double base);
  *   cos and sin of the pair's frequency i at position pos[t]:
  *     out_a = a*c - b*s,  out_b = b*c + a*s   (each product rounded to f32, then the sum)
  *   written back rounded to bf16.  v heads and out-of-range tokens are left unchanged.
+ * flags: 0, or ORC_INPUT_F16: qkv, qw and kw are IEEE binary16 and the result is rounded to
+ * binary16 (nearest even, overflow to infinity).
  * Returns 0, or -1 on an invalid argument (D even, D >= 2). */
 int orc_qk_norm_rope(uint16_t* qkv, const uint16_t* qw, const uint16_t* kw, const float* cache,
                      const int64_t* pos, float eps, int64_t T, int64_t Hq, int64_t Hkv,
-                     int64_t D, int64_t max_pos, int neox);
+                     int64_t D, int64_t max_pos, int neox, unsigned flags);
 
 /* ---- SiLU+Mul -> quantization (vLLM docs "Fusion torch.compile passes", section "SiLU+Mul +
  * quantization (fuse_act_quant)": the gated up-projection activation silu_and_mul fused with the

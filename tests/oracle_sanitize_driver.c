@@ -198,14 +198,16 @@ static void pad_all(void) {
   const int64_t pads[] = {0, 8, 128};
   for (int hi = 0; hi < 3; ++hi)
     for (int pi = 0; pi < 3; ++pi)
-      for (int res = 0; res < 2; ++res) {
+      for (int res = 0; res < 4; ++res) {
+        const int f16 = res >> 1;
         const int64_t T = 5, H = Hs[hi], ld = H + pads[pi];
-        uint16_t* x = bf16_array(T * H, 1.0f);
-        uint16_t* r = res ? bf16_array(T * H, 1.0f) : NULL;
-        uint16_t* w = bf16_array(H, 1.0f);
+        uint16_t* x = in16_array(T * H, 1.0f, f16);
+        uint16_t* r = (res & 1) ? in16_array(T * H, 1.0f, f16) : NULL;
+        uint16_t* w = in16_array(H, 1.0f, f16);
         uint16_t* out = (uint16_t*)xalloc((size_t)(T * ld) * 2);
-        uint16_t* ro = res ? (uint16_t*)xalloc((size_t)(T * H) * 2) : NULL;
-        EXPECT(orc_rms_norm_pad(x, r, w, 1e-5f, out, ro, T, H, ld) == 0, "orc_rms_norm_pad");
+        uint16_t* ro = (res & 1) ? (uint16_t*)xalloc((size_t)(T * H) * 2) : NULL;
+        EXPECT(orc_rms_norm_pad(x, r, w, 1e-5f, out, ro, T, H, ld, f16 ? ORC_INPUT_F16 : 0) == 0,
+               "orc_rms_norm_pad");
         for (int64_t t = 0; t < T; ++t)
           for (int64_t i = H; i < ld; ++i) EXPECT(out[t * ld + i] == 0, "padding not zero");
         free(x);
@@ -219,16 +221,18 @@ static void pad_all(void) {
 static void rope_all(void) {
   const int64_t Ds[] = {2, 8, 64, 128, 256};
   for (int di = 0; di < 5; ++di)
-    for (int neox = 0; neox < 2; ++neox) {
+    for (int variant = 0; variant < 4; ++variant) {
+      const int neox = variant & 1, f16 = variant >> 1;
       const int64_t D = Ds[di], T = 9, Hq = 4, Hkv = 2, mp = 33;
       float* cache = (float*)xalloc((size_t)(mp * D) * 4);
       orc_rope_cache(cache, mp, D, 10000.0);
-      uint16_t* qkv = bf16_array(T * (Hq + 2 * Hkv) * D, 3.0f);
-      uint16_t* qw = bf16_array(D, 1.0f);
-      uint16_t* kw = bf16_array(D, 1.0f);
+      uint16_t* qkv = in16_array(T * (Hq + 2 * Hkv) * D, 3.0f, f16);
+      uint16_t* qw = in16_array(D, 1.0f, f16);
+      uint16_t* kw = in16_array(D, 1.0f, f16);
       int64_t* pos = (int64_t*)xalloc((size_t)T * 8);
       for (int64_t t = 0; t < T; ++t) pos[t] = (int64_t)(next_u32() % 50) - 8;  /* some out of range */
-      EXPECT(orc_qk_norm_rope(qkv, qw, kw, cache, pos, 1e-6f, T, Hq, Hkv, D, mp, neox) == 0,
+      EXPECT(orc_qk_norm_rope(qkv, qw, kw, cache, pos, 1e-6f, T, Hq, Hkv, D, mp, neox,
+                              f16 ? ORC_INPUT_F16 : 0) == 0,
              "orc_qk_norm_rope D %lld", (long long)D);
       free(cache);
       free(qkv);
@@ -239,7 +243,9 @@ static void rope_all(void) {
   uint16_t h = 0;
   float c = 0.0f;
   int64_t p = 0;
-  EXPECT(orc_qk_norm_rope(&h, &h, &h, &c, &p, 1e-6f, 1, 1, 1, 3, 1, 1) == -1, "odd D accepted");
+  EXPECT(orc_qk_norm_rope(&h, &h, &h, &c, &p, 1e-6f, 1, 1, 1, 3, 1, 1, 0) == -1, "odd D accepted");
+  EXPECT(orc_qk_norm_rope(&h, &h, &h, &c, &p, 1e-6f, 1, 1, 1, 2, 1, 1, 1u) == -1,
+         "unknown flag accepted");
 }
 
 static void silu_all(void) {

@@ -119,3 +119,102 @@ def test_silu_mul_on_binary16(orc):
     assert np.array_equal(tk["scales"], s)
     assert np.array_equal(tk["q"], torch_e4m3(a * (np.float32(1) / s)[:, None]))
     assert not np.array_equal(orc.silu_mul(x), a)  # read as bf16 it is another activation
+
+
+def test_padding_on_binary16(orc):
+    """RMSNorm + padding on binary16: the first H outputs are the pinned y rounded by numpy to
+    binary16, the rest zero; the new residual is the fused op's; read as bf16 it differs."""
+    x, r, w = _inputs(5, 2880, 11)
+    out, rout = orc.rms_norm_pad(x, r, w, 1e-5, 3072, flags=orc.INPUT_F16)
+    y = orc.rms_y(x, r, w, 1e-5, f16=True)
+    assert np.array_equal(out[:, :2880], f16_bits(y))
+    assert np.all(out[:, 2880:] == 0)
+    fused = orc.fused(x, r, w, 1e-5, orc.FP8_TOKEN, flags=orc.INPUT_F16)
+    assert np.array_equal(rout, fused["residual_out"])
+    plain, none = orc.rms_norm_pad(x, None, w, 1e-5, 2880, flags=orc.INPUT_F16)
+    assert none is None and np.array_equal(plain, f16_bits(orc.rms_y(x, None, w, 1e-5, f16=True)))
+    assert not np.array_equal(orc.rms_norm_pad(x, r, w, 1e-5, 3072)[0], out)
+
+
+def test_padding_output_overflows_to_infinity(orc):
+    """A row with one non-zero element a normalizes to sqrt(H) * sign(a) there: with H = 64 and a
+    weight of 10000 that is 80000, past binary16's 65504, so the output is +-infinity (bf16,
+    with its wider range, stays finite)."""
+    H = 64
+    x = np.zeros((2, H), np.uint16)
+    x[0, 0], x[1, 0] = f16_bits(3.0), f16_bits(-3.0)
+    w = f16_bits(np.full(H, 10000.0))
+    out, _ = orc.rms_norm_pad(x, None, w, 1e-6, H, flags=orc.INPUT_F16)
+    assert out[0, 0] == 0x7C00 and out[1, 0] == 0xFC00
+    assert np.all(out[:, 1:] == 0)
+    xb = np.zeros((1, H), np.uint16)
+    xb[0, 0] = 0x4040  # 3.0 in bf16
+    wb = np.full(H, 0x461C, np.uint16)  # 9984 in bf16
+    outb, _ = orc.rms_norm_pad(xb, None, wb, 1e-6, H)
+    assert np.isfinite(orc.bf16_to_f32(outb[0, 0]))
+
+
+RQ, RKV, RD = 4, 2, 64
+
+
+def _rope_inputs(T, seed, scale=2.0):
+    rng = np.random.default_rng(seed)
+    qkv = f16_bits(rng.standard_normal((T, (RQ + 2 * RKV) * RD)) * scale)
+    qw = f16_bits(rng.uniform(0.5, 1.5, RD))
+    kw = f16_bits(rng.uniform(-1.5, 1.5, RD))
+    return qkv, qw, kw
+
+
+def test_rope_position_zero_and_quarter_turn_on_binary16(orc):
+    """Position 0 (cos 1, sin 0) leaves the normalized head, rounded to binary16; a cache with
+    cos 0 and sin 1 maps each NeoX pair (a, b) to (-b, a).  v heads are not touched."""
+    T = 3
+    qkv, qw, kw = _rope_inputs(T, 12)
+    heads = qkv.reshape(T, RQ + 2 * RKV, RD)
+    cache = orc.rope_cache(8, RD)
+    out = orc.qk_norm_rope(qkv, qw, kw, cache, np.zeros(T, np.int64), 1e-6, RQ, RKV, RD,
+                           flags=orc.INPUT_F16).reshape(heads.shape)
+    turn = np.zeros((4, RD), np.float32)
+    turn[:, RD // 2:] = 1.0
+    out_t = orc.qk_norm_rope(qkv, qw, kw, turn, np.full(T, 2, np.int64), 1e-6, RQ, RKV, RD,
+                             flags=orc.INPUT_F16).reshape(heads.shape)
+    for hd in range(RQ + RKV):
+        y = orc.rms_y(np.ascontiguousarray(heads[:, hd]), None, qw if hd < RQ else kw, 1e-6,
+                      f16=True)
+        assert np.array_equal(out[:, hd], f16_bits(y))
+        a, b = y[:, :RD // 2], y[:, RD // 2:]
+        assert np.array_equal(out_t[:, hd], f16_bits(np.concatenate([-b, a], axis=1)))
+    assert np.array_equal(out[:, RQ + RKV:], heads[:, RQ + RKV:])
+
+
+@pytest.mark.parametrize("neox", [True, False])
+def test_rope_on_binary16_matches_torch_float64(orc, neox):
+    T = 8
+    qkv, qw, kw = _rope_inputs(T, 13)
+    cache = orc.rope_cache(100, RD, 10000.0)
+    pos = np.random.default_rng(14).integers(0, 100, T)
+    out = orc.qk_norm_rope(qkv, qw, kw, cache, pos, 1e-6, RQ, RKV, RD, neox, flags=orc.INPUT_F16)
+    x = torch.from_numpy(qkv.view(np.float16).astype(np.float64)).reshape(T, RQ + 2 * RKV, RD)
+    c = torch.from_numpy(cache[pos, :RD // 2]).double()[:, None, :]
+    s = torch.from_numpy(cache[pos, RD // 2:]).double()[:, None, :]
+    res = []
+    for hs, w in ((slice(0, RQ), qw), (slice(RQ, RQ + RKV), kw)):
+        wt = torch.from_numpy(w.view(np.float16).astype(np.float64))
+        y = torch.nn.functional.rms_norm(x[:, hs], (RD,), wt, 1e-6)
+        if neox:
+            a, b = y[..., :RD // 2], y[..., RD // 2:]
+            res.append(torch.cat([a * c - b * s, b * c + a * s], dim=-1))
+        else:
+            a, b = y[..., 0::2], y[..., 1::2]
+            rr = torch.empty_like(y)
+            rr[..., 0::2], rr[..., 1::2] = a * c - b * s, b * c + a * s
+            res.append(rr)
+    ref = torch.cat(res, dim=1)
+    got = torch.from_numpy(out.view(np.float16).astype(np.float64)).reshape(
+        T, RQ + 2 * RKV, RD)[:, :RQ + RKV]
+    # binary16 output: half a binary16 ulp of the value plus the f32 steps, relative to the pair
+    tol = ref.abs().amax(dim=-1, keepdim=True) * 2.0 ** -11 * 1.05
+    assert torch.all((got - ref).abs() <= tol)
+    # the same bits read as bf16 are another input altogether
+    assert not np.array_equal(out, orc.qk_norm_rope(qkv, qw, kw, cache, pos, 1e-6, RQ, RKV, RD,
+                                                    neox))

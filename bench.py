@@ -151,7 +151,7 @@ def rope_leg(args, wl, T, D):
     sh = stream.cuda_stream
     status = []
     argsets = [(q.data_ptr(), qw_d.data_ptr(), kw_d.data_ptr(), cache.data_ptr(),
-                pos_d.data_ptr(), float(wl.eps), T, hq, hkv, D, wl.max_position, 1, hpb, hpl)
+                pos_d.data_ptr(), float(wl.eps), T, hq, hkv, D, wl.max_position, 1, 0, hpb, hpl)
                for q in sets]
 
     def launch(a, e0, e1, hs):
@@ -376,7 +376,7 @@ def gpu_leg(args, wl, T, H, mode, G, flags):
     status = []
     if pad:
         argsets = [(ptr(s["x"]), ptr(s["r"]), wd.data_ptr(), float(wl.eps), ptr(s["q"]),
-                    ptr(s["ro"]), T, H, ld) for s in sets]
+                    ptr(s["ro"]), T, H, ld, 0) for s in sets]
 
         def launch_on(a, hs):
             return lib.rmsq_rms_norm_pad_ex(*a, lref, None, None, hs)

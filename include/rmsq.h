@@ -45,7 +45,7 @@ extern "C" {
 #define RMSQ_API
 #endif
 
-#define RMSQ_ABI_VERSION 1
+#define RMSQ_ABI_VERSION 2
 #define RMSQ_MAX_HIDDEN 65536 /* largest H one workgroup keeps in registers */
 
 /* ---- status codes ---- */
@@ -75,9 +75,9 @@ enum {
   RMSQ_SCALE_E8M0_U8 = 1u << 2   /* same rounding, stored as the E8M0 byte (exponent + 127)  */
 };
 
-/* ---- activation type flag, any mode of rmsq_fused and rmsq_silu_mul_quant (docs "Fusion
- *      torch.compile passes" and the blog's type check: x and the weight share the model's
- *      activation dtype) ---- */
+/* ---- activation type flag: any mode of rmsq_fused and rmsq_silu_mul_quant, and
+ *      rmsq_rms_norm_pad and rmsq_qk_norm_rope (docs "Fusion torch.compile passes" and the
+ *      blog's type check: x and the weight share the model's activation dtype) ---- */
 enum {
   RMSQ_INPUT_F16 = 1u << 8 /* x, residual, weight, residual_out are IEEE binary16, not bf16 */
 };
@@ -173,35 +173,39 @@ RMSQ_API int rmsq_fused_timed(const void* x, const void* residual, const void* w
                               void* start_event, void* stop_event, void* stream);
 
 /*
- * rmsq_rms_norm_pad -- (residual add ->) RMSNorm -> bf16 output in a padded row layout, in one
+ * rmsq_rms_norm_pad -- (residual add ->) RMSNorm -> 16-bit output in a padded row layout, in one
  * launch (vLLM docs "Fusion torch.compile passes", section "RMSNorm + padding
  * (fuse_act_padding)": the residual add and RMSNorm fused with padding the hidden dimension --
  * 2880 for the model named there -- to the multiple a downstream GEMM needs).
  *
  *  x, residual, weight, eps, residual_out, tokens, hidden
  *               exactly as for rmsq_fused (residual NULL: plain RMSNorm).
- *  out          [T, out_ld] bf16, 16-byte aligned: out[t, i] = bf16(y_i) (round to nearest
- *               even) for i < H and 0 for H <= i < out_ld.  Must not overlap any input or
- *               residual_out.
+ *  out          [T, out_ld], the type of x, 16-byte aligned: out[t, i] = y_i rounded to that
+ *               type (nearest even; binary16 overflows to infinity) for i < H and 0 for
+ *               H <= i < out_ld.  Must not overlap any input or residual_out.
  *  out_ld       the padded row length: H <= out_ld <= RMSQ_MAX_HIDDEN, out_ld % 8 == 0.
+ *  flags        0 (bf16) or RMSQ_INPUT_F16 (x, residual, weight, residual_out and out are IEEE
+ *               binary16); any other bit is RMSQ_EUNSUPPORTED.
  * Returns RMSQ_OK or a negative status.
  */
 RMSQ_API int rmsq_rms_norm_pad(const void* x, const void* residual, const void* weight,
                                float eps, void* out, void* residual_out, int64_t tokens,
-                               int64_t hidden, int64_t out_ld, void* stream);
+                               int64_t hidden, int64_t out_ld, unsigned flags, void* stream);
 
 /* rmsq_rms_norm_pad with an explicit launch shape (NULL: the default, see
  * rmsq_rms_norm_pad_query_launch; a shape must cover out_ld) and optional dispatch-stamped
  * events. */
 RMSQ_API int rmsq_rms_norm_pad_ex(const void* x, const void* residual, const void* weight,
                                   float eps, void* out, void* residual_out, int64_t tokens,
-                                  int64_t hidden, int64_t out_ld, const rmsq_launch* launch,
-                                  void* start_event, void* stop_event, void* stream);
+                                  int64_t hidden, int64_t out_ld, unsigned flags,
+                                  const rmsq_launch* launch, void* start_event, void* stop_event,
+                                  void* stream);
 
 /* Host-only argument check of rmsq_rms_norm_pad (no HIP call, no dereference). */
 RMSQ_API int rmsq_rms_norm_pad_validate(const void* x, const void* residual, const void* weight,
                                         float eps, const void* out, const void* residual_out,
-                                        int64_t tokens, int64_t hidden, int64_t out_ld);
+                                        int64_t tokens, int64_t hidden, int64_t out_ld,
+                                        unsigned flags);
 
 /*
  * rmsq_silu_mul_quant -- SiLU+Mul -> quantization in one launch (vLLM docs "Fusion
@@ -245,14 +249,15 @@ RMSQ_API int rmsq_silu_mul_quant_validate(const void* x, int mode, const float* 
  * + RoPE": for models that normalize Q and K per head, the split of the packed qkv tensor, the
  * two RMSNorms and the rotary embedding become one kernel).
  *
- *  qkv          [T, (Hq + 2 Hkv) * D] bf16, 16-byte aligned, row t = Hq q heads, Hkv k heads,
- *               Hkv v heads of D elements each.  Rewritten in place: every q head h becomes
- *               rope(rmsnorm(h) * q_weight), every k head rope(rmsnorm(h) * k_weight), rounded
- *               once to bf16 (nearest even) from f32; v heads are not touched.
+ *  qkv          [T, (Hq + 2 Hkv) * D] bf16 (IEEE binary16 with RMSQ_INPUT_F16), 16-byte
+ *               aligned, row t = Hq q heads, Hkv k heads, Hkv v heads of D elements each.
+ *               Rewritten in place: every q head h becomes rope(rmsnorm(h) * q_weight), every k
+ *               head rope(rmsnorm(h) * k_weight), rounded once from f32 to the type of qkv
+ *               (nearest even; binary16 overflows to infinity); v heads are not touched.
  *  rmsnorm      y_i = (h_i * inv) * w_i in f32, inv = 1/sqrt(sum h_i^2 / D + eps) from a
  *               binary64 sum, rounded to f32 (as rmsq_fused, over one head of D elements).
  *  q_weight, k_weight
- *               [D] bf16, 16-byte aligned, read only.
+ *               [D], the type of qkv, 16-byte aligned, read only.
  *  cos_sin_cache
  *               [max_position, D] f32, 16-byte aligned: row p = cos(p * f_i) for i < D/2, then
  *               sin(p * f_i); the caller builds it (any base).  Read only.
@@ -263,12 +268,14 @@ RMSQ_API int rmsq_silu_mul_quant_validate(const void* x, int mode, const float* 
  *               each product rounded to f32 before the sum.
  *  tokens       T >= 0 (0 is a no-op); num_q_heads Hq >= 1, num_kv_heads Hkv >= 1,
  *               (Hq + 2 Hkv) * D <= 2^20; head_dim D in {64, 128, 256}; max_position >= 1.
+ *  flags        0 (bf16) or RMSQ_INPUT_F16 (qkv and both weights IEEE binary16); any other bit
+ *               is RMSQ_EUNSUPPORTED.
  * qkv must not overlap the other arguments.  Returns RMSQ_OK or a negative status.
  */
 RMSQ_API int rmsq_qk_norm_rope(void* qkv, const void* q_weight, const void* k_weight,
                                const float* cos_sin_cache, const int64_t* positions, float eps,
                                int64_t tokens, int num_q_heads, int num_kv_heads, int head_dim,
-                               int64_t max_position, int is_neox, void* stream);
+                               int64_t max_position, int is_neox, unsigned flags, void* stream);
 
 /* rmsq_qk_norm_rope with an explicit launch shape and optional dispatch-stamped events (as
  * rmsq_fused_timed; NULL: none).  A head is held by D/16 lanes (16 elements each); a lane group
@@ -279,15 +286,15 @@ RMSQ_API int rmsq_qk_norm_rope_ex(void* qkv, const void* q_weight, const void* k
                                   const float* cos_sin_cache, const int64_t* positions,
                                   float eps, int64_t tokens, int num_q_heads, int num_kv_heads,
                                   int head_dim, int64_t max_position, int is_neox,
-                                  int heads_per_block, int heads_per_lane, void* start_event,
-                                  void* stop_event, void* stream);
+                                  unsigned flags, int heads_per_block, int heads_per_lane,
+                                  void* start_event, void* stop_event, void* stream);
 
 /* Host-only argument check of rmsq_qk_norm_rope (no HIP call, no dereference). */
 RMSQ_API int rmsq_qk_norm_rope_validate(const void* qkv, const void* q_weight,
                                         const void* k_weight, const float* cos_sin_cache,
                                         const int64_t* positions, float eps, int64_t tokens,
                                         int num_q_heads, int num_kv_heads, int head_dim,
-                                        int64_t max_position);
+                                        int64_t max_position, unsigned flags);
 
 /* The default launch shape of rmsq_qk_norm_rope (heads per workgroup, heads per lane group) and
  * its grid size (tokens times the workgroups per token).  Host only; makes no HIP call.

@@ -34,6 +34,7 @@ RMSQ_CVT_E4M3, RMSQ_CVT_E2M1, RMSQ_CVT_BF16 = 0, 1, 2
 RMSQ_LAUNCH_XCD_RANGES = 1
 RMSQ_LAUNCH_ROW_TILES = 2
 RMSQ_MAX_HIDDEN = 65536
+RMSQ_ABI_VERSION = 2  # the argument lists below are those of this version
 
 
 class RmsqError(RuntimeError):
@@ -72,7 +73,7 @@ def lib():
         L.rmsq_fused_timed.restype = i32
         L.rmsq_validate.argtypes = fused_args
         L.rmsq_validate.restype = i32
-        pad_args = [p, p, p, f32, p, p, i64, i64, i64]
+        pad_args = [p, p, p, f32, p, p, i64, i64, i64, u32]
         L.rmsq_rms_norm_pad.argtypes = pad_args + [p]
         L.rmsq_rms_norm_pad.restype = i32
         L.rmsq_rms_norm_pad_ex.argtypes = pad_args + [C.POINTER(rmsq_launch), p, p, p]
@@ -87,11 +88,11 @@ def lib():
         L.rmsq_silu_mul_quant_validate.argtypes = act_args
         L.rmsq_silu_mul_quant_validate.restype = i32
         rope_args = [p, p, p, p, p, f32, i64, i32, i32, i32, i64]
-        L.rmsq_qk_norm_rope.argtypes = rope_args + [i32, p]
+        L.rmsq_qk_norm_rope.argtypes = rope_args + [i32, u32, p]
         L.rmsq_qk_norm_rope.restype = i32
-        L.rmsq_qk_norm_rope_ex.argtypes = rope_args + [i32, i32, i32, p, p, p]
+        L.rmsq_qk_norm_rope_ex.argtypes = rope_args + [i32, u32, i32, i32, p, p, p]
         L.rmsq_qk_norm_rope_ex.restype = i32
-        L.rmsq_qk_norm_rope_validate.argtypes = rope_args
+        L.rmsq_qk_norm_rope_validate.argtypes = rope_args + [u32]
         L.rmsq_qk_norm_rope_validate.restype = i32
         L.rmsq_qk_norm_rope_query_launch.argtypes = [i64, i32, i32, i32, C.POINTER(i32),
                                                      C.POINTER(i32), C.POINTER(i64)]
@@ -113,6 +114,10 @@ def lib():
         L.rmsq_status_string.restype = C.c_char_p
         L.rmsq_abi_version.argtypes = []
         L.rmsq_abi_version.restype = i32
+        if L.rmsq_abi_version() != RMSQ_ABI_VERSION:
+            raise RuntimeError(
+                f"{LIB_PATH} has ABI version {L.rmsq_abi_version()}, this binding needs "
+                f"{RMSQ_ABI_VERSION}: rebuild it")
         _lib = L
     return _lib
 
@@ -197,13 +202,14 @@ def rmsq_fused_timed(x, residual, weight, eps, mode, scale_in, out_q, out_scales
 
 def rmsq_rms_norm_pad(x, residual, weight, eps, out, residual_out, tokens=None, hidden=None,
                       out_ld=None, stream=None, launch=None, start_event=None, stop_event=None,
-                      check=True) -> int:
-    """(Residual add ->) RMSNorm -> bf16 out [T, out_ld] with zero padding columns."""
+                      check=True, flags=0) -> int:
+    """(Residual add ->) RMSNorm -> out [T, out_ld] (bf16, or binary16 with RMSQ_INPUT_F16)
+    with zero padding columns."""
     T = x.shape[0] if tokens is None else tokens
     H = x.shape[-1] if hidden is None else hidden
     ld = out.shape[-1] if out_ld is None else out_ld
     args = (_ptr(x), _ptr(residual), _ptr(weight), float(eps), _ptr(out), _ptr(residual_out),
-            int(T), int(H), int(ld))
+            int(T), int(H), int(ld), int(flags))
     if launch is None and start_event is None and stop_event is None:
         st = lib().rmsq_rms_norm_pad(*args, _stream(stream))
     else:
@@ -215,10 +221,10 @@ def rmsq_rms_norm_pad(x, residual, weight, eps, out, residual_out, tokens=None, 
 
 
 def rmsq_rms_norm_pad_validate(x, residual, weight, eps, out, residual_out, tokens, hidden,
-                               out_ld) -> int:
+                               out_ld, flags=0) -> int:
     """Host-only argument check; pointers are plain integers (or None)."""
     return lib().rmsq_rms_norm_pad_validate(x, residual, weight, float(eps), out, residual_out,
-                                            int(tokens), int(hidden), int(out_ld))
+                                            int(tokens), int(hidden), int(out_ld), int(flags))
 
 
 def rmsq_silu_mul_quant(x, mode, scale_in, out_q, out_scales, tokens=None, inter=None,
@@ -251,33 +257,35 @@ def rmsq_silu_mul_quant_validate(x, mode, scale_in, out_q, out_scales, tokens, i
 def rmsq_qk_norm_rope(qkv, q_weight, k_weight, cos_sin_cache, positions, eps, num_q_heads,
                       num_kv_heads, head_dim, is_neox=True, tokens=None, max_position=None,
                       stream=None, heads_per_block=0, heads_per_lane=0, start_event=None,
-                      stop_event=None, check=True) -> int:
+                      stop_event=None, check=True, flags=0) -> int:
     """In-place per-head RMSNorm + rotary embedding of the q and k heads of qkv
-    [T, (Hq + 2 Hkv) * D]; cos_sin_cache [max_position, D] f32, positions [T] int64.  With a
-    launch shape (heads per workgroup and per lane group) or events it goes through
-    rmsq_qk_norm_rope_ex."""
+    [T, (Hq + 2 Hkv) * D] (bf16, or binary16 with flags=RMSQ_INPUT_F16); cos_sin_cache
+    [max_position, D] f32, positions [T] int64.  With a launch shape (heads per workgroup and
+    per lane group) or events it goes through rmsq_qk_norm_rope_ex."""
     T = qkv.shape[0] if tokens is None else tokens
     mp = cos_sin_cache.shape[0] if max_position is None else max_position
     args = (_ptr(qkv), _ptr(q_weight), _ptr(k_weight), _ptr(cos_sin_cache), _ptr(positions),
             float(eps), int(T), int(num_q_heads), int(num_kv_heads), int(head_dim), int(mp))
     if heads_per_block == 0 and heads_per_lane == 0 and start_event is None and \
             stop_event is None:
-        st = lib().rmsq_qk_norm_rope(*args, int(bool(is_neox)), _stream(stream))
+        st = lib().rmsq_qk_norm_rope(*args, int(bool(is_neox)), int(flags), _stream(stream))
     else:
-        st = lib().rmsq_qk_norm_rope_ex(*args, int(bool(is_neox)), int(heads_per_block),
-                                        int(heads_per_lane), start_event, stop_event,
-                                        _stream(stream))
+        st = lib().rmsq_qk_norm_rope_ex(*args, int(bool(is_neox)), int(flags),
+                                        int(heads_per_block), int(heads_per_lane), start_event,
+                                        stop_event, _stream(stream))
     if check:
         _check(st, "rmsq_qk_norm_rope")
     return st
 
 
 def rmsq_qk_norm_rope_validate(qkv, q_weight, k_weight, cos_sin_cache, positions, eps, tokens,
-                               num_q_heads, num_kv_heads, head_dim, max_position) -> int:
+                               num_q_heads, num_kv_heads, head_dim, max_position,
+                               flags=0) -> int:
     """Host-only argument check; pointers are plain integers (or None)."""
     return lib().rmsq_qk_norm_rope_validate(qkv, q_weight, k_weight, cos_sin_cache, positions,
                                             float(eps), int(tokens), int(num_q_heads),
-                                            int(num_kv_heads), int(head_dim), int(max_position))
+                                            int(num_kv_heads), int(head_dim), int(max_position),
+                                            int(flags))
 
 
 def rmsq_qk_norm_rope_query_launch(tokens, num_q_heads, num_kv_heads, head_dim):
@@ -442,20 +450,23 @@ def silu_and_mul_quant(x, mode, scale=None, group_size=0, col_major=False, e8m0=
 
 
 def fused_add_rms_norm_pad(x, residual, weight, eps, multiple=256, inplace=True):
-    """(out [T, H padded up to `multiple`] bf16 with zero padding, residual_out): residual add
-    + RMSNorm with the hidden dimension padded for a downstream GEMM."""
+    """(out [T, H padded up to `multiple`] in x's dtype with zero padding, residual_out):
+    residual add + RMSNorm with the hidden dimension padded for a downstream GEMM."""
     T, H = x.shape
+    flags = _act_flag(x, weight, residual)
     ld = -(-H // multiple) * multiple
-    out = torch.empty((T, ld), dtype=torch.bfloat16, device=x.device)
+    out = torch.empty((T, ld), dtype=x.dtype, device=x.device)
     rout = None if residual is None else (residual if inplace else torch.empty_like(residual))
-    rmsq_rms_norm_pad(x, residual, weight, eps, out, rout)
+    rmsq_rms_norm_pad(x, residual, weight, eps, out, rout, flags=flags)
     return out, rout
 
 
 def qk_norm_rope(qkv, positions, q_weight, k_weight, cos_sin_cache, eps, num_q_heads,
                  num_kv_heads, is_neox=True):
-    """The fused QK-norm + RoPE op on qkv [T, (Hq + 2 Hkv) * D] bf16, in place; returns qkv."""
+    """The fused QK-norm + RoPE op on qkv [T, (Hq + 2 Hkv) * D] (bf16 or float16, the weights
+    of the same dtype), in place; returns qkv."""
     D = q_weight.shape[0]
+    flags = _act_flag(qkv, q_weight, k_weight)
     rmsq_qk_norm_rope(qkv, q_weight, k_weight, cos_sin_cache, positions, eps, num_q_heads,
-                      num_kv_heads, D, is_neox)
+                      num_kv_heads, D, is_neox, flags=flags)
     return qkv

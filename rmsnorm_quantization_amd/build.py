@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 # host side, and the kernel instantiation tables (rmsq_kernel_table.hpp)
 SRC = [os.path.join(PKG, "csrc", f) for f in ("rmsq.hip", "table_fused_bf16.hip",
                                               "table_fused_f16.hip", "table_act.hip",
-                                              "table_misc.hip")]
+                                              "table_misc.hip", "table_rope_f16.hip")]
 KERNEL_SOURCES = [os.path.join(PKG, "csrc", "rmsq_device.hpp"),
                   os.path.join(PKG, "csrc", "rmsq_kernels.hpp"),
                   os.path.join(PKG, "csrc", "rmsq_kernel_table.hpp")]

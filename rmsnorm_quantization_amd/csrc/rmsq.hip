@@ -246,9 +246,10 @@ int fused_impl(const void* x, const void* res, const void* w, float eps, int mod
                        stop_event);
 }
 
-// ---- residual add + RMSNorm -> padded bf16 --------------------------------------------------
+// ---- residual add + RMSNorm -> padded 16-bit output ------------------------------------------
 int validate_pad(const void* x, const void* res, const void* w, float eps, const void* out,
-                 const void* res_out, int64_t T, int64_t H, int64_t out_ld) {
+                 const void* res_out, int64_t T, int64_t H, int64_t out_ld, unsigned flags) {
+  if ((flags & ~(unsigned)RMSQ_INPUT_F16) != 0) return RMSQ_EUNSUPPORTED;
   if (T < 0 || T > 0x7FFFFFFFLL) return RMSQ_EINVAL;
   if (H < 8 || H > RMSQ_MAX_HIDDEN || (H % 8) != 0) return RMSQ_EINVAL;
   if (out_ld < H || out_ld > RMSQ_MAX_HIDDEN || (out_ld % 8) != 0) return RMSQ_EINVAL;
@@ -284,16 +285,17 @@ rmsq_launch default_pad_launch(int64_t ld) {
 }
 
 int pad_impl(const void* x, const void* res, const void* w, float eps, void* out, void* res_out,
-             int64_t T, int64_t H, int64_t out_ld, const rmsq_launch* launch, void* start_event,
-             void* stop_event, void* stream) {
-  int st = validate_pad(x, res, w, eps, out, res_out, T, H, out_ld);
+             int64_t T, int64_t H, int64_t out_ld, unsigned flags, const rmsq_launch* launch,
+             void* start_event, void* stop_event, void* stream) {
+  int st = validate_pad(x, res, w, eps, out, res_out, T, H, out_ld, flags);
   if (st != RMSQ_OK) return st;
   const rmsq_launch l = launch ? *launch : default_pad_launch(out_ld);
   if (!valid_launch(l, out_ld)) return RMSQ_EINVAL;  // the launch covers the padded row
   if (T == 0) return RMSQ_OK;
   st = check_device();
   if (st != RMSQ_OK) return st;
-  const void* fn = pad_kernel(res != nullptr, l.chunks_per_thread);
+  const void* fn = (flags & RMSQ_INPUT_F16) ? pad_kernel_f16(res != nullptr, l.chunks_per_thread)
+                                            : pad_kernel_bf16(res != nullptr, l.chunks_per_thread);
   if (!fn) return RMSQ_EINVAL;
   const int64_t nblk = (T + l.rows_per_block - 1) / l.rows_per_block;
   KArgs a;
@@ -402,7 +404,8 @@ bool valid_rope_hpl(int hpl) { return hpl >= 1 && hpl <= 6; }
 
 int validate_rope(const void* qkv, const void* qw, const void* kw, const float* cache,
                   const int64_t* pos, float eps, int64_t T, int hq, int hkv, int D,
-                  int64_t max_pos) {
+                  int64_t max_pos, unsigned flags) {
+  if ((flags & ~(unsigned)RMSQ_INPUT_F16) != 0) return RMSQ_EUNSUPPORTED;
   if (T < 0 || T > 0x7FFFFFFFLL) return RMSQ_EINVAL;
   if (D != 64 && D != 128 && D != 256) return RMSQ_EINVAL;
   if (hq < 1 || hkv < 1 || (int64_t)(hq + 2LL * hkv) * D > kMaxQkvWidth) return RMSQ_EINVAL;
@@ -495,9 +498,9 @@ void default_rope_shape(int64_t T, int nh, int D, int* hpl_out, int* hpb_out) {
 
 int rope_impl(void* qkv, const void* qw, const void* kw, const float* cache, const int64_t* pos,
               float eps, int64_t T, int hq, int hkv, int D, int64_t max_pos, int neox,
-              int heads_per_block, int heads_per_lane, void* start_event, void* stop_event,
-              void* stream) {
-  int st = validate_rope(qkv, qw, kw, cache, pos, eps, T, hq, hkv, D, max_pos);
+              unsigned flags, int heads_per_block, int heads_per_lane, void* start_event,
+              void* stop_event, void* stream) {
+  int st = validate_rope(qkv, qw, kw, cache, pos, eps, T, hq, hkv, D, max_pos, flags);
   if (st != RMSQ_OK) return st;
   const int nh = hq + hkv;
   int hpl = heads_per_lane, hpb = heads_per_block;
@@ -508,7 +511,8 @@ int rope_impl(void* qkv, const void* qw, const void* kw, const float* cache, con
   if (T == 0) return RMSQ_OK;
   st = check_device();
   if (st != RMSQ_OK) return st;
-  const void* fn = rope_kernel(D, neox != 0, hpl);
+  const void* fn = (flags & RMSQ_INPUT_F16) ? rope_kernel_f16(D, neox != 0, hpl)
+                                            : rope_kernel_bf16(D, neox != 0, hpl);
   if (!fn) return RMSQ_EINVAL;
   const int64_t nhb = (nh + hpb - 1) / hpb;
   RArgs a;
@@ -572,23 +576,24 @@ int rmsq_validate(const void* x, const void* residual, const void* weight, float
 
 int rmsq_rms_norm_pad(const void* x, const void* residual, const void* weight, float eps,
                       void* out, void* residual_out, int64_t tokens, int64_t hidden,
-                      int64_t out_ld, void* stream) {
-  return pad_impl(x, residual, weight, eps, out, residual_out, tokens, hidden, out_ld, nullptr,
-                  nullptr, nullptr, stream);
+                      int64_t out_ld, unsigned flags, void* stream) {
+  return pad_impl(x, residual, weight, eps, out, residual_out, tokens, hidden, out_ld, flags,
+                  nullptr, nullptr, nullptr, stream);
 }
 
 int rmsq_rms_norm_pad_ex(const void* x, const void* residual, const void* weight, float eps,
                          void* out, void* residual_out, int64_t tokens, int64_t hidden,
-                         int64_t out_ld, const rmsq_launch* launch, void* start_event,
-                         void* stop_event, void* stream) {
-  return pad_impl(x, residual, weight, eps, out, residual_out, tokens, hidden, out_ld, launch,
-                  start_event, stop_event, stream);
+                         int64_t out_ld, unsigned flags, const rmsq_launch* launch,
+                         void* start_event, void* stop_event, void* stream) {
+  return pad_impl(x, residual, weight, eps, out, residual_out, tokens, hidden, out_ld, flags,
+                  launch, start_event, stop_event, stream);
 }
 
 int rmsq_rms_norm_pad_validate(const void* x, const void* residual, const void* weight, float eps,
                                const void* out, const void* residual_out, int64_t tokens,
-                               int64_t hidden, int64_t out_ld) {
-  return validate_pad(x, residual, weight, eps, out, residual_out, tokens, hidden, out_ld);
+                               int64_t hidden, int64_t out_ld, unsigned flags) {
+  return validate_pad(x, residual, weight, eps, out, residual_out, tokens, hidden, out_ld,
+                      flags);
 }
 
 int rmsq_silu_mul_quant(const void* x, int mode, const float* scale_in, void* out_q,
@@ -657,27 +662,29 @@ int rmsq_silu_mul_query_launch(int mode, int64_t tokens, int64_t inter, int grou
 int rmsq_qk_norm_rope(void* qkv, const void* q_weight, const void* k_weight,
                       const float* cos_sin_cache, const int64_t* positions, float eps,
                       int64_t tokens, int num_q_heads, int num_kv_heads, int head_dim,
-                      int64_t max_position, int is_neox, void* stream) {
+                      int64_t max_position, int is_neox, unsigned flags, void* stream) {
   return rope_impl(qkv, q_weight, k_weight, cos_sin_cache, positions, eps, tokens, num_q_heads,
-                   num_kv_heads, head_dim, max_position, is_neox, 0, 0, nullptr, nullptr, stream);
+                   num_kv_heads, head_dim, max_position, is_neox, flags, 0, 0, nullptr, nullptr,
+                   stream);
 }
 
 int rmsq_qk_norm_rope_ex(void* qkv, const void* q_weight, const void* k_weight,
                          const float* cos_sin_cache, const int64_t* positions, float eps,
                          int64_t tokens, int num_q_heads, int num_kv_heads, int head_dim,
-                         int64_t max_position, int is_neox, int heads_per_block,
-                         int heads_per_lane, void* start_event, void* stop_event, void* stream) {
+                         int64_t max_position, int is_neox, unsigned flags,
+                         int heads_per_block, int heads_per_lane, void* start_event,
+                         void* stop_event, void* stream) {
   return rope_impl(qkv, q_weight, k_weight, cos_sin_cache, positions, eps, tokens, num_q_heads,
-                   num_kv_heads, head_dim, max_position, is_neox, heads_per_block,
+                   num_kv_heads, head_dim, max_position, is_neox, flags, heads_per_block,
                    heads_per_lane, start_event, stop_event, stream);
 }
 
 int rmsq_qk_norm_rope_validate(const void* qkv, const void* q_weight, const void* k_weight,
                                const float* cos_sin_cache, const int64_t* positions, float eps,
                                int64_t tokens, int num_q_heads, int num_kv_heads, int head_dim,
-                               int64_t max_position) {
+                               int64_t max_position, unsigned flags) {
   return validate_rope(qkv, q_weight, k_weight, cos_sin_cache, positions, eps, tokens,
-                       num_q_heads, num_kv_heads, head_dim, max_position);
+                       num_q_heads, num_kv_heads, head_dim, max_position, flags);
 }
 
 int rmsq_qk_norm_rope_query_launch(int64_t tokens, int num_q_heads, int num_kv_heads,

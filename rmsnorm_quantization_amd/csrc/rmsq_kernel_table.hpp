@@ -11,14 +11,42 @@ namespace rmsq {
 // fused (residual add ->) RMSNorm -> quantization, bf16 or IEEE binary16 activations
 const void* fused_kernel_bf16(int mode, bool res, int gs, int vpt, bool exact);
 const void* fused_kernel_f16(int mode, bool res, int gs, int vpt, bool exact);
-// (residual add ->) RMSNorm -> padded bf16 output (launches always masked)
-const void* pad_kernel(bool res, int vpt);
+// (residual add ->) RMSNorm -> padded 16-bit output (launches always masked)
+const void* pad_kernel_bf16(bool res, int vpt);
+const void* pad_kernel_f16(bool res, int vpt);
 // SiLU+Mul -> quantization, whole rows or row tiles
 const void* act_kernel_bf16(bool tiled, bool exact, int mode, int gs, int vpt);
 const void* act_kernel_f16(bool tiled, bool exact, int mode, int gs, int vpt);
 // QK-norm + RoPE
-const void* rope_kernel(int D, bool neox, int hpl);
+const void* rope_kernel_bf16(int D, bool neox, int hpl);
+const void* rope_kernel_f16(int D, bool neox, int hpl);
 // the diagnostic converters
 const void* convert_kernel_ptr();
+
+// The QK-norm + RoPE instantiation for (D, NEOX, heads per lane), one 16-bit type per table unit.
+template <int DT, int D, bool NEOX>
+const void* pick_rope_hpl(int hpl) {
+  switch (hpl) {
+    case 1: return reinterpret_cast<const void*>(&qk_norm_rope_kernel<D, NEOX, 1, DT>);
+    case 2: return reinterpret_cast<const void*>(&qk_norm_rope_kernel<D, NEOX, 2, DT>);
+    case 3: return reinterpret_cast<const void*>(&qk_norm_rope_kernel<D, NEOX, 3, DT>);
+    case 4: return reinterpret_cast<const void*>(&qk_norm_rope_kernel<D, NEOX, 4, DT>);
+    case 5: return reinterpret_cast<const void*>(&qk_norm_rope_kernel<D, NEOX, 5, DT>);
+    case 6: return reinterpret_cast<const void*>(&qk_norm_rope_kernel<D, NEOX, 6, DT>);
+    default: return nullptr;
+  }
+}
+
+template <int DT>
+const void* pick_rope(int D, bool neox, int hpl) {
+  switch (D) {
+    case 64: return neox ? pick_rope_hpl<DT, 64, true>(hpl) : pick_rope_hpl<DT, 64, false>(hpl);
+    case 128:
+      return neox ? pick_rope_hpl<DT, 128, true>(hpl) : pick_rope_hpl<DT, 128, false>(hpl);
+    case 256:
+      return neox ? pick_rope_hpl<DT, 256, true>(hpl) : pick_rope_hpl<DT, 256, false>(hpl);
+    default: return nullptr;
+  }
+}
 
 }  // namespace rmsq

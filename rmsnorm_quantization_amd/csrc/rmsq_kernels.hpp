@@ -28,9 +28,10 @@
 namespace rmsq {
 
 constexpr int kMaxWavesPerBlock = 16;
-// Internal mode of fused_kernel: the normalized row rounded to bf16 and written with a padded
-// row stride (ld), the padding columns zero.  Not a quantization scheme, so not in rmsq_mode.
-constexpr int kModeBf16Pad = 4;
+// Internal mode of fused_kernel: the normalized row rounded to the 16-bit input type and written
+// with a padded row stride (ld), the padding columns zero.  Not a quantization scheme, so not in
+// rmsq_mode.
+constexpr int kModePad = 4;
 
 struct KArgs {
   const uint16_t* x;
@@ -82,7 +83,8 @@ struct RowOut {
 //   per-token  s = absmax(row)/448, q = e4m3(y * (1/s)); s == 0 gives 0 codes
 //   per-group  s = absmax(group)/448 (E8M0: rounded up to a power of two), same rule
 //   FP4        sf = e4m3(absmax(block16) * gs / 6), q = e2m1(y * (gs / decode(sf)))
-template <int MODE, int VPT, int GS, class YF>
+// DT (the 16-bit output type of the padded mode only): 0 bf16, 1 IEEE binary16.
+template <int MODE, int VPT, int GS, int DT = 0, class YF>
 __device__ __forceinline__ void quantize_store(const YF& Y, const bool (&ok)[VPT], const RowOut& o,
                                                float scale_val, float* s_mx) {
   if constexpr (MODE == RMSQ_FP8_STATIC) {
@@ -161,8 +163,8 @@ __device__ __forceinline__ void quantize_store(const YF& Y, const bool (&ok)[VPT
         }
       }
     }
-  } else if constexpr (MODE == kModeBf16Pad) {
-    // bf16 row of n values at a stride of ld elements; chunks n/8 .. ld/8-1 are zero padding.
+  } else if constexpr (MODE == kModePad) {
+    // 16-bit row of n values at a stride of ld elements; chunks n/8 .. ld/8-1 are zero padding.
     // The launch covers ld/8 chunks per row (ok[] marks the chunks below n).
     const uint32_t nchp = (uint32_t)(o.ld >> 3);
     u32x4* orow = reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(o.q) + o.obase);
@@ -172,7 +174,7 @@ __device__ __forceinline__ void quantize_store(const YF& Y, const bool (&ok)[VPT
       u32x4 v = (u32x4){0u, 0u, 0u, 0u};
       if (ok[k]) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = pack_bf16x2(Y(k, 2 * j), Y(k, 2 * j + 1));
+        for (int j = 0; j < 4; ++j) v[j] = pack_in<DT>(Y(k, 2 * j), Y(k, 2 * j + 1));
       }
       if (o.row_ok && c < nchp) __builtin_nontemporal_store(v, orow + c);
     }
@@ -301,7 +303,7 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
   o.scales = a.scales;
   o.row = row;
   o.row_ok = row_ok;
-  o.obase = (MODE == kModeBf16Pad) ? (size_t)(row_ok ? row : 0) * (size_t)a.ld : base;
+  o.obase = (MODE == kModePad) ? (size_t)(row_ok ? row : 0) * (size_t)a.ld : base;
   o.n = a.H;
   o.ld = a.ld;
   o.flags = a.flags;
@@ -310,7 +312,7 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
   o.wpr = wpr;
   o.rib = rib;
   o.tid = tid;
-  quantize_store<MODE, VPT, GS>(
+  quantize_store<MODE, VPT, GS, DT>(
       [&](int k, int e) { return y_of<DT>(hv[k], wv[k], e, inv); }, ok, o, scale_val, s_mx);
 }
 
@@ -495,7 +497,7 @@ __global__ void __launch_bounds__(1024) silu_mul_tile_kernel(AArgs a) {
 // hpb / HPT lane groups; group g takes heads g, g + groups, ... (HPT of them), so each load
 // instruction of a wave reads whole 128-byte lines and every lane has 2*HPT chunks in flight.
 struct RArgs {
-  uint16_t* qkv;           // [T, (Hq + 2 Hkv) * D] bf16, q and k heads rewritten in place
+  uint16_t* qkv;           // [T, (Hq + 2 Hkv) * D] 16-bit, q and k heads rewritten in place
   const uint16_t* qw;      // [D]
   const uint16_t* kw;      // [D]
   const float* cache;      // [max_pos, D]: cos | sin
@@ -522,7 +524,9 @@ __device__ __forceinline__ double group_sum(double v) {
   return v;
 }
 
-template <int D, bool NEOX, int HPT>
+// DT: the 16-bit type of qkv and the weights (0 bf16, 1 IEEE binary16); the arithmetic is f32
+// (binary64 sum of squares) either way and the result is rounded back to DT.
+template <int D, bool NEOX, int HPT, int DT>
 __global__ void __launch_bounds__(1024) qk_norm_rope_kernel(RArgs a) {
   constexpr int L = D / 16;   // lanes per head
   constexpr int CH = D / 8;   // 16-byte chunks per head
@@ -582,7 +586,8 @@ __global__ void __launch_bounds__(1024) qk_norm_rope_kernel(RArgs a) {
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const double lo = (double)bf16_lo(xv[k][hh][j]), hi = (double)bf16_hi(xv[k][hh][j]);
+        const double lo = (double)in_lo<DT>(xv[k][hh][j]);
+        const double hi = (double)in_hi<DT>(xv[k][hh][j]);
         ss0 = fma(lo, lo, ss0);
         ss1 = fma(hi, hi, ss1);
       }
@@ -594,8 +599,8 @@ __global__ void __launch_bounds__(1024) qk_norm_rope_kernel(RArgs a) {
     float y0[8], y1[8], o0[8], o1[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      y0[e] = y_of(xv[k][0], w0, e, inv);
-      y1[e] = y_of(xv[k][1], w1, e, inv);
+      y0[e] = y_of<DT>(xv[k][0], w0, e, inv);
+      y1[e] = y_of<DT>(xv[k][1], w1, e, inv);
     }
     if constexpr (NEOX) {
 #pragma unroll
@@ -624,12 +629,12 @@ __global__ void __launch_bounds__(1024) qk_norm_rope_kernel(RArgs a) {
     }
     if (h < a.nh) {
       __builtin_nontemporal_store(
-          (u32x4){pack_bf16x2(o0[0], o0[1]), pack_bf16x2(o0[2], o0[3]),
-                  pack_bf16x2(o0[4], o0[5]), pack_bf16x2(o0[6], o0[7])},
+          (u32x4){pack_in<DT>(o0[0], o0[1]), pack_in<DT>(o0[2], o0[3]),
+                  pack_in<DT>(o0[4], o0[5]), pack_in<DT>(o0[6], o0[7])},
           row + h * CH + c);
       __builtin_nontemporal_store(
-          (u32x4){pack_bf16x2(o1[0], o1[1]), pack_bf16x2(o1[2], o1[3]),
-                  pack_bf16x2(o1[4], o1[5]), pack_bf16x2(o1[6], o1[7])},
+          (u32x4){pack_in<DT>(o1[0], o1[1]), pack_in<DT>(o1[2], o1[3]),
+                  pack_in<DT>(o1[4], o1[5]), pack_in<DT>(o1[6], o1[7])},
           row + h * CH + c + L);
     }
   }

@@ -1,4 +1,5 @@
-// table_fused_bf16.hip -- instantiations of fused_kernel for bf16 activations, and the padded-output mode.
+// table_fused_bf16.hip -- instantiations of fused_kernel for bf16 activations, and the
+// padded-output mode for them.
 #include "rmsq_kernel_table.hpp"
 
 namespace rmsq {
@@ -48,9 +49,8 @@ const void* fused_kernel_bf16(int mode, bool res, int gs, int vpt, bool exact) {
   return pick_kernel_dt<0>(mode, res, gs, vpt, exact);
 }
 
-const void* pad_kernel(bool res, int vpt) {
-  return res ? pick_vpt<kModeBf16Pad, true, 0, false>(vpt)
-             : pick_vpt<kModeBf16Pad, false, 0, false>(vpt);
+const void* pad_kernel_bf16(bool res, int vpt) {
+  return res ? pick_vpt<kModePad, true, 0, false>(vpt) : pick_vpt<kModePad, false, 0, false>(vpt);
 }
 
 }  // namespace rmsq

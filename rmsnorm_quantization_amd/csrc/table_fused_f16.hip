@@ -1,4 +1,5 @@
-// table_fused_f16.hip -- instantiations of fused_kernel for IEEE binary16 activations.
+// table_fused_f16.hip -- instantiations of fused_kernel for IEEE binary16 activations, and the
+// padded-output mode for them.
 #include "rmsq_kernel_table.hpp"
 
 namespace rmsq {
@@ -46,6 +47,11 @@ const void* pick_kernel_dt(int mode, bool res, int gs, int vpt, bool exact) {
 
 const void* fused_kernel_f16(int mode, bool res, int gs, int vpt, bool exact) {
   return pick_kernel_dt<1>(mode, res, gs, vpt, exact);
+}
+
+const void* pad_kernel_f16(bool res, int vpt) {
+  return res ? pick_vpt<kModePad, true, 0, false, 1>(vpt)
+             : pick_vpt<kModePad, false, 0, false, 1>(vpt);
 }
 
 }  // namespace rmsq

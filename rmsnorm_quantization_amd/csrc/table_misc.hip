@@ -1,24 +1,8 @@
-// table_misc.hip -- instantiations of the QK-norm + RoPE kernels, and the converter kernel.
+// table_misc.hip -- instantiations of the QK-norm + RoPE kernels for bf16, and the converter
+// kernel.
 #include "rmsq_kernel_table.hpp"
 
 namespace rmsq {
-namespace {
-
-template <int D, bool NEOX>
-const void* pick_rope_hpl(int hpl) {
-  switch (hpl) {
-    case 1: return reinterpret_cast<const void*>(&qk_norm_rope_kernel<D, NEOX, 1>);
-    case 2: return reinterpret_cast<const void*>(&qk_norm_rope_kernel<D, NEOX, 2>);
-    case 3: return reinterpret_cast<const void*>(&qk_norm_rope_kernel<D, NEOX, 3>);
-    case 4: return reinterpret_cast<const void*>(&qk_norm_rope_kernel<D, NEOX, 4>);
-    case 5: return reinterpret_cast<const void*>(&qk_norm_rope_kernel<D, NEOX, 5>);
-    case 6: return reinterpret_cast<const void*>(&qk_norm_rope_kernel<D, NEOX, 6>);
-    default: return nullptr;
-  }
-}
-
-
-}  // namespace
 
 // The kernels' own converters over a flat f32 array, 8 elements per thread.
 __global__ void __launch_bounds__(256) convert_kernel(int fmt, const float* in, void* out,
@@ -39,14 +23,7 @@ __global__ void __launch_bounds__(256) convert_kernel(int fmt, const float* in, 
   }
 }
 
-const void* rope_kernel(int D, bool neox, int hpl) {
-  switch (D) {
-    case 64: return neox ? pick_rope_hpl<64, true>(hpl) : pick_rope_hpl<64, false>(hpl);
-    case 128: return neox ? pick_rope_hpl<128, true>(hpl) : pick_rope_hpl<128, false>(hpl);
-    case 256: return neox ? pick_rope_hpl<256, true>(hpl) : pick_rope_hpl<256, false>(hpl);
-    default: return nullptr;
-  }
-}
+const void* rope_kernel_bf16(int D, bool neox, int hpl) { return pick_rope<0>(D, neox, hpl); }
 
 const void* convert_kernel_ptr() { return reinterpret_cast<const void*>(&convert_kernel); }
 

@@ -56,7 +56,7 @@ def test_library_exports_every_declared_symbol(B):
 
 
 def test_abi_version_and_status_strings(B):
-    assert B.rmsq_abi_version() == 1
+    assert B.rmsq_abi_version() == B.RMSQ_ABI_VERSION == 2
     for st in (0, -1, -2, -3, -4, -5, -6):
         assert B.rmsq_status_string(st) and B.rmsq_status_string(st) != "unknown status"
     assert B.rmsq_status_string(-99) == "unknown status"
@@ -206,8 +206,8 @@ def test_act_query_launch(B):
 
 
 # ------------------------------------------------------------------ RMSNorm -> padded bf16
-def VP(B, x=X, r=R, w=W, eps=1e-6, out=Q, ro=RO, t=T, h=H, ld=H + 64):
-    return B.rmsq_rms_norm_pad_validate(x, r, w, eps, out, ro, t, h, ld)
+def VP(B, x=X, r=R, w=W, eps=1e-6, out=Q, ro=RO, t=T, h=H, ld=H + 64, f=0):
+    return B.rmsq_rms_norm_pad_validate(x, r, w, eps, out, ro, t, h, ld, f)
 
 
 def test_pad_query_launch(B):
@@ -246,7 +246,7 @@ def test_pad_bad_arguments(B, kw, status):
     assert B.lib().rmsq_rms_norm_pad(kw.get("x", X), kw.get("r", R), kw.get("w", W),
                                      kw.get("eps", 1e-6), kw.get("out", Q), kw.get("ro", RO),
                                      kw.get("t", T), kw.get("h", H), kw.get("ld", H + 64),
-                                     None) == code
+                                     0, None) == code
 
 
 # ------------------------------------------------------------------ QK-norm + RoPE
@@ -254,8 +254,9 @@ HQ, HKV, D, MP = 4, 2, 128, 64
 QKV, QW, KW, CS, POS = X, W, R, S, SC
 
 
-def VR(B, qkv=QKV, qw=QW, kw=KW, cs=CS, pos=POS, eps=1e-6, t=T, hq=HQ, hkv=HKV, d=D, mp=MP):
-    return B.rmsq_qk_norm_rope_validate(qkv, qw, kw, cs, pos, eps, t, hq, hkv, d, mp)
+def VR(B, qkv=QKV, qw=QW, kw=KW, cs=CS, pos=POS, eps=1e-6, t=T, hq=HQ, hkv=HKV, d=D, mp=MP,
+       f=0):
+    return B.rmsq_qk_norm_rope_validate(qkv, qw, kw, cs, pos, eps, t, hq, hkv, d, mp, f)
 
 
 def test_rope_valid_calls(B):
@@ -288,13 +289,14 @@ def test_rope_bad_arguments(B, kw, status):
     a = dict(qkv=QKV, qw=QW, kw=KW, cs=CS, pos=POS, eps=1e-6, t=T, hq=HQ, hkv=HKV, d=D, mp=MP)
     a.update(kw)
     assert B.lib().rmsq_qk_norm_rope(a["qkv"], a["qw"], a["kw"], a["cs"], a["pos"], a["eps"],
-                                     a["t"], a["hq"], a["hkv"], a["d"], a["mp"], 1, None) == code
+                                     a["t"], a["hq"], a["hkv"], a["d"], a["mp"], 1, 0,
+                                     None) == code
 
 
 def test_rope_launch_shape_is_checked(B):
     """Bad explicit shapes are rejected before any device call."""
     def ex(hpb, hpl):
-        return B.lib().rmsq_qk_norm_rope_ex(QKV, QW, KW, CS, POS, 1e-6, T, HQ, HKV, D, MP, 1,
+        return B.lib().rmsq_qk_norm_rope_ex(QKV, QW, KW, CS, POS, 1e-6, T, HQ, HKV, D, MP, 1, 0,
                                             hpb, hpl, None, None, None)
     L = D // 16
     for hpb, hpl in ((1024 // L + 1, 1), (6, 4), (-1, 1), (4, -1), (0, 2), (2, 0), (7, 7),
@@ -365,3 +367,18 @@ def test_input_f16_flag_is_accepted_by_the_quantizing_ops(B):
     assert VA(B, f=F) == B.RMSQ_OK
     assert VA(B, mode=B.RMSQ_FP8_GROUP, g=128, f=F | B.RMSQ_SCALE_E8M0) == B.RMSQ_OK
     assert VA(B, f=F | (1 << 9)) == B.RMSQ_EUNSUPPORTED
+
+
+def test_input_f16_flag_for_padding_and_rope(B):
+    """The padded-output and QK-norm + RoPE ops take RMSQ_INPUT_F16 (binary16 activations and
+    weights); any other flag bit is refused before any device call, by the entry points too."""
+    F = B.RMSQ_INPUT_F16
+    assert VP(B, f=F) == B.RMSQ_OK and VP(B, r=None, ro=None, f=F) == B.RMSQ_OK
+    assert VR(B, f=F) == B.RMSQ_OK
+    for bad in (1, 1 << 9, F | 2):
+        assert VP(B, f=bad) == B.RMSQ_EUNSUPPORTED
+        assert VR(B, f=bad) == B.RMSQ_EUNSUPPORTED
+        assert B.lib().rmsq_rms_norm_pad(X, R, W, 1e-6, Q, RO, T, H, H + 64, bad,
+                                         None) == B.RMSQ_EUNSUPPORTED
+        assert B.lib().rmsq_qk_norm_rope(QKV, QW, KW, CS, POS, 1e-6, T, HQ, HKV, D, MP, 1, bad,
+                                         None) == B.RMSQ_EUNSUPPORTED

@@ -25,6 +25,13 @@ def _bf16(a):
     return torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16)
 
 
+def _to16(flags):
+    """float array -> 16-bit patterns of the type flags selects (bf16, or binary16)."""
+    if flags & O.INPUT_F16:
+        return lambda a: np.asarray(a, np.float32).astype(np.float16).view(np.uint16)
+    return lambda a: synth.bits(_bf16(a))
+
+
 def _random_launch(rng, n_chunks):
     """A valid launch shape covering n_chunks 16-byte chunks per row, or None (the default)."""
     if rng.random() < 0.3:
@@ -146,22 +153,24 @@ def test_random_rms_norm_pad(seed):
     x = rng.standard_normal((T, H)) * float(rng.choice([1e-2, 1.0, 50.0]))
     r = rng.standard_normal((T, H)) if residual else None
     w = rng.uniform(-1.5, 1.5, H)
-    xb, wb = synth.bits(_bf16(x)), synth.bits(_bf16(w))
-    rb = None if r is None else synth.bits(_bf16(r))
     launch = _random_launch(rng, ld // 8)
+    flags = O.INPUT_F16 if rng.random() < 0.3 else 0  # IEEE binary16 instead of bf16
+    to16 = _to16(flags)
+    xb, wb = to16(x), to16(w)
+    rb = None if r is None else to16(r)
     shape = None if launch is None else launch.as_tuple()
-    print(f"[random] seed={seed} pad T={T} H={H} ld={ld} residual={residual} launch={shape}",
-          flush=True)
+    print(f"[random] seed={seed} pad T={T} H={H} ld={ld} residual={residual} launch={shape} "
+          f"flags={flags}", flush=True)
     out = GH.Guarded(T * ld * 2)
     rout = GH.Guarded(T * H * 2) if residual else None
     B.rmsq_rms_norm_pad(synth.from_bits(xb).to("cuda"),
                         None if rb is None else synth.from_bits(rb).to("cuda"),
                         synth.from_bits(wb).to("cuda"), 1e-5, out.data.view(torch.bfloat16),
                         None if rout is None else rout.data.view(torch.bfloat16),
-                        tokens=T, hidden=H, out_ld=ld, launch=launch)
+                        tokens=T, hidden=H, out_ld=ld, launch=launch, flags=flags)
     torch.cuda.synchronize()
     out.check("out")
-    ref, rref = O.rms_norm_pad(xb, rb, wb, 1e-5, ld)
+    ref, rref = O.rms_norm_pad(xb, rb, wb, 1e-5, ld, flags=flags)
     assert np.array_equal(out.data.view(torch.int16).cpu().numpy().view(np.uint16).reshape(T, ld),
                           ref)
     if residual:
@@ -180,9 +189,8 @@ def test_random_qk_norm_rope(seed):
     mp = int(rng.integers(1, 300))
     neox = bool(rng.random() < 0.5)
     qkv = rng.standard_normal((T, (hq + 2 * hkv) * D)) * float(rng.choice([0.1, 1.0, 20.0]))
-    qkvb = synth.bits(_bf16(qkv))
-    qwb = synth.bits(_bf16(rng.uniform(-1.5, 1.5, D)))
-    kwb = synth.bits(_bf16(rng.uniform(0.5, 1.5, D)))
+    qw = rng.uniform(-1.5, 1.5, D)
+    kw = rng.uniform(0.5, 1.5, D)
     pos = rng.integers(-3, mp + 3, T).astype(np.int64)
     cache = O.rope_cache(mp, D, float(rng.choice([1e4, 1e6])))
     hpl = hpb = 0
@@ -191,17 +199,20 @@ def test_random_qk_norm_rope(seed):
         hpl = int(rng.integers(1, 7))
         groups = int(rng.integers(1, 1024 // L + 1))
         hpb = hpl * groups
+    flags = O.INPUT_F16 if rng.random() < 0.3 else 0  # IEEE binary16 instead of bf16
+    to16 = _to16(flags)
+    qkvb, qwb, kwb = to16(qkv), to16(qw), to16(kw)
     print(f"[random] seed={seed} rope T={T} hq={hq} hkv={hkv} D={D} neox={neox} mp={mp} "
-          f"hpb={hpb} hpl={hpl}", flush=True)
+          f"hpb={hpb} hpl={hpl} flags={flags}", flush=True)
     g = GH.Guarded(qkvb.size * 2)
     dev = g.data.view(torch.int16)
     dev.copy_(torch.from_numpy(qkvb.reshape(-1).view(np.int16)))
     B.rmsq_qk_norm_rope(dev, synth.from_bits(qwb).to("cuda"), synth.from_bits(kwb).to("cuda"),
                         torch.from_numpy(cache).to("cuda"), torch.from_numpy(pos).to("cuda"),
                         1e-6, hq, hkv, D, neox, tokens=T, heads_per_block=hpb,
-                        heads_per_lane=hpl)
+                        heads_per_lane=hpl, flags=flags)
     torch.cuda.synchronize()
     g.check("qkv")
     got = dev.cpu().numpy().view(np.uint16).reshape(qkvb.shape)
-    ref = O.qk_norm_rope(qkvb, qwb, kwb, cache, pos, 1e-6, hq, hkv, D, neox)
+    ref = O.qk_norm_rope(qkvb, qwb, kwb, cache, pos, 1e-6, hq, hkv, D, neox, flags=flags)
     assert np.array_equal(got, ref)

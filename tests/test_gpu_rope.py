@@ -2,9 +2,9 @@
 
 The op (vLLM docs "Fusion torch.compile passes", section "QK Norm + RoPE") rewrites the q and k
 heads of the packed qkv tensor in place.  Both sides sum the squares of a head in binary64 (exact
-for bf16 inputs), round the same inverse RMS to f32, and form y = (h * inv) * w and the rotated
-pair (a c - b s, b c + a s) from separately rounded f32 products, so the bf16 result is asserted
-bit-exact: every element of every head, v heads and skipped tokens included (they must come back
+for bf16 and binary16 inputs), round the same inverse RMS to f32, and form y = (h * inv) * w and
+the rotated pair (a c - b s, b c + a s) from separately rounded f32 products, so the 16-bit
+result (bf16, or IEEE binary16 with RMSQ_INPUT_F16) is asserted bit-exact: every element of every head, v heads and skipped tokens included (they must come back
 unchanged).  A guard band around qkv catches stray writes.
 """
 import numpy as np
@@ -38,8 +38,9 @@ def cache_for(max_pos, D, base=1e6):
 
 
 def run_rope(qkv_bits, qw_bits, kw_bits, pos, hq, hkv, D, neox=True, eps=1e-6, max_pos=None,
-             hpb=0, hpl=0, base=1e6):
-    """Run the kernel on a guarded copy of qkv; returns (gpu bits, oracle bits)."""
+             hpb=0, hpl=0, base=1e6, flags=0):
+    """Run the kernel on a guarded copy of qkv; returns (gpu bits, oracle bits).  flags:
+    RMSQ_INPUT_F16 reads the bit patterns as IEEE binary16 on both sides."""
     T = qkv_bits.shape[0]
     cache, cache_d = cache_for(max_pos if max_pos is not None else 4096, D, base)
     g = G.Guarded(qkv_bits.size * 2)
@@ -48,12 +49,15 @@ def run_rope(qkv_bits, qw_bits, kw_bits, pos, hq, hkv, D, neox=True, eps=1e-6, m
     qw = torch.from_numpy(qw_bits.view(np.int16)).to("cuda")
     kw = torch.from_numpy(kw_bits.view(np.int16)).to("cuda")
     pos_d = torch.as_tensor(np.asarray(pos, np.int64)).to("cuda")
+    print(f"[rope] T={T} hq={hq} hkv={hkv} D={D} neox={neox} hpb={hpb} hpl={hpl} flags={flags}",
+          flush=True)
     B.rmsq_qk_norm_rope(dev, qw, kw, cache_d, pos_d, eps, hq, hkv, D, neox, tokens=T,
-                        heads_per_block=hpb, heads_per_lane=hpl)
+                        heads_per_block=hpb, heads_per_lane=hpl, flags=flags)
     torch.cuda.synchronize()
     g.check("qkv")
     got = dev.cpu().numpy().view(np.uint16).reshape(qkv_bits.shape)
-    ref = O.qk_norm_rope(qkv_bits, qw_bits, kw_bits, cache, pos, eps, hq, hkv, D, neox)
+    ref = O.qk_norm_rope(qkv_bits, qw_bits, kw_bits, cache, pos, eps, hq, hkv, D, neox,
+                         flags=flags)
     return got, ref
 
 
@@ -188,3 +192,85 @@ def test_fused_op_helper():
     assert out.data_ptr() == qkv.data_ptr()
     ref = O.qk_norm_rope(x, qw, kw, cache, pos, 1e-6, 32, 8, 128)
     assert_same(synth.bits(out), ref, "helper")
+
+
+# ------------------------------------------------------------------ IEEE binary16 (RMSQ_INPUT_F16)
+F16 = B.RMSQ_INPUT_F16
+
+
+def f16_inputs(T, hq, hkv, D, seed, scale=1.0, max_pos=4096):
+    rng = np.random.default_rng(seed)
+    f16 = (lambda a: np.asarray(a, np.float32).astype(np.float16).view(np.uint16))
+    qkv = f16(rng.standard_normal((T, (hq + 2 * hkv) * D)) * scale)
+    qw = f16(rng.uniform(-1.5, 1.5, D))
+    kw = f16(rng.uniform(0.5, 1.5, D))
+    pos = rng.integers(0, max_pos, T).astype(np.int64)
+    return qkv, qw, kw, pos
+
+
+@pytest.mark.parametrize("T", [1, 256, 4096])
+def test_binary16_workload_shape(T):
+    x, qw, kw, pos = f16_inputs(T, 32, 8, 128, T, max_pos=32768)
+    for neox in (True, False):
+        got, ref = run_rope(x, qw, kw, pos, 32, 8, 128, neox, max_pos=32768, flags=F16)
+        assert_same(got, ref, f"binary16 T={T} neox={neox}")
+        assert not np.array_equal(got, x)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("hq,hkv", [(1, 1), (12, 4), (64, 8)])
+def test_binary16_head_sizes_and_counts(D, hq, hkv):
+    x, qw, kw, pos = f16_inputs(37, hq, hkv, D, D + hq)
+    for neox in (True, False):
+        got, ref = run_rope(x, qw, kw, pos, hq, hkv, D, neox, flags=F16)
+        assert_same(got, ref, f"binary16 D={D} hq={hq} hkv={hkv} neox={neox}")
+
+
+@pytest.mark.parametrize("hpb,hpl", [(1, 1), (7, 1), (8, 2), (30, 3), (40, 5), (36, 6)])
+def test_binary16_launch_shapes(hpb, hpl):
+    x, qw, kw, pos = f16_inputs(19, 32, 8, 128, 3)
+    got, ref = run_rope(x, qw, kw, pos, 32, 8, 128, True, hpb=hpb, hpl=hpl, flags=F16)
+    assert_same(got, ref, f"binary16 hpb={hpb} hpl={hpl}")
+
+
+def test_binary16_extremes_and_type_selection():
+    """Zero heads, binary16 subnormal heads, values near 65504, out-of-range positions, and
+    outputs that overflow binary16 (weights of 10000 on a one-hot head); the same bits read as
+    bf16 give another result."""
+    T, hq, hkv, D = 7, 4, 2, 128
+    x, qw, kw, pos = f16_inputs(T, hq, hkv, D, 9)
+    h = x.view(np.float16).astype(np.float32).reshape(T, hq + 2 * hkv, D)
+    h[0] = 0.0
+    h[1] *= 1e-6
+    h[2] = np.clip(h[2] * 30000.0, -65504, 65504)
+    h[3] = 0.0
+    h[3, :, 9] = 2.0
+    x2 = h.reshape(T, -1).astype(np.float16).view(np.uint16)
+    big = np.full(D, np.float16(10000.0)).view(np.uint16)
+    pos = pos.copy()
+    pos[5], pos[6] = -1, 4096
+    for neox in (True, False):
+        got, ref = run_rope(x2, big, qw, pos, hq, hkv, D, neox, flags=F16)
+        assert_same(got, ref, f"binary16 extremes neox={neox}")
+        assert np.all(got[0, :(hq + hkv) * D] & 0x7FFF == 0)
+        # y = sqrt(D) * 10000 at the spike; its larger rotated part exceeds 65504
+        assert np.any((got[3, :hq * D] & 0x7FFF) == 0x7C00)
+        assert np.array_equal(got[5:], x2[5:])
+    as_bf16, _ = run_rope(x, qw, kw, pos, hq, hkv, D)
+    as_f16, _ = run_rope(x, qw, kw, pos, hq, hkv, D, flags=F16)
+    assert not np.array_equal(as_bf16, as_f16)
+
+
+def test_binary16_helper_follows_the_dtype():
+    x, qw, kw, pos = f16_inputs(16, 32, 8, 128, 10)
+    cache, cache_d = cache_for(4096, 128)
+    t16 = (lambda b: torch.from_numpy(b.view(np.float16)).to("cuda"))
+    qkv = t16(x)
+    out = B.qk_norm_rope(qkv, torch.as_tensor(pos).to("cuda"), t16(qw), t16(kw), cache_d, 1e-6,
+                         32, 8)
+    torch.cuda.synchronize()
+    ref = O.qk_norm_rope(x, qw, kw, cache, pos, 1e-6, 32, 8, 128, flags=O.INPUT_F16)
+    assert_same(out.cpu().view(torch.int16).numpy().view(np.uint16), ref, "binary16 helper")
+    with pytest.raises(TypeError):
+        B.qk_norm_rope(qkv, torch.as_tensor(pos).to("cuda"), t16(qw).to(torch.bfloat16), t16(kw),
+                       cache_d, 1e-6, 32, 8)

@@ -80,6 +80,10 @@ def lib():
         L.orc_fused.argtypes = [p, p, p, C.c_float, C.c_int, C.c_float, p, p, p,
                                 i64, i64, C.c_int, C.c_uint, i64, p]
         L.orc_fused.restype = C.c_int
+        L.orc_fp4_global_scale.argtypes = [C.c_float]
+        L.orc_fp4_global_scale.restype = C.c_float
+        L.orc_fused_fp4_dynamic.argtypes = [p, p, p, C.c_float, p, p, p, p, i64, i64, C.c_uint, p]
+        L.orc_fused_fp4_dynamic.restype = C.c_int
         L.rmsq_ref_fused.argtypes = [p, p, p, C.c_float, C.c_int, p, p, p, p, i64, i64,
                                      C.c_int, C.c_uint, i64]
         L.rmsq_ref_fused.restype = C.c_int
@@ -229,6 +233,31 @@ def fused(x, residual, weight, eps, mode, scale_in=0.0, group_size=0, flags=0, s
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (rc={rc})")
     return {"q": q, "scales": scales, "residual_out": rout, "pre": pre}
+
+
+def fp4_global_scale(amax):
+    """(448 * 6) / amax in f32, FLT_MAX where that is not finite."""
+    return np.float32(lib().orc_fp4_global_scale(float(amax)))
+
+
+def fused_fp4_dynamic(x, residual, weight, eps, flags=0, want_pre=False):
+    """FP4 block-16 with the global scale taken from the batch: dict with q, scales,
+    residual_out, global_scale (np.float32) and optionally pre."""
+    x = _c(x, np.uint16)
+    T, H = x.shape
+    r = None if residual is None else _c(residual, np.uint16)
+    w = _c(weight, np.uint16)
+    q = np.zeros((T, H // 2), np.uint8)
+    scales = np.zeros((T, H // 16), np.uint8)
+    rout = None if r is None else np.zeros_like(r)
+    gs = np.zeros(1, np.float32)
+    pre = np.zeros((T, H), np.float32) if want_pre else None
+    rc = lib().orc_fused_fp4_dynamic(_ptr(x), _ptr(r), _ptr(w), float(eps), _ptr(q),
+                                     _ptr(scales), _ptr(rout), _ptr(gs), T, H, int(flags),
+                                     _ptr(pre))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (rc={rc})")
+    return {"q": q, "scales": scales, "residual_out": rout, "global_scale": gs[0], "pre": pre}
 
 
 def quantize_row(y, mode, scale_in=0.0, group_size=0, flags=0):

@@ -18,6 +18,7 @@
  */
 #include "rmsq_oracle.h"
 
+#include <float.h>
 #include <math.h>
 #include <stddef.h>
 #include <stdlib.h>
@@ -399,7 +400,48 @@ int orc_fused(const uint16_t* x, const uint16_t* residual, const uint16_t* weigh
   return 0;
 }
 
-/* ------------------------------------------------------------------ RMSNorm -> padded bf16 */
+/* ------------------------------------------------------------------ FP4, batch global scale */
+float orc_fp4_global_scale(float amax) {
+  /* the largest e4m3 magnitude times the largest e2m1 magnitude, over the batch's absmax */
+  const float gs = (448.0f * 6.0f) / amax;
+  return (gs <= FLT_MAX) ? gs : FLT_MAX; /* amax == 0 (gs = inf) or tinier than 2688 / FLT_MAX */
+}
+
+int orc_fused_fp4_dynamic(const uint16_t* x, const uint16_t* residual, const uint16_t* weight,
+                          float eps, uint8_t* out_q, uint8_t* out_scales, uint16_t* residual_out,
+                          float* global_scale_out, int64_t T, int64_t H, unsigned flags,
+                          float* pre_q) {
+  if (T < 0 || H <= 0 || (H % 16) || !x || !weight || !out_q || !out_scales || !global_scale_out)
+    return -1;
+  if ((residual == NULL) != (residual_out == NULL)) return -1;
+  if (!(eps >= 0.0f) || isinf(eps)) return -1;
+  if (flags & ~(unsigned)ORC_INPUT_F16) return -1;
+  const int f16 = (flags & ORC_INPUT_F16) != 0;
+  uint16_t* h = (uint16_t*)malloc((size_t)H * sizeof(uint16_t));
+  float* y = (float*)malloc((size_t)H * sizeof(float));
+  if (!h || !y) {
+    free(h);
+    free(y);
+    return -1;
+  }
+  /* pass 1: the largest |y| of the whole batch */
+  float amax = 0.0f;
+  for (int64_t t = 0; t < T; ++t) {
+    if (residual) orc_residual_add_dt(x + t * H, residual + t * H, h, H, f16);
+    else memcpy(h, x + t * H, (size_t)H * sizeof(uint16_t));
+    orc_normalize_dt(h, weight, orc_inv_rms_dt(h, H, eps, f16), y, H, f16);
+    for (int64_t i = 0; i < H; ++i) amax = fmaxf(amax, fabsf(y[i]));
+  }
+  free(h);
+  free(y);
+  const float gs = orc_fp4_global_scale(amax);
+  *global_scale_out = gs;
+  /* pass 2: the block-16 quantization with that global scale */
+  return orc_fused(x, residual, weight, eps, ORC_FP4_BLOCK16, gs, out_q, out_scales, residual_out,
+                   T, H, 16, flags, 0, pre_q);
+}
+
+/* ------------------------------------------------------------------ host twin of rmsq_fused */
 int rmsq_ref_fused(const void* x, const void* residual, const void* weight, float eps, int mode,
                    const float* scale_in, void* out_q, void* out_scales, void* residual_out,
                    int64_t tokens, int64_t hidden, int group_size, unsigned flags,

@@ -106,6 +106,20 @@ int orc_fused(const uint16_t* x, const uint16_t* residual, const uint16_t* weigh
               int64_t T, int64_t H, int group_size, unsigned flags, int64_t scale_ld,
               float* pre_q);
 
+/* ---- FP4 block-16 with the global encode scale taken from the batch itself (the PR #51925
+ * summary's test derives an NVFP4 global scale as 448 * 6 over a tensor's absmax; here the
+ * tensor is the normalized batch y of every row). ----
+ * orc_fp4_global_scale: (448 * 6) / amax in f32, or FLT_MAX when that exceeds FLT_MAX (amax
+ * zero or below 2688 / FLT_MAX).
+ * orc_fused_fp4_dynamic: amax = max |y| over all T rows (y exactly as in orc_fused), gs from
+ * it, written to *global_scale_out, then orc_fused(ORC_FP4_BLOCK16, scale_in = gs).  flags: 0 or
+ * ORC_INPUT_F16.  Returns 0, or -1 on an invalid argument. */
+float orc_fp4_global_scale(float amax);
+int orc_fused_fp4_dynamic(const uint16_t* x, const uint16_t* residual, const uint16_t* weight,
+                          float eps, uint8_t* out_q, uint8_t* out_scales, uint16_t* residual_out,
+                          float* global_scale_out, int64_t T, int64_t H, unsigned flags,
+                          float* pre_q);
+
 /* The whole operation with the argument list of the GPU library's fused entry point, on host
  * buffers and without a stream: the oracle's counterpart of that call, so that a caller can run
  * both sides of a parity check with one set of arguments.  scale_in points at one f32 (FP8

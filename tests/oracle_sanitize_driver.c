@@ -277,9 +277,45 @@ static void silu_all(void) {
   }
 }
 
+static void fp4_dynamic_all(void) {
+  const int64_t Hs[] = {16, 48, 2048};
+  for (int hi = 0; hi < 3; ++hi)
+    for (int variant = 0; variant < 4; ++variant) {
+      const int res = variant & 1, f16 = variant >> 1;
+      const int64_t T = 7, H = Hs[hi];
+      uint16_t* x = in16_array(T * H, 2.0f, f16);
+      uint16_t* r = res ? in16_array(T * H, 2.0f, f16) : NULL;
+      uint16_t* w = in16_array(H, 1.0f, f16);
+      uint8_t* q = (uint8_t*)xalloc((size_t)(T * H / 2));
+      uint8_t* sf = (uint8_t*)xalloc((size_t)(T * H / 16));
+      uint16_t* ro = res ? (uint16_t*)xalloc((size_t)(T * H) * 2) : NULL;
+      float* pre = (float*)xalloc((size_t)(T * H) * 4);
+      float gs = 0.0f;
+      EXPECT(orc_fused_fp4_dynamic(x, r, w, 1e-6f, q, sf, ro, &gs, T, H,
+                                   f16 ? ORC_INPUT_F16 : 0, pre) == 0,
+             "orc_fused_fp4_dynamic H %lld", (long long)H);
+      EXPECT(gs > 0.0f, "global scale not positive");
+      free(x);
+      free(r);
+      free(w);
+      free(q);
+      free(sf);
+      free(ro);
+      free(pre);
+    }
+  uint16_t h = 0;
+  uint8_t b = 0;
+  float g = 0.0f;
+  EXPECT(orc_fused_fp4_dynamic(&h, NULL, &h, 1e-6f, &b, &b, NULL, &g, 1, 8, 0, NULL) == -1,
+         "H not a multiple of 16 accepted");
+  EXPECT(orc_fused_fp4_dynamic(&h, NULL, &h, 1e-6f, &b, &b, NULL, NULL, 1, 16, 0, NULL) == -1,
+         "missing global scale output accepted");
+}
+
 int main(void) {
   formats();
   fused_all();
+  fp4_dynamic_all();
   pad_all();
   rope_all();
   silu_all();

@@ -16,8 +16,9 @@ data.  Prints ONE JSON line:
                  copy's counters) when the committed counters match the current kernel source
   cpu_baseline   the CPU oracle on a bounded sample of the same workload, one core
 
-Other workloads (--workload w0..w7; w5 is SiLU+Mul -> quant with --quant
-static|token|group|fp4, w6 add+RMSNorm -> padded bf16, w7 QK-norm + RoPE) and forced launch
+Other workloads (--workload w0..w8; w5 is SiLU+Mul -> quant with --quant
+static|token|group|fp4, w6 add+RMSNorm -> padded bf16, w7 QK-norm + RoPE, w8 add+RMSNorm -> FP4
+with the global scale taken from the batch, three launches timed as one step) and forced launch
 shapes (--launch tpr,vpt,rpb[,options]; for w7 --launch heads_per_block,heads_per_lane) are
 for exploration;
 only one GPU is supported (--gpus above 1 exits with a message).
@@ -37,7 +38,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 FOOTPRINT_BYTES = 1536 << 20   # rotating buffer sets: at least 6x the 256 MB MALL
 MODE_NAMES = {0: "fp8_static", 1: "fp8_per_token", 2: "fp8_per_group", 3: "fp4_block16",
-              4: "bf16_padded", 5: "bf16_qk_norm_rope"}
+              4: "bf16_padded", 5: "bf16_qk_norm_rope", 6: "fp4_block16_batch_scale"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -64,6 +65,8 @@ def workload_spec(args):
         mode = 5  # not a quantization scheme: normalized and rotated heads, bf16 in place
     elif wl.kind == "pad":
         mode = 4  # not a quantization scheme: the normalized row as padded bf16
+    elif wl.kind == "fp4dyn":
+        mode = 6  # FP4 block-16 whose global scale the library derives from the batch
     elif wl.kind == "act":
         mode = {"static": B.RMSQ_FP8_STATIC, "token": B.RMSQ_FP8_TOKEN,
                 "group": B.RMSQ_FP8_GROUP, "fp4": B.RMSQ_FP4_BLOCK16}[args.quant]
@@ -111,6 +114,107 @@ def rope_bytes(T, hq, hkv, D):
     launch, each token's position and its cos/sin cache row (D f32) once."""
     qk = 2 * T * (hq + hkv) * D
     return qk + 2 * 2 * D + 8 * T + 4 * D * T, qk
+
+
+def fp4dyn_bytes(T, H, residual=True):
+    """FP4 with the global scale from the batch, as three launches: the row pass reads x (and
+    the residual) and the weight and writes the new residual and T row maxima; the reduction
+    reads the maxima and writes gs; the block pass reads the normalized input again (the new
+    residual, or x), the weight and gs and writes codes and block scales.  The second read of
+    the input (2H per token) is inherent: gs depends on every row."""
+    rd = 2 * T * H + (2 * T * H if residual else 0) + 2 * H + 4 * T + 2 * T * H + 2 * H + 4
+    wr = (2 * T * H if residual else 0) + 4 * T + 4 + T * H // 2 + T * (H // 16)
+    return rd, wr
+
+
+def fp4dyn_leg(args, wl, T, H):
+    """GPU timing of rmsq_fused_fp4_dynamic (three launches per step), structured like gpu_leg;
+    the per-step duration runs from the first launch's dispatch to the last one's end."""
+    import torch
+
+    from rmsnorm_quantization_amd import binding as B
+    from rmsnorm_quantization_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x, r, w = synth.make_inputs(wl.index, T, H)
+    rd, wr = fp4dyn_bytes(T, H, True)
+    nsets = max(2, math.ceil(FOOTPRINT_BYTES / (rd + wr)))
+    xd, rdv, wd = x.to(dev), r.to(dev), w.to(dev).contiguous()
+    sets = []
+    for _ in range(nsets):
+        s = {"x": xd.clone(), "r": rdv.clone(), "ro": torch.empty_like(xd),
+             "q": torch.empty((T, H // 2), dtype=torch.uint8, device=dev),
+             "s": torch.empty((T, H // 16), dtype=torch.uint8, device=dev),
+             "g": torch.empty((1,), dtype=torch.float32, device=dev)}
+        if args.inplace:
+            s["ro"] = s["r"]
+        sets.append(s)
+    if args.launch:
+        vals = [int(v) for v in args.launch.split(",")]
+        launch = B.rmsq_launch(*(vals + [0] * (4 - len(vals))))
+    else:
+        launch = B.rmsq_query_launch(B.RMSQ_FP4_BLOCK16, T, H, 16)[0]
+    import ctypes
+
+    lib = B.lib()
+    lref = ctypes.byref(launch)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    status = []
+    argsets = [(s_["x"].data_ptr(), s_["r"].data_ptr(), wd.data_ptr(), float(wl.eps),
+                s_["q"].data_ptr(), s_["s"].data_ptr(), s_["ro"].data_ptr(), s_["g"].data_ptr(),
+                T, H, 0) for s_ in sets]
+
+    def launch_on(a, e0, e1, hs):
+        st = lib.rmsq_fused_fp4_dynamic_ex(*a, lref, e0, e1, hs)
+        if st:
+            status.append(st)
+
+    for i in range(args.warmup):
+        launch_on(argsets[i % nsets], None, None, sh)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        launch_on(argsets[i % nsets], None, None, sh)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    ms_per_step_graph = None
+    if args.graph:
+        g_ = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_, stream=torch.cuda.Stream()):
+            hs = torch.cuda.current_stream().cuda_stream
+            for i in range(args.steps):
+                launch_on(argsets[i % nsets], None, None, hs)
+        g_.replay()
+        torch.cuda.synchronize()
+        t0.record(stream)
+        g_.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms_per_step_graph = t0.elapsed_time(t1) / args.steps
+        del g_
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a_, b_ in evs:
+        a_.record(stream)
+        b_.record(stream)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        launch_on(argsets[i % nsets], evs[i][0].cuda_event, evs[i][1].cuda_event, sh)
+    torch.cuda.synchronize()
+    if status:
+        raise RuntimeError(f"rmsq_fused_fp4_dynamic failed: {B.rmsq_status_string(status[0])}")
+    per = sorted(a.elapsed_time(b) for a, b in evs)
+    copy_gbs = copy_ceiling(dev, stream)
+    return {"ms_per_step": ms_per_step, "ms_per_step_graph": ms_per_step_graph,
+            "avg_launch_ms": sum(per) / len(per), "median_launch_ms": per[len(per) // 2],
+            "p10_launch_ms": per[len(per) // 10], "p90_launch_ms": per[(9 * len(per)) // 10],
+            "bytes": rd + wr, "read": rd, "write": wr, "sets": nsets,
+            "launch": launch.as_tuple(), "copy_gbs": copy_gbs,
+            "device": torch.cuda.get_device_name(dev)}
 
 
 def rope_cache(max_pos, D, base):
@@ -568,6 +672,16 @@ def cpu_leg(wl, T, H, mode, G, flags, budget_s=12.0):
         def nbytes(rows):
             return sum(algorithmic_bytes(mode, rows, H, G4, flags, False, "act"))
         unit = "rows"
+    elif wl.kind == "fp4dyn":
+        x, r, w = synth.make_inputs(wl.index, T, H)
+        xb, rb, wb = synth.bits(x), synth.bits(r), synth.bits(w)
+
+        def run_rows(lo, hi):  # each span takes its own batch scale: the same work per row
+            O.fused_fp4_dynamic(xb[lo:hi], rb[lo:hi], wb, wl.eps)
+
+        def nbytes(rows):
+            return sum(fp4dyn_bytes(rows, H))
+        unit = "rows"
     elif wl.kind == "pad":
         ld = -(-H // wl.pad_multiple) * wl.pad_multiple
         x, r, w = synth.make_inputs(wl.index, T, H)
@@ -736,9 +850,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="w1", choices=["w0", "w1", "w2", "w3", "w4", "w5", "w6", "w7"],
+    ap.add_argument("--workload", default="w1",
+                    choices=["w0", "w1", "w2", "w3", "w4", "w5", "w6", "w7", "w8"],
                     help="w0-w4: (residual add ->) RMSNorm -> quant workloads; w5: SiLU+Mul -> "
-                         "quant; w6: add+RMSNorm -> padded bf16; w7: QK-norm + RoPE (default w1: "
+                         "quant; w6: add+RMSNorm -> padded bf16; w7: QK-norm + RoPE; w8: add+RMSNorm "
+                         "-> FP4 with the global scale from the batch (default w1: "
                          "add+RMSNorm -> FP8 "
                          "static, 4096 x 4096)")
     ap.add_argument("--quant", default="static", choices=["static", "token", "group", "fp4"],
@@ -794,7 +910,12 @@ def main():
 
     wl, T, H, mode, G, flags = workload_spec(args)
     rope = wl.kind == "rope"
-    g = rope_leg(args, wl, T, H) if rope else gpu_leg(args, wl, T, H, mode, G, flags)
+    if rope:
+        g = rope_leg(args, wl, T, H)
+    elif wl.kind == "fp4dyn":
+        g = fp4dyn_leg(args, wl, T, H)
+    else:
+        g = gpu_leg(args, wl, T, H, mode, G, flags)
     eager_gbs = g["bytes"] / (g["ms_per_step"] * 1e-3) / 1e9
     step_ms = g["ms_per_step_graph"] if g["ms_per_step_graph"] else g["ms_per_step"]
     gbs = g["bytes"] / (step_ms * 1e-3) / 1e9
@@ -829,6 +950,8 @@ def main():
             "tokens": T, "hidden": H, "mode": MODE_NAMES[mode], "group_size": G,
             "flags": flags, "residual": wl.residual, "eps": wl.eps,
             "io": "bf16 in; " + {3: "e2m1 + e4m3 block scales out",
+                                 6: "e2m1 + e4m3 block scales + f32 global scale out (three "
+                                    "launches; the input is read twice)",
                                  4: f"bf16 out, rows padded to a multiple of {wl.pad_multiple}",
                                  5: "q and k heads rewritten in place (bf16), f32 cos/sin cache"
                                  }.get(mode, "e4m3fn out"),

@@ -173,6 +173,51 @@ RMSQ_API int rmsq_fused_timed(const void* x, const void* residual, const void* w
                               void* start_event, void* stop_event, void* stream);
 
 /*
+ * rmsq_fused_fp4_dynamic -- (residual add ->) RMSNorm -> FP4 block-16 with the global encode scale
+ * taken from the batch itself (prhub summary of vLLM PR #51925: NVFP4 output with block scales and
+ * a global scale; its test derives a global scale as 448 * 6 over a tensor's absmax -- here the
+ * tensor is the normalized batch):
+ *
+ *   amax = max |y| over all T rows (y exactly as in rmsq_fused)
+ *   gs   = (448 * 6) / amax in f32, or FLT_MAX where that is not finite (an all-zero batch)
+ *   then exactly RMSQ_FP4_BLOCK16 with that gs.
+ *
+ *  x, residual, weight, eps, residual_out, tokens, hidden
+ *               as for rmsq_fused; hidden % 16 == 0.
+ *  out_q, out_scales
+ *               as for rmsq_fused in RMSQ_FP4_BLOCK16.  out_q also holds the T row maxima (f32,
+ *               its first 4T bytes) between the launches; its final contents are the codes.
+ *  global_scale device f32, 4-byte aligned, written with gs (the dequantization needs it: value =
+ *               e2m1 * decode(sf) / gs).  Must not overlap any other argument.
+ *  flags        0 (bf16) or RMSQ_INPUT_F16; any other bit is RMSQ_EUNSUPPORTED.
+ * The global scale depends on every row, so the work is three launches on `stream`: the residual
+ * add and normalization, writing the new residual and each row's largest |y|; a one-workgroup
+ * reduction to gs; the block quantization, which normalizes the new residual (or x) again.  That
+ * second read of the normalized input (2H bytes per token) is the price of the batch scale.
+ * Returns RMSQ_OK or a negative status.
+ */
+RMSQ_API int rmsq_fused_fp4_dynamic(const void* x, const void* residual, const void* weight,
+                                    float eps, void* out_q, void* out_scales, void* residual_out,
+                                    float* global_scale, int64_t tokens, int64_t hidden,
+                                    unsigned flags, void* stream);
+
+/* rmsq_fused_fp4_dynamic with an explicit launch shape for the two row passes (NULL: the default,
+ * as rmsq_fused) and optional dispatch-stamped events: start_event is stamped by the first launch,
+ * stop_event by the last (NULL: none). */
+RMSQ_API int rmsq_fused_fp4_dynamic_ex(const void* x, const void* residual, const void* weight,
+                                       float eps, void* out_q, void* out_scales,
+                                       void* residual_out, float* global_scale, int64_t tokens,
+                                       int64_t hidden, unsigned flags, const rmsq_launch* launch,
+                                       void* start_event, void* stop_event, void* stream);
+
+/* Host-only argument check of rmsq_fused_fp4_dynamic (no HIP call, no dereference). */
+RMSQ_API int rmsq_fused_fp4_dynamic_validate(const void* x, const void* residual,
+                                             const void* weight, float eps, const void* out_q,
+                                             const void* out_scales, const void* residual_out,
+                                             const float* global_scale, int64_t tokens,
+                                             int64_t hidden, unsigned flags);
+
+/*
  * rmsq_rms_norm_pad -- (residual add ->) RMSNorm -> 16-bit output in a padded row layout, in one
  * launch (vLLM docs "Fusion torch.compile passes", section "RMSNorm + padding
  * (fuse_act_padding)": the residual add and RMSNorm fused with padding the hidden dimension --

@@ -6,7 +6,8 @@ the binding raises -- there is no fallback path.
 
 Function names match the C ABI (rmsq_fused, rmsq_fused_with_launch, rmsq_fused_timed,
 rmsq_silu_mul_quant, rmsq_silu_mul_quant_ex, rmsq_silu_mul_quant_validate,
-rmsq_silu_mul_query_launch, rmsq_rms_norm_pad, rmsq_rms_norm_pad_ex, rmsq_rms_norm_pad_validate,
+rmsq_silu_mul_query_launch, rmsq_fused_fp4_dynamic, rmsq_fused_fp4_dynamic_ex,
+rmsq_fused_fp4_dynamic_validate, rmsq_rms_norm_pad, rmsq_rms_norm_pad_ex, rmsq_rms_norm_pad_validate,
 rmsq_rms_norm_pad_query_launch,
 rmsq_qk_norm_rope, rmsq_qk_norm_rope_ex, rmsq_qk_norm_rope_validate,
 rmsq_qk_norm_rope_query_launch, rmsq_validate,
@@ -73,6 +74,13 @@ def lib():
         L.rmsq_fused_timed.restype = i32
         L.rmsq_validate.argtypes = fused_args
         L.rmsq_validate.restype = i32
+        dyn_args = [p, p, p, f32, p, p, p, p, i64, i64, u32]
+        L.rmsq_fused_fp4_dynamic.argtypes = dyn_args + [p]
+        L.rmsq_fused_fp4_dynamic.restype = i32
+        L.rmsq_fused_fp4_dynamic_ex.argtypes = dyn_args + [C.POINTER(rmsq_launch), p, p, p]
+        L.rmsq_fused_fp4_dynamic_ex.restype = i32
+        L.rmsq_fused_fp4_dynamic_validate.argtypes = dyn_args
+        L.rmsq_fused_fp4_dynamic_validate.restype = i32
         pad_args = [p, p, p, f32, p, p, i64, i64, i64, u32]
         L.rmsq_rms_norm_pad.argtypes = pad_args + [p]
         L.rmsq_rms_norm_pad.restype = i32
@@ -198,6 +206,34 @@ def rmsq_fused_timed(x, residual, weight, eps, mode, scale_in, out_q, out_scales
     if check:
         _check(st, "rmsq_fused_timed")
     return st
+
+
+def rmsq_fused_fp4_dynamic(x, residual, weight, eps, out_q, out_scales, residual_out,
+                           global_scale, tokens=None, hidden=None, flags=0, stream=None,
+                           launch=None, start_event=None, stop_event=None, check=True) -> int:
+    """(Residual add ->) RMSNorm -> FP4 block-16 with the global scale taken from the batch
+    (written to global_scale, one f32).  With a launch shape or events it goes through
+    rmsq_fused_fp4_dynamic_ex."""
+    T = x.shape[0] if tokens is None else tokens
+    H = x.shape[-1] if hidden is None else hidden
+    args = (_ptr(x), _ptr(residual), _ptr(weight), float(eps), _ptr(out_q), _ptr(out_scales),
+            _ptr(residual_out), _ptr(global_scale), int(T), int(H), int(flags))
+    if launch is None and start_event is None and stop_event is None:
+        st = lib().rmsq_fused_fp4_dynamic(*args, _stream(stream))
+    else:
+        st = lib().rmsq_fused_fp4_dynamic_ex(*args, None if launch is None else C.byref(launch),
+                                             start_event, stop_event, _stream(stream))
+    if check:
+        _check(st, "rmsq_fused_fp4_dynamic")
+    return st
+
+
+def rmsq_fused_fp4_dynamic_validate(x, residual, weight, eps, out_q, out_scales, residual_out,
+                                    global_scale, tokens, hidden, flags=0) -> int:
+    """Host-only argument check; pointers are plain integers (or None)."""
+    return lib().rmsq_fused_fp4_dynamic_validate(x, residual, weight, float(eps), out_q,
+                                                 out_scales, residual_out, global_scale,
+                                                 int(tokens), int(hidden), int(flags))
 
 
 def rmsq_rms_norm_pad(x, residual, weight, eps, out, residual_out, tokens=None, hidden=None,
@@ -418,6 +454,20 @@ def fused_add_rms_norm_fp4_quant(x, residual, weight, global_scale, eps, inplace
     rmsq_fused(x, residual, weight, eps, RMSQ_FP4_BLOCK16, _scalar(global_scale, x.device), q,
                sf, rout, group_size=16, flags=_act_flag(x, weight, residual))
     return q, sf, rout
+
+
+def fused_add_rms_norm_fp4_quant_dynamic(x, residual, weight, eps, inplace=True):
+    """(packed e2m1 uint8 [T,H/2], e4m3 block scales uint8 [T,H/16], global scale f32 [1],
+    residual_out or None): FP4 with the global encode scale gs = 448 * 6 / max|y| of the batch
+    (dequant value = e2m1 * decode(sf) / gs).  residual may be None (plain RMSNorm)."""
+    T, H = x.shape
+    q = torch.empty((T, H // 2), dtype=torch.uint8, device=x.device)
+    sf = torch.empty((T, H // 16), dtype=torch.uint8, device=x.device)
+    gs = torch.empty((1,), dtype=torch.float32, device=x.device)
+    rout = None if residual is None else (residual if inplace else torch.empty_like(residual))
+    rmsq_fused_fp4_dynamic(x, residual, weight, eps, q, sf, rout, gs,
+                           flags=_act_flag(x, weight, residual))
+    return q, sf, gs, rout
 
 
 def silu_and_mul_quant(x, mode, scale=None, group_size=0, col_major=False, e8m0=False,

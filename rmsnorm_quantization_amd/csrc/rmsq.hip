@@ -246,6 +246,84 @@ int fused_impl(const void* x, const void* res, const void* w, float eps, int mod
                        stop_event);
 }
 
+// ---- FP4 block-16 with the global scale taken from the batch --------------------------------
+// Everything the static FP4 call checks, with global_scale in the place of scale_in; as an output
+// it must not overlap x, the residual or the weight either.
+int validate_fp4_dynamic(const void* x, const void* res, const void* w, float eps, const void* q,
+                         const void* scales, const void* res_out, const float* global_scale,
+                         int64_t T, int64_t H, unsigned flags) {
+  if ((flags & ~(unsigned)RMSQ_INPUT_F16) != 0) return RMSQ_EUNSUPPORTED;
+  int st = validate(x, res, w, eps, RMSQ_FP4_BLOCK16, global_scale, q, scales, res_out, T, H, 16,
+                    flags, 0);
+  if (st != RMSQ_OK || T == 0) return st;
+  const size_t act = (size_t)T * (size_t)H * 2;
+  const Span g = span(global_scale, 4);
+  if (overlap(g, span(x, act)) || overlap(g, span(w, (size_t)H * 2)) ||
+      (res && overlap(g, span(res, act))))
+    return RMSQ_EALIAS;
+  return RMSQ_OK;
+}
+
+// Three launches, one launch shape for both row passes (so that both reduce each row's squares
+// in the same order and see the same y): (1) residual add + RMSNorm, each row's largest |y| staged
+// as f32 in the first 4T bytes of out_q; (2) one workgroup: the batch's largest |y| -> gs;
+// (3) the FP4 block-16 kernel without a residual on the normalized input (the new residual, or
+// x), reading gs from device memory.
+int fp4_dynamic_impl(const void* x, const void* res, const void* w, float eps, void* q,
+                     void* scales, void* res_out, float* global_scale, int64_t T, int64_t H,
+                     unsigned flags, const rmsq_launch* launch, void* start_event,
+                     void* stop_event, void* stream) {
+  int st = validate_fp4_dynamic(x, res, w, eps, q, scales, res_out, global_scale, T, H, flags);
+  if (st != RMSQ_OK) return st;
+  const rmsq_launch l = launch ? *launch : default_launch(H);
+  if (!valid_launch(l, H)) return RMSQ_EINVAL;
+  if (T == 0) return RMSQ_OK;
+  st = check_device();
+  if (st != RMSQ_OK) return st;
+  const bool exact = exact_fit(l, T, H), f16 = (flags & RMSQ_INPUT_F16) != 0;
+  const int vpt = l.chunks_per_thread;
+  const void* pass1 = f16 ? amax_kernel_f16(res != nullptr, vpt, exact)
+                          : amax_kernel_bf16(res != nullptr, vpt, exact);
+  const void* pass3 = f16 ? fused_kernel_f16(RMSQ_FP4_BLOCK16, false, 16, vpt, exact)
+                          : fused_kernel_bf16(RMSQ_FP4_BLOCK16, false, 16, vpt, exact);
+  if (!pass1 || !pass3) return RMSQ_EINVAL;
+  const int64_t nblk = (T + l.rows_per_block - 1) / l.rows_per_block;
+  const int threads = l.threads_per_row * l.rows_per_block;
+  KArgs a;
+  a.x = static_cast<const uint16_t*>(x);
+  a.res = static_cast<const uint16_t*>(res);
+  a.w = static_cast<const uint16_t*>(w);
+  a.res_out = static_cast<uint16_t*>(res_out);
+  a.q = nullptr;
+  a.scales = q;  // the row maxima, [T] f32 at the start of out_q
+  a.scale_in = nullptr;
+  a.T = T;
+  a.H = H;
+  a.ld = 0;
+  a.eps = eps;
+  a.flags = 0;
+  a.tpr = l.threads_per_row;
+  a.rpb = l.rows_per_block;
+  a.nblk = (uint32_t)nblk;
+  a.xcd_ranges = (l.options & RMSQ_LAUNCH_XCD_RANGES) ? 1 : 0;
+  st = launch_kernel(pass1, nblk, threads, &a, stream, start_event, nullptr);
+  if (st != RMSQ_OK) return st;
+  GArgs g;
+  g.row_amax = static_cast<const float*>(q);
+  g.gs = global_scale;
+  g.T = T;
+  st = launch_kernel(fp4_global_scale_kernel_ptr(), 1, 1024, &g, stream, nullptr, nullptr);
+  if (st != RMSQ_OK) return st;
+  KArgs b = a;
+  b.x = res ? static_cast<const uint16_t*>(res_out) : static_cast<const uint16_t*>(x);
+  b.res = nullptr;
+  b.res_out = nullptr;
+  b.q = static_cast<uint8_t*>(q);
+  b.scales = scales;
+  b.scale_in = global_scale;
+  return launch_kernel(pass3, nblk, threads, &b, stream, nullptr, stop_event);
+}
+
 // ---- residual add + RMSNorm -> padded 16-bit output ------------------------------------------
 int validate_pad(const void* x, const void* res, const void* w, float eps, const void* out,
                  const void* res_out, int64_t T, int64_t H, int64_t out_ld, unsigned flags) {
@@ -572,6 +650,30 @@ int rmsq_validate(const void* x, const void* residual, const void* weight, float
                   unsigned flags, int64_t scale_ld) {
   return validate(x, residual, weight, eps, mode, scale_in, out_q, out_scales, residual_out,
                   tokens, hidden, group_size, flags, scale_ld);
+}
+
+int rmsq_fused_fp4_dynamic(const void* x, const void* residual, const void* weight, float eps,
+                           void* out_q, void* out_scales, void* residual_out, float* global_scale,
+                           int64_t tokens, int64_t hidden, unsigned flags, void* stream) {
+  return fp4_dynamic_impl(x, residual, weight, eps, out_q, out_scales, residual_out, global_scale,
+                          tokens, hidden, flags, nullptr, nullptr, nullptr, stream);
+}
+
+int rmsq_fused_fp4_dynamic_ex(const void* x, const void* residual, const void* weight, float eps,
+                              void* out_q, void* out_scales, void* residual_out,
+                              float* global_scale, int64_t tokens, int64_t hidden, unsigned flags,
+                              const rmsq_launch* launch, void* start_event, void* stop_event,
+                              void* stream) {
+  return fp4_dynamic_impl(x, residual, weight, eps, out_q, out_scales, residual_out, global_scale,
+                          tokens, hidden, flags, launch, start_event, stop_event, stream);
+}
+
+int rmsq_fused_fp4_dynamic_validate(const void* x, const void* residual, const void* weight,
+                                    float eps, const void* out_q, const void* out_scales,
+                                    const void* residual_out, const float* global_scale,
+                                    int64_t tokens, int64_t hidden, unsigned flags) {
+  return validate_fp4_dynamic(x, residual, weight, eps, out_q, out_scales, residual_out,
+                              global_scale, tokens, hidden, flags);
 }
 
 int rmsq_rms_norm_pad(const void* x, const void* residual, const void* weight, float eps,

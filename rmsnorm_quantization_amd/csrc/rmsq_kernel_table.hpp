@@ -11,6 +11,9 @@ namespace rmsq {
 // fused (residual add ->) RMSNorm -> quantization, bf16 or IEEE binary16 activations
 const void* fused_kernel_bf16(int mode, bool res, int gs, int vpt, bool exact);
 const void* fused_kernel_f16(int mode, bool res, int gs, int vpt, bool exact);
+// (residual add ->) RMSNorm -> each row's largest |y| (first pass of FP4 with a batch scale)
+const void* amax_kernel_bf16(bool res, int vpt, bool exact);
+const void* amax_kernel_f16(bool res, int vpt, bool exact);
 // (residual add ->) RMSNorm -> padded 16-bit output (launches always masked)
 const void* pad_kernel_bf16(bool res, int vpt);
 const void* pad_kernel_f16(bool res, int vpt);
@@ -22,6 +25,8 @@ const void* rope_kernel_bf16(int D, bool neox, int hpl);
 const void* rope_kernel_f16(int D, bool neox, int hpl);
 // the diagnostic converters
 const void* convert_kernel_ptr();
+// the reduction of row maxima to the FP4 global scale
+const void* fp4_global_scale_kernel_ptr();
 
 // The QK-norm + RoPE instantiation for (D, NEOX, heads per lane), one 16-bit type per table unit.
 template <int DT, int D, bool NEOX>

@@ -32,6 +32,9 @@ constexpr int kMaxWavesPerBlock = 16;
 // with a padded row stride (ld), the padding columns zero.  Not a quantization scheme, so not in
 // rmsq_mode.
 constexpr int kModePad = 4;
+// Internal mode of fused_kernel: no codes, only the row's largest |y| (f32) to scales[row] -- the
+// first pass of FP4 with the global scale taken from the batch.
+constexpr int kModeRowAmax = 5;
 
 struct KArgs {
   const uint16_t* x;
@@ -163,6 +166,20 @@ __device__ __forceinline__ void quantize_store(const YF& Y, const bool (&ok)[VPT
         }
       }
     }
+  } else if constexpr (MODE == kModeRowAmax) {
+    float mx = 0.0f;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(Y(k, e)));
+    mx = wave_max(mx);
+    if (o.wpr > 1) {  // uniform over the block
+      if ((o.tid & 63) == 0) s_mx[o.tid >> 6] = mx;
+      __syncthreads();
+      mx = 0.0f;
+      for (int i = 0; i < o.wpr; ++i) mx = fmaxf(mx, s_mx[o.rib * o.wpr + i]);
+    }
+    if (o.lr == 0 && o.row_ok) static_cast<float*>(o.scales)[o.row] = mx;
   } else if constexpr (MODE == kModePad) {
     // 16-bit row of n values at a stride of ld elements; chunks n/8 .. ld/8-1 are zero padding.
     // The launch covers ld/8 chunks per row (ok[] marks the chunks below n).
@@ -315,6 +332,18 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
   quantize_store<MODE, VPT, GS, DT>(
       [&](int k, int e) { return y_of<DT>(hv[k], wv[k], e, inv); }, ok, o, scale_val, s_mx);
 }
+
+// ------------------------------------------------------------------ FP4 global scale of a batch
+// The middle launch of FP4 with the global scale taken from the batch (PR #51925 summary: NVFP4
+// with block scales and a global scale; its test derives a global scale as 448 * 6 over a
+// tensor's absmax): one workgroup reduces the T row maxima to the batch's largest |y| and writes
+// gs = (448 * 6) / amax (IEEE division), or FLT_MAX where that is not finite (amax == 0).  The
+// kernel (fp4_global_scale_kernel) is defined in table_misc.hip.
+struct GArgs {
+  const float* row_amax;  // [T], non-negative
+  float* gs;              // [1]
+  int64_t T;
+};
 
 // ------------------------------------------------------------------ SiLU+Mul -> quantization
 // vLLM docs "Fusion torch.compile passes", section "SiLU+Mul + quantization (fuse_act_quant)":

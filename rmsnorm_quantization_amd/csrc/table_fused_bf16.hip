@@ -53,4 +53,12 @@ const void* pad_kernel_bf16(bool res, int vpt) {
   return res ? pick_vpt<kModePad, true, 0, false>(vpt) : pick_vpt<kModePad, false, 0, false>(vpt);
 }
 
+const void* amax_kernel_bf16(bool res, int vpt, bool exact) {
+  if (res)
+    return exact ? pick_vpt<kModeRowAmax, true, 0, true, 0>(vpt)
+                 : pick_vpt<kModeRowAmax, true, 0, false, 0>(vpt);
+  return exact ? pick_vpt<kModeRowAmax, false, 0, true, 0>(vpt)
+               : pick_vpt<kModeRowAmax, false, 0, false, 0>(vpt);
+}
+
 }  // namespace rmsq

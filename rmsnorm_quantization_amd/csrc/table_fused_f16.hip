@@ -54,4 +54,12 @@ const void* pad_kernel_f16(bool res, int vpt) {
              : pick_vpt<kModePad, false, 0, false, 1>(vpt);
 }
 
+const void* amax_kernel_f16(bool res, int vpt, bool exact) {
+  if (res)
+    return exact ? pick_vpt<kModeRowAmax, true, 0, true, 1>(vpt)
+                 : pick_vpt<kModeRowAmax, true, 0, false, 1>(vpt);
+  return exact ? pick_vpt<kModeRowAmax, false, 0, true, 1>(vpt)
+               : pick_vpt<kModeRowAmax, false, 0, false, 1>(vpt);
+}
+
 }  // namespace rmsq

@@ -1,5 +1,5 @@
-// table_misc.hip -- instantiations of the QK-norm + RoPE kernels for bf16, and the converter
-// kernel.
+// table_misc.hip -- instantiations of the QK-norm + RoPE kernels for bf16, the converter kernel
+// and the FP4 global-scale reduction.
 #include "rmsq_kernel_table.hpp"
 
 namespace rmsq {
@@ -26,5 +26,25 @@ __global__ void __launch_bounds__(256) convert_kernel(int fmt, const float* in, 
 const void* rope_kernel_bf16(int D, bool neox, int hpl) { return pick_rope<0>(D, neox, hpl); }
 
 const void* convert_kernel_ptr() { return reinterpret_cast<const void*>(&convert_kernel); }
+
+// One workgroup of 1024 threads: the batch's largest row maximum, then its FP4 global scale.
+__global__ void __launch_bounds__(1024) fp4_global_scale_kernel(GArgs a) {
+  __shared__ float s_mx[kMaxWavesPerBlock];
+  float m = 0.0f;
+  for (int64_t i = threadIdx.x; i < a.T; i += blockDim.x) m = fmaxf(m, a.row_amax[i]);
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) s_mx[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float amax = 0.0f;
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) amax = fmaxf(amax, s_mx[i]);
+    const float g = (kFp8Max * kFp4Max) / amax;
+    a.gs[0] = (g <= __FLT_MAX__) ? g : __FLT_MAX__;
+  }
+}
+
+const void* fp4_global_scale_kernel_ptr() {
+  return reinterpret_cast<const void*>(&fp4_global_scale_kernel);
+}
 
 }  // namespace rmsq

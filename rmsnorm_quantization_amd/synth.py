@@ -57,7 +57,8 @@ class Workload:
     warmup_shape: Optional[Tuple[int, int]] = None  # batch the static scale is derived from
     group_sizes: Tuple[int, ...] = field(default_factory=tuple)
     kind: str = "norm"   # "norm": (residual add ->) RMSNorm -> quant; "act": SiLU+Mul -> quant;
-    #                      "pad": (residual add ->) RMSNorm -> padded bf16; "rope": QK-norm + RoPE
+    #                      "pad": (residual add ->) RMSNorm -> padded bf16; "rope": QK-norm + RoPE;
+    #                      "fp4dyn": add + RMSNorm -> FP4 with the global scale from the batch
     pad_multiple: int = 0
     heads: Tuple[int, int] = (0, 0)   # (q heads, kv heads) of a "rope" workload; hidden = head size
     max_position: int = 0
@@ -79,6 +80,9 @@ WORKLOADS = {
                 pad_multiple=256),
     7: Workload(7, "qk_norm_rope", (1, 256, 4096), (128,), 1e-6, False, kind="rope",
                 heads=(32, 8), max_position=32768, rope_base=1e6),
+    # the FP4 shapes of workload 4, with the global scale computed from the batch itself
+    8: Workload(8, "add_rmsnorm_fp4_batch_scale", (1, 32, 256, 4096), (2048,), 1e-6, True,
+                kind="fp4dyn"),
 }
 
 X, RESIDUAL, WEIGHT, OUTLIERS, WARM_X, WARM_R, K_WEIGHT, POSITIONS = 1, 2, 3, 4, 5, 6, 7, 8

@@ -4,6 +4,7 @@ and the host-side argument checks return the documented status for each kind of 
 Nothing here touches a device: rmsq_validate makes no HIP call, and rmsq_fused is only called
 with arguments rmsq_validate has already rejected (it then returns the same status before
 reaching the device)."""
+import ctypes as C
 import os
 import re
 import subprocess
@@ -382,3 +383,51 @@ def test_input_f16_flag_for_padding_and_rope(B):
                                          None) == B.RMSQ_EUNSUPPORTED
         assert B.lib().rmsq_qk_norm_rope(QKV, QW, KW, CS, POS, 1e-6, T, HQ, HKV, D, MP, 1, bad,
                                          None) == B.RMSQ_EUNSUPPORTED
+
+
+# ------------------------------------------------------------------ FP4 with a batch global scale
+GSO = SC  # the global scale output
+
+
+def VD(B, x=X, r=R, w=W, eps=1e-6, q=Q, s=S, ro=RO, gs=GSO, t=T, h=H, f=0):
+    return B.rmsq_fused_fp4_dynamic_validate(x, r, w, eps, q, s, ro, gs, t, h, f)
+
+
+def test_fp4_dynamic_valid_calls(B):
+    assert VD(B) == B.RMSQ_OK
+    assert VD(B, r=None, ro=None) == B.RMSQ_OK
+    assert VD(B, ro=R) == B.RMSQ_OK                          # new residual in place
+    assert VD(B, f=B.RMSQ_INPUT_F16) == B.RMSQ_OK
+    assert VD(B, t=0, x=None, q=None, s=None, gs=None) == B.RMSQ_OK
+    assert VD(B, gs=X + T * H * 2) == B.RMSQ_OK              # just past x
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(h=264), "EINVAL"), (dict(h=8), "EINVAL"), (dict(t=-1), "EINVAL"),
+    (dict(eps=0.0), "EINVAL"), (dict(gs=None), "EINVAL"), (dict(s=None), "EINVAL"),
+    (dict(q=None), "EINVAL"), (dict(ro=None), "EINVAL"), (dict(x=None), "EINVAL"),
+    (dict(f=1), "EUNSUPPORTED"), (dict(f=4), "EUNSUPPORTED"), (dict(f=1 << 9), "EUNSUPPORTED"),
+    (dict(gs=GSO + 2), "EALIGN"), (dict(q=Q + 2), "EALIGN"), (dict(x=X + 8), "EALIGN"),
+    (dict(gs=X + 64), "EALIAS"), (dict(gs=W), "EALIAS"), (dict(gs=R + 4), "EALIAS"),
+    (dict(gs=Q + 8), "EALIAS"), (dict(gs=S), "EALIAS"), (dict(gs=RO + 4), "EALIAS"),
+    (dict(q=X), "EALIAS"), (dict(s=R), "EALIAS"), (dict(ro=W), "EALIAS"),
+])
+def test_fp4_dynamic_bad_arguments(B, kw, status):
+    code = getattr(B, "RMSQ_" + status)
+    assert VD(B, **kw) == code
+    a = dict(x=X, r=R, w=W, eps=1e-6, q=Q, s=S, ro=RO, gs=GSO, t=T, h=H, f=0)
+    a.update(kw)
+    assert B.lib().rmsq_fused_fp4_dynamic(a["x"], a["r"], a["w"], a["eps"], a["q"], a["s"],
+                                          a["ro"], a["gs"], a["t"], a["h"], a["f"],
+                                          None) == code
+    shape = B.rmsq_launch(64, 1, 1, 0)  # a valid shape: the status is the argument check's
+    assert B.lib().rmsq_fused_fp4_dynamic_ex(a["x"], a["r"], a["w"], a["eps"], a["q"], a["s"],
+                                             a["ro"], a["gs"], a["t"], a["h"], a["f"],
+                                             C.byref(shape), None, None, None) == code
+
+
+def test_fp4_dynamic_launch_shape_is_checked(B):
+    short = B.rmsq_launch(64, 1, 1, 0)  # 512 elements: too few for H = 1024
+    assert B.lib().rmsq_fused_fp4_dynamic_ex(X, R, W, 1e-6, Q, S, RO, GSO, T, 1024, 0,
+                                             C.byref(short), None, None,
+                                             None) == B.RMSQ_EINVAL

@@ -1,4 +1,4 @@
-"""The fused launch inside a captured HIP graph: every replay equals the eager launch.
+"""Every entry point inside a captured HIP graph: every replay equals the eager launch.
 
 Replays are interleaved with eager launches of the same op on other buffers, output wipes
 (torch fill kernels, not memsets) and device synchronizations."""
@@ -156,3 +156,22 @@ def test_graph_qk_norm_rope():
         B.rmsq_qk_norm_rope(o[0], qw, kw, cache, pos, 1e-6, hq, hkv, D, True, stream=stream)
 
     _replay_check(launch, outs, "qk_norm_rope", inplace_source=qkv0)
+
+
+def test_graph_fp4_dynamic():
+    """Three launches (row pass, global-scale reduction, block quantization) in one graph."""
+    T, H = 40, 2048
+    g = torch.Generator().manual_seed(81)
+    x = torch.randn((T, H), generator=g).to(torch.bfloat16).cuda()
+    r = torch.randn((T, H), generator=g).to(torch.bfloat16).cuda()
+    w = (torch.rand((H,), generator=g) + 0.5).to(torch.bfloat16).cuda()
+
+    def outs():
+        return [torch.empty((T, H // 2), dtype=torch.uint8, device="cuda"),
+                torch.empty((T, H // 16), dtype=torch.uint8, device="cuda"),
+                torch.empty_like(r), torch.empty((1,), dtype=torch.float32, device="cuda")]
+
+    def launch(o, stream=None):
+        B.rmsq_fused_fp4_dynamic(x, r, w, 1e-6, o[0], o[1], o[2], o[3], stream=stream)
+
+    _replay_check(launch, outs, "fp4_dynamic")

@@ -216,3 +216,43 @@ def test_random_qk_norm_rope(seed):
     got = dev.cpu().numpy().view(np.uint16).reshape(qkvb.shape)
     ref = O.qk_norm_rope(qkvb, qwb, kwb, cache, pos, 1e-6, hq, hkv, D, neox, flags=flags)
     assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_fp4_dynamic(seed):
+    rng = np.random.default_rng(9400 + seed)
+    H = 16 * int(rng.integers(1, 512))
+    T = int(rng.integers(1, 60))
+    residual = bool(rng.random() < 0.7)
+    sigma = float(rng.choice([1e-3, 1.0, 30.0]))
+    x = rng.standard_normal((T, H)) * sigma
+    r = rng.standard_normal((T, H)) * sigma if residual else None
+    w = rng.uniform(-1.5, 1.5, H)
+    launch = _random_launch(rng, H // 8)
+    flags = O.INPUT_F16 if rng.random() < 0.3 else 0
+    to16 = _to16(flags)
+    xb, wb = to16(x), to16(w)
+    rb = None if r is None else to16(r)
+    shape = None if launch is None else launch.as_tuple()
+    print(f"[random] seed={seed} fp4dyn T={T} H={H} residual={residual} launch={shape} "
+          f"flags={flags}", flush=True)
+    gq, gsf, gg = GH.Guarded(T * H // 2), GH.Guarded(T * H // 16), GH.Guarded(4)
+    grs = GH.Guarded(T * H * 2) if residual else None
+    dev = (lambda b: None if b is None else synth.from_bits(b).to("cuda"))
+    B.rmsq_fused_fp4_dynamic(dev(xb), dev(rb), dev(wb), 1e-6, gq.data, gsf.data,
+                             None if grs is None else grs.data.view(torch.bfloat16),
+                             gg.data.view(torch.float32), tokens=T, hidden=H, flags=flags,
+                             launch=launch)
+    torch.cuda.synchronize()
+    for g, what in ((gq, "out_q"), (gsf, "out_scales"), (gg, "global_scale")):
+        g.check(what)
+    ref = O.fused_fp4_dynamic(xb, rb, wb, 1e-6, flags=flags, want_pre=True)
+    gs = gg.data.view(torch.float32).cpu().numpy()[0]
+    assert gs.view(np.uint32) == ref["global_scale"].view(np.uint32)
+    gpu = {"q": gq.data.view(T, H // 2).cpu().numpy(),
+           "scales": gsf.data.view(T, H // 16).cpu().numpy(),
+           "residual_out": None if grs is None else
+           grs.data.view(torch.int16).cpu().numpy().view(np.uint16).reshape(T, H)}
+    if grs is not None:
+        grs.check("residual_out")
+    compare(O.FP4_BLOCK16, gpu, ref, T=T, H=H, group_size=16, scale_in=float(gs))

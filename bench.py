@@ -779,17 +779,29 @@ def summarize(ktrace_db, fetch_db, write_db, key, title, commands, out_md, util=
     top = _db_rows(ktrace_db, "select name, total_calls, total_duration, average, percentage "
                               "from top_kernels")
     mine = [r for r in top if "rmsq::" in r[0]]
-    main_k = max(mine, key=lambda r: r[1])  # the benched instantiation (most calls)
+    # the benched instantiation has the most calls; a step of several launches (the FP4 path
+    # with a batch scale) has several kernels with that count, and its figures are their sums
+    ncalls = max(r[1] for r in mine)
+    step_k = [r for r in mine if r[1] == ncalls]
+    main_k = step_k[0] if len(step_k) == 1 else (
+        " + ".join(r[0] for r in step_k), ncalls, sum(r[2] for r in step_k),
+        sum(r[3] for r in step_k), sum(r[4] for r in step_k))
     durs = [r[0] for r in _db_rows(ktrace_db, "select duration from kernels where name = '%s'"
-                                   % main_k[0].replace("'", "''"))]
+                                   % step_k[0][0].replace("'", "''"))]
+    if len(step_k) > 1:  # per step: the sum of its kernels' durations, in dispatch order
+        per = [[d for (d,) in _db_rows(ktrace_db, "select duration from kernels where name = "
+                                       "'%s' order by start" % r[0].replace("'", "''"))]
+               for r in step_k]
+        durs = [sum(ds) for ds in zip(*per)]
 
     def counter(db, name):
         rows = _db_rows(db, "select kernel_name, value from counters_collection "
                             "where counter_name = '%s'" % name)
-        mine = [v for k, v in rows if k == main_k[0]]
+        med = [statistics.median([v for k, v in rows if k == r[0]]) for r in step_k]
+        n = len([v for k, v in rows if k == step_k[0][0]])
         copies = sorted((v for k, v in rows if k.startswith("__amd_rocclr_copyBuffer")),
                         reverse=True)[:10]
-        return statistics.median(mine), statistics.median(copies), len(mine)
+        return sum(med), statistics.median(copies), n
 
     f_k, f_copy, nf = counter(fetch_db, "FETCH_SIZE")
     w_k, w_copy, nw = counter(write_db, "WRITE_SIZE")
@@ -820,7 +832,9 @@ def summarize(ktrace_db, fetch_db, write_db, key, title, commands, out_md, util=
               "| kernel | calls | total us | average us | % |", "|---|---|---|---|---|"]
     for r in top[:8]:
         lines.append(f"| `{r[0][:90]}` | {r[1]} | {r[2]:.1f} | {r[3]:.3f} | {r[4]:.1f} |")
-    lines += ["", f"Benched kernel `{main_k[0]}`: {len(durs)} dispatches, average "
+    what = ("Benched kernel" if len(step_k) == 1 else
+            f"Benched step ({len(step_k)} kernels per step, figures summed over them)")
+    lines += ["", f"{what} `{main_k[0]}`: {len(durs)} dispatches, average "
               f"{main_k[3]:.3f} us, median {statistics.median(durs) / 1e3:.3f} us, "
               f"min {min(durs) / 1e3:.3f} us, max {max(durs) / 1e3:.3f} us.", "",
               "## HBM traffic (rocprofv3 --pmc, one counter per run)", "",
@@ -885,8 +899,8 @@ def main():
 
         wl, T, H, mode, G, flags = workload_spec(args)
         key = f"{args.workload}_T{T}_H{H}_{MODE_NAMES[mode]}_G{G}_f{flags}"
-        family = {"act": "silu_mul_kernel", "rope": "qk_norm_rope_kernel"}.get(wl.kind,
-                                                                             "fused_kernel")
+        family = {"act": "silu_mul_kernel", "rope": "qk_norm_rope_kernel",
+                  "fp4dyn": "fused_kernel_x3"}.get(wl.kind, "fused_kernel")
         md = args.summary_md or os.path.join(ROOT, "profiles", f"{family}_{key}.md")
         if wl.kind == "rope":
             title = (f"{family}, {wl.name}: {T} tokens x {wl.heads[0]} q + {wl.heads[1]} k heads "

@@ -153,6 +153,8 @@ def test_degenerate_rows(mode, G, scale):
     x[3] = 1e-30                   # tiny row
     r[3] = 0.0
     x[4, ::2] = -x[4, ::2]         # mixed signs
+    x[5] = x[5] * 1e-39            # bf16 subnormals (below 2^-126): eps dominates the root
+    r[5] = 0.0
     _run_and_compare(mode, x, r, w, eps=1e-6, scale_in=scale, G=G)
 
 

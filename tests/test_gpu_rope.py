@@ -274,3 +274,17 @@ def test_binary16_helper_follows_the_dtype():
     with pytest.raises(TypeError):
         B.qk_norm_rope(qkv, torch.as_tensor(pos).to("cuda"), t16(qw).to(torch.bfloat16), t16(kw),
                        cache_d, 1e-6, 32, 8)
+
+
+@pytest.mark.parametrize("hq,hkv,D", [(4064, 8, 256), (8176, 8, 128), (16352, 8, 64)])
+def test_widest_rows(hq, hkv, D):
+    """qkv rows at the documented maximum of 2^20 elements (one of them exactly), default and
+    explicit launch shapes, bf16 and binary16."""
+    x, qw, kw, pos = wl_inputs(3, hq, hkv, D)
+    got, ref = run_rope(x, qw, kw, pos, hq, hkv, D)
+    assert_same(got, ref, f"widest D={D}")
+    got, ref = run_rope(x, qw, kw, pos, hq, hkv, D, False, hpb=12, hpl=3)
+    assert_same(got, ref, f"widest D={D} hpb=12 hpl=3")
+    x16, qw16, kw16, pos16 = f16_inputs(2, hq, hkv, D, D)
+    got, ref = run_rope(x16, qw16, kw16, pos16, hq, hkv, D, flags=F16)
+    assert_same(got, ref, f"widest binary16 D={D}")

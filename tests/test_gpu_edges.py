@@ -231,3 +231,24 @@ def test_timed_launch_matches_and_stamps_events():
         outs.append((q.cpu(), s.cpu(), ro.cpu()))
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("mode,G", [(O.FP8_TOKEN, 0), (O.FP8_GROUP, 128), (O.FP8_GROUP, 64)])
+def test_scale_whose_reciprocal_overflows(mode, G):
+    """Rows so small that absmax/448 is a subnormal below 1/FLT_MAX: 1/s is +infinity, so every
+    non-zero element saturates (bit-exact on both sides, as are the scales), while an exact zero
+    becomes 0 * inf = NaN -- the oracle's literal encoding gives the NaN code, the kernel's clamp
+    a saturated code.  Those zeros are outside the contract; everything else is compared."""
+    g = torch.Generator().manual_seed(21)
+    x = (torch.randn((4, 1024), generator=g)).to(torch.bfloat16) * 3e-40
+    w = (torch.rand((1024,), generator=g) + 0.5).to(torch.bfloat16)
+    xb, wb = synth.bits(x), synth.bits(w)
+    print(f"[edge] reciprocal overflow mode={mode} G={G}", flush=True)
+    gpu = GH.run(mode, GH.to_dev(x), None, GH.to_dev(w), 1e-6, group_size=G)
+    ref = O.fused(xb, None, wb, 1e-6, mode, group_size=G)
+    assert np.array_equal(gpu["scales"], ref["scales"])
+    y = O.rms_y(xb, None, wb, 1e-6)
+    nan = (ref["q"] & 0x7F) == 0x7F  # the oracle's NaN codes: zeros of rows/groups with 1/s = inf
+    assert nan.any() and np.all(y[nan] == 0)
+    assert np.all((gpu["q"][nan] & 0x7F) == 0x7E)
+    assert np.array_equal(gpu["q"][~nan], ref["q"][~nan])

@@ -103,8 +103,8 @@ enum {
  *               RMSQ_SCALE_E8M0_U8.  FP4_BLOCK16: [T,H/16] e4m3 bytes, row-major.  f32 scales
  *               need 4-byte alignment.  Column-major padding (columns T..ld-1) is not written.
  *  residual_out [T,H] same type as x, 16-byte aligned; receives h = x + residual rounded to
- *               that type (nearest even; binary16 overflows to infinity).  Non-NULL iff residual is;
- *               may equal residual exactly (in-place update, as vLLM's fused_add_rms_norm
+ *               that type (nearest even; binary16 overflows to infinity).  Non-NULL iff
+ *               residual is; may equal residual exactly (in-place update, as vLLM's fused_add_rms_norm
  *               does), must not otherwise overlap anything.
  *  tokens       T >= 0; T == 0 is a successful no-op (pointers are then not checked).
  *  hidden       H: 8 <= H <= RMSQ_MAX_HIDDEN, H % 8 == 0, and H % group_size == 0.
@@ -116,10 +116,10 @@ enum {
  *  stream       hipStream_t to enqueue on.
  * Returns RMSQ_OK or a negative status (see rmsq_status_string).
  */
-RMSQ_API int rmsq_fused(const void* x, const void* residual, const void* weight, float eps, int mode,
-               const float* scale_in, void* out_q, void* out_scales, void* residual_out,
-               int64_t tokens, int64_t hidden, int group_size, unsigned flags, int64_t scale_ld,
-               void* stream);
+RMSQ_API int rmsq_fused(const void* x, const void* residual, const void* weight, float eps,
+                        int mode, const float* scale_in, void* out_q, void* out_scales,
+                        void* residual_out, int64_t tokens, int64_t hidden, int group_size,
+                        unsigned flags, int64_t scale_ld, void* stream);
 
 /* Host-only argument check of rmsq_fused: returns exactly the status rmsq_fused would return
  * for these arguments before it touches the device (RMSQ_OK when they are valid).  Makes no HIP
@@ -156,11 +156,11 @@ typedef struct rmsq_launch {
 
 /* rmsq_fused with an explicit launch shape (for tuning sweeps); launch == NULL behaves as
  * rmsq_fused.  Results are identical for every valid shape. */
-RMSQ_API int rmsq_fused_with_launch(const void* x, const void* residual, const void* weight, float eps,
-                           int mode, const float* scale_in, void* out_q, void* out_scales,
-                           void* residual_out, int64_t tokens, int64_t hidden, int group_size,
-                           unsigned flags, int64_t scale_ld, const rmsq_launch* launch,
-                           void* stream);
+RMSQ_API int rmsq_fused_with_launch(const void* x, const void* residual, const void* weight,
+                                    float eps, int mode, const float* scale_in, void* out_q,
+                                    void* out_scales, void* residual_out, int64_t tokens,
+                                    int64_t hidden, int group_size, unsigned flags,
+                                    int64_t scale_ld, const rmsq_launch* launch, void* stream);
 
 /* rmsq_fused_with_launch for measurement: the kernel is dispatched with hipExtLaunchKernel so
  * that start_event and stop_event (hipEvent_t created by the caller, either may be NULL) are

@@ -142,7 +142,8 @@ __device__ __forceinline__ float group_max(float v) {
 template <int CTRL>
 __device__ __forceinline__ double dpp(double v) {
   const uint64_t u = (uint64_t)__double_as_longlong(v);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+  const uint32_t lo =
+      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
   const uint32_t hi =
       (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));

@@ -60,7 +60,8 @@ const void* pick_act_mode(int mode, int gs, int vpt) {
 template <int DT>
 const void* act_kernel_dt(bool tiled, bool exact, int mode, int gs, int vpt) {
   if (tiled)
-    return exact ? pick_tile_mode<true, DT>(mode, gs, vpt) : pick_tile_mode<false, DT>(mode, gs, vpt);
+    return exact ? pick_tile_mode<true, DT>(mode, gs, vpt)
+                 : pick_tile_mode<false, DT>(mode, gs, vpt);
   return exact ? pick_act_mode<true, DT>(mode, gs, vpt) : pick_act_mode<false, DT>(mode, gs, vpt);
 }
 

@@ -82,7 +82,7 @@ def _fused_case(seed):
                 launch=launch, xb=xb, rb=rb, wb=wb)
 
 
-@pytest.mark.parametrize("seed", range(40))
+@pytest.mark.parametrize("seed", range(120))
 def test_random_fused(seed):
     c = _fused_case(9000 + seed)
     shape = None if c["launch"] is None else c["launch"].as_tuple()
@@ -110,7 +110,7 @@ def test_random_fused(seed):
             scale_in=c["scale"], raw_group_scales=raw)
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(48))
 def test_random_silu_mul_quant(seed):
     rng = np.random.default_rng(9100 + seed)
     mode = int(rng.integers(0, 4))
@@ -143,7 +143,7 @@ def test_random_silu_mul_quant(seed):
             raw_group_scales=raw)
 
 
-@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("seed", range(30))
 def test_random_rms_norm_pad(seed):
     rng = np.random.default_rng(9200 + seed)
     H = 8 * int(rng.integers(1, 1200))
@@ -179,7 +179,7 @@ def test_random_rms_norm_pad(seed):
             rout.data.view(torch.int16).cpu().numpy().view(np.uint16).reshape(T, H), rref)
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(36))
 def test_random_qk_norm_rope(seed):
     rng = np.random.default_rng(9300 + seed)
     D = int(rng.choice([64, 128, 256]))
@@ -218,7 +218,7 @@ def test_random_qk_norm_rope(seed):
     assert np.array_equal(got, ref)
 
 
-@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("seed", range(30))
 def test_random_fp4_dynamic(seed):
     rng = np.random.default_rng(9400 + seed)
     H = 16 * int(rng.integers(1, 512))

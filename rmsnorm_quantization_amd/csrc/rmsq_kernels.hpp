@@ -312,7 +312,12 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
     ss = 0.0;
     for (int i = 0; i < wpr; ++i) ss += s_ss[rib * wpr + i];
   }
-  const float inv = (float)(1.0 / sqrt(ss / (double)a.H + (double)a.eps));
+  // ss / H: for a power-of-two H an exact scaling by 2^-k (ldexp), bit-identical to the IEEE
+  // quotient and free of the binary64 division sequence; the branch is uniform over the grid
+  const int64_t H = a.H;
+  const double mean =
+      ((H & (H - 1)) == 0) ? ldexp(ss, -__builtin_ctzll((unsigned long long)H)) : ss / (double)H;
+  const float inv = (float)(1.0 / sqrt(mean + (double)a.eps));
 
   // ---- quantize ----
   RowOut o;
@@ -622,7 +627,8 @@ __global__ void __launch_bounds__(1024) qk_norm_rope_kernel(RArgs a) {
       }
     }
     const double ss = group_sum<L>(ss0 + ss1);
-    const float inv = (float)(1.0 / sqrt(ss / (double)D + (double)a.eps));
+    // D is a power of two: ss * (1/D) is exact, the same value as the quotient ss / D
+    const float inv = (float)(1.0 / sqrt(ss * (1.0 / D) + (double)a.eps));
     const bool isq = h < a.hq;
     const u32x4 w0 = isq ? wq0 : wk0, w1 = isq ? wq1 : wk1;
     float y0[8], y1[8], o0[8], o1[8];

@@ -826,7 +826,7 @@ def summarize(ktrace_db, fetch_db, write_db, key, title, commands, out_md, util=
         json.dump(allt, fh, indent=1, sort_keys=True)
         fh.write("\n")
 
-    lines = [f"# {title}", "", "Commands (from the repository root on the GPU box):", ""]
+    lines = [f"# {title}", "", "Commands (from the repository root, on an MI355X host):", ""]
     lines += [f"    {c}" for c in commands]
     lines += ["", "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
               "| kernel | calls | total us | average us | % |", "|---|---|---|---|---|"]
@@ -916,7 +916,7 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
+        print(f"bench.py: runs on exactly one GPU; --gpus {args.gpus} is not "
               f"supported: token rows shard across GPUs with no exchange, and one GPU's share "
               f"is what this benchmark measures",
               file=sys.stderr)

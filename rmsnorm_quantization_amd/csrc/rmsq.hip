@@ -225,7 +225,7 @@ int fused_impl(const void* x, const void* res, const void* w, float eps, int mod
                        : fused_kernel_bf16(mode, res != nullptr, gs, l.chunks_per_thread, exact);
   if (!fn) return RMSQ_EINVAL;
   const int64_t nblk = (T + l.rows_per_block - 1) / l.rows_per_block;
-  KArgs a;
+  KArgs a{};
   a.x = static_cast<const uint16_t*>(x);
   a.res = static_cast<const uint16_t*>(res);
   a.w = static_cast<const uint16_t*>(w);
@@ -264,11 +264,14 @@ int validate_fp4_dynamic(const void* x, const void* res, const void* w, float ep
   return RMSQ_OK;
 }
 
-// Three launches, one launch shape for both row passes (so that both reduce each row's squares
-// in the same order and see the same y): (1) residual add + RMSNorm, each row's largest |y| staged
-// as f32 in the first 4T bytes of out_q; (2) one workgroup: the batch's largest |y| -> gs;
-// (3) the FP4 block-16 kernel without a residual on the normalized input (the new residual, or
-// x), reading gs from device memory.
+// Three launches: (1) residual add + RMSNorm, each row's largest |y| staged as f32 in the first
+// 4T bytes of out_q; (2) one workgroup: the batch's largest |y| -> gs; (3) the FP4 block-16
+// kernel without a residual on the normalized input (the new residual, or x), reading gs from
+// device memory.  Pass 3 must see pass 1's y.  Where a row's block scales can hold an f32
+// (H % 64 == 0, out_scales 4-byte aligned) and a row fits one wave (H <= 4096), pass 1 also
+// stages each row's inverse RMS there and pass 3 runs one wave per row and reads it: only that
+// wave later writes those bytes.  Otherwise both passes use one launch shape, so that both
+// reduce each row's squares in the same order.
 int fp4_dynamic_impl(const void* x, const void* res, const void* w, float eps, void* q,
                      void* scales, void* res_out, float* global_scale, int64_t T, int64_t H,
                      unsigned flags, const rmsq_launch* launch, void* start_event,
@@ -282,14 +285,22 @@ int fp4_dynamic_impl(const void* x, const void* res, const void* w, float eps, v
   if (st != RMSQ_OK) return st;
   const bool exact = exact_fit(l, T, H), f16 = (flags & RMSQ_INPUT_F16) != 0;
   const int vpt = l.chunks_per_thread;
+  const bool stage = (H % 64) == 0 && H <= 4096 && aligned(scales, 4);
+  rmsq_launch l3 = l;  // pass 3's shape
+  if (stage) {
+    l3 = default_launch(H);  // one wave per row (several rows per workgroup for H <= 1024)
+    if (l3.threads_per_row != 64) l3 = rmsq_launch{64, (int32_t)((H / 8 + 63) / 64), 1, 0};
+  }
+  const bool exact3 = exact_fit(l3, T, H);
   const void* pass1 = f16 ? amax_kernel_f16(res != nullptr, vpt, exact)
                           : amax_kernel_bf16(res != nullptr, vpt, exact);
-  const void* pass3 = f16 ? fused_kernel_f16(RMSQ_FP4_BLOCK16, false, 16, vpt, exact)
-                          : fused_kernel_bf16(RMSQ_FP4_BLOCK16, false, 16, vpt, exact);
+  const void* pass3 =
+      f16 ? fused_kernel_f16(RMSQ_FP4_BLOCK16, false, 16, l3.chunks_per_thread, exact3)
+          : fused_kernel_bf16(RMSQ_FP4_BLOCK16, false, 16, l3.chunks_per_thread, exact3);
   if (!pass1 || !pass3) return RMSQ_EINVAL;
   const int64_t nblk = (T + l.rows_per_block - 1) / l.rows_per_block;
   const int threads = l.threads_per_row * l.rows_per_block;
-  KArgs a;
+  KArgs a{};
   a.x = static_cast<const uint16_t*>(x);
   a.res = static_cast<const uint16_t*>(res);
   a.w = static_cast<const uint16_t*>(w);
@@ -306,6 +317,8 @@ int fp4_dynamic_impl(const void* x, const void* res, const void* w, float eps, v
   a.rpb = l.rows_per_block;
   a.nblk = (uint32_t)nblk;
   a.xcd_ranges = (l.options & RMSQ_LAUNCH_XCD_RANGES) ? 1 : 0;
+  a.inv_rows = stage ? static_cast<uint8_t*>(scales) : nullptr;
+  a.inv_stride = H / 16;
   st = launch_kernel(pass1, nblk, threads, &a, stream, start_event, nullptr);
   if (st != RMSQ_OK) return st;
   GArgs g;
@@ -321,7 +334,13 @@ int fp4_dynamic_impl(const void* x, const void* res, const void* w, float eps, v
   b.q = static_cast<uint8_t*>(q);
   b.scales = scales;
   b.scale_in = global_scale;
-  return launch_kernel(pass3, nblk, threads, &b, stream, nullptr, stop_event);
+  b.tpr = l3.threads_per_row;
+  b.rpb = l3.rows_per_block;
+  const int64_t nblk3 = (T + l3.rows_per_block - 1) / l3.rows_per_block;
+  b.nblk = (uint32_t)nblk3;
+  b.xcd_ranges = (l3.options & RMSQ_LAUNCH_XCD_RANGES) ? 1 : 0;
+  return launch_kernel(pass3, nblk3, l3.threads_per_row * l3.rows_per_block, &b, stream, nullptr,
+                       stop_event);
 }
 
 // ---- residual add + RMSNorm -> padded 16-bit output ------------------------------------------
@@ -376,7 +395,7 @@ int pad_impl(const void* x, const void* res, const void* w, float eps, void* out
                                             : pad_kernel_bf16(res != nullptr, l.chunks_per_thread);
   if (!fn) return RMSQ_EINVAL;
   const int64_t nblk = (T + l.rows_per_block - 1) / l.rows_per_block;
-  KArgs a;
+  KArgs a{};
   a.x = static_cast<const uint16_t*>(x);
   a.res = static_cast<const uint16_t*>(res);
   a.w = static_cast<const uint16_t*>(w);

@@ -53,6 +53,11 @@ struct KArgs {
   int32_t rpb;    // rows per block
   uint32_t nblk;  // workgroups in the grid
   int32_t xcd_ranges;  // XCD-contiguous row-block ranges instead of launch order
+  // FP4 with a batch global scale: row t's inverse RMS as f32 at inv_rows + t * inv_stride
+  // (the first bytes of that row's block scales), written by the row-absmax pass and read by
+  // the block pass instead of normalizing again; null otherwise
+  uint8_t* inv_rows;
+  int64_t inv_stride;
 };
 
 // One element of y = (h * inv) * w from the packed 16-bit chunk dwords (DT: 0 bf16, 1 binary16).
@@ -293,31 +298,44 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
     }
   }
 
-  // ---- sum of squares (binary64; two chains, the products are exact) -> inv_rms ----
-  double ss0 = 0.0, ss1 = 0.0;
+  float inv;
+  if (MODE == RMSQ_FP4_BLOCK16 && a.inv_rows != nullptr) {
+    // the block pass of FP4 with a batch scale (one wave per row, uniform branch): the row
+    // pass's inverse RMS, staged in this row's own block-scale bytes; every store of this wave
+    // depends on it, so the load completes before the wave overwrites those bytes
+    inv = *reinterpret_cast<const float*>(a.inv_rows +
+                                          (size_t)(row_ok ? row : 0) * (size_t)a.inv_stride);
+  } else {
+    // ---- sum of squares (binary64; two chains, the products are exact) -> inv_rms ----
+    double ss0 = 0.0, ss1 = 0.0;
 #pragma unroll
-  for (int k = 0; k < VPT; ++k) {
+    for (int k = 0; k < VPT; ++k) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const double lo = (double)in_lo<DT>(hv[k][j]);
-      const double hi = (double)in_hi<DT>(hv[k][j]);
-      ss0 = fma(lo, lo, ss0);
-      ss1 = fma(hi, hi, ss1);
+      for (int j = 0; j < 4; ++j) {
+        const double lo = (double)in_lo<DT>(hv[k][j]);
+        const double hi = (double)in_hi<DT>(hv[k][j]);
+        ss0 = fma(lo, lo, ss0);
+        ss1 = fma(hi, hi, ss1);
+      }
     }
+    double ss = wave_sum(ss0 + ss1);
+    if (wpr > 1) {  // uniform over the block
+      if ((tid & 63) == 0) s_ss[tid >> 6] = ss;
+      __syncthreads();
+      ss = 0.0;
+      for (int i = 0; i < wpr; ++i) ss += s_ss[rib * wpr + i];
+    }
+    // ss / H: for a power-of-two H an exact scaling by 2^-k (ldexp), bit-identical to the IEEE
+    // quotient and free of the binary64 division sequence; the branch is uniform over the grid
+    const int64_t H = a.H;
+    const double mean =
+        ((H & (H - 1)) == 0) ? ldexp(ss, -__builtin_ctzll((unsigned long long)H)) : ss / (double)H;
+    inv = (float)(1.0 / sqrt(mean + (double)a.eps));
   }
-  double ss = wave_sum(ss0 + ss1);
-  if (wpr > 1) {  // uniform over the block
-    if ((tid & 63) == 0) s_ss[tid >> 6] = ss;
-    __syncthreads();
-    ss = 0.0;
-    for (int i = 0; i < wpr; ++i) ss += s_ss[rib * wpr + i];
+  if constexpr (MODE == kModeRowAmax) {  // stage it for the block pass
+    if (a.inv_rows != nullptr && lr == 0 && row_ok)
+      *reinterpret_cast<float*>(a.inv_rows + (size_t)row * (size_t)a.inv_stride) = inv;
   }
-  // ss / H: for a power-of-two H an exact scaling by 2^-k (ldexp), bit-identical to the IEEE
-  // quotient and free of the binary64 division sequence; the branch is uniform over the grid
-  const int64_t H = a.H;
-  const double mean =
-      ((H & (H - 1)) == 0) ? ldexp(ss, -__builtin_ctzll((unsigned long long)H)) : ss / (double)H;
-  const float inv = (float)(1.0 / sqrt(mean + (double)a.eps));
 
   // ---- quantize ----
   RowOut o;

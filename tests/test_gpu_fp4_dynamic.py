@@ -37,14 +37,18 @@ def _bits(t):
     return None if t is None else t.contiguous().view(torch.int16).numpy().view(np.uint16)
 
 
-def run(x, r, w, eps=1e-6, launch=None, inplace=False):
-    """Run on device copies of CPU tensors; returns (gpu dict, oracle dict)."""
+def run(x, r, w, eps=1e-6, launch=None, inplace=False, scale_offset=0):
+    """Run on device copies of CPU tensors; returns (gpu dict, oracle dict).  scale_offset: place
+    the block scales that many bytes into their buffer (1: not 4-byte aligned)."""
     T, H = x.shape
     f16 = x.dtype == torch.float16
     flags = B.RMSQ_INPUT_F16 if f16 else 0
     print(f"[fp4dyn] T={T} H={H} residual={r is not None} f16={f16} inplace={inplace} "
-          f"launch={None if launch is None else launch.as_tuple()}", flush=True)
-    gq, gs_, gg = GH.Guarded(T * H // 2), GH.Guarded(T * H // 16), GH.Guarded(4)
+          f"launch={None if launch is None else launch.as_tuple()} scale_offset={scale_offset}",
+          flush=True)
+    gq, gg = GH.Guarded(T * H // 2), GH.Guarded(4)
+    gs_ = GH.Guarded(T * H // 16 + scale_offset)
+    sdata = gs_.data[scale_offset:]
     rd = None if r is None else GH.to_dev(r).clone()
     grs = None
     if rd is None:
@@ -54,7 +58,7 @@ def run(x, r, w, eps=1e-6, launch=None, inplace=False):
     else:
         grs = GH.Guarded(T * H * 2)
         rout = grs.data.view(x.dtype)
-    B.rmsq_fused_fp4_dynamic(GH.to_dev(x), rd, GH.to_dev(w), eps, gq.data, gs_.data, rout,
+    B.rmsq_fused_fp4_dynamic(GH.to_dev(x), rd, GH.to_dev(w), eps, gq.data, sdata, rout,
                              gg.data.view(torch.float32), flags=flags, launch=launch)
     torch.cuda.synchronize()
     for g, what in ((gq, "out_q"), (gs_, "out_scales"), (gg, "global_scale")):
@@ -62,7 +66,7 @@ def run(x, r, w, eps=1e-6, launch=None, inplace=False):
     if grs is not None:
         grs.check("residual_out")
     gpu = {"q": gq.data.view(T, H // 2).cpu().numpy(),
-           "scales": gs_.data.view(T, H // 16).cpu().numpy(),
+           "scales": sdata.view(T, H // 16).cpu().numpy(),
            "residual_out": None if rout is None else _bits(rout.cpu()).reshape(T, H),
            "global_scale": gg.data.view(torch.float32).cpu().numpy()[0]}
     ref = O.fused_fp4_dynamic(_bits(x), _bits(r), _bits(w), eps, flags=flags, want_pre=True)
@@ -79,8 +83,11 @@ def check(x, r, w, **kw):
     return gpu, ref
 
 
+# H % 64 == 0 and H <= 4096: the block pass reads the row pass's inverse RMS (one wave per row);
+# the others (H 16, 48, 80, 4160, 5120, 65536) normalize again with the row pass's launch shape
 @pytest.mark.parametrize("T,H", [(1, 2048), (32, 2048), (256, 2048), (4096, 2048), (37, 5120),
-                                 (5, 16), (9, 48), (3, 65536)])
+                                 (5, 16), (9, 48), (3, 65536), (33, 64), (17, 1024), (20, 4096),
+                                 (7, 80), (5, 4160)])
 @pytest.mark.parametrize("residual", [True, False])
 def test_shapes(T, H, residual):
     x, r, w = _inputs(T, H, T * 3 + H, residual=residual)
@@ -108,6 +115,15 @@ def test_inplace_and_value_ranges():
     for scale in (1e-30, 1e-3, 1e4, 1e30):   # the global scale follows the batch's magnitude
         x, r, w = _inputs(16, 2048, 7, scale=scale)
         gpu, _ = check(x, r, w)
+
+
+@pytest.mark.parametrize("H", [1024, 2048])
+def test_unaligned_block_scales(H):
+    """Block scales not 4-byte aligned: no staging, the block pass normalizes again -- the same
+    results."""
+    x, r, w = _inputs(29, H, H + 3)
+    check(x, r, w, scale_offset=1)
+    check(x, r, w, scale_offset=2, launch=B.rmsq_launch(128, H // 1024 or 1, 2, 0))
 
 
 def test_zero_batch_gives_flt_max_and_zero_codes():

@@ -140,6 +140,26 @@ def test_query_launch(B):
         B.rmsq_query_launch(1, 10, 12)
 
 
+@pytest.mark.parametrize("T,H,shape", [
+    (4096, 2048, (64, 4, 1, 0)),     # in flight at once: one wave per row
+    (1024, 2048, (64, 4, 1, 0)),
+    (2048, 1536, (64, 3, 1, 0)),
+    (8192, 2048, (128, 2, 1, 0)),    # more than 2^20 chunks: several waves per row
+    (1024, 4096, (256, 2, 1, 0)),    # rows of more than four waves' worth of chunks
+    (2048, 4096, (256, 2, 1, 0)),
+    (1023, 2048, (128, 2, 1, 0)),    # below 1024 rows
+    (64, 2048, (128, 2, 1, 0)),
+    (1024, 2880, (192, 2, 1, 0)),    # rows that do not fill whole waves
+    (1024, 5120, (320, 2, 1, 0)),    # longer than one wave's 8 chunks per lane
+    (4096, 1024, (64, 2, 4, 0)),     # short rows: four to a workgroup
+])
+def test_query_launch_batch_rule(B, T, H, shape):
+    for mode in (0, 1, 3):
+        l, grid = B.rmsq_query_launch(mode, T, H, 16 if mode == 3 else 0)
+        assert l.as_tuple() == shape
+        assert grid == -(-T // shape[2])
+
+
 @pytest.mark.parametrize("grid", [1, 2, 7, 8, 9, 15, 16, 17, 255, 256, 1000, 4096, 16385])
 def test_block_to_rowblock_is_a_bijection(B, grid):
     got = [B.rmsq_block_to_rowblock(b, grid) for b in range(grid)]

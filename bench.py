@@ -849,8 +849,12 @@ def summarize(ktrace_db, fetch_db, write_db, key, title, commands, out_md, util=
         for name, db in util:
             rows = _db_rows(db, "select kernel_name, value from counters_collection "
                                 "where counter_name = '%s'" % name)
-            vals = [v for k, v in rows if k == main_k[0]]
-            lines.append(f"| {name} | {statistics.median(vals):.2f} | {len(vals)} |")
+            for r in step_k:  # one row per kernel of the step
+                vals = [v for k, v in rows if k == r[0]]
+                label = name if len(step_k) == 1 else (
+                    f"{name}, `{r[0].split('(')[0].replace('void ', '')}`")
+                if vals:
+                    lines.append(f"| {label} | {statistics.median(vals):.2f} | {len(vals)} |")
         lines += ["", "VALUBusy: % of GPU time the vector ALUs issue; MemUnitStalled: % of GPU time "
                   "the texture/memory unit stalls on data; OccupancyPercent: resident waves as % "
                   "of the maximum.", ""]

@@ -373,9 +373,12 @@ RMSQ_API int64_t rmsq_block_to_rowblock(int64_t block, int64_t grid);
  *  RMSQ_CVT_E2M1  out: n/2 bytes, element 2k in the low nibble (the FP4 epilogue's conversion);
  *                 n must be a multiple of 8
  *  RMSQ_CVT_BF16  out: n uint16 bf16 patterns (the residual-add rounding)
+ *  RMSQ_CVT_INV_SQRT
+ *                 out: n f32, the kernels' inverse RMS of m = in[i] widened to binary64, i.e.
+ *                 (float)(1.0 / sqrt(m)) with binary64 root and quotient (m > 0 assumed)
  *  n must be a multiple of 8; in/out 16-byte aligned.  Used to pin gfx950's conversion
- *  instructions against the reference definitions of the formats. */
-enum { RMSQ_CVT_E4M3 = 0, RMSQ_CVT_E2M1 = 1, RMSQ_CVT_BF16 = 2 };
+ *  instructions, and the inverse-RMS sequence, against the reference definitions. */
+enum { RMSQ_CVT_E4M3 = 0, RMSQ_CVT_E2M1 = 1, RMSQ_CVT_BF16 = 2, RMSQ_CVT_INV_SQRT = 3 };
 RMSQ_API int rmsq_convert(int format, const float* in, void* out, int64_t n, void* stream);
 
 /* Human-readable text for a status code (static storage). */

@@ -31,7 +31,7 @@ RMSQ_OK, RMSQ_EINVAL, RMSQ_EALIGN, RMSQ_EALIAS, RMSQ_EUNSUPPORTED, RMSQ_ELAUNCH,
 RMSQ_FP8_STATIC, RMSQ_FP8_TOKEN, RMSQ_FP8_GROUP, RMSQ_FP4_BLOCK16 = 0, 1, 2, 3
 RMSQ_SCALE_COLMAJOR, RMSQ_SCALE_E8M0, RMSQ_SCALE_E8M0_U8 = 1, 2, 4
 RMSQ_INPUT_F16 = 1 << 8
-RMSQ_CVT_E4M3, RMSQ_CVT_E2M1, RMSQ_CVT_BF16 = 0, 1, 2
+RMSQ_CVT_E4M3, RMSQ_CVT_E2M1, RMSQ_CVT_BF16, RMSQ_CVT_INV_SQRT = 0, 1, 2, 3
 RMSQ_LAUNCH_XCD_RANGES = 1
 RMSQ_LAUNCH_ROW_TILES = 2
 RMSQ_MAX_HIDDEN = 65536

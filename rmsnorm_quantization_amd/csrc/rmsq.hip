@@ -843,13 +843,17 @@ int64_t rmsq_block_to_rowblock(int64_t block, int64_t grid) {
 }
 
 int rmsq_convert(int format, const float* in, void* out, int64_t n, void* stream) {
-  if (format != RMSQ_CVT_E4M3 && format != RMSQ_CVT_E2M1 && format != RMSQ_CVT_BF16)
+  if (format != RMSQ_CVT_E4M3 && format != RMSQ_CVT_E2M1 && format != RMSQ_CVT_BF16 &&
+      format != RMSQ_CVT_INV_SQRT)
     return RMSQ_EINVAL;
   if (n < 0 || (n % 8) != 0) return RMSQ_EINVAL;
   if (n == 0) return RMSQ_OK;
   if (!in || !out) return RMSQ_EINVAL;
   if (!aligned(in, 16) || !aligned(out, 16)) return RMSQ_EALIGN;
-  const size_t ob = format == RMSQ_CVT_E4M3 ? (size_t)n : format == RMSQ_CVT_E2M1 ? n / 2 : n * 2;
+  const size_t ob = format == RMSQ_CVT_E4M3   ? (size_t)n
+                    : format == RMSQ_CVT_E2M1 ? (size_t)n / 2
+                    : format == RMSQ_CVT_BF16 ? (size_t)n * 2
+                                              : (size_t)n * 4;
   if (overlap(span(in, (size_t)n * 4), span(out, ob))) return RMSQ_EALIAS;
   const int st = check_device();
   if (st != RMSQ_OK) return st;

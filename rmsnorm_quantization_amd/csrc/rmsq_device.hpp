@@ -121,6 +121,25 @@ __device__ __forceinline__ uint32_t e8m0_ceil(float s, float* p2) {
   return byte;
 }
 
+// ---- inverse RMS ----------------------------------------------------------------------------
+// (float)(1.0 / sqrt(m)): the binary32 rounding of the correctly rounded binary64 quotient of one
+// by the correctly rounded binary64 root, as the plain definition of the inverse RMS computes it,
+// without that definition's two long binary64 sequences in the common case.  The hardware
+// estimate (v_rsq_f64) is refined by three Newton steps y <- y + (y/2)(1 - m y^2), which leave y
+// within a few binary64 ulps of 1/sqrt(m) from any estimate better than 2^-6; the definition's
+// value lies within two ulps of 1/sqrt(m) as well.  Rounding to binary32 is monotonic, so when
+// y(1 - 2^-40) and y(1 + 2^-40) round to the same binary32 value every value between them does,
+// the definition's included; otherwise (about one value in 2^16, and NaN or infinite m) the
+// definition's own sequence runs.
+__device__ __forceinline__ float inv_sqrt_f32(double m) {
+  double y = __builtin_amdgcn_rsq(m);
+#pragma unroll
+  for (int i = 0; i < 3; ++i) y = fma(0.5 * y, fma(-m, y * y, 1.0), y);
+  const float lo = (float)(y * (1.0 - 0x1p-40)), hi = (float)(y * (1.0 + 0x1p-40));
+  if (lo == hi) return lo;
+  return (float)(1.0 / sqrt(m));
+}
+
 // ---- cross-lane reductions ---------------------------------------------------------------
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {

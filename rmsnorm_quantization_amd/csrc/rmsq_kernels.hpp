@@ -330,7 +330,7 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
     const int64_t H = a.H;
     const double mean =
         ((H & (H - 1)) == 0) ? ldexp(ss, -__builtin_ctzll((unsigned long long)H)) : ss / (double)H;
-    inv = (float)(1.0 / sqrt(mean + (double)a.eps));
+    inv = inv_sqrt_f32(mean + (double)a.eps);
   }
   if constexpr (MODE == kModeRowAmax) {  // stage it for the block pass
     if (a.inv_rows != nullptr && lr == 0 && row_ok)
@@ -646,7 +646,7 @@ __global__ void __launch_bounds__(1024) qk_norm_rope_kernel(RArgs a) {
     }
     const double ss = group_sum<L>(ss0 + ss1);
     // D is a power of two: ss * (1/D) is exact, the same value as the quotient ss / D
-    const float inv = (float)(1.0 / sqrt(ss * (1.0 / D) + (double)a.eps));
+    const float inv = inv_sqrt_f32(ss * (1.0 / D) + (double)a.eps);
     const bool isq = h < a.hq;
     const u32x4 w0 = isq ? wq0 : wk0, w1 = isq ? wq1 : wk1;
     float y0[8], y1[8], o0[8], o1[8];

@@ -17,6 +17,12 @@ __global__ void __launch_bounds__(256) convert_kernel(int fmt, const float* in, 
         (u32x2){fp8x4(v[0], v[1], v[2], v[3]), fp8x4(v[4], v[5], v[6], v[7])};
   } else if (fmt == RMSQ_CVT_E2M1) {
     reinterpret_cast<uint32_t*>(out)[c] = fp4x8(v);
+  } else if (fmt == RMSQ_CVT_INV_SQRT) {
+    float r[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = inv_sqrt_f32((double)v[e]);
+    reinterpret_cast<f32x4*>(out)[2 * c] = (f32x4){r[0], r[1], r[2], r[3]};
+    reinterpret_cast<f32x4*>(out)[2 * c + 1] = (f32x4){r[4], r[5], r[6], r[7]};
   } else {
     reinterpret_cast<u32x4*>(out)[c] = (u32x4){pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
                                                pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};

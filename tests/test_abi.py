@@ -178,6 +178,11 @@ def test_convert_argument_checks(B):
     assert L.rmsq_convert(0, X, Q, 0, None) == B.RMSQ_OK
     assert L.rmsq_convert(0, X + 4, Q, 8, None) == B.RMSQ_EALIGN
     assert L.rmsq_convert(0, X, X + 16, 8, None) == B.RMSQ_EALIAS
+    # the inverse-RMS output is 4 bytes per value: 32 bytes just below the 8 inputs overlap
+    # them from 16 bytes below, where 8 e4m3 bytes do not
+    assert L.rmsq_convert(3, X, X - 16, 8, None) == B.RMSQ_EALIAS
+    assert L.rmsq_convert(0, X, X - 16, 8, None) != B.RMSQ_EALIAS
+    assert L.rmsq_convert(3, X, X - 32, 8, None) != B.RMSQ_EALIAS
 
 
 # ------------------------------------------------------------------ SiLU+Mul -> quant checks

@@ -49,7 +49,8 @@ def _inputs(table, sat):
 def _convert(fmt, v):
     vin = torch.from_numpy(v).to("cuda")
     n = v.size
-    nbytes = {B.RMSQ_CVT_E4M3: n, B.RMSQ_CVT_E2M1: n // 2, B.RMSQ_CVT_BF16: 2 * n}[fmt]
+    nbytes = {B.RMSQ_CVT_E4M3: n, B.RMSQ_CVT_E2M1: n // 2, B.RMSQ_CVT_BF16: 2 * n,
+              B.RMSQ_CVT_INV_SQRT: 4 * n}[fmt]
     g = GH.Guarded(nbytes)
     print(f"[convert] fmt={fmt} n={n}", flush=True)
     B.rmsq_convert(fmt, vin, g.data, n)
@@ -85,4 +86,34 @@ def test_bf16_rounding_matches_oracle():
     got = _convert(B.RMSQ_CVT_BF16, v).view(np.uint16)
     exp = O.f32_to_bf16(v)
     bad = got != exp
+    assert not bad.any(), f"{bad.sum()} mismatches, e.g. {v[bad][:8]} -> {got[bad][:8]} vs {exp[bad][:8]}"
+
+
+def test_inverse_rms_sequence_matches_definition():
+    """The kernels' inverse RMS of m (a refined hardware estimate, with the exact binary64
+    sequence where the estimate's binary32 rounding is in doubt) against the definition the
+    oracle follows: the binary64 root and quotient, each correctly rounded (numpy's binary64
+    sqrt and division are), rounded once to binary32.  Inputs span every binary32 binade of
+    positive m, and include every value of a large random sample whose binary64 result lies
+    within 2^-38 of a binary32 rounding boundary, which the kernels resolve the slow way."""
+    rng = np.random.default_rng(2024)
+    bits = rng.integers(1, 0x7F800000, 4_000_000, dtype=np.uint64).astype(np.uint32)
+    m = bits.view(np.float32)
+    exact = 1.0 / np.sqrt(m.astype(np.float64))
+    f = exact.astype(np.float32)
+    # distance to the nearest binary32 rounding boundary, relative to the value
+    up = np.nextafter(f, np.float32(np.inf)).astype(np.float64)
+    dn = np.nextafter(f, np.float32(0)).astype(np.float64)
+    fd = f.astype(np.float64)
+    gap = np.minimum(np.abs(exact - (fd + up) / 2), np.abs(exact - (fd + dn) / 2)) / exact
+    hard = m[gap < 2.0 ** -38]
+    assert hard.size > 100
+    special = np.array([np.float32(2.0 ** -149), np.finfo(np.float32).tiny, 1.0, 2.0, 4.0, 0.5,
+                        1e-5, 1e-6, np.finfo(np.float32).max], np.float32)
+    powers = (2.0 ** np.arange(-149, 128)).astype(np.float32)
+    v = _pad8(np.concatenate([m[:1_000_000], hard, special, powers]).astype(np.float32))
+    v[v == 0] = 1.0
+    got = _convert(B.RMSQ_CVT_INV_SQRT, v).view(np.float32)
+    exp = (1.0 / np.sqrt(v.astype(np.float64))).astype(np.float32)
+    bad = got.view(np.uint32) != exp.view(np.uint32)
     assert not bad.any(), f"{bad.sum()} mismatches, e.g. {v[bad][:8]} -> {got[bad][:8]} vs {exp[bad][:8]}"

@@ -202,6 +202,8 @@ def fp4dyn_leg(args, wl, T, H):
         a_.record(stream)
         b_.record(stream)
     torch.cuda.synchronize()
+    for i in range(args.warmup):  # lead-in: the timed dispatches do not start from an idle GPU
+        launch_on(argsets[i % nsets], None, None, sh)
     for i in range(args.steps):
         launch_on(argsets[i % nsets], evs[i][0].cuda_event, evs[i][1].cuda_event, sh)
     torch.cuda.synchronize()
@@ -294,6 +296,8 @@ def rope_leg(args, wl, T, D):
         a_.record(stream)
         b_.record(stream)
     torch.cuda.synchronize()
+    for i in range(args.warmup):  # lead-in: the timed dispatches do not start from an idle GPU
+        launch(argsets[i % nsets], None, None, sh)
     for i in range(args.steps):
         launch(argsets[i % nsets], evs[i][0].cuda_event, evs[i][1].cuda_event, sh)
     torch.cuda.synchronize()
@@ -340,11 +344,11 @@ def copy_ceiling(dev, stream):
     for a_, b_ in evs:
         a_.record(stream)
         b_.record(stream)
-    for i in range(4):
+    torch.cuda.synchronize()
+    for i in range(4):  # lead-in, no host synchronization before the timed copies
         src, dst = pairs[i % 2]
         L.rmsq_probe_stream(src.data_ptr(), None, dst.data_ptr(), None, rows, H, 0, 256, 2,
                             None, None, sh)
-    torch.cuda.synchronize()
     for i, (a_, b_) in enumerate(evs):
         src, dst = pairs[i % 2]
         st = L.rmsq_probe_stream(src.data_ptr(), None, dst.data_ptr(), None, rows, H, 0, 256, 2,
@@ -553,6 +557,11 @@ def gpu_leg(args, wl, T, H, mode, G, flags):
         a_.record(stream)
         b_.record(stream)
     torch.cuda.synchronize()
+    # lead-in, untimed and with no host synchronization before the timed launches: the first
+    # dispatches after an idle gap run slower (about 1.6x at the default workload), which is
+    # the measurement's own synchronization, not the kernel
+    for i in range(args.warmup):
+        step(i)
     for i in range(args.steps):
         st = launch_timed(argsets[i % nsets], evs[i][0].cuda_event, evs[i][1].cuda_event, sh)
         if st:
@@ -591,13 +600,13 @@ def probe_leg(args, sets, T, H, mode, shape, stream, evs):
     sh = stream.cuda_stream
     argsets = [(ptr(s_["x"]), ptr(s_["r"]), ptr(s_["ro"]), ptr(s_["q"]), T, H, out1, shape[0],
                 shape[1]) for s_ in sets]
-    for i in range(args.warmup):
-        st = L.rmsq_probe_stream(*argsets[i % len(sets)], None, None, sh)
-        if st:
-            raise RuntimeError(f"rmsq_probe_stream failed ({st})")
     import torch
 
     torch.cuda.synchronize()
+    for i in range(args.warmup):  # lead-in, as for the fused kernel
+        st = L.rmsq_probe_stream(*argsets[i % len(sets)], None, None, sh)
+        if st:
+            raise RuntimeError(f"rmsq_probe_stream failed ({st})")
     for i in range(args.steps):
         st = L.rmsq_probe_stream(*argsets[i % len(sets)], evs[i][0].cuda_event,
                                  evs[i][1].cuda_event, sh)

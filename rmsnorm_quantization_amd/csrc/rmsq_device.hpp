@@ -4,8 +4,10 @@
 // Formats (the pages name FP8 e4m3 and NVFP4-style e2m1 outputs -- vLLM docs "Fusion
 // torch.compile passes", "RMSNorm + quantization"; PR #51925 summary, "Motivation" -- but not
 // their bit layouts; the OCP definitions are used): e4m3fn saturates at 448, e2m1 at 6, both
-// round to nearest even.  The hardware converters are fed values already clamped to the
-// format's range, so saturation never depends on the instruction's overflow behaviour.
+// round to nearest even.  The FP8 converter is fed values already clamped to the format's
+// range, so its saturation never depends on the instruction's overflow behaviour; the FP4
+// converter saturates by itself (e2m1 has no infinity or NaN code: every finite or infinite
+// magnitude from 6 up gives +-6, pinned against the oracle by the converter tests).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -91,17 +93,14 @@ __device__ __forceinline__ float fp8_decode(uint32_t byte) {
 
 // ---- FP4 e2m1 ----------------------------------------------------------------------------
 // Eight f32 -> eight e2m1 nibbles in one dword, element 2k in the low nibble of byte k
-// (v_cvt_scalef32_pk_fp4_f32 with a unit scale, so the instruction's scale does nothing).
+// (v_cvt_scalef32_pk_fp4_f32 with a unit scale, so the instruction's scale does nothing; it
+// rounds to nearest even and saturates to +-6 without a clamp).
 __device__ __forceinline__ uint32_t fp4x8(const float* v) {
   uint32_t w = 0;
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clamp_sym(v[0], kFp4Max),
-                                               clamp_sym(v[1], kFp4Max), 1.0f, 0);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clamp_sym(v[2], kFp4Max),
-                                               clamp_sym(v[3], kFp4Max), 1.0f, 1);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clamp_sym(v[4], kFp4Max),
-                                               clamp_sym(v[5], kFp4Max), 1.0f, 2);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clamp_sym(v[6], kFp4Max),
-                                               clamp_sym(v[7], kFp4Max), 1.0f, 3);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
   return w;
 }
 
@@ -125,16 +124,17 @@ __device__ __forceinline__ uint32_t e8m0_ceil(float s, float* p2) {
 // (float)(1.0 / sqrt(m)): the binary32 rounding of the correctly rounded binary64 quotient of one
 // by the correctly rounded binary64 root, as the plain definition of the inverse RMS computes it,
 // without that definition's two long binary64 sequences in the common case.  The hardware
-// estimate (v_rsq_f64) is refined by three Newton steps y <- y + (y/2)(1 - m y^2), which leave y
-// within a few binary64 ulps of 1/sqrt(m) from any estimate better than 2^-6; the definition's
-// value lies within two ulps of 1/sqrt(m) as well.  Rounding to binary32 is monotonic, so when
+// estimate (v_rsq_f64, within 2^-24 relative on gfx950 over 2^24 sampled m) is refined by two
+// Newton steps y <- y + (y/2)(1 - m y^2), which leave y within a few binary64 ulps of 1/sqrt(m)
+// from any estimate better than 2^-12; the definition's value lies within two ulps of 1/sqrt(m)
+// as well.  Rounding to binary32 is monotonic, so when
 // y(1 - 2^-40) and y(1 + 2^-40) round to the same binary32 value every value between them does,
 // the definition's included; otherwise (about one value in 2^16, and NaN or infinite m) the
 // definition's own sequence runs.
 __device__ __forceinline__ float inv_sqrt_f32(double m) {
   double y = __builtin_amdgcn_rsq(m);
 #pragma unroll
-  for (int i = 0; i < 3; ++i) y = fma(0.5 * y, fma(-m, y * y, 1.0), y);
+  for (int i = 0; i < 2; ++i) y = fma(0.5 * y, fma(-m, y * y, 1.0), y);
   const float lo = (float)(y * (1.0 - 0x1p-40)), hi = (float)(y * (1.0 + 0x1p-40));
   if (lo == hi) return lo;
   return (float)(1.0 / sqrt(m));

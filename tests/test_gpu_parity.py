@@ -111,3 +111,25 @@ def test_w4_add_rmsnorm_fp4_block16(T):
     _, _, _, xb, rb, wb = GH.workload_inputs(4, T, 2048)
     gs = fp4_global_scale(xb, rb, wb, synth.WORKLOADS[4].eps)
     _check(4, T, 2048, O.FP4_BLOCK16, scale_in=gs, group_size=16)
+
+
+# ---------------------------------------------------------------- batch-size launch rule
+# Batches in flight all at once with 1536- or 2048-wide rows run one wave per row (64 x 3 or
+# 64 x 4); every scheme at those default shapes, row-sampled against the oracle.
+@pytest.mark.parametrize("T,H", [(1024, 1536), (2048, 2048)])
+@pytest.mark.parametrize("mode,G,flags", [(O.FP8_STATIC, 0, 0), (O.FP8_TOKEN, 0, 0),
+                                          (O.FP8_GROUP, 128, O.SCALE_COLMAJOR),
+                                          (O.FP8_GROUP, 64, O.SCALE_E8M0),
+                                          (O.FP4_BLOCK16, 16, 0)])
+def test_one_wave_row_default_shapes(T, H, mode, G, flags):
+    from rmsnorm_quantization_amd import binding as B
+
+    assert B.rmsq_query_launch(mode, T, H, G)[0].as_tuple() == (64, H // 512, 1, 0)
+    _, _, _, xb, rb, wb = GH.workload_inputs(4, T, H)
+    scale_in = 0.0
+    if mode == O.FP4_BLOCK16:
+        scale_in = fp4_global_scale(xb, rb, wb, synth.WORKLOADS[4].eps)
+    elif mode == O.FP8_STATIC:
+        scale_in = 0.01
+    rep = _check(4, T, H, mode, scale_in=scale_in, group_size=G, flags=flags, label="one-wave")
+    assert rep.code_mismatch == 0

@@ -202,6 +202,21 @@ __device__ __forceinline__ void quantize_store(const YF& Y, const bool (&ok)[VPT
     }
   } else {  // RMSQ_FP4_BLOCK16
     const float gs = scale_val;
+    // Both divisions of the scheme, exactly as IEEE division rounds them, without a division
+    // sequence per chunk:
+    //  * (a * gs) / 6: p * RN(1/6) corrected once by its FMA residual is the correctly rounded
+    //    quotient for every binary32 p (checked exhaustively over [1, 4), both binades of the
+    //    quotient; powers of two carry it to every p whose quotient can give a non-zero e4m3
+    //    code).  An infinite p is replaced by FLT_MAX, which encodes to the same saturated code.
+    //  * gs / decode(sf): decode(sf) = (1 + j/8) * 2^e, so the quotient is (gs / (1 + j/8)) * 2^-e,
+    //    and scaling a binary32 value by a power of two is exact for normal results and
+    //    overflows exactly when the quotient does.  Lane i of each wave holds gs / (1 + (i mod 8)/8)
+    //    (one IEEE division per lane) and a chunk fetches its j with ds_bpermute.  When |gs| is
+    //    below 2^-100 a quotient could be subnormal, and the IEEE division runs instead (the
+    //    branch is uniform: gs is one value per launch).
+    const bool by_table = fabsf(gs) >= 0x1p-100f;
+    const float g_tab = gs / (1.0f + (float)(o.tid & 7) * 0.125f);
+    constexpr float kSixth = 1.0f / 6.0f;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
       const uint32_t c = o.lr + (uint32_t)(k * o.tpr);
@@ -213,11 +228,19 @@ __device__ __forceinline__ void quantize_store(const YF& Y, const bool (&ok)[VPT
         m = fmaxf(m, fabsf(y[e]));
       }
       m = group_max<2>(m);  // a 16-element block is two neighbouring lanes
-      const uint32_t sf = fp8x1((m * gs) / 6.0f);
+      const float p = fminf(m * gs, __FLT_MAX__);
+      const float q0 = p * kSixth;
+      const uint32_t sf = fp8x1(fmaf(fmaf(-q0, 6.0f, p), kSixth, q0));
       const float d = fp8_decode(sf);
+      const uint32_t db = __float_as_uint(d);
+      // every lane takes part in the exchange, before any branch
+      const float g = __int_as_float(
+          __builtin_amdgcn_ds_bpermute((int)(((db >> 20) & 7u) << 2), __float_as_int(g_tab)));
       uint32_t qc = 0u;
       if (d > 0.0f) {
-        const float mul = gs / d;
+        float mul;
+        if (by_table) mul = __builtin_amdgcn_ldexpf(g, 127 - (int)((db >> 23) & 0xFFu));
+        else mul = gs / d;
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[e] *= mul;
         qc = fp4x8(y);

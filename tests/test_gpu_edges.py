@@ -252,3 +252,16 @@ def test_scale_whose_reciprocal_overflows(mode, G):
     assert nan.any() and np.all(y[nan] == 0)
     assert np.all((gpu["q"][nan] & 0x7F) == 0x7E)
     assert np.array_equal(gpu["q"][~nan], ref["q"][~nan])
+
+
+@pytest.mark.parametrize("gs", [1e-31, 1e-29, 1e-3, 7.0, 300.0, 1e10, 1e30, 3.0e38])
+def test_fp4_global_scale_range(gs):
+    """FP4 block-16 over the range of a caller's global scale: below 2^-100 (where the kernel
+    divides by decode(sf) directly), just above it, ordinary values, and scales large enough that
+    a * gs overflows to infinity and gs / decode(sf) overflows for the small block scales.  Codes
+    and block scales must equal the oracle's bit for bit."""
+    x, r, w = _inputs(8, 1024, seed=31)
+    x[3] = x[3] * 1e-4             # one spike in a row of small values: after normalization the
+    x[3, 5] = 100.0                # other blocks are tiny, so their block scales are small and
+    r[3] = 0.0                     # gs / decode(sf) is large
+    _run_and_compare(O.FP4_BLOCK16, x, r, w, scale_in=float(np.float32(gs)), G=16)

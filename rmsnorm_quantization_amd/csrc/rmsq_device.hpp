@@ -24,6 +24,20 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr float kFp8Max = 448.0f;
 constexpr float kFp4Max = 6.0f;
 
+// ---- addressing --------------------------------------------------------------------------
+// A row pointer plus a 32-bit byte offset.  The address stays (row base, uniform over the wave)
+// + (32-bit lane offset), which the global load and store instructions take directly with the
+// base in scalar registers: no 64-bit address is built per lane and access.  Every offset the
+// kernels form this way is below 2^22 (at most a row of 2^20 16-bit elements).
+template <class T>
+__device__ __forceinline__ T* boff(T* p, uint32_t bytes) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(p) + bytes);
+}
+template <class T>
+__device__ __forceinline__ const T* boff(const T* p, uint32_t bytes) {
+  return reinterpret_cast<const T*>(reinterpret_cast<const char*>(p) + bytes);
+}
+
 // ---- bf16 ------------------------------------------------------------------------------
 // A dword holds two bf16 values, element 2j in the low half.  bf16 is the upper half of an
 // f32 pattern, so widening is a shift or a mask.

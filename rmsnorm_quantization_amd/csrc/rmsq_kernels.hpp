@@ -105,7 +105,7 @@ __device__ __forceinline__ void quantize_store(const YF& Y, const bool (&ok)[VPT
       const u32x2 qc = {fp8x4(v[0], v[1], v[2], v[3]), fp8x4(v[4], v[5], v[6], v[7])};
       if (ok[k]) {
         const uint32_t c = o.lr + (uint32_t)(k * o.tpr);
-        __builtin_nontemporal_store(qc, reinterpret_cast<u32x2*>(o.q + o.obase) + c);
+        __builtin_nontemporal_store(qc, boff(reinterpret_cast<u32x2*>(o.q + o.obase), c << 3));
       }
     }
   } else if constexpr (MODE == RMSQ_FP8_TOKEN) {
@@ -134,7 +134,7 @@ __device__ __forceinline__ void quantize_store(const YF& Y, const bool (&ok)[VPT
       if (zero) qc = (u32x2){0u, 0u};
       if (ok[k]) {
         const uint32_t c = o.lr + (uint32_t)(k * o.tpr);
-        __builtin_nontemporal_store(qc, reinterpret_cast<u32x2*>(o.q + o.obase) + c);
+        __builtin_nontemporal_store(qc, boff(reinterpret_cast<u32x2*>(o.q + o.obase), c << 3));
       }
     }
   } else if constexpr (MODE == RMSQ_FP8_GROUP) {
@@ -162,7 +162,7 @@ __device__ __forceinline__ void quantize_store(const YF& Y, const bool (&ok)[VPT
                   fp8x4(y[4] * r, y[5] * r, y[6] * r, y[7] * r)};
       if (zero) qc = (u32x2){0u, 0u};
       if (ok[k]) {
-        __builtin_nontemporal_store(qc, reinterpret_cast<u32x2*>(o.q + o.obase) + c);
+        __builtin_nontemporal_store(qc, boff(reinterpret_cast<u32x2*>(o.q + o.obase), c << 3));
         if ((o.lr % L) == 0) {
           const int64_t g = c / L;
           const int64_t idx = col ? g * o.ld + o.row : o.row * (o.n / GS) + g;
@@ -198,7 +198,7 @@ __device__ __forceinline__ void quantize_store(const YF& Y, const bool (&ok)[VPT
 #pragma unroll
         for (int j = 0; j < 4; ++j) v[j] = pack_in<DT>(Y(k, 2 * j), Y(k, 2 * j + 1));
       }
-      if (o.row_ok && c < nchp) __builtin_nontemporal_store(v, orow + c);
+      if (o.row_ok && c < nchp) __builtin_nontemporal_store(v, boff(orow, c << 4));
     }
   } else {  // RMSQ_FP4_BLOCK16
     const float gs = scale_val;
@@ -246,7 +246,7 @@ __device__ __forceinline__ void quantize_store(const YF& Y, const bool (&ok)[VPT
         qc = fp4x8(y);
       }
       if (ok[k]) {
-        reinterpret_cast<uint32_t*>(o.q + o.obase / 2)[c] = qc;
+        *boff(reinterpret_cast<uint32_t*>(o.q + o.obase / 2), c << 2) = qc;
         if ((c & 1) == 0) static_cast<uint8_t*>(o.scales)[o.obase / 16 + c / 2] = (uint8_t)sf;
       }
     }
@@ -295,15 +295,15 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
     hv[k] = (u32x4){0u, 0u, 0u, 0u};
     rv[k] = (u32x4){0u, 0u, 0u, 0u};
     if (ok[k]) {
-      hv[k] = __builtin_nontemporal_load(xrow + c);
-      if (RES) rv[k] = __builtin_nontemporal_load(rrow + c);
+      hv[k] = __builtin_nontemporal_load(boff(xrow, c << 4));
+      if (RES) rv[k] = __builtin_nontemporal_load(boff(rrow, c << 4));
     }
   }
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
     const uint32_t c = lr + (uint32_t)(k * tpr);
     wv[k] = (u32x4){0u, 0u, 0u, 0u};
-    if (ok[k]) wv[k] = wrow[c];
+    if (ok[k]) wv[k] = *boff(wrow, c << 4);
   }
 
   // ---- residual add: h = round16(x + r), written back as the new residual ----
@@ -317,7 +317,7 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
         h[j] = pack_in<DT>(in_lo<DT>(hv[k][j]) + in_lo<DT>(rv[k][j]),
                            in_hi<DT>(hv[k][j]) + in_hi<DT>(rv[k][j]));
       hv[k] = h;
-      if (ok[k]) __builtin_nontemporal_store(h, orow + lr + (uint32_t)(k * tpr));
+      if (ok[k]) __builtin_nontemporal_store(h, boff(orow, (lr + (uint32_t)(k * tpr)) << 4));
     }
   }
 
@@ -467,8 +467,8 @@ __global__ void __launch_bounds__(1024) silu_mul_kernel(AArgs a) {
     gv[k] = (u32x4){0u, 0u, 0u, 0u};
     uv[k] = (u32x4){0u, 0u, 0u, 0u};
     if (ok[k]) {
-      gv[k] = __builtin_nontemporal_load(grow + c);
-      uv[k] = __builtin_nontemporal_load(urow + c);
+      gv[k] = __builtin_nontemporal_load(boff(grow, c << 4));
+      uv[k] = __builtin_nontemporal_load(boff(urow, c << 4));
     }
   }
   float act[VPT][8];
@@ -528,8 +528,8 @@ __global__ void __launch_bounds__(1024) silu_mul_tile_kernel(AArgs a) {
     gv[k] = (u32x4){0u, 0u, 0u, 0u};
     uv[k] = (u32x4){0u, 0u, 0u, 0u};
     if (ok[k]) {
-      gv[k] = __builtin_nontemporal_load(grow + c);
-      uv[k] = __builtin_nontemporal_load(urow + c);
+      gv[k] = __builtin_nontemporal_load(boff(grow, c << 4));
+      uv[k] = __builtin_nontemporal_load(boff(urow, c << 4));
     }
   }
   float act[VPT][8];

@@ -45,7 +45,9 @@ extern "C" {
 #define RMSQ_API
 #endif
 
-#define RMSQ_ABI_VERSION 2
+/* 3: rmsq_rms_norm_pad_query_launch takes the call's flags (the default shape depends on the
+ *    activation type); 2: the padding and QK-norm + RoPE entry points take flags. */
+#define RMSQ_ABI_VERSION 3
 #define RMSQ_MAX_HIDDEN 65536 /* largest H one workgroup keeps in registers */
 
 /* ---- status codes ---- */
@@ -353,10 +355,12 @@ RMSQ_API int rmsq_qk_norm_rope_query_launch(int64_t tokens, int num_q_heads, int
 RMSQ_API int rmsq_query_launch(int mode, int64_t tokens, int64_t hidden, int group_size,
                                int has_residual, rmsq_launch* launch, int64_t* grid);
 
-/* The launch shape rmsq_rms_norm_pad picks for (T, H, out_ld) and its grid size.  Host only;
- * makes no HIP call.  Returns RMSQ_OK or RMSQ_EINVAL. */
+/* The launch shape rmsq_rms_norm_pad picks for (T, H, out_ld, flags) and its grid size: flags
+ * as passed to rmsq_rms_norm_pad (0 or RMSQ_INPUT_F16; the default shape depends on the
+ * activation type).  Host only; makes no HIP call.  Returns RMSQ_OK or RMSQ_EINVAL. */
 RMSQ_API int rmsq_rms_norm_pad_query_launch(int64_t tokens, int64_t hidden, int64_t out_ld,
-                                            rmsq_launch* launch, int64_t* grid);
+                                            unsigned flags, rmsq_launch* launch,
+                                            int64_t* grid);
 
 /* The launch shape rmsq_silu_mul_quant picks for (mode, T, I, group_size) and its grid size.
  * Host only; makes no HIP call.  Returns RMSQ_OK or RMSQ_EINVAL. */

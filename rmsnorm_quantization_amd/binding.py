@@ -35,7 +35,7 @@ RMSQ_CVT_E4M3, RMSQ_CVT_E2M1, RMSQ_CVT_BF16, RMSQ_CVT_INV_SQRT = 0, 1, 2, 3
 RMSQ_LAUNCH_XCD_RANGES = 1
 RMSQ_LAUNCH_ROW_TILES = 2
 RMSQ_MAX_HIDDEN = 65536
-RMSQ_ABI_VERSION = 2  # the argument lists below are those of this version
+RMSQ_ABI_VERSION = 3  # the argument lists below are those of this version
 
 
 class RmsqError(RuntimeError):
@@ -108,8 +108,8 @@ def lib():
         L.rmsq_query_launch.argtypes = [i32, i64, i64, i32, i32, C.POINTER(rmsq_launch),
                                         C.POINTER(i64)]
         L.rmsq_query_launch.restype = i32
-        L.rmsq_rms_norm_pad_query_launch.argtypes = [i64, i64, i64, C.POINTER(rmsq_launch),
-                                                     C.POINTER(i64)]
+        L.rmsq_rms_norm_pad_query_launch.argtypes = [i64, i64, i64, u32,
+                                                     C.POINTER(rmsq_launch), C.POINTER(i64)]
         L.rmsq_rms_norm_pad_query_launch.restype = i32
         L.rmsq_silu_mul_query_launch.argtypes = [i32, i64, i64, i32, C.POINTER(rmsq_launch),
                                                  C.POINTER(i64)]
@@ -353,11 +353,12 @@ def rmsq_query_launch(mode, tokens, hidden, group_size=0, has_residual=True):
     return l, grid.value
 
 
-def rmsq_rms_norm_pad_query_launch(tokens, hidden, out_ld):
+def rmsq_rms_norm_pad_query_launch(tokens, hidden, out_ld, flags=0):
     l = rmsq_launch()
     grid = C.c_int64(0)
-    _check(lib().rmsq_rms_norm_pad_query_launch(int(tokens), int(hidden), int(out_ld), C.byref(l),
-                                                C.byref(grid)), "rmsq_rms_norm_pad_query_launch")
+    _check(lib().rmsq_rms_norm_pad_query_launch(int(tokens), int(hidden), int(out_ld), int(flags),
+                                                C.byref(l), C.byref(grid)),
+           "rmsq_rms_norm_pad_query_launch")
     return l, grid.value
 
 

@@ -390,9 +390,16 @@ int validate_pad(const void* x, const void* res, const void* w, float eps, const
 // the padded row fits (ld <= 4096: 64 threads x ceil(ld/512) chunks), else the quantizing
 // kernel's rule.  Measured on MI355X for 2880 -> 3072 (4096 rows): 17.1 us against 18.3 us
 // for 192 threads x 2 chunks; equal at 4000 -> 4096; better at 2000 -> 2048.
-rmsq_launch default_pad_launch(int64_t ld) {
+//
+// Binary16 activations take the one-wave shape only up to 5 chunks per lane: their conversions
+// keep more values live, and from 6 chunks per lane the kernel needs more than the 128 VGPRs a
+// 1024-thread launch bound allows and spills to scratch (2880 -> 3072, 4096 rows: 69 us at
+// 64 x 6 against 18.8 us at 192 x 2); longer binary16 rows take the quantizing kernel's rule.
+rmsq_launch default_pad_launch(int64_t ld, unsigned flags) {
   const int64_t nch = ld / 8;
-  if (nch > 128 && nch <= 512) return rmsq_launch{64, (int32_t)((nch + 63) / 64), 1, 0};
+  const int64_t max_chunks = (flags & RMSQ_INPUT_F16) ? 5 : 8;
+  if (nch > 128 && (nch + 63) / 64 <= max_chunks)
+    return rmsq_launch{64, (int32_t)((nch + 63) / 64), 1, 0};
   return default_launch(ld);
 }
 
@@ -401,7 +408,7 @@ int pad_impl(const void* x, const void* res, const void* w, float eps, void* out
              void* start_event, void* stop_event, void* stream) {
   int st = validate_pad(x, res, w, eps, out, res_out, T, H, out_ld, flags);
   if (st != RMSQ_OK) return st;
-  const rmsq_launch l = launch ? *launch : default_pad_launch(out_ld);
+  const rmsq_launch l = launch ? *launch : default_pad_launch(out_ld, flags);
   if (!valid_launch(l, out_ld)) return RMSQ_EINVAL;  // the launch covers the padded row
   if (T == 0) return RMSQ_OK;
   st = check_device();
@@ -768,11 +775,11 @@ int rmsq_query_launch(int mode, int64_t tokens, int64_t hidden, int group_size,
 }
 
 int rmsq_rms_norm_pad_query_launch(int64_t tokens, int64_t hidden, int64_t out_ld,
-                                   rmsq_launch* launch, int64_t* grid) {
+                                   unsigned flags, rmsq_launch* launch, int64_t* grid) {
   if (tokens < 0 || hidden < 8 || (hidden % 8) != 0 || out_ld < hidden ||
-      out_ld > RMSQ_MAX_HIDDEN || (out_ld % 8) != 0)
+      out_ld > RMSQ_MAX_HIDDEN || (out_ld % 8) != 0 || (flags & ~(unsigned)RMSQ_INPUT_F16) != 0)
     return RMSQ_EINVAL;
-  const rmsq_launch l = rmsq::default_pad_launch(out_ld);
+  const rmsq_launch l = rmsq::default_pad_launch(out_ld, flags);
   if (launch) *launch = l;
   if (grid) *grid = (tokens + l.rows_per_block - 1) / l.rows_per_block;
   return RMSQ_OK;

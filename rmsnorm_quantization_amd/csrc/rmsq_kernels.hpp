@@ -13,12 +13,15 @@
 //   * a row of H bf16 is split into 16-byte chunks of 8 elements; chunk c of a row lives on
 //     thread (c mod threads_per_row) of the row's waves, in registers, for the whole kernel, so
 //     every input byte is loaded exactly once (128-bit non-temporal loads);
+//     the row's base address is wave-uniform (scalar registers) and each lane adds a 32-bit
+//     byte offset;
 //   * sum of squares in binary64 (exact products of bf16 values), DPP butterfly within the
-//     wave, LDS only across the waves of one row; inv_rms rounded once to f32;
+//     wave, LDS only across the waves of one row; inv_rms rounded once to f32 (inv_sqrt_f32);
 //   * per-group (64/128) and per-block (16) absmax: a group is 8 / 16 consecutive lanes (2 for
 //     an FP4 block), reduced with DPP row operations -- no LDS, no barrier;
 //   * hardware conversions: v_cvt_pk_bf16_f32, v_cvt_pk_fp8_f32 (OCP e4m3fn on gfx950),
-//     v_cvt_scalef32_pk_fp4_f32 (unit scale), v_cvt_f32_fp8;
+//     v_cvt_scalef32_pk_fp4_f32 (unit scale), v_cvt_f32_fp8; the FP4 block scale and element
+//     multiplier are exact quotients formed without a division sequence per chunk;
 //   * no MFMA: there is no contraction here, the op is HBM-bandwidth bound.
 #pragma once
 

@@ -57,7 +57,7 @@ def test_library_exports_every_declared_symbol(B):
 
 
 def test_abi_version_and_status_strings(B):
-    assert B.rmsq_abi_version() == B.RMSQ_ABI_VERSION == 2
+    assert B.rmsq_abi_version() == B.RMSQ_ABI_VERSION == 3
     for st in (0, -1, -2, -3, -4, -5, -6):
         assert B.rmsq_status_string(st) and B.rmsq_status_string(st) != "unknown status"
     assert B.rmsq_status_string(-99) == "unknown status"
@@ -239,6 +239,13 @@ def VP(B, x=X, r=R, w=W, eps=1e-6, out=Q, ro=RO, t=T, h=H, ld=H + 64, f=0):
 def test_pad_query_launch(B):
     l, grid = B.rmsq_rms_norm_pad_query_launch(4096, 2880, 3072)
     assert l.as_tuple() == (64, 6, 1, 0) and grid == 4096   # one wave per padded row
+    # binary16 rows take one wave per row only up to 5 chunks per lane (no register spills)
+    l, grid = B.rmsq_rms_norm_pad_query_launch(4096, 2880, 3072, B.RMSQ_INPUT_F16)
+    assert l.as_tuple() == (192, 2, 1, 0) and grid == 4096
+    l, _ = B.rmsq_rms_norm_pad_query_launch(64, 2496, 2560, B.RMSQ_INPUT_F16)
+    assert l.as_tuple() == (64, 5, 1, 0)
+    with pytest.raises(B.RmsqError):
+        B.rmsq_rms_norm_pad_query_launch(4, 64, 64, 1 << 7)
     l, grid = B.rmsq_rms_norm_pad_query_launch(100, 8192, 8192)
     assert l.as_tuple() == B.rmsq_query_launch(0, 100, 8192, 0)[0].as_tuple()
     l, _ = B.rmsq_rms_norm_pad_query_launch(8, 520, 1024)

@@ -23,30 +23,52 @@ struct ProbeArgs {
   int32_t tpr;
 };
 
-template <int VPT, int OUT1>
-__global__ void __launch_bounds__(1024) stream_probe_kernel(ProbeArgs a) {
-  const size_t base = (size_t)blockIdx.x * (size_t)a.nch;
+// Row base pointers are uniform over the workgroup (scalar registers) and each lane adds a 32-bit
+// byte offset, the addressing form of the fused kernel.
+template <class T>
+__device__ __forceinline__ T* boff(T* p, uint32_t bytes) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(p) + bytes);
+}
+template <class T>
+__device__ __forceinline__ const T* boff(const T* p, uint32_t bytes) {
+  return reinterpret_cast<const T*>(reinterpret_cast<const char*>(p) + bytes);
+}
+
+// One row; IN1 / OUT0: whether the second input and the first output are present (uniform
+// over the launch, so each combination is its own straight-line body).
+template <int VPT, int OUT1, bool IN1, bool OUT0>
+__device__ __forceinline__ void probe_row(const ProbeArgs& a) {
+  const size_t base = (size_t)blockIdx.x * (size_t)a.nch;  // the row's first chunk
   const uint32_t lr = threadIdx.x;
   u32x4 v[VPT];
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
-    const size_t c = base + lr + (size_t)k * a.tpr;
-    v[k] = __builtin_nontemporal_load(a.in0 + c);
-    if (a.in1) v[k] ^= __builtin_nontemporal_load(a.in1 + c);
+    const uint32_t c = lr + (uint32_t)(k * a.tpr);
+    v[k] = __builtin_nontemporal_load(boff(a.in0 + base, c << 4));
+    if constexpr (IN1) v[k] ^= __builtin_nontemporal_load(boff(a.in1 + base, c << 4));
   }
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
-    const size_t c = base + lr + (size_t)k * a.tpr;
-    if (a.out0) __builtin_nontemporal_store(v[k], a.out0 + c);
+    const uint32_t c = lr + (uint32_t)(k * a.tpr);
+    if constexpr (OUT0) __builtin_nontemporal_store(v[k], boff(a.out0 + base, c << 4));
     if constexpr (OUT1 == 8) {
-      if (a.out1)
-        __builtin_nontemporal_store((u32x2){v[k][0] ^ v[k][2], v[k][1] ^ v[k][3]},
-                                    reinterpret_cast<u32x2*>(a.out1) + c);
+      __builtin_nontemporal_store((u32x2){v[k][0] ^ v[k][2], v[k][1] ^ v[k][3]},
+                                  boff(reinterpret_cast<u32x2*>(a.out1) + base, c << 3));
     } else if constexpr (OUT1 == 4) {
-      if (a.out1)
-        __builtin_nontemporal_store(v[k][0] ^ v[k][1] ^ v[k][2] ^ v[k][3],
-                                    reinterpret_cast<uint32_t*>(a.out1) + c);
+      __builtin_nontemporal_store(v[k][0] ^ v[k][1] ^ v[k][2] ^ v[k][3],
+                                  boff(reinterpret_cast<uint32_t*>(a.out1) + base, c << 2));
     }
+  }
+}
+
+template <int VPT, int OUT1>
+__global__ void __launch_bounds__(1024) stream_probe_kernel(ProbeArgs a) {
+  if (a.in1) {
+    if (a.out0) probe_row<VPT, OUT1, true, true>(a);
+    else probe_row<VPT, OUT1, true, false>(a);
+  } else {
+    if (a.out0) probe_row<VPT, OUT1, false, true>(a);
+    else probe_row<VPT, OUT1, false, false>(a);
   }
 }
 
@@ -82,14 +104,15 @@ extern "C" int rmsq_probe_stream(const void* in0, const void* in1, void* out0, v
   if (rows == 0) return 0;
   if (!in0) return -1;
   if (!aligned16(in0) || !aligned16(in1) || !aligned16(out0) || !aligned16(out1)) return -2;
-  const void* fn = out1_bytes_per_chunk == 8   ? pick<8>(chunks_per_thread)
-                   : out1_bytes_per_chunk == 4 ? pick<4>(chunks_per_thread)
-                                               : pick<0>(chunks_per_thread);
+  const int ob = out1 ? out1_bytes_per_chunk : 0;  // no out1 buffer: nothing written there
+  const void* fn = ob == 8 ? pick<8>(chunks_per_thread)
+                   : ob == 4 ? pick<4>(chunks_per_thread)
+                             : pick<0>(chunks_per_thread);
   ProbeArgs a;
   a.in0 = static_cast<const u32x4*>(in0);
   a.in1 = static_cast<const u32x4*>(in1);
   a.out0 = static_cast<u32x4*>(out0);
-  a.out1 = out1_bytes_per_chunk ? static_cast<uint8_t*>(out1) : nullptr;
+  a.out1 = ob ? static_cast<uint8_t*>(out1) : nullptr;
   a.nch = hidden / 8;
   a.tpr = threads_per_row;
   void* args[] = {&a};

@@ -45,3 +45,36 @@ def test_probe_outputs(L, H, tpr, vpt, out1):
     else:
         ref = (x[..., 0] ^ x[..., 1] ^ x[..., 2] ^ x[..., 3])[..., None]
     assert torch.equal(d.data.view(torch.int32).view(T, H // 8, out1 // 4), ref)
+
+
+@pytest.mark.parametrize("with_in1,with_out0,out1", [(False, True, 0), (False, False, 8),
+                                                     (True, False, 4), (False, True, 8)])
+def test_probe_stream_subsets(L, with_in1, with_out0, out1):
+    """The probe with streams left out (a plain copy, codes-only output, ...): each present
+    output holds its function of the present inputs, and nothing else is written."""
+    T, H, tpr, vpt = 29, 2048, 128, 2
+    g = torch.Generator().manual_seed(7 + out1)
+    a = torch.randint(-2**31, 2**31 - 1, (T, H // 2), generator=g, dtype=torch.int32).cuda()
+    b = torch.randint(-2**31, 2**31 - 1, (T, H // 2), generator=g, dtype=torch.int32).cuda()
+    c = GH.Guarded(T * H * 2)
+    d = GH.Guarded(max(1, T * H * out1 // 8))
+    print(f"[probe] in1={with_in1} out0={with_out0} out1={out1}", flush=True)
+    st = L.rmsq_probe_stream(a.data_ptr(), b.data_ptr() if with_in1 else None,
+                             c.data.data_ptr() if with_out0 else None,
+                             d.data.data_ptr() if out1 else None, T, H, out1, tpr, vpt, None,
+                             None, torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    c.check("out0")
+    d.check("out1")
+    x = (a ^ b if with_in1 else a).view(T, H // 8, 4)
+    if with_out0:
+        assert torch.equal(c.data.view(torch.int32).view(T, H // 8, 4), x)
+    else:
+        assert torch.all(c.data == GH.FILL)
+    if out1 == 8:
+        ref = torch.stack([x[..., 0] ^ x[..., 2], x[..., 1] ^ x[..., 3]], dim=-1)
+        assert torch.equal(d.data.view(torch.int32).view(T, H // 8, 2), ref)
+    elif out1 == 4:
+        ref = (x[..., 0] ^ x[..., 1] ^ x[..., 2] ^ x[..., 3])[..., None]
+        assert torch.equal(d.data.view(torch.int32).view(T, H // 8, 1), ref)

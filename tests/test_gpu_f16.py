@@ -64,7 +64,7 @@ MODES = [(O.FP8_STATIC, 0, 0), (O.FP8_TOKEN, 0, 0), (O.FP8_GROUP, 128, 0),
 
 
 @pytest.mark.parametrize("mode,G,flags", MODES)
-@pytest.mark.parametrize("T,H", [(1, 4096), (37, 2048), (512, 4096), (64, 5120)])
+@pytest.mark.parametrize("T,H", [(1, 4096), (37, 2048), (512, 4096), (64, 5120), (1024, 2048)])
 def test_modes_and_shapes(mode, G, flags, T, H):
     x, r, w = _inputs(T, H, T * 7 + H)
     _check(mode, x, r, w, G=G, flags=flags)

@@ -94,7 +94,7 @@ def test_shapes(T, H, residual):
     check(x, r, w)
 
 
-@pytest.mark.parametrize("T,H", [(1, 2048), (37, 2048), (512, 4096)])
+@pytest.mark.parametrize("T,H", [(1, 2048), (37, 2048), (512, 4096), (1024, 2048)])
 def test_binary16(T, H):
     x, r, w = _inputs(T, H, T + H + 1, dtype=torch.float16)
     check(x, r, w)

@@ -82,7 +82,7 @@ def _fused_case(seed):
                 launch=launch, xb=xb, rb=rb, wb=wb)
 
 
-@pytest.mark.parametrize("seed", range(120))
+@pytest.mark.parametrize("seed", range(240))
 def test_random_fused(seed):
     c = _fused_case(9000 + seed)
     shape = None if c["launch"] is None else c["launch"].as_tuple()
@@ -110,7 +110,7 @@ def test_random_fused(seed):
             scale_in=c["scale"], raw_group_scales=raw)
 
 
-@pytest.mark.parametrize("seed", range(48))
+@pytest.mark.parametrize("seed", range(96))
 def test_random_silu_mul_quant(seed):
     rng = np.random.default_rng(9100 + seed)
     mode = int(rng.integers(0, 4))
@@ -218,7 +218,7 @@ def test_random_qk_norm_rope(seed):
     assert np.array_equal(got, ref)
 
 
-@pytest.mark.parametrize("seed", range(30))
+@pytest.mark.parametrize("seed", range(60))
 def test_random_fp4_dynamic(seed):
     rng = np.random.default_rng(9400 + seed)
     H = 16 * int(rng.integers(1, 512))

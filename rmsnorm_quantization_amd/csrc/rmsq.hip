@@ -391,13 +391,12 @@ int validate_pad(const void* x, const void* res, const void* w, float eps, const
 // kernel's rule.  Measured on MI355X for 2880 -> 3072 (4096 rows): 17.1 us against 18.3 us
 // for 192 threads x 2 chunks; equal at 4000 -> 4096; better at 2000 -> 2048.
 //
-// Binary16 activations take the one-wave shape only up to 5 chunks per lane: their conversions
-// keep more values live, and from 6 chunks per lane the kernel needs more than the 128 VGPRs a
-// 1024-thread launch bound allows and spills to scratch (2880 -> 3072, 4096 rows: 69 us at
-// 64 x 6 against 18.8 us at 192 x 2); longer binary16 rows take the quantizing kernel's rule.
+// Binary16 activations take the one-wave shape only up to 6 chunks per lane (4096 rows,
+// 2880 -> 3072: 17.6 us at 64 x 6 against 18.0 us at 192 x 2; 4000 -> 4096: 24.4 us at 64 x 8
+// against 23.9 us at 256 x 2); longer binary16 rows take the quantizing kernel's rule.
 rmsq_launch default_pad_launch(int64_t ld, unsigned flags) {
   const int64_t nch = ld / 8;
-  const int64_t max_chunks = (flags & RMSQ_INPUT_F16) ? 5 : 8;
+  const int64_t max_chunks = (flags & RMSQ_INPUT_F16) ? 6 : 8;
   if (nch > 128 && (nch + 63) / 64 <= max_chunks)
     return rmsq_launch{64, (int32_t)((nch + 63) / 64), 1, 0};
   return default_launch(ld);

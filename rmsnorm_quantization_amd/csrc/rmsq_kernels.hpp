@@ -297,7 +297,19 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
     ok[k] = EXACT || (row_ok && c < (uint32_t)nch);
     hv[k] = (u32x4){0u, 0u, 0u, 0u};
     rv[k] = (u32x4){0u, 0u, 0u, 0u};
-    if (ok[k]) {
+    if constexpr (DT == 1) {
+      // binary16: a masked chunk loads chunk 0 of the row (always present; row 0 for a row
+      // past T) and discards it.  Without a branch around the loads the binary16 instantiations
+      // stay within their register budget at many chunks per lane (with it, 6-8 chunks spill);
+      // bf16 keeps the branch, which measured faster for it.
+      const uint32_t cs = ok[k] ? c : 0u;
+      const u32x4 xl = __builtin_nontemporal_load(boff(xrow, cs << 4));
+      hv[k] = ok[k] ? xl : hv[k];
+      if constexpr (RES) {
+        const u32x4 rl = __builtin_nontemporal_load(boff(rrow, cs << 4));
+        rv[k] = ok[k] ? rl : rv[k];
+      }
+    } else if (ok[k]) {
       hv[k] = __builtin_nontemporal_load(boff(xrow, c << 4));
       if (RES) rv[k] = __builtin_nontemporal_load(boff(rrow, c << 4));
     }
@@ -306,7 +318,12 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
   for (int k = 0; k < VPT; ++k) {
     const uint32_t c = lr + (uint32_t)(k * tpr);
     wv[k] = (u32x4){0u, 0u, 0u, 0u};
-    if (ok[k]) wv[k] = *boff(wrow, c << 4);
+    if constexpr (DT == 1) {
+      const u32x4 wl = *boff(wrow, (ok[k] ? c : 0u) << 4);
+      wv[k] = ok[k] ? wl : wv[k];
+    } else if (ok[k]) {
+      wv[k] = *boff(wrow, c << 4);
+    }
   }
 
   // ---- residual add: h = round16(x + r), written back as the new residual ----
@@ -469,7 +486,13 @@ __global__ void __launch_bounds__(1024) silu_mul_kernel(AArgs a) {
     ok[k] = EXACT || (row_ok && c < (uint32_t)nch);
     gv[k] = (u32x4){0u, 0u, 0u, 0u};
     uv[k] = (u32x4){0u, 0u, 0u, 0u};
-    if (ok[k]) {
+    if constexpr (DT == 1) {  // binary16: branch-free masked loads, as in fused_kernel
+      const uint32_t cs = ok[k] ? c : 0u;
+      const u32x4 gl = __builtin_nontemporal_load(boff(grow, cs << 4));
+      const u32x4 ul = __builtin_nontemporal_load(boff(urow, cs << 4));
+      gv[k] = ok[k] ? gl : gv[k];
+      uv[k] = ok[k] ? ul : uv[k];
+    } else if (ok[k]) {
       gv[k] = __builtin_nontemporal_load(boff(grow, c << 4));
       uv[k] = __builtin_nontemporal_load(boff(urow, c << 4));
     }
@@ -530,7 +553,13 @@ __global__ void __launch_bounds__(1024) silu_mul_tile_kernel(AArgs a) {
     ok[k] = EXACT || c < (uint32_t)nch;
     gv[k] = (u32x4){0u, 0u, 0u, 0u};
     uv[k] = (u32x4){0u, 0u, 0u, 0u};
-    if (ok[k]) {
+    if constexpr (DT == 1) {  // binary16: branch-free masked loads, as in fused_kernel
+      const uint32_t cs = ok[k] ? c : 0u;
+      const u32x4 gl = __builtin_nontemporal_load(boff(grow, cs << 4));
+      const u32x4 ul = __builtin_nontemporal_load(boff(urow, cs << 4));
+      gv[k] = ok[k] ? gl : gv[k];
+      uv[k] = ok[k] ? ul : uv[k];
+    } else if (ok[k]) {
       gv[k] = __builtin_nontemporal_load(boff(grow, c << 4));
       uv[k] = __builtin_nontemporal_load(boff(urow, c << 4));
     }

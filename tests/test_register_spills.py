@@ -1,10 +1,8 @@
-"""No kernel instantiation of librmsq spills registers to scratch memory, except the binary16
-ones with masked chunks at many chunks per lane (fused_kernel with 6-8 chunks per lane and
-SiLU+Mul with 5-8, binary16, with a residual and an inexact fit): their binary16 conversions
-keep more values live than the 128 VGPRs a 1024-thread launch bound allows.  The default launch
-rules avoid those (the padded-output rule caps binary16 rows at 5 chunks per lane), so a spill
-anywhere else is a regression of speed, found here by compiling the instantiation tables for
-gfx950 with the compiler's resource report (no GPU needed)."""
+"""No kernel instantiation of librmsq spills registers to scratch memory.  A spill is a large
+loss of speed (a binary16 padded-output row at 6 chunks per lane once took 69 us instead of
+18 us), so every instantiation the tables define -- bf16 and binary16, exact and masked, 1 to 8
+chunks per lane -- is compiled for gfx950 with the compiler's resource report and checked (no
+GPU needed)."""
 import os
 import re
 import subprocess
@@ -33,24 +31,11 @@ def _report(src):
     return list(zip(names, scratch))
 
 
-def _allowed(name):
-    m = FUSED.search(name)
-    if m:
-        mode, res, vpt, gs, exact, dt = (int(g) for g in m.groups())
-        return dt == 1 and res == 1 and exact == 0 and vpt >= 6
-    m = SILU.search(name)
-    if m:
-        mode, vpt, gs, exact, dt = (int(g) for g in m.groups())
-        return dt == 1 and exact == 0 and vpt >= 5
-    return False
-
-
 @pytest.mark.slow
-def test_no_unexpected_register_spills():
+def test_no_register_spills():
     with ThreadPoolExecutor(max_workers=min(len(TABLES), os.cpu_count() or 1)) as ex:
         reports = list(ex.map(_report, TABLES))
+    names = [n for rep in reports for n, _ in rep]
+    assert any(FUSED.search(n) for n in names) and any(SILU.search(n) for n in names)
     spills = [(n, s) for rep in reports for n, s in rep if s > 0]
-    unexpected = [(n, s) for n, s in spills if not _allowed(n)]
-    assert not unexpected, f"instantiations spilling to scratch: {unexpected[:8]}"
-    # every bf16 instantiation is free of spills
-    assert all(not (FUSED.search(n) and FUSED.search(n).group(6) == "0") for n, _ in spills)
+    assert not spills, f"instantiations spilling to scratch: {spills[:8]}"

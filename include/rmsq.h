@@ -351,7 +351,8 @@ RMSQ_API int rmsq_qk_norm_rope_query_launch(int64_t tokens, int num_q_heads, int
                                             int* heads_per_lane, int64_t* grid);
 
 /* The launch shape rmsq_fused picks for (mode, T, H, group_size, residual?) and its grid size
- * (number of workgroups).  Host only; makes no HIP call.  Returns RMSQ_OK or RMSQ_EINVAL. */
+ * (number of workgroups); the same shape is the default of rmsq_fused_fp4_dynamic's first
+ * pass.  Host only; makes no HIP call.  Returns RMSQ_OK or RMSQ_EINVAL. */
 RMSQ_API int rmsq_query_launch(int mode, int64_t tokens, int64_t hidden, int group_size,
                                int has_residual, rmsq_launch* launch, int64_t* grid);
 

@@ -238,10 +238,16 @@ static float absmax(const float* y, int64_t n) {
 }
 
 /* ------------------------------------------------------------------ quantizers (one row) */
+/* The value an element's code is encoded from: the element times the reciprocal scale (FP8)
+ * or the block multiplier (FP4).  A zero element stays the zero it is, sign included, whatever
+ * the multiplier: scaling zero gives zero, also where the multiplier has overflowed to infinity
+ * (a scale below 1/FLT_MAX), where the literal product 0 * inf would be NaN. */
+static float scaled(float y, float mul) { return (y == 0.0f) ? y : y * mul; }
+
 static void quant_static(const float* y, int64_t H, float scale, uint8_t* q, float* pre) {
   float r = 1.0f / scale;
   for (int64_t i = 0; i < H; ++i) {
-    float v = y[i] * r;
+    float v = scaled(y[i], r);
     q[i] = orc_e4m3_encode(v);
     if (pre) pre[i] = v;
   }
@@ -268,7 +274,7 @@ static float quant_group_fp8(const float* y, int64_t n, int e8m0, uint8_t* q, fl
   }
   float r = 1.0f / s;
   for (int64_t i = 0; i < n; ++i) {
-    float v = y[i] * r;
+    float v = scaled(y[i], r);
     q[i] = orc_e4m3_encode(v);
     if (pre) pre[i] = v;
   }
@@ -288,7 +294,7 @@ static void quant_fp4(const float* y, int64_t H, float gs, uint8_t* qrow, uint8_
     if (d > 0.0f) {
       float m = gs / d;
       for (int i = 0; i < 16; ++i) {
-        float v = yb[i] * m;
+        float v = scaled(yb[i], m);
         codes[i] = orc_e2m1_encode(v);
         if (pre) pre[b * 16 + i] = v;
       }

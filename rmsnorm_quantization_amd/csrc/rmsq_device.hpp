@@ -105,6 +105,28 @@ __device__ __forceinline__ float fp8_decode(uint32_t byte) {
   return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
 }
 
+// ---- scaled values ---------------------------------------------------------------------------
+// True in every lane when p holds in some lane of the wave: a wave-uniform value, so a branch on
+// it is a scalar branch.  Must run with all lanes of the wave active.
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+// A multiplier that is not a finite binary32 value: a reciprocal scale (or an FP4 block
+// multiplier) that overflowed to infinity.
+__device__ __forceinline__ bool not_finite(float m) { return !(fabsf(m) <= __FLT_MAX__); }
+
+// The codes are encoded from y * m, where m is a reciprocal scale (or an FP4 block multiplier)
+// that overflows to infinity for a scale below 1/FLT_MAX.  There a non-zero y gives an infinity,
+// which saturates, but a zero y gives NaN, while scaling a zero gives that zero.  In such a lane,
+// (y * 2^64) * 2^100 takes the place of y * m: a zero stays the zero it is, sign included, and every
+// non-zero finite y ends at least 2^15 in magnitude (or infinite), past the largest code of either
+// format -- the same codes, with no select per element.  zero_safe rewrites y and m that way
+// where `inf` holds; callers evaluate the condition once per row or per chunk.
+__device__ __forceinline__ void zero_safe(float (&y)[8], float& m, bool inf) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = inf ? y[e] * 0x1p64f : y[e];
+  m = inf ? 0x1p100f : m;
+}
+
 // ---- FP4 e2m1 ----------------------------------------------------------------------------
 // Eight f32 -> eight e2m1 nibbles in one dword, element 2k in the low nibble of byte k
 // (v_cvt_scalef32_pk_fp4_f32 with a unit scale, so the instruction's scale does nothing; it

@@ -94,17 +94,23 @@ struct RowOut {
 //   per-token  s = absmax(row)/448, q = e4m3(y * (1/s)); s == 0 gives 0 codes
 //   per-group  s = absmax(group)/448 (E8M0: rounded up to a power of two), same rule
 //   FP4        sf = e4m3(absmax(block16) * gs / 6), q = e2m1(y * (gs / decode(sf)))
+// A zero element gives the zero code of its own sign in every scheme, also where the reciprocal
+// scale or the FP4 multiplier has overflowed to infinity (zero_safe).
 // DT (the 16-bit output type of the padded mode only): 0 bf16, 1 IEEE binary16.
 template <int MODE, int VPT, int GS, int DT = 0, class YF>
 __device__ __forceinline__ void quantize_store(const YF& Y, const bool (&ok)[VPT], const RowOut& o,
                                                float scale_val, float* s_mx) {
   if constexpr (MODE == RMSQ_FP8_STATIC) {
-    const float r = 1.0f / scale_val;
+    float r = 1.0f / scale_val;
+    const bool inf = wave_any(not_finite(r));  // uniform: one scale per launch
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
       float v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = Y(k, e) * r;
+      for (int e = 0; e < 8; ++e) v[e] = Y(k, e);
+      if (inf) zero_safe(v, r, true);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] *= r;
       const u32x2 qc = {fp8x4(v[0], v[1], v[2], v[3]), fp8x4(v[4], v[5], v[6], v[7])};
       if (ok[k]) {
         const uint32_t c = o.lr + (uint32_t)(k * o.tpr);
@@ -127,12 +133,16 @@ __device__ __forceinline__ void quantize_store(const YF& Y, const bool (&ok)[VPT
     const float s = mx / kFp8Max;
     if (o.lr == 0 && o.row_ok) static_cast<float*>(o.scales)[o.row] = s;
     const bool zero = (s == 0.0f);
-    const float r = zero ? 0.0f : 1.0f / s;
+    float r = zero ? 0.0f : 1.0f / s;
+    const bool inf = wave_any(not_finite(r));  // uniform: one scale per row
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
       float v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = Y(k, e) * r;
+      for (int e = 0; e < 8; ++e) v[e] = Y(k, e);
+      if (inf) zero_safe(v, r, true);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] *= r;
       u32x2 qc = {fp8x4(v[0], v[1], v[2], v[3]), fp8x4(v[4], v[5], v[6], v[7])};
       if (zero) qc = (u32x2){0u, 0u};
       if (ok[k]) {
@@ -160,7 +170,9 @@ __device__ __forceinline__ void quantize_store(const YF& Y, const bool (&ok)[VPT
       const bool zero = (s == 0.0f);
       uint32_t byte = 0;
       if (e8) byte = e8m0_ceil(s, &s);
-      const float r = 1.0f / s;
+      float r = 1.0f / s;
+      const bool inf = !zero && not_finite(r);
+      if (wave_any(inf)) zero_safe(y, r, inf);  // uniform over the wave
       u32x2 qc = {fp8x4(y[0] * r, y[1] * r, y[2] * r, y[3] * r),
                   fp8x4(y[4] * r, y[5] * r, y[6] * r, y[7] * r)};
       if (zero) qc = (u32x2){0u, 0u};
@@ -239,15 +251,13 @@ __device__ __forceinline__ void quantize_store(const YF& Y, const bool (&ok)[VPT
       // every lane takes part in the exchange, before any branch
       const float g = __int_as_float(
           __builtin_amdgcn_ds_bpermute((int)(((db >> 20) & 7u) << 2), __float_as_int(g_tab)));
-      uint32_t qc = 0u;
-      if (d > 0.0f) {
-        float mul;
-        if (by_table) mul = __builtin_amdgcn_ldexpf(g, 127 - (int)((db >> 23) & 0xFFu));
-        else mul = gs / d;
+      const bool live = d > 0.0f;  // a zero block scale gives zero codes
+      float mul = by_table ? __builtin_amdgcn_ldexpf(g, 127 - (int)((db >> 23) & 0xFFu)) : gs / d;
+      const bool inf = live && not_finite(mul);
+      if (wave_any(inf)) zero_safe(y, mul, inf);  // uniform over the wave
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] *= mul;
-        qc = fp4x8(y);
-      }
+      for (int e = 0; e < 8; ++e) y[e] *= mul;
+      const uint32_t qc = live ? fp4x8(y) : 0u;
       if (ok[k]) {
         *boff(reinterpret_cast<uint32_t*>(o.q + o.obase / 2), c << 2) = qc;
         if ((c & 1) == 0) static_cast<uint8_t*>(o.scales)[o.obase / 16 + c / 2] = (uint8_t)sf;
@@ -297,11 +307,12 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
     ok[k] = EXACT || (row_ok && c < (uint32_t)nch);
     hv[k] = (u32x4){0u, 0u, 0u, 0u};
     rv[k] = (u32x4){0u, 0u, 0u, 0u};
-    if constexpr (DT == 1) {
+    if constexpr (DT == 1 || (MODE == RMSQ_FP8_TOKEN && VPT >= 7)) {
       // binary16: a masked chunk loads chunk 0 of the row (always present; row 0 for a row
       // past T) and discards it.  Without a branch around the loads the binary16 instantiations
       // stay within their register budget at many chunks per lane (with it, 6-8 chunks spill);
-      // bf16 keeps the branch, which measured faster for it.
+      // bf16 keeps the branch, which measured faster for it, except for the per-token scheme at
+      // 7-8 chunks per lane (rows beyond 57344 elements), which needs the registers.
       const uint32_t cs = ok[k] ? c : 0u;
       const u32x4 xl = __builtin_nontemporal_load(boff(xrow, cs << 4));
       hv[k] = ok[k] ? xl : hv[k];

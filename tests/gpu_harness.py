@@ -120,12 +120,106 @@ def sample_rows(T, n=48, seed=0):
     return np.array(sorted(pick))
 
 
+def host_threads():
+    """Threads for the oracle on the host: the CPUs this process may use, at most 16 (one GPU's
+    share of a GPU host)."""
+    import os
+
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _spans(T, nthr):
+    step = max(1, -(-T // (4 * nthr)))
+    return [(lo, min(lo + step, T)) for lo in range(0, T, step)]
+
+
+def _join(parts, key, axis=0):
+    vals = [p[key] for p in parts]
+    if vals[0] is None:
+        return None
+    return np.concatenate(vals, axis=axis)
+
+
+def oracle_threaded(mode, xb, rb, wb, eps, scale_in=0.0, group_size=0, flags=0, want_pre=True):
+    """The oracle over every row of a batch, rows split over host_threads() threads (the oracle
+    is C called through ctypes, which releases the GIL).  Rows are independent, so the result is
+    the whole-batch call's; column-major scales come back [H/G, T]."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    T = xb.shape[0]
+    spans = _spans(T, host_threads())
+
+    def run_span(sp):
+        lo, hi = sp
+        return O.fused(xb[lo:hi], None if rb is None else rb[lo:hi], wb, eps, mode,
+                       scale_in=scale_in, group_size=group_size, flags=flags, want_pre=want_pre)
+
+    with ThreadPoolExecutor(max_workers=host_threads()) as ex:
+        parts = list(ex.map(run_span, spans))
+    col = mode == O.FP8_GROUP and bool(flags & O.SCALE_COLMAJOR)
+    return {"q": _join(parts, "q"), "scales": _join(parts, "scales", axis=1 if col else 0),
+            "residual_out": _join(parts, "residual_out"), "pre": _join(parts, "pre")}
+
+
+def oracle_act_threaded(mode, xb, scale_in=0.0, group_size=0, flags=0, want_pre=True):
+    """SiLU+Mul -> quant by the oracle over every row, split over host threads."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    T = xb.shape[0]
+
+    def run_span(sp):
+        lo, hi = sp
+        return O.silu_mul_quant(xb[lo:hi], mode, scale_in=scale_in, group_size=group_size,
+                                flags=flags, want_pre=want_pre)
+
+    with ThreadPoolExecutor(max_workers=host_threads()) as ex:
+        parts = list(ex.map(run_span, _spans(T, host_threads())))
+    col = mode == O.FP8_GROUP and bool(flags & O.SCALE_COLMAJOR)
+    return {"q": _join(parts, "q"), "scales": _join(parts, "scales", axis=1 if col else 0),
+            "residual_out": None, "pre": _join(parts, "pre")}
+
+
+def rms_y_threaded(xb, rb, wb, eps, f16=False):
+    """The oracle's normalized rows y over every row, split over host threads."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    T = xb.shape[0]
+
+    def run_span(sp):
+        lo, hi = sp
+        return O.rms_y(xb[lo:hi], None if rb is None else rb[lo:hi], wb, eps, f16=f16)
+
+    with ThreadPoolExecutor(max_workers=host_threads()) as ex:
+        return np.concatenate(list(ex.map(run_span, _spans(T, host_threads()))), axis=0)
+
+
 def oracle_on_rows(mode, xb, rb, wb, eps, rows, scale_in=0.0, group_size=0, flags=0):
     """Oracle outputs for the given rows (col-major scales come back [H/G, len(rows)])."""
     xs = xb if rows is None else xb[rows]
     rs = None if rb is None else (rb if rows is None else rb[rows])
     return O.fused(xs, rs, wb, eps, mode, scale_in=scale_in, group_size=group_size,
                    flags=flags, want_pre=True)
+
+
+def y_ref_norm(xb, rb, wb, eps, rows=None, f16=False):
+    """The y_ref callback of tests.parity.compare for a norm launch: the oracle's normalized f32
+    rows for row indices into the compared arrays (into `rows` when only those were compared)."""
+    def f(idx):
+        sel = np.asarray(idx) if rows is None else np.asarray(rows)[np.asarray(idx)]
+        return O.rms_y(xb[sel], None if rb is None else rb[sel], wb, eps, f16=f16)
+    return f
+
+
+def y_ref_act(xb, rows=None, f16=False):
+    """The y_ref callback of tests.parity.compare for SiLU+Mul: the oracle's activation rows."""
+    def f(idx):
+        sel = np.asarray(idx) if rows is None else np.asarray(rows)[np.asarray(idx)]
+        return O.silu_mul(xb[sel], f16=f16)
+    return f
 
 
 def run_act(mode, x, scale_in=None, group_size=0, flags=0, scale_ld=0, launch=None, rows=None):

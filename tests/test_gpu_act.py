@@ -18,7 +18,6 @@ from tests import gpu_harness as GH
 from tests.parity import compare
 
 pytestmark = pytest.mark.gpu
-FULL_LIMIT = 600_000
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -39,21 +38,20 @@ def static_scale():
 
 
 def _check(T, I, mode, scale_in=0.0, G=0, flags=0, launch=None, xb=None, xd=None):
+    """Every row compared; the oracle's rows split over the host's threads."""
     if xd is None:
         xd, xb = act_inputs(T, I)
-    rows = None if T * I <= FULL_LIMIT else GH.sample_rows(T)
-    print(f"[act] T={T} I={I} mode={mode} G={G} flags={flags} rows="
-          f"{'all' if rows is None else len(rows)}", flush=True)
+    print(f"[act] T={T} I={I} mode={mode} G={G} flags={flags} rows=all", flush=True)
     gpu = GH.run_act(mode, xd, scale_in=scale_in if mode in (O.FP8_STATIC, O.FP4_BLOCK16) else None,
-                     group_size=G, flags=flags, launch=launch, rows=rows)
-    xs = xb if rows is None else xb[rows]
-    ref = O.silu_mul_quant(xs, mode, scale_in=scale_in, group_size=G, flags=flags, want_pre=True)
+                     group_size=G, flags=flags, launch=launch)
+    ref = GH.oracle_act_threaded(mode, xb, scale_in=scale_in, group_size=G, flags=flags)
     raw = None
-    if mode == O.FP8_GROUP and flags & (O.SCALE_E8M0 | O.SCALE_E8M0_U8):
-        raw = O.silu_mul_quant(xs, mode, group_size=G, flags=flags & O.SCALE_COLMAJOR)["scales"]
-    n = T if rows is None else len(rows)
-    rep = compare(mode, gpu, ref, T=n, H=I, group_size=G, flags=flags, scale_in=scale_in,
-                  raw_group_scales=raw)
+    if (mode == O.FP8_GROUP and flags & (O.SCALE_E8M0 | O.SCALE_E8M0_U8)
+            and not np.array_equal(gpu["scales"], ref["scales"])):
+        raw = GH.oracle_act_threaded(mode, xb, group_size=G, flags=flags & O.SCALE_COLMAJOR,
+                                     want_pre=False)["scales"]
+    rep = compare(mode, gpu, ref, T=T, H=I, group_size=G, flags=flags, scale_in=scale_in,
+                  raw_group_scales=raw, y_ref=GH.y_ref_act(xb))
     print(f"[act]   {rep}", flush=True)
     return gpu, rep
 

@@ -52,7 +52,7 @@ def _run_and_compare(mode, x, r, w, eps=1e-6, scale_in=0.0, G=0, flags=0, ld=0, 
         if flags & O.SCALE_COLMAJOR and ld:
             raw = raw[:, :T]
     rep = compare(mode, gpu, ref, T=T, H=H, group_size=G, flags=flags, scale_in=scale_in,
-                  raw_group_scales=raw)
+                  raw_group_scales=raw, y_ref=GH.y_ref_norm(xb, rb, wb, eps))
     if exact:
         assert rep.code_mismatch == 0 and rep.scale_mismatch == 0, str(rep)
     return gpu, ref
@@ -233,25 +233,95 @@ def test_timed_launch_matches_and_stamps_events():
         assert torch.equal(a, b)
 
 
+def _tiny_with_zeros(T, H, seed):
+    """Rows of magnitude ~3e-40 (with eps = 1e-4 the normalized values stay ~3e-38, so every
+    row's and group's absmax/448 is a subnormal whose reciprocal overflows) with exact +0 and
+    -0 scattered in them."""
+    g = torch.Generator().manual_seed(seed)
+    x = (torch.randn((T, H), generator=g) * 3e-40).to(torch.bfloat16)
+    u = torch.rand((T, H), generator=g)
+    x[u < 0.05] = 0.0
+    x[(u >= 0.05) & (u < 0.10)] = -0.0
+    w = (torch.rand((H,), generator=g) + 0.5).to(torch.bfloat16)
+    return x, w
+
+
 @pytest.mark.parametrize("mode,G", [(O.FP8_TOKEN, 0), (O.FP8_GROUP, 128), (O.FP8_GROUP, 64)])
 def test_scale_whose_reciprocal_overflows(mode, G):
-    """Rows so small that absmax/448 is a subnormal below 1/FLT_MAX: 1/s is +infinity, so every
-    non-zero element saturates (bit-exact on both sides, as are the scales), while an exact zero
-    becomes 0 * inf = NaN -- the oracle's literal encoding gives the NaN code, the kernel's clamp
-    a saturated code.  Those zeros are outside the contract; everything else is compared."""
-    g = torch.Generator().manual_seed(21)
-    x = (torch.randn((4, 1024), generator=g)).to(torch.bfloat16) * 3e-40
-    w = (torch.rand((1024,), generator=g) + 0.5).to(torch.bfloat16)
+    """Rows so small that absmax/448 is a subnormal below 1/FLT_MAX: 1/s is +infinity, every
+    non-zero element saturates and every zero keeps the zero code of its sign.  Every code and
+    scale is compared bit for bit with the oracle."""
+    x, w = _tiny_with_zeros(4, 1024, seed=21)
     xb, wb = synth.bits(x), synth.bits(w)
     print(f"[edge] reciprocal overflow mode={mode} G={G}", flush=True)
-    gpu = GH.run(mode, GH.to_dev(x), None, GH.to_dev(w), 1e-6, group_size=G)
-    ref = O.fused(xb, None, wb, 1e-6, mode, group_size=G)
+    gpu = GH.run(mode, GH.to_dev(x), None, GH.to_dev(w), 1e-4, group_size=G)
+    ref = O.fused(xb, None, wb, 1e-4, mode, group_size=G)
+    s = ref["scales"].astype(np.float32)
+    with np.errstate(divide="ignore", over="ignore"):
+        assert np.all(np.isinf(np.float32(1) / s[s > 0]))  # the case under test
+    assert ((xb & 0x7FFF) == 0).any()
     assert np.array_equal(gpu["scales"], ref["scales"])
-    y = O.rms_y(xb, None, wb, 1e-6)
-    nan = (ref["q"] & 0x7F) == 0x7F  # the oracle's NaN codes: zeros of rows/groups with 1/s = inf
-    assert nan.any() and np.all(y[nan] == 0)
-    assert np.all((gpu["q"][nan] & 0x7F) == 0x7E)
-    assert np.array_equal(gpu["q"][~nan], ref["q"][~nan])
+    assert np.array_equal(gpu["q"], ref["q"])
+
+
+def test_static_scale_whose_reciprocal_overflows():
+    """A static scale below 1/FLT_MAX (the smallest subnormal): every non-zero element saturates,
+    every zero (+0 and -0) keeps its signed zero code; all codes bit-exact."""
+    x, r, w = _inputs(8, 1024, seed=24)
+    x[:, ::7] = 0.0
+    x[:, 3::11] = -0.0
+    print("[edge] static scale 1e-45", flush=True)
+    gpu, ref = _run_and_compare(O.FP8_STATIC, x, None, w, scale_in=float(np.float32(1e-45)))
+    assert np.array_equal(gpu["q"], ref["q"])
+    assert ((ref["q"] & 0x7F) == 0).any() and ((ref["q"] & 0x7F) == 0x7E).any()
+
+
+def test_fp4_multiplier_overflow_keeps_zero_codes():
+    """FP4 with a global scale near FLT_MAX over tiny rows with zeros (eps = 1 keeps y ~1e-39, so
+    the block scales come out ~0.05 and gs / decode(sf) overflows): non-zero elements take the
+    +-6 code and zeros their signed zero code; bit-exact."""
+    x, w = _tiny_with_zeros(8, 1024, seed=25)
+    xb, wb = synth.bits(x), synth.bits(w)
+    eps = 1.0
+    y = O.rms_y(xb, None, wb, eps)
+    gs = float(np.float32(3.0e38))
+    print("[edge] FP4 multiplier overflow", flush=True)
+    gpu = GH.run(O.FP4_BLOCK16, GH.to_dev(x), None, GH.to_dev(w), eps, scale_in=gs,
+                 group_size=16)
+    ref = O.fused(xb, None, wb, eps, O.FP4_BLOCK16, scale_in=gs, group_size=16)
+    d = O.e4m3_decode(ref["scales"]).astype(np.float32)
+    with np.errstate(divide="ignore", over="ignore"):
+        assert np.isinf(np.float32(gs) / d[d > 0]).any()  # the case under test
+    assert (y == 0).any()
+    assert np.array_equal(gpu["scales"], ref["scales"])
+    assert np.array_equal(gpu["q"], ref["q"])
+
+
+@pytest.mark.parametrize("mode,G", [(O.FP8_STATIC, 0), (O.FP8_TOKEN, 0), (O.FP8_GROUP, 128)])
+def test_silu_mul_reciprocal_overflow_keeps_zero_codes(mode, G):
+    """SiLU+Mul rows whose activations are ~2e-38 or exactly zero (gate 0): the reciprocal scale
+    overflows (dynamic schemes) or the static scale is the smallest subnormal; bit-exact.  A gate
+    of 64 makes silu exact on both sides (exp(-64) vanishes next to 1), so a = 64 * up exactly."""
+    g = torch.Generator().manual_seed(26)
+    T, I = 4, 1024
+    gate = torch.full((T, I), 64.0).to(torch.bfloat16)
+    gate[:, ::5] = 0.0
+    gate[:, 2::9] = -0.0
+    up = (torch.randn((T, I), generator=g) * 3e-40).to(torch.bfloat16)
+    x = torch.cat([gate, up], dim=1).contiguous()
+    xb = synth.bits(x)
+    s_in = float(np.float32(1e-45)) if mode == O.FP8_STATIC else None
+    print(f"[edge] SiLU+Mul reciprocal overflow mode={mode} G={G}", flush=True)
+    gpu = GH.run_act(mode, GH.to_dev(x), scale_in=s_in, group_size=G)
+    ref = O.silu_mul_quant(xb, mode, scale_in=s_in or 0.0, group_size=G)
+    a = O.silu_mul(xb)
+    assert (a == 0).any()
+    if mode != O.FP8_STATIC:
+        s = ref["scales"].astype(np.float32)
+        with np.errstate(divide="ignore", over="ignore"):
+            assert np.all(np.isinf(np.float32(1) / s[s > 0]))
+        assert np.array_equal(gpu["scales"], ref["scales"])
+    assert np.array_equal(gpu["q"], ref["q"])
 
 
 @pytest.mark.parametrize("gs", [1e-31, 1e-29, 1e-3, 7.0, 300.0, 1e10, 1e30, 3.0e38])

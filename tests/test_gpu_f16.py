@@ -55,7 +55,7 @@ def _check(mode, x, r, w, eps=1e-6, G=0, flags=0, launch=None, scale=None):
         raw = O.fused(xb, rb, wb, eps, mode, group_size=G,
                       flags=flags & (O.SCALE_COLMAJOR | F16))["scales"]
     return compare(mode, gpu, ref, T=T, H=H, group_size=G, flags=flags, scale_in=scale,
-                   raw_group_scales=raw)
+                   raw_group_scales=raw, y_ref=GH.y_ref_norm(xb, rb, wb, eps, f16=True))
 
 
 MODES = [(O.FP8_STATIC, 0, 0), (O.FP8_TOKEN, 0, 0), (O.FP8_GROUP, 128, 0),
@@ -140,7 +140,7 @@ def test_silu_mul_quant(mode, G, flags, T, I):
         raw = O.silu_mul_quant(xb, mode, group_size=G,
                                flags=flags & (O.SCALE_COLMAJOR | F16))["scales"]
     compare(mode, gpu, ref, T=T, H=I, group_size=G, flags=flags, scale_in=scale,
-            raw_group_scales=raw)
+            raw_group_scales=raw, y_ref=GH.y_ref_act(xb, f16=True))
 
 
 def test_silu_flag_selects_the_type():

@@ -78,8 +78,11 @@ def check(x, r, w, **kw):
     T, H = x.shape
     assert gpu["global_scale"].view(np.uint32) == ref["global_scale"].view(np.uint32), (
         gpu["global_scale"], ref["global_scale"])
+    eps = kw.get("eps", 1e-6)
     compare(O.FP4_BLOCK16, gpu, ref, T=T, H=H, group_size=16,
-            scale_in=float(ref["global_scale"]))
+            scale_in=float(ref["global_scale"]),
+            y_ref=GH.y_ref_norm(_bits(x), _bits(r), _bits(w), eps,
+                                f16=x.dtype == torch.float16))
     return gpu, ref
 
 

@@ -107,7 +107,9 @@ def test_random_fused(seed):
         if raw is not None:
             raw = raw[:, :c["T"]]
     compare(c["mode"], gpu, ref, T=c["T"], H=c["H"], group_size=c["G"], flags=c["flags"],
-            scale_in=c["scale"], raw_group_scales=raw)
+            scale_in=c["scale"], raw_group_scales=raw,
+            y_ref=GH.y_ref_norm(c["xb"], c["rb"], c["wb"], c["eps"],
+                                f16=bool(c["flags"] & O.INPUT_F16)))
 
 
 @pytest.mark.parametrize("seed", range(96))
@@ -140,7 +142,7 @@ def test_random_silu_mul_quant(seed):
     if mode == O.FP8_GROUP and flags & O.SCALE_E8M0:
         raw = O.silu_mul_quant(xb, mode, group_size=G, flags=flags & O.SCALE_COLMAJOR)["scales"]
     compare(mode, gpu, ref, T=T, H=I, group_size=G, flags=flags, scale_in=scale,
-            raw_group_scales=raw)
+            raw_group_scales=raw, y_ref=GH.y_ref_act(xb))
 
 
 @pytest.mark.parametrize("seed", range(30))
@@ -255,4 +257,5 @@ def test_random_fp4_dynamic(seed):
            grs.data.view(torch.int16).cpu().numpy().view(np.uint16).reshape(T, H)}
     if grs is not None:
         grs.check("residual_out")
-    compare(O.FP4_BLOCK16, gpu, ref, T=T, H=H, group_size=16, scale_in=float(gs))
+    compare(O.FP4_BLOCK16, gpu, ref, T=T, H=H, group_size=16, scale_in=float(gs),
+            y_ref=GH.y_ref_norm(xb, rb, wb, 1e-6, f16=bool(flags & O.INPUT_F16)))

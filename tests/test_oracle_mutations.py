@@ -52,6 +52,10 @@ MUTANTS = [
      "ib = neox ? (i + D / 2 + 1) % D : 2 * i + 1;", 0),
     ("SiLU sign", "(1.0 + exp(-gd))", "(1.0 + exp(gd))", 0),
     ("batch FP4 scale without the e2m1 maximum", "(448.0f * 6.0f) / amax", "448.0f / amax", 0),
+    ("zero element times an infinite multiplier", "return (y == 0.0f) ? y : y * mul;",
+     "return y * mul;", 0),
+    ("FP4 elements truncated toward zero", "codes[i] = orc_e2m1_encode(v);",
+     "codes[i] = orc_e2m1_encode(truncf(v * 2.0f) * 0.5f);", 0),
 ]
 
 

@@ -233,6 +233,33 @@ def test_half_step_invariant(orc, mode):
     assert np.all(err[~sat] <= bound[~sat])
 
 
+def test_fp4_half_step_invariant(orc):
+    """Round to nearest, in the units of the data: every non-saturated FP4 element's dequantized
+    value e2m1(q) * d / gs lies within half the e2m1 gap on y's side of the code (the distance
+    to the next magnitude above when y is beyond the code, to the one below when y is short of
+    it) times d / gs, plus the rounding of y * (gs / d) itself."""
+    x, r, w, y = _workload_y(orc, 8, 2048, seed=37)
+    gs = np.float32(448 * 6) / np.abs(y).max() * np.float32(0.8)  # some blocks saturate
+    out = orc.fused(x, r, w, 1e-6, orc.FP4_BLOCK16, scale_in=float(gs), group_size=16)
+    mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float64)
+    nib = orc.unpack_fp4(out["q"]).reshape(8, 128, 16)
+    code = (nib & 7).astype(np.int64)
+    sign = np.where(nib & 8, -1.0, 1.0)
+    unit = (orc.e4m3_decode(out["scales"]).astype(np.float64) / np.float64(gs))[:, :, None]
+    dq = sign * mags[code] * unit
+    yb = y.reshape(8, 128, 16).astype(np.float64)
+    beyond = np.abs(yb) > mags[code] * unit  # |y| past the code's magnitude
+    above = mags[np.minimum(code + 1, 7)] - mags[code]
+    below = mags[code] - mags[np.maximum(code - 1, 0)]
+    half = 0.5 * np.where(beyond, above, below) * unit
+    sat = (code == 7) & beyond
+    live = unit > 0
+    err = np.abs(dq - yb)
+    bound = half + np.abs(yb) * 2.0 ** -22
+    ok = sat | ~np.broadcast_to(live, yb.shape) | (err <= bound)
+    assert sat.any() and np.all(ok), f"{int((~ok).sum())} elements off by more than half a step"
+
+
 def test_zero_residual_equals_plain(orc):
     rng = np.random.default_rng(41)
     T, H = 4, 384
@@ -286,6 +313,74 @@ def test_zero_row_gives_zero_codes(orc):
     assert np.all(gp["q"] == 0) and np.all(gp["scales"] == 0)  # E8M0 byte 0 = 2^-127
     f4 = orc.fused(x, None, w, 1e-6, orc.FP4_BLOCK16, scale_in=10.0, group_size=16)
     assert np.all(f4["q"] == 0) and np.all(f4["scales"] == 0)
+
+
+# ------------------------------------------------------------------ zero elements
+# Reading: scaling a zero element gives that zero, sign included, in every scheme -- also where
+# the reciprocal scale (or the FP4 block multiplier) has overflowed to +infinity, where the
+# literal product 0 * inf would be NaN.  The expected codes below come from that definition
+# alone: the zero code with the element's sign for a zero, the saturated code for everything
+# else (a non-zero element times an infinite multiplier).
+def _tiny_rows_with_zeros(T, H, seed):
+    """bf16 rows of magnitude ~3e-40 with exact +0 and -0 scattered in them.  With eps = 1e-4 the
+    mean of squares is negligible, so y stays ~3e-38 and absmax/448 is a subnormal far below
+    1/FLT_MAX."""
+    rng = np.random.default_rng(seed)
+    x = bf16_bits(rng.standard_normal((T, H)).astype(np.float32) * np.float32(3e-40))
+    u = rng.random((T, H))
+    x[u < 0.05] = 0x0000
+    x[(u >= 0.05) & (u < 0.10)] = 0x8000
+    return x
+
+
+def _expected_saturated(x_bits, zero_code, sat_code, sign_bit):
+    zero = (x_bits & 0x7FFF) == 0
+    neg = (x_bits & 0x8000) != 0
+    return np.where(zero, zero_code, sat_code) | np.where(neg, sign_bit, 0)
+
+
+@pytest.mark.parametrize("mode,G", [("token", 0), ("group", 64), ("group", 128)])
+def test_zero_elements_keep_zero_code_when_reciprocal_overflows(orc, mode, G):
+    T, H = 4, 512
+    x = _tiny_rows_with_zeros(T, H, seed=61 + G)
+    w = bf16_bits(np.random.default_rng(62).uniform(0.5, 1.5, H))
+    m = orc.FP8_TOKEN if mode == "token" else orc.FP8_GROUP
+    out = orc.fused(x, None, w, 1e-4, m, group_size=G)
+    s = out["scales"].astype(np.float32)
+    with np.errstate(divide="ignore", over="ignore"):
+        assert np.all(np.isinf(np.float32(1) / s)) and np.all(s > 0)  # the case under test
+    assert np.array_equal(out["q"], _expected_saturated(x, 0x00, 0x7E, 0x80))
+
+
+def test_zero_elements_with_static_scale_below_reciprocal_range(orc):
+    rng = np.random.default_rng(63)
+    T, H = 3, 256
+    x = bf16_bits(rng.standard_normal((T, H)))
+    x[:, ::7] = 0x0000
+    x[:, 3::11] = 0x8000
+    w = bf16_bits(rng.uniform(0.5, 1.5, H))
+    scale = np.float32(1e-45)  # the smallest subnormal: 1/scale is +infinity
+    with np.errstate(divide="ignore", over="ignore"):
+        assert np.isinf(np.float32(1) / scale)
+    out = orc.fused(x, None, w, 1e-6, orc.FP8_STATIC, scale_in=float(scale))
+    assert np.array_equal(out["q"], _expected_saturated(x, 0x00, 0x7E, 0x80))
+
+
+def test_zero_elements_with_fp4_multiplier_overflow(orc):
+    """FP4 block of +-2^-127 with zeros, gs = 1.5 * 2^127: (a * gs) / 6 = 0.25 exactly, so the
+    block scale is e4m3 0.25 (byte 0x28) and gs / 0.25 = 1.5 * 2^129 overflows."""
+    H = 32
+    y = np.full(H, np.ldexp(np.float32(1), -127), np.float32)
+    y[1::2] = -y[1::2]
+    y[[2, 9, 20]] = 0.0
+    y[[5, 30]] = -0.0
+    gs = np.float32(1.5) * np.ldexp(np.float32(1), 127)
+    q, sf, _ = orc.quantize_row(y, orc.FP4_BLOCK16, scale_in=float(gs), group_size=16)
+    assert np.all(sf == 0x28)
+    nib = orc.unpack_fp4(q)
+    zero = y == 0
+    exp = np.where(zero, 0x0, 0x7) | np.where(np.signbit(y), 0x8, 0x0)
+    assert np.array_equal(nib, exp)
 
 
 def test_empty_and_invalid(orc):

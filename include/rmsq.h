@@ -24,11 +24,17 @@
  *   RMSQ_FP4_BLOCK16  per 16-element block: sf = e4m3(absmax * gs / 6), d = decode(sf),
  *                     q = e2m1(y * (gs / d)), 0 codes when d == 0; gs = *scale_in, the global
  *                     encode scale (dequant: value = e2m1 * d / gs)
+ * In every mode a zero element (y = +0 or -0) gives the zero code of its sign, also where the
+ * reciprocal scale 1/s or the FP4 multiplier gs/d overflows to infinity (a scale below
+ * 1/FLT_MAX); every other element times an infinite multiplier saturates.
  *
  * Ownership and threading: the caller owns every buffer.  The library never allocates, frees
  * or synchronizes; work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and all
  * pointers except where noted are DEVICE pointers.  Argument errors are returned synchronously
  * before anything is enqueued.  No C++ exception crosses this boundary.  Calls are thread-safe.
+ * Library state: one process-wide table remembers, per HIP device index below 64, whether that
+ * device is a gfx950 (read with hipGetDeviceProperties by the first call that launches on it;
+ * devices at index 64 and above are queried on every call).  Nothing else is kept between calls.
  */
 #ifndef RMSQ_H
 #define RMSQ_H
@@ -45,9 +51,10 @@ extern "C" {
 #define RMSQ_API
 #endif
 
-/* 3: rmsq_rms_norm_pad_query_launch takes the call's flags (the default shape depends on the
+/* 4: rmsq_query_launch takes the call's flags in place of a residual flag it never used;
+ * 3: rmsq_rms_norm_pad_query_launch takes the call's flags (the default shape depends on the
  *    activation type); 2: the padding and QK-norm + RoPE entry points take flags. */
-#define RMSQ_ABI_VERSION 3
+#define RMSQ_ABI_VERSION 4
 #define RMSQ_MAX_HIDDEN 65536 /* largest H one workgroup keeps in registers */
 
 /* ---- status codes ---- */
@@ -350,11 +357,14 @@ RMSQ_API int rmsq_qk_norm_rope_query_launch(int64_t tokens, int num_q_heads, int
                                             int head_dim, int* heads_per_block,
                                             int* heads_per_lane, int64_t* grid);
 
-/* The launch shape rmsq_fused picks for (mode, T, H, group_size, residual?) and its grid size
+/* The launch shape rmsq_fused picks for (mode, T, H, group_size, flags) and its grid size
  * (number of workgroups); the same shape is the default of rmsq_fused_fp4_dynamic's first
- * pass.  Host only; makes no HIP call.  Returns RMSQ_OK or RMSQ_EINVAL. */
+ * pass.  The arguments are checked as rmsq_fused checks them (flags: RMSQ_SCALE_* for
+ * FP8_GROUP, RMSQ_INPUT_F16 in any mode).  The shape depends on T and H only: it is the same
+ * with and without a residual and for either activation type.  Host only; makes no HIP call.
+ * Returns RMSQ_OK, RMSQ_EINVAL or RMSQ_EUNSUPPORTED (a flag the mode does not take). */
 RMSQ_API int rmsq_query_launch(int mode, int64_t tokens, int64_t hidden, int group_size,
-                               int has_residual, rmsq_launch* launch, int64_t* grid);
+                               unsigned flags, rmsq_launch* launch, int64_t* grid);
 
 /* The launch shape rmsq_rms_norm_pad picks for (T, H, out_ld, flags) and its grid size: flags
  * as passed to rmsq_rms_norm_pad (0 or RMSQ_INPUT_F16; the default shape depends on the

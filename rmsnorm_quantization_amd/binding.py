@@ -35,7 +35,7 @@ RMSQ_CVT_E4M3, RMSQ_CVT_E2M1, RMSQ_CVT_BF16, RMSQ_CVT_INV_SQRT = 0, 1, 2, 3
 RMSQ_LAUNCH_XCD_RANGES = 1
 RMSQ_LAUNCH_ROW_TILES = 2
 RMSQ_MAX_HIDDEN = 65536
-RMSQ_ABI_VERSION = 3  # the argument lists below are those of this version
+RMSQ_ABI_VERSION = 4  # the argument lists below are those of this version
 
 
 class RmsqError(RuntimeError):
@@ -105,7 +105,7 @@ def lib():
         L.rmsq_qk_norm_rope_query_launch.argtypes = [i64, i32, i32, i32, C.POINTER(i32),
                                                      C.POINTER(i32), C.POINTER(i64)]
         L.rmsq_qk_norm_rope_query_launch.restype = i32
-        L.rmsq_query_launch.argtypes = [i32, i64, i64, i32, i32, C.POINTER(rmsq_launch),
+        L.rmsq_query_launch.argtypes = [i32, i64, i64, i32, u32, C.POINTER(rmsq_launch),
                                         C.POINTER(i64)]
         L.rmsq_query_launch.restype = i32
         L.rmsq_rms_norm_pad_query_launch.argtypes = [i64, i64, i64, u32,
@@ -143,6 +143,63 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+# ---- argument checks on tensors (raw integer pointers are the caller's responsibility) --------
+# Everything below runs before any pointer is taken: a tensor that cannot hold what the call
+# reads or writes raises ValueError instead of becoming an out-of-bounds access on the GPU.
+def _need(t, what: str, nbytes: int, kind: str):
+    """t (a tensor; None and integers are not checked) must be of `kind` and hold nbytes:
+    "act" 16-bit activations (any 2-byte type: the call's RMSQ_INPUT_F16 flag, not the tensor's
+    dtype, says whether the bits are bf16 or binary16), "f32", "i64", "byte" (any 1-byte
+    type)."""
+    if not isinstance(t, torch.Tensor):
+        return
+    if kind == "act" and t.element_size() != 2:
+        raise ValueError(f"rmsq: {what} must have 16-bit elements (bfloat16 or float16), "
+                         f"not {t.dtype}")
+    elif kind == "f32" and t.dtype != torch.float32:
+        raise ValueError(f"rmsq: {what} must be float32, not {t.dtype}")
+    elif kind == "i64" and t.dtype != torch.int64:
+        raise ValueError(f"rmsq: {what} must be int64, not {t.dtype}")
+    elif kind == "byte" and t.element_size() != 1:
+        raise ValueError(f"rmsq: {what} must have 1-byte elements, not {t.dtype}")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"rmsq: {what} holds {have} bytes, the call needs {nbytes}")
+
+
+def _rows_cols(t, what: str, rows, cols, cols_of=lambda c: c):
+    """(rows, cols) of a call whose sizes default to a 2-D tensor's shape."""
+    if rows is not None and cols is not None:
+        return int(rows), int(cols)
+    if not isinstance(t, torch.Tensor) or t.dim() != 2:
+        raise ValueError(f"rmsq: {what} must be a 2-D tensor, or pass the sizes explicitly")
+    return int(t.shape[0] if rows is None else rows), int(cols_of(t.shape[1]) if cols is None
+                                                         else cols)
+
+
+def _scale_nbytes(mode, T, n, group_size, flags, ld) -> int:
+    """Bytes of the scales output of a quantization of T rows of n values."""
+    if mode == RMSQ_FP8_TOKEN:
+        return 4 * T
+    if mode == RMSQ_FP8_GROUP and group_size in (64, 128) and T > 0:
+        ng = n // group_size
+        el = 1 if flags & RMSQ_SCALE_E8M0_U8 else 4
+        if flags & RMSQ_SCALE_COLMAJOR:
+            return ((ng - 1) * (ld or T) + T) * el
+        return T * ng * el
+    if mode == RMSQ_FP4_BLOCK16:
+        return T * (n // 16)
+    return 0
+
+
+def _check_quant_outputs(mode, scale_in, out_q, out_scales, T, n, group_size, flags, ld):
+    _need(scale_in, "scale_in", 4, "f32")
+    _need(out_q, "out_q", T * n // 2 if mode == RMSQ_FP4_BLOCK16 else T * n, "byte")
+    sb = _scale_nbytes(mode, T, n, group_size, flags, ld)
+    f32 = mode == RMSQ_FP8_TOKEN or (mode == RMSQ_FP8_GROUP and not flags & RMSQ_SCALE_E8M0_U8)
+    _need(out_scales, "out_scales", sb, "f32" if f32 else "byte")
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -169,9 +226,10 @@ def rmsq_fused(x, residual, weight, eps, mode, scale_in, out_q, out_scales, resi
                tokens=None, hidden=None, group_size=0, flags=0, scale_ld=0, stream=None,
                launch: Optional[rmsq_launch] = None, check=True) -> int:
     """Enqueue one fused launch.  Tensors are passed by device pointer; sizes default to x's
-    shape.  Raises RmsqError on a non-zero status unless check=False."""
-    T = x.shape[0] if tokens is None else tokens
-    H = x.shape[-1] if hidden is None else hidden
+    shape ([T, H], 2-D).  Raises ValueError when a tensor cannot hold what the call reads or
+    writes, and RmsqError on a non-zero status unless check=False."""
+    T, H = _check_fused(x, residual, weight, mode, scale_in, out_q, out_scales, residual_out,
+                        tokens, hidden, group_size, flags, scale_ld)
     args = (_ptr(x), _ptr(residual), _ptr(weight), float(eps), int(mode), _ptr(scale_in),
             _ptr(out_q), _ptr(out_scales), _ptr(residual_out), int(T), int(H), int(group_size),
             int(flags), int(scale_ld))
@@ -182,6 +240,17 @@ def rmsq_fused(x, residual, weight, eps, mode, scale_in, out_q, out_scales, resi
     if check:
         _check(st, "rmsq_fused")
     return st
+
+
+def _check_fused(x, residual, weight, mode, scale_in, out_q, out_scales, residual_out, tokens,
+                 hidden, group_size, flags, scale_ld):
+    T, H = _rows_cols(x, "x", tokens, hidden)
+    act = 2 * T * H
+    for t, what in ((x, "x"), (residual, "residual"), (residual_out, "residual_out")):
+        _need(t, what, act, "act")
+    _need(weight, "weight", 2 * H, "act")
+    _check_quant_outputs(mode, scale_in, out_q, out_scales, T, H, group_size, flags, scale_ld)
+    return T, H
 
 
 def rmsq_fused_with_launch(x, residual, weight, eps, mode, scale_in, out_q, out_scales,
@@ -196,8 +265,8 @@ def rmsq_fused_timed(x, residual, weight, eps, mode, scale_in, out_q, out_scales
                      start_event=None, stop_event=None, stream=None, check=True) -> int:
     """One launch whose start/stop events (raw hipEvent_t handles, e.g. a recorded
     torch.cuda.Event's .cuda_event) are stamped by the dispatch itself."""
-    T = x.shape[0] if tokens is None else tokens
-    H = x.shape[-1] if hidden is None else hidden
+    T, H = _check_fused(x, residual, weight, mode, scale_in, out_q, out_scales, residual_out,
+                        tokens, hidden, group_size, flags, scale_ld)
     st = lib().rmsq_fused_timed(_ptr(x), _ptr(residual), _ptr(weight), float(eps), int(mode),
                                 _ptr(scale_in), _ptr(out_q), _ptr(out_scales),
                                 _ptr(residual_out), int(T), int(H), int(group_size), int(flags),
@@ -214,8 +283,8 @@ def rmsq_fused_fp4_dynamic(x, residual, weight, eps, out_q, out_scales, residual
     """(Residual add ->) RMSNorm -> FP4 block-16 with the global scale taken from the batch
     (written to global_scale, one f32).  With a launch shape or events it goes through
     rmsq_fused_fp4_dynamic_ex."""
-    T = x.shape[0] if tokens is None else tokens
-    H = x.shape[-1] if hidden is None else hidden
+    T, H = _check_fused(x, residual, weight, RMSQ_FP4_BLOCK16, global_scale, out_q, out_scales,
+                        residual_out, tokens, hidden, 16, flags, 0)
     args = (_ptr(x), _ptr(residual), _ptr(weight), float(eps), _ptr(out_q), _ptr(out_scales),
             _ptr(residual_out), _ptr(global_scale), int(T), int(H), int(flags))
     if launch is None and start_event is None and stop_event is None:
@@ -241,9 +310,17 @@ def rmsq_rms_norm_pad(x, residual, weight, eps, out, residual_out, tokens=None, 
                       check=True, flags=0) -> int:
     """(Residual add ->) RMSNorm -> out [T, out_ld] (bf16, or binary16 with RMSQ_INPUT_F16)
     with zero padding columns."""
-    T = x.shape[0] if tokens is None else tokens
-    H = x.shape[-1] if hidden is None else hidden
-    ld = out.shape[-1] if out_ld is None else out_ld
+    T, H = _rows_cols(x, "x", tokens, hidden)
+    if out_ld is None:
+        if not isinstance(out, torch.Tensor) or out.dim() != 2:
+            raise ValueError("rmsq: out must be a 2-D tensor [T, out_ld], or pass out_ld")
+        ld = int(out.shape[1])
+    else:
+        ld = int(out_ld)
+    for t, what in ((x, "x"), (residual, "residual"), (residual_out, "residual_out")):
+        _need(t, what, 2 * T * H, "act")
+    _need(weight, "weight", 2 * H, "act")
+    _need(out, "out", 2 * T * ld, "act")
     args = (_ptr(x), _ptr(residual), _ptr(weight), float(eps), _ptr(out), _ptr(residual_out),
             int(T), int(H), int(ld), int(flags))
     if launch is None and start_event is None and stop_event is None:
@@ -268,8 +345,9 @@ def rmsq_silu_mul_quant(x, mode, scale_in, out_q, out_scales, tokens=None, inter
                         start_event=None, stop_event=None, check=True) -> int:
     """SiLU+Mul -> quant of x [T, 2I] (gate first).  With a launch shape or events it goes
     through rmsq_silu_mul_quant_ex."""
-    T = x.shape[0] if tokens is None else tokens
-    I = x.shape[-1] // 2 if inter is None else inter
+    T, I = _rows_cols(x, "x", tokens, inter, cols_of=lambda c: c // 2)
+    _need(x, "x", 4 * T * I, "act")
+    _check_quant_outputs(mode, scale_in, out_q, out_scales, T, I, group_size, flags, scale_ld)
     args = (_ptr(x), int(mode), _ptr(scale_in), _ptr(out_q), _ptr(out_scales), int(T), int(I),
             int(group_size), int(flags), int(scale_ld))
     if launch is None and start_event is None and stop_event is None:
@@ -298,8 +376,24 @@ def rmsq_qk_norm_rope(qkv, q_weight, k_weight, cos_sin_cache, positions, eps, nu
     [T, (Hq + 2 Hkv) * D] (bf16, or binary16 with flags=RMSQ_INPUT_F16); cos_sin_cache
     [max_position, D] f32, positions [T] int64.  With a launch shape (heads per workgroup and
     per lane group) or events it goes through rmsq_qk_norm_rope_ex."""
-    T = qkv.shape[0] if tokens is None else tokens
-    mp = cos_sin_cache.shape[0] if max_position is None else max_position
+    D = int(head_dim)
+    width = (int(num_q_heads) + 2 * int(num_kv_heads)) * D
+    T, _ = _rows_cols(qkv, "qkv", tokens, width)
+    if max_position is None:
+        if not isinstance(cos_sin_cache, torch.Tensor) or cos_sin_cache.dim() != 2 \
+                or cos_sin_cache.shape[1] != D:
+            raise ValueError(f"rmsq: cos_sin_cache must be a 2-D tensor [max_position, {D}], "
+                             f"or pass max_position")
+        mp = int(cos_sin_cache.shape[0])
+    else:
+        mp = int(max_position)
+    if isinstance(qkv, torch.Tensor) and tokens is None and qkv.shape[1] != width:
+        raise ValueError(f"rmsq: qkv rows hold {qkv.shape[1]} values, the heads need {width}")
+    _need(qkv, "qkv", 2 * T * width, "act")
+    _need(q_weight, "q_weight", 2 * D, "act")
+    _need(k_weight, "k_weight", 2 * D, "act")
+    _need(cos_sin_cache, "cos_sin_cache", 4 * mp * D, "f32")
+    _need(positions, "positions", 8 * T, "i64")
     args = (_ptr(qkv), _ptr(q_weight), _ptr(k_weight), _ptr(cos_sin_cache), _ptr(positions),
             float(eps), int(T), int(num_q_heads), int(num_kv_heads), int(head_dim), int(mp))
     if heads_per_block == 0 and heads_per_lane == 0 and start_event is None and \
@@ -344,11 +438,12 @@ def rmsq_validate(x, residual, weight, eps, mode, scale_in, out_q, out_scales, r
                                int(group_size), int(flags), int(scale_ld))
 
 
-def rmsq_query_launch(mode, tokens, hidden, group_size=0, has_residual=True):
+def rmsq_query_launch(mode, tokens, hidden, group_size=0, flags=0):
+    """The default launch shape of rmsq_fused for these arguments, and its grid size."""
     l = rmsq_launch()
     grid = C.c_int64(0)
     _check(lib().rmsq_query_launch(int(mode), int(tokens), int(hidden), int(group_size),
-                                   int(bool(has_residual)), C.byref(l), C.byref(grid)),
+                                   int(flags), C.byref(l), C.byref(grid)),
            "rmsq_query_launch")
     return l, grid.value
 

@@ -77,7 +77,9 @@ Span span(const void* p, size_t bytes) {
 }
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-std::atomic<int> g_arch[64];  // per device: 0 unknown, 1 gfx950, 2 other
+// Per device index below 64: 0 unknown, 1 gfx950, 2 other (the library's only state, stated in
+// rmsq.h); filled by the first call that launches on the device.
+std::atomic<int> g_arch[64];
 
 int check_device() {
   int dev = -1;
@@ -761,12 +763,12 @@ int rmsq_silu_mul_quant_validate(const void* x, int mode, const float* scale_in,
                       scale_ld);
 }
 
-int rmsq_query_launch(int mode, int64_t tokens, int64_t hidden, int group_size,
-                      int has_residual, rmsq_launch* launch, int64_t* grid) {
-  (void)has_residual;
+int rmsq_query_launch(int mode, int64_t tokens, int64_t hidden, int group_size, unsigned flags,
+                      rmsq_launch* launch, int64_t* grid) {
   if (!launch) return RMSQ_EINVAL;
-  const unsigned flags = 0;
-  const int st = check_quant_scalars(tokens, hidden, mode, group_size, flags, 0);
+  // the activation type; the rest describes the scales, as in rmsq_fused
+  const int st = check_quant_scalars(tokens, hidden, mode, group_size,
+                                     flags & ~(unsigned)RMSQ_INPUT_F16, 0);
   if (st != RMSQ_OK) return st;
   *launch = default_fused_launch(tokens, hidden);
   if (grid) *grid = (tokens + launch->rows_per_block - 1) / launch->rows_per_block;

@@ -236,7 +236,7 @@ static void validate_only(void) {
   CHECK(strlen(rmsq_status_string(RMSQ_EALIAS)) > 0, "empty status string");
   int64_t grid = 0;
   rmsq_launch l;
-  CHECK(rmsq_query_launch(RMSQ_FP8_STATIC, 4096, 4096, 0, 1, &l, &grid) == RMSQ_OK &&
+  CHECK(rmsq_query_launch(RMSQ_FP8_STATIC, 4096, 4096, 0, 0, &l, &grid) == RMSQ_OK &&
             l.threads_per_row == 256 && l.chunks_per_thread == 2 && grid == 4096,
         "default launch of 4096 x 4096");
 }

@@ -57,7 +57,7 @@ def test_library_exports_every_declared_symbol(B):
 
 
 def test_abi_version_and_status_strings(B):
-    assert B.rmsq_abi_version() == B.RMSQ_ABI_VERSION == 3
+    assert B.rmsq_abi_version() == B.RMSQ_ABI_VERSION == 4
     for st in (0, -1, -2, -3, -4, -5, -6):
         assert B.rmsq_status_string(st) and B.rmsq_status_string(st) != "unknown status"
     assert B.rmsq_status_string(-99) == "unknown status"
@@ -138,6 +138,22 @@ def test_query_launch(B):
         assert grid == -(-1000 // rpb)
     with pytest.raises(B.RmsqError):
         B.rmsq_query_launch(1, 10, 12)
+
+
+def test_query_launch_takes_the_calls_flags(B):
+    """The query checks the flags as rmsq_fused does; the shape depends on T and H only."""
+    base = B.rmsq_query_launch(2, 1024, 5120, 128)[0].as_tuple()
+    for f in (B.RMSQ_SCALE_COLMAJOR, B.RMSQ_SCALE_E8M0, B.RMSQ_SCALE_E8M0_U8,
+              B.RMSQ_SCALE_COLMAJOR | B.RMSQ_SCALE_E8M0, B.RMSQ_INPUT_F16,
+              B.RMSQ_INPUT_F16 | B.RMSQ_SCALE_COLMAJOR):
+        assert B.rmsq_query_launch(2, 1024, 5120, 128, f)[0].as_tuple() == base
+    for mode, G in ((0, 0), (1, 0), (3, 16)):
+        plain = B.rmsq_query_launch(mode, 4096, 2048, G)[0].as_tuple()
+        assert B.rmsq_query_launch(mode, 4096, 2048, G, B.RMSQ_INPUT_F16)[0].as_tuple() == plain
+        with pytest.raises(B.RmsqError):  # scale-layout flags belong to the per-group mode
+            B.rmsq_query_launch(mode, 4096, 2048, G, B.RMSQ_SCALE_COLMAJOR)
+    with pytest.raises(B.RmsqError):
+        B.rmsq_query_launch(2, 1024, 5120, 128, B.RMSQ_SCALE_E8M0 | B.RMSQ_SCALE_E8M0_U8)
 
 
 @pytest.mark.parametrize("T,H,shape", [

@@ -387,7 +387,7 @@ def scale_layout(mode, T, H, G, flags):
     return (T, H // 16), torch.uint8
 
 
-def gpu_leg(args, wl, T, H, mode, G, flags):
+def gpu_leg(args, wl, T, H, mode, G, flags, with_copy=True):
     import torch
 
     from rmsnorm_quantization_amd import binding as B
@@ -408,7 +408,9 @@ def gpu_leg(args, wl, T, H, mode, G, flags):
     else:
         rd, wr = algorithmic_bytes(mode, T, H, G, flags, residual, wl.kind)
     set_bytes = rd + wr
-    nsets = max(2, math.ceil(FOOTPRINT_BYTES / set_bytes))
+    # enough sets that the footprint dwarfs the last-level cache, and never more than the
+    # launches that use them (every launch of a timed pass reads its own set)
+    nsets = max(2, min(math.ceil(FOOTPRINT_BYTES / set_bytes), args.steps + args.warmup))
     xd, rdv, wd = x.to(dev), (r.to(dev) if residual else None), w.to(dev)
     sshape, sdt = scale_layout(mode, T, H, G, flags) if not pad else (None, None)
     qcols = H // 2 if mode == 3 else H
@@ -469,7 +471,7 @@ def gpu_leg(args, wl, T, H, mode, G, flags):
     elif act:
         shape = B.rmsq_silu_mul_query_launch(mode, T, H, 16 if mode == 3 else G)[0].as_tuple()
     else:
-        shape = B.rmsq_query_launch(mode, T, H, G, residual)[0].as_tuple()
+        shape = B.rmsq_query_launch(mode, T, H, G, flags)[0].as_tuple()
     if act and mode == 3:
         G = 16
     stream = torch.cuda.current_stream()
@@ -580,7 +582,7 @@ def gpu_leg(args, wl, T, H, mode, G, flags):
         ceiling = probe_leg(args, sets, T, H, mode, shape, stream, evs)
 
     # a plain device copy, for context (practical HBM ceiling)
-    copy_gbs = copy_ceiling(dev, stream)
+    copy_gbs = copy_ceiling(dev, stream) if with_copy else None
 
     return {"ms_per_step": ms_per_step, "ms_per_step_graph": ms_per_step_graph,
             "avg_launch_ms": avg_launch_ms,
@@ -588,6 +590,70 @@ def gpu_leg(args, wl, T, H, mode, G, flags):
             "p90_launch_ms": per[(9 * len(per)) // 10], "bytes": rd + wr, "read": rd, "write": wr,
             "sets": nsets, "launch": shape, "copy_gbs": copy_gbs, "ceiling": ceiling,
             "device": torch.cuda.get_device_name(dev)}
+
+
+# The five configurations of the fused add + RMSNorm + quant family, each timed in the default
+# run: (label, workload, tokens, hidden, group, scale flags).  The 1024-token shapes are the
+# smallest batches the >= 80%-of-peak target is stated for (every wave of the launch resident at
+# once).
+CONFIG_LEGS = [
+    ("rmsnorm_fp8_static 16 x 4096 (latency)", "w0", 16, 4096, 128, ""),
+    ("add_rmsnorm_fp8_static 1024 x 4096", "w1", 1024, 4096, 128, ""),
+    ("add_rmsnorm_fp8_static 4096 x 4096", "w1", 4096, 4096, 128, ""),
+    ("add_rmsnorm_fp8_static 16384 x 4096", "w1", 16384, 4096, 128, ""),
+    ("add_rmsnorm_fp8_per_token 8192 x 8192", "w2", 8192, 8192, 128, ""),
+    ("add_rmsnorm_fp8_per_group G128 1024 x 5120", "w3", 1024, 5120, 128, ""),
+    ("add_rmsnorm_fp8_per_group G128 1024 x 7168", "w3", 1024, 7168, 128, ""),
+    ("add_rmsnorm_fp8_per_group G128 16384 x 7168", "w3", 16384, 7168, 128, ""),
+    ("add_rmsnorm_fp4_block16 4096 x 2048", "w4", 4096, 2048, 128, ""),
+]
+
+
+def leg_summary(label, wl, T, H, mode, G, flags, g):
+    """One configuration's line of the configs list: kernel time from dispatch-stamped events,
+    algorithmic GB/s and fraction of 8 TB/s, graph-replay latency per launch, the memory-only
+    probe's time on the same buffers and launch shape, HBM traffic when profiled."""
+    kern_us = g["avg_launch_ms"] * 1e3
+    gbs = g["bytes"] / (kern_us * 1e-6) / 1e9
+    step_ms = g["ms_per_step_graph"] or g["ms_per_step"]
+    key = f"w{wl.index}_T{T}_H{H}_{MODE_NAMES[mode]}_G{G}_f{flags}"
+    tr = load_traffic(key)
+    c = g.get("ceiling")
+    return {
+        "config": label, "workload": wl.name, "tokens": T, "hidden": H,
+        "mode": MODE_NAMES[mode], "group_size": G, "flags": flags,
+        "launch": list(g["launch"]), "bytes": g["bytes"],
+        "kernel_us": {"mean": round(kern_us, 3), "median": round(g["median_launch_ms"] * 1e3, 3),
+                      "p10": round(g["p10_launch_ms"] * 1e3, 3),
+                      "p90": round(g["p90_launch_ms"] * 1e3, 3)},
+        "GBs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "tokens_per_s": round(T / (kern_us * 1e-6), 1),
+        "latency_us_per_launch": round(step_ms * 1e3, 3),
+        "probe": None if not c else {
+            "kernel_us": round(c["kernel_us"], 3),
+            "probe_time_over_kernel_time": round(c["kernel_us"] / kern_us, 4)},
+        "traffic": None if tr is None else tr["bytes_per_launch"],
+    }
+
+
+def configs_leg(args, main):
+    """Time every entry of CONFIG_LEGS (the main line's own configuration reuses its numbers)."""
+    import torch
+
+    out = []
+    for label, w, T, H, G, fl in CONFIG_LEGS:
+        a = argparse.Namespace(**vars(args))
+        a.workload, a.tokens, a.hidden, a.group, a.flags, a.launch = w, T, H, G, fl, ""
+        wl, T, H, mode, G, flags = workload_spec(a)
+        if main is not None and (wl.index, T, H, mode, G, flags) == main[0]:
+            g = main[1]
+        else:
+            g = gpu_leg(a, wl, T, H, mode, G, flags, with_copy=False)
+            torch.cuda.empty_cache()
+        out.append(leg_summary(label, wl, T, H, mode, G, flags, g))
+        print(f"bench: {label}: {out[-1]['kernel_us']['mean']} us, "
+              f"{out[-1]['frac_of_peak']:.3f} of peak", file=sys.stderr, flush=True)
+    return out
 
 
 def probe_leg(args, sets, T, H, mode, shape, stream, evs):
@@ -898,6 +964,10 @@ def main():
                     help="time eager back-to-back launches only (default: also a HIP-graph "
                          "replay of the same K launches, which is what value reports)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--configs", choices=["auto", "on", "off"], default="auto",
+                    help="also time every configuration of the add + RMSNorm + quant family "
+                         "and report them under 'configs' (auto: only for the default "
+                         "workload with no size or launch override)")
     ap.add_argument("--summarize", nargs=3, metavar=("KTRACE_DB", "FETCH_DB", "WRITE_DB"),
                     help="write the profiles/ summary and traffic entry for this configuration "
                          "from three rocprofv3 databases, then exit")
@@ -1009,6 +1079,10 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "timing": (f"achieved = algorithmic bytes / the mean kernel duration of {args.steps} "
+                       "launches, each bracketed by a HIP event pair that its own dispatch "
+                       "stamps (hipExtLaunchKernel) on the launch stream"),
+            "kernel_us": round(g["avg_launch_ms"] * 1e3, 3),
             "frac_of_copy_ceiling": round(achieved / g["copy_gbs"]["copy_GBs"], 4),
             "traffic": None if tr is None else tr["bytes_per_launch"],
         },
@@ -1025,6 +1099,12 @@ def main():
     if tr is not None:
         out["roofline"]["traffic_detail"] = {k: tr[k] for k in ("fetch_bytes", "write_bytes",
                                                                 "calibration") if k in tr}
+    want_configs = args.configs == "on" or (
+        args.configs == "auto" and args.workload == "w1" and not args.tokens and not args.hidden
+        and not args.launch)
+    if want_configs:
+        main_key = (wl.index, T, H, mode, G, flags)
+        out["configs"] = configs_leg(args, None if rope or wl.kind != "norm" else (main_key, g))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_leg(wl, T, H, mode, G, flags, args.cpu_budget)
     print(json.dumps(out), flush=True)

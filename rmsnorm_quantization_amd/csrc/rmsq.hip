@@ -254,6 +254,7 @@ int fused_impl(const void* x, const void* res, const void* w, float eps, int mod
   a.H = H;
   a.ld = (flags & RMSQ_SCALE_COLMAJOR) ? (ld ? ld : T) : 0;
   a.eps = eps;
+  a.inv_h = 1.0 / (double)H;
   a.flags = flags;
   a.tpr = l.threads_per_row;
   a.rpb = l.rows_per_block;
@@ -329,6 +330,7 @@ int fp4_dynamic_impl(const void* x, const void* res, const void* w, float eps, v
   a.H = H;
   a.ld = 0;
   a.eps = eps;
+  a.inv_h = 1.0 / (double)H;
   a.flags = 0;
   a.tpr = l.threads_per_row;
   a.rpb = l.rows_per_block;
@@ -430,6 +432,7 @@ int pad_impl(const void* x, const void* res, const void* w, float eps, void* out
   a.H = H;
   a.ld = out_ld;
   a.eps = eps;
+  a.inv_h = 1.0 / (double)H;
   a.flags = 0;
   a.tpr = l.threads_per_row;
   a.rpb = l.rows_per_block;

@@ -140,6 +140,23 @@ __device__ __forceinline__ uint32_t fp4x8(const float* v) {
   return w;
 }
 
+// ---- per-group scale ------------------------------------------------------------------------
+// absmax / 448 exactly as IEEE division rounds it: m * RN(1/448) corrected once by its FMA
+// residual equals the correctly rounded quotient for every m >= 2^-120 (checked exhaustively
+// over all binary32 m on the host); below that the quotient is subnormal and may differ, so a
+// wave holding such an m takes the IEEE division (a uniform branch).  m == 0 gives 0 either way.
+// Must run with all lanes of the wave active.
+__device__ __forceinline__ float div448(float m) {
+  constexpr float kInv448 = 1.0f / 448.0f;
+  const float q0 = m * kInv448;
+  float s = fmaf(fmaf(-q0, 448.0f, m), kInv448, q0);
+  if (wave_any(m > 0.0f && m < 0x1p-120f)) {
+    asm volatile("");  // keeps the division in its branch (not computed for every wave)
+    s = m / 448.0f;
+  }
+  return s;
+}
+
 // ---- E8M0 ---------------------------------------------------------------------------------
 // Round a non-negative f32 scale up to the next power of two 2^k, k in [-127, 127], from its
 // bit pattern: a normal s with a non-zero mantissa moves up one binade; s == 0 and the
@@ -165,15 +182,38 @@ __device__ __forceinline__ uint32_t e8m0_ceil(float s, float* p2) {
 // from any estimate better than 2^-12; the definition's value lies within two ulps of 1/sqrt(m)
 // as well.  Rounding to binary32 is monotonic, so when
 // y(1 - 2^-40) and y(1 + 2^-40) round to the same binary32 value every value between them does,
-// the definition's included; otherwise (about one value in 2^16, and NaN or infinite m) the
-// definition's own sequence runs.
-__device__ __forceinline__ float inv_sqrt_f32(double m) {
+// the definition's included; then inv_sqrt_window stores it and returns true.  Otherwise (about
+// one value in 2^16, and NaN or infinite m) the caller runs the definition's own sequence.
+__device__ __forceinline__ bool inv_sqrt_window(double m, float* out) {
   double y = __builtin_amdgcn_rsq(m);
 #pragma unroll
   for (int i = 0; i < 2; ++i) y = fma(0.5 * y, fma(-m, y * y, 1.0), y);
   const float lo = (float)(y * (1.0 - 0x1p-40)), hi = (float)(y * (1.0 + 0x1p-40));
-  if (lo == hi) return lo;
+  *out = lo;
+  return lo == hi;
+}
+
+__device__ __forceinline__ float inv_sqrt_f32(double m) {
+  float v;
+  if (inv_sqrt_window(m, &v)) return v;
   return (float)(1.0 / sqrt(m));
+}
+
+// The inverse RMS of a row from its binary64 sum of squares: (float)(1 / sqrt(ss/H + eps)) with
+// the quotient, sum, root and reciprocal in binary64, as the plain definition computes it.  For
+// a power-of-two H the mean is an exact scaling by 2^-k.  Otherwise ss * RN(1/H) (inv_h, from the
+// host) stands in for the quotient: it lies within 2^-51 (relative) of it, which moves 1/sqrt by
+// about 2^-52, far inside the 2^-40 window of inv_sqrt_window, so the window decides the rounding
+// exactly as it would for the quotient itself; where the window straddles a binary32 rounding
+// boundary, the quotient and the definition's own sequence run.  The branch on H is uniform.
+__device__ __forceinline__ float inv_rms(double ss, int64_t H, double inv_h, float eps) {
+  const bool pow2 = (H & (H - 1)) == 0;
+  const double mean =
+      pow2 ? ldexp(ss, -__builtin_ctzll((unsigned long long)H)) : ss * inv_h;
+  float v;
+  if (inv_sqrt_window(mean + (double)eps, &v)) return v;
+  const double exact = pow2 ? mean : ss / (double)H;
+  return (float)(1.0 / sqrt(exact + (double)eps));
 }
 
 // ---- cross-lane reductions ---------------------------------------------------------------
@@ -182,16 +222,24 @@ __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-// Max over aligned groups of LANES consecutive lanes (2, 4, 8 or 16: one DPP row at most);
-// every lane of a group ends with the group's max.  Must run with all lanes of the wave active.
+// Max over aligned groups of LANES consecutive lanes (2, 4, 8 or 16: one DPP row at most) of
+// non-negative values (absolute values: no NaN, no negative zero); every lane of a group ends with
+// the group's max.  Non-negative binary32 values order like their bit patterns as unsigned
+// integers, so the integer max takes its DPP operand directly (no move, no canonicalization).
+// Must run with all lanes of the wave active.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
 template <int LANES>
 __device__ __forceinline__ float group_max(float v) {
   static_assert(LANES == 1 || LANES == 2 || LANES == 4 || LANES == 8 || LANES == 16, "lanes");
-  if (LANES >= 2) v = fmaxf(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]: lane ^ 1
-  if (LANES >= 4) v = fmaxf(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]: lane ^ 2
-  if (LANES >= 8) v = fmaxf(v, dpp<0x141>(v));  // row_half_mirror: other quad of the 8
-  if (LANES >= 16) v = fmaxf(v, dpp<0x140>(v)); // row_mirror: other half of the 16
-  return v;
+  uint32_t u = __float_as_uint(v);
+  if (LANES >= 2) u = max(u, dpp_u32<0xB1>(u));   // quad_perm [1,0,3,2]: lane ^ 1
+  if (LANES >= 4) u = max(u, dpp_u32<0x4E>(u));   // quad_perm [2,3,0,1]: lane ^ 2
+  if (LANES >= 8) u = max(u, dpp_u32<0x141>(u));  // row_half_mirror: other quad of the 8
+  if (LANES >= 16) u = max(u, dpp_u32<0x140>(u)); // row_mirror: other half of the 16
+  return __uint_as_float(u);
 }
 
 template <int CTRL>
@@ -223,6 +271,7 @@ __device__ __forceinline__ double wave_sum(double v) {
   v += dpp<0x140>(v);
   return (readlane(v, 0) + readlane(v, 16)) + (readlane(v, 32) + readlane(v, 48));
 }
+// (non-negative values, as group_max)
 __device__ __forceinline__ float wave_max(float v) {
   v = group_max<16>(v);
   const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));

@@ -50,6 +50,7 @@ struct KArgs {
   int64_t T;
   int64_t H;
   int64_t ld;
+  double inv_h;   // RN(1/H) in binary64 (inv_rms)
   float eps;
   uint32_t flags;
   int32_t tpr;    // threads per row (multiple of 64)
@@ -166,11 +167,16 @@ __device__ __forceinline__ void quantize_store(const YF& Y, const bool (&ok)[VPT
         m = fmaxf(m, fabsf(y[e]));
       }
       m = group_max<L>(m);
-      float s = m / kFp8Max;
+      float s = div448(m);
       const bool zero = (s == 0.0f);
       uint32_t byte = 0;
-      if (e8) byte = e8m0_ceil(s, &s);
-      float r = 1.0f / s;
+      float r;
+      if (e8) {  // uniform: a power of two 2^(byte-127), whose reciprocal is exact
+        byte = e8m0_ceil(s, &s);
+        r = __builtin_amdgcn_ldexpf(1.0f, 127 - (int)byte);
+      } else {
+        r = 1.0f / s;
+      }
       const bool inf = !zero && not_finite(r);
       if (wave_any(inf)) zero_safe(y, r, inf);  // uniform over the wave
       u32x2 qc = {fp8x4(y[0] * r, y[1] * r, y[2] * r, y[3] * r),
@@ -379,12 +385,7 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
       ss = 0.0;
       for (int i = 0; i < wpr; ++i) ss += s_ss[rib * wpr + i];
     }
-    // ss / H: for a power-of-two H an exact scaling by 2^-k (ldexp), bit-identical to the IEEE
-    // quotient and free of the binary64 division sequence; the branch is uniform over the grid
-    const int64_t H = a.H;
-    const double mean =
-        ((H & (H - 1)) == 0) ? ldexp(ss, -__builtin_ctzll((unsigned long long)H)) : ss / (double)H;
-    inv = inv_sqrt_f32(mean + (double)a.eps);
+    inv = inv_rms(ss, a.H, a.inv_h, a.eps);
   }
   if constexpr (MODE == kModeRowAmax) {  // stage it for the block pass
     if (a.inv_rows != nullptr && lr == 0 && row_ok)

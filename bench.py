@@ -930,9 +930,25 @@ def summarize(ktrace_db, fetch_db, write_db, key, title, commands, out_md, util=
                     f"{name}, `{r[0].split('(')[0].replace('void ', '')}`")
                 if vals:
                     lines.append(f"| {label} | {statistics.median(vals):.2f} | {len(vals)} |")
+        med = {}
+        for name, db in util:
+            rows = _db_rows(db, "select kernel_name, value from counters_collection "
+                                "where counter_name = '%s'" % name)
+            vals = [v for k, v in rows if k == step_k[0][0]]
+            if vals:
+                med[name] = statistics.median(vals)
+        if med.get("SQ_WAVES"):
+            per_wave = [(n, med[n] / med["SQ_WAVES"]) for n in
+                        ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_WAVE_CYCLES",
+                         "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU") if n in med]
+            if per_wave:
+                lines += ["", "Per wave (the counter's median over dispatches / SQ_WAVES): " +
+                          ", ".join(f"{n} {v:,.1f}" for n, v in per_wave) + "."]
         lines += ["", "VALUBusy: % of GPU time the vector ALUs issue; MemUnitStalled: % of GPU time "
                   "the texture/memory unit stalls on data; OccupancyPercent: resident waves as % "
-                  "of the maximum.", ""]
+                  "of the maximum.  SQ_* are raw counts per dispatch: waves launched, vector / "
+                  "scalar / LDS instructions issued, wave-cycles resident, wave-cycles waiting on "
+                  "any dependency, cycles the vector ALU was busy for a wave.", ""]
     with open(out_md, "w") as fh:
         fh.write("\n".join(lines))
     return entry

@@ -158,39 +158,54 @@ __device__ __forceinline__ void quantize_store(const YF& Y, const bool (&ok)[VPT
     const bool e8 = (o.flags & (RMSQ_SCALE_E8M0 | RMSQ_SCALE_E8M0_U8)) != 0;
     const bool u8 = (o.flags & RMSQ_SCALE_E8M0_U8) != 0;
     const bool col = (o.flags & RMSQ_SCALE_COLMAJOR) != 0;
+    // Chunks in phases as for FP4 below (scales, codes, stores), up to four at a time: the
+    // chunks' reciprocal chains interleave and no divergent scale store separates them.
+    constexpr int KB = VPT <= 4 ? VPT : 1;
+    float y[VPT][8], s[VPT], r[VPT];
+    uint32_t byte[VPT];
+    bool zero[VPT];
 #pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      const uint32_t c = o.lr + (uint32_t)(k * o.tpr);
-      float y[8];
-      float m = 0.0f;
+    for (int k0 = 0; k0 < VPT; k0 += KB) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        y[e] = Y(k, e);
-        m = fmaxf(m, fabsf(y[e]));
+      for (int k = k0; k < k0 + KB; ++k) {  // scales
+        float m = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          y[k][e] = Y(k, e);
+          m = fmaxf(m, fabsf(y[k][e]));
+        }
+        m = group_max<L>(m);
+        s[k] = div448(m);
+        zero[k] = (s[k] == 0.0f);  // before the E8M0 rounding turns it into 2^-127
+        byte[k] = 0;
+        if (e8) {  // uniform: a power of two 2^(byte-127), whose reciprocal is exact
+          byte[k] = e8m0_ceil(s[k], &s[k]);
+          r[k] = __builtin_amdgcn_ldexpf(1.0f, 127 - (int)byte[k]);
+        } else {
+          r[k] = 1.0f / s[k];
+        }
       }
-      m = group_max<L>(m);
-      float s = div448(m);
-      const bool zero = (s == 0.0f);
-      uint32_t byte = 0;
-      float r;
-      if (e8) {  // uniform: a power of two 2^(byte-127), whose reciprocal is exact
-        byte = e8m0_ceil(s, &s);
-        r = __builtin_amdgcn_ldexpf(1.0f, 127 - (int)byte);
-      } else {
-        r = 1.0f / s;
+      u32x2 qc[VPT];
+#pragma unroll
+      for (int k = k0; k < k0 + KB; ++k) {  // codes; a zero scale (zero group) gives zero codes
+        const bool inf = !zero[k] && not_finite(r[k]);
+        if (wave_any(inf)) zero_safe(y[k], r[k], inf);  // uniform over the wave
+        const float rk = r[k];
+        qc[k] = (u32x2){fp8x4(y[k][0] * rk, y[k][1] * rk, y[k][2] * rk, y[k][3] * rk),
+                        fp8x4(y[k][4] * rk, y[k][5] * rk, y[k][6] * rk, y[k][7] * rk)};
+        if (zero[k]) qc[k] = (u32x2){0u, 0u};
       }
-      const bool inf = !zero && not_finite(r);
-      if (wave_any(inf)) zero_safe(y, r, inf);  // uniform over the wave
-      u32x2 qc = {fp8x4(y[0] * r, y[1] * r, y[2] * r, y[3] * r),
-                  fp8x4(y[4] * r, y[5] * r, y[6] * r, y[7] * r)};
-      if (zero) qc = (u32x2){0u, 0u};
-      if (ok[k]) {
-        __builtin_nontemporal_store(qc, boff(reinterpret_cast<u32x2*>(o.q + o.obase), c << 3));
-        if ((o.lr % L) == 0) {
-          const int64_t g = c / L;
-          const int64_t idx = col ? g * o.ld + o.row : o.row * (o.n / GS) + g;
-          if (u8) static_cast<uint8_t*>(o.scales)[idx] = (uint8_t)byte;
-          else static_cast<float*>(o.scales)[idx] = s;
+#pragma unroll
+      for (int k = k0; k < k0 + KB; ++k) {  // stores
+        const uint32_t c = o.lr + (uint32_t)(k * o.tpr);
+        if (ok[k]) {
+          __builtin_nontemporal_store(qc[k], boff(reinterpret_cast<u32x2*>(o.q + o.obase), c << 3));
+          if ((o.lr % L) == 0) {
+            const int64_t g = c / L;
+            const int64_t idx = col ? g * o.ld + o.row : o.row * (o.n / GS) + g;
+            if (u8) static_cast<uint8_t*>(o.scales)[idx] = (uint8_t)byte[k];
+            else static_cast<float*>(o.scales)[idx] = s[k];
+          }
         }
       }
     }

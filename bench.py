@@ -609,6 +609,9 @@ CONFIG_LEGS = [
 ]
 
 
+CONFIG_STEPS = 200  # dispatch-stamped launches per configuration leg (at least)
+
+
 def leg_summary(label, wl, T, H, mode, G, flags, g):
     """One configuration's line of the configs list: kernel time from dispatch-stamped events,
     algorithmic GB/s and fraction of 8 TB/s, graph-replay latency per launch, the memory-only
@@ -630,8 +633,9 @@ def leg_summary(label, wl, T, H, mode, G, flags, g):
         "tokens_per_s": round(T / (kern_us * 1e-6), 1),
         "latency_us_per_launch": round(step_ms * 1e3, 3),
         "probe": None if not c else {
-            "kernel_us": round(c["kernel_us"], 3),
-            "probe_time_over_kernel_time": round(c["kernel_us"] / kern_us, 4)},
+            "kernel_us": round(c["kernel_us"], 3), "median_us": round(c["median_us"], 3),
+            "probe_time_over_kernel_time": round(c["kernel_us"] / kern_us, 4),
+            "median_ratio": round(c["median_us"] / (g["median_launch_ms"] * 1e3), 4)},
         "traffic": None if tr is None else tr["bytes_per_launch"],
     }
 
@@ -644,8 +648,10 @@ def configs_leg(args, main):
     for label, w, T, H, G, fl in CONFIG_LEGS:
         a = argparse.Namespace(**vars(args))
         a.workload, a.tokens, a.hidden, a.group, a.flags, a.launch = w, T, H, G, fl, ""
+        a.steps = max(args.steps, CONFIG_STEPS)  # a few ms each: enough launches for a median
         wl, T, H, mode, G, flags = workload_spec(a)
-        if main is not None and (wl.index, T, H, mode, G, flags) == main[0]:
+        if main is not None and (wl.index, T, H, mode, G, flags) == main[0] and \
+                args.steps >= CONFIG_STEPS:
             g = main[1]
         else:
             g = gpu_leg(a, wl, T, H, mode, G, flags, with_copy=False)
@@ -679,10 +685,11 @@ def probe_leg(args, sets, T, H, mode, shape, stream, evs):
         if st:
             raise RuntimeError(f"rmsq_probe_stream failed ({st})")
     torch.cuda.synchronize()
-    per = [a.elapsed_time(b) for a, b in evs]
+    per = sorted(a.elapsed_time(b) for a, b in evs)
     nbytes = T * (2 * H + (2 * H if sets[0]["r"] is not None else 0)
                   + (2 * H if sets[0]["ro"] is not None else 0) + H * out1 // 8)
-    return {"kernel_us": sum(per) / len(per) * 1e3, "bytes": nbytes}
+    return {"kernel_us": sum(per) / len(per) * 1e3, "median_us": per[len(per) // 2] * 1e3,
+            "bytes": nbytes}
 
 
 def cpu_model():
@@ -939,7 +946,7 @@ def summarize(ktrace_db, fetch_db, write_db, key, title, commands, out_md, util=
                 med[name] = statistics.median(vals)
         if med.get("SQ_WAVES"):
             per_wave = [(n, med[n] / med["SQ_WAVES"]) for n in
-                        ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_WAVE_CYCLES",
+                        ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_WAIT_ANY",
                          "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU") if n in med]
             if per_wave:
                 lines += ["", "Per wave (the counter's median over dispatches / SQ_WAVES): " +
@@ -947,8 +954,9 @@ def summarize(ktrace_db, fetch_db, write_db, key, title, commands, out_md, util=
         lines += ["", "VALUBusy: % of GPU time the vector ALUs issue; MemUnitStalled: % of GPU time "
                   "the texture/memory unit stalls on data; OccupancyPercent: resident waves as % "
                   "of the maximum.  SQ_* are raw counts per dispatch: waves launched, vector / "
-                  "scalar / LDS instructions issued, wave-cycles resident, wave-cycles waiting on "
-                  "any dependency, cycles the vector ALU was busy for a wave.", ""]
+                  "scalar / LDS instructions issued, wave-cycles waiting on anything / on an "
+                  "instruction dependency, cycles the vector ALU was busy for a wave, and the "
+                  "cycles the sequencers were busy.", ""]
     with open(out_md, "w") as fh:
         fh.write("\n".join(lines))
     return entry
@@ -1111,7 +1119,9 @@ def main():
             "kernel": "memory-only probe, same traffic and launch shape (librmsq_probe.so)",
             "kernel_us": round(c["kernel_us"], 3), "bytes": c["bytes"],
             "GBs": round(c_gbs, 1), "frac_of_peak": round(c_gbs / HBM_PEAK_GBS, 4),
-            "probe_time_over_kernel_time": round(c["kernel_us"] / (g["avg_launch_ms"] * 1e3), 4)}
+            "probe_time_over_kernel_time": round(c["kernel_us"] / (g["avg_launch_ms"] * 1e3), 4),
+            "median_us": round(c["median_us"], 3),
+            "median_ratio": round(c["median_us"] / (g["median_launch_ms"] * 1e3), 4)}
     if tr is not None:
         out["roofline"]["traffic_detail"] = {k: tr[k] for k in ("fetch_bytes", "write_bytes",
                                                                 "calibration") if k in tr}

@@ -51,10 +51,11 @@ extern "C" {
 #define RMSQ_API
 #endif
 
-/* 4: rmsq_query_launch takes the call's flags in place of a residual flag it never used;
+/* 5: rmsq_convert accepts RMSQ_CVT_E4M3_IN_RANGE;
+ * 4: rmsq_query_launch takes the call's flags in place of a residual flag it never used;
  * 3: rmsq_rms_norm_pad_query_launch takes the call's flags (the default shape depends on the
  *    activation type); 2: the padding and QK-norm + RoPE entry points take flags. */
-#define RMSQ_ABI_VERSION 4
+#define RMSQ_ABI_VERSION 5
 #define RMSQ_MAX_HIDDEN 65536 /* largest H one workgroup keeps in registers */
 
 /* ---- status codes ---- */
@@ -194,24 +195,33 @@ RMSQ_API int rmsq_fused_timed(const void* x, const void* residual, const void* w
  *  x, residual, weight, eps, residual_out, tokens, hidden
  *               as for rmsq_fused; hidden % 16 == 0.
  *  out_q, out_scales
- *               as for rmsq_fused in RMSQ_FP4_BLOCK16.  out_q also holds the T row maxima (f32,
- *               its first 4T bytes) between the launches; its final contents are the codes.
+ *               as for rmsq_fused in RMSQ_FP4_BLOCK16.  out_q also holds the row pass's
+ *               per-workgroup maxima (f32, at most its first 4T bytes) between the launches; its
+ *               final contents are the codes.
  *  global_scale device f32, 4-byte aligned, written with gs (the dequantization needs it: value =
- *               e2m1 * decode(sf) / gs).  Must not overlap any other argument.
+ *               e2m1 * decode(sf) / gs).  Must not overlap any other argument.  Also the word
+ *               through which the launches hand gs over (cleared to 0 first).
  *  flags        0 (bf16) or RMSQ_INPUT_F16; any other bit is RMSQ_EUNSUPPORTED.
- * The global scale depends on every row, so the work is three launches on `stream`: the residual
- * add and normalization, writing the new residual and each row's largest |y|; a one-workgroup
- * reduction to gs; the block quantization, which normalizes the new residual (or x) again.  That
- * second read of the normalized input (2H bytes per token) is the price of the batch scale.
- * Returns RMSQ_OK or a negative status.
+ * The global scale depends on every row, so the work is two launches on `stream`: (1) the
+ * residual add and normalization, writing the new residual and each workgroup's largest |y|
+ * (and clearing global_scale); (2) the block quantization, which normalizes the new residual (or
+ * x) again.  Launch 2's first workgroup reduces the maxima to gs and stores it to global_scale;
+ * the other workgroups load their rows meanwhile and then wait for a non-zero global_scale (a
+ * bounded wait: the first workgroup is dispatched before them and does not wait on anything).
+ * No workgroup writes out_q, where the maxima are, before gs exists.  Where that workgroup could
+ * not reduce the maxima in one round of loads (more than eight per thread: very large T, or a
+ * caller's shape with one row per workgroup), a one-workgroup reduction launch runs between the
+ * two instead.  The second read of the normalized input (2H bytes per token) is the price of the
+ * batch scale.  Returns RMSQ_OK or a negative status.
  */
 RMSQ_API int rmsq_fused_fp4_dynamic(const void* x, const void* residual, const void* weight,
                                     float eps, void* out_q, void* out_scales, void* residual_out,
                                     float* global_scale, int64_t tokens, int64_t hidden,
                                     unsigned flags, void* stream);
 
-/* rmsq_fused_fp4_dynamic with an explicit launch shape for the two row passes (NULL: the default,
- * as rmsq_fused) and optional dispatch-stamped events: start_event is stamped by the first launch,
+/* rmsq_fused_fp4_dynamic with an explicit launch shape for the row pass, and for the block pass
+ * where it normalizes again (NULL: the default, as rmsq_fused but with up to 16 rows to a
+ * workgroup) and optional dispatch-stamped events: start_event is stamped by the first launch,
  * stop_event by the last (NULL: none). */
 RMSQ_API int rmsq_fused_fp4_dynamic_ex(const void* x, const void* residual, const void* weight,
                                        float eps, void* out_q, void* out_scales,
@@ -384,7 +394,12 @@ RMSQ_API int rmsq_silu_mul_query_launch(int mode, int64_t tokens, int64_t inter,
 RMSQ_API int64_t rmsq_block_to_rowblock(int64_t block, int64_t grid);
 
 /* Diagnostic: run the kernels' own converters over n f32 values (device pointers).
- *  RMSQ_CVT_E4M3  out: n bytes, saturating e4m3fn (the FP8 epilogue's conversion)
+ *  RMSQ_CVT_E4M3  out: n bytes, saturating e4m3fn (the static and per-token schemes'
+ *                 conversion, and the FP4 block scales')
+ *  RMSQ_CVT_E4M3_IN_RANGE
+ *                 out: n bytes, e4m3fn without the clamp (the per-group scheme's conversion,
+ *                 whose inputs stay within 448 (1 + 2^-20)): the saturating code for
+ *                 |v| <= 464, the NaN code of v's sign above that
  *  RMSQ_CVT_E2M1  out: n/2 bytes, element 2k in the low nibble (the FP4 epilogue's conversion);
  *                 n must be a multiple of 8
  *  RMSQ_CVT_BF16  out: n uint16 bf16 patterns (the residual-add rounding)
@@ -393,7 +408,13 @@ RMSQ_API int64_t rmsq_block_to_rowblock(int64_t block, int64_t grid);
  *                 (float)(1.0 / sqrt(m)) with binary64 root and quotient (m > 0 assumed)
  *  n must be a multiple of 8; in/out 16-byte aligned.  Used to pin gfx950's conversion
  *  instructions, and the inverse-RMS sequence, against the reference definitions. */
-enum { RMSQ_CVT_E4M3 = 0, RMSQ_CVT_E2M1 = 1, RMSQ_CVT_BF16 = 2, RMSQ_CVT_INV_SQRT = 3 };
+enum {
+  RMSQ_CVT_E4M3 = 0,
+  RMSQ_CVT_E2M1 = 1,
+  RMSQ_CVT_BF16 = 2,
+  RMSQ_CVT_INV_SQRT = 3,
+  RMSQ_CVT_E4M3_IN_RANGE = 4
+};
 RMSQ_API int rmsq_convert(int format, const float* in, void* out, int64_t n, void* stream);
 
 /* Human-readable text for a status code (static storage). */

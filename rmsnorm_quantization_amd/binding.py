@@ -32,10 +32,11 @@ RMSQ_FP8_STATIC, RMSQ_FP8_TOKEN, RMSQ_FP8_GROUP, RMSQ_FP4_BLOCK16 = 0, 1, 2, 3
 RMSQ_SCALE_COLMAJOR, RMSQ_SCALE_E8M0, RMSQ_SCALE_E8M0_U8 = 1, 2, 4
 RMSQ_INPUT_F16 = 1 << 8
 RMSQ_CVT_E4M3, RMSQ_CVT_E2M1, RMSQ_CVT_BF16, RMSQ_CVT_INV_SQRT = 0, 1, 2, 3
+RMSQ_CVT_E4M3_IN_RANGE = 4
 RMSQ_LAUNCH_XCD_RANGES = 1
 RMSQ_LAUNCH_ROW_TILES = 2
 RMSQ_MAX_HIDDEN = 65536
-RMSQ_ABI_VERSION = 4  # the argument lists below are those of this version
+RMSQ_ABI_VERSION = 5  # the argument lists below are those of this version
 
 
 class RmsqError(RuntimeError):

@@ -290,17 +290,30 @@ int validate_fp4_dynamic(const void* x, const void* res, const void* w, float ep
 // stages each row's inverse RMS there and pass 3 runs one wave per row and reads it: only that
 // wave later writes those bytes.  Otherwise both passes use one launch shape, so that both
 // reduce each row's squares in the same order.
+// Rows per workgroup for the two passes of FP4 with a batch global scale when the caller gives
+// no shape: raised from the default shape's up to 16 (within 1024 threads) while the grid keeps at
+// least 256 workgroups, so a batch in flight all at once still spreads over every CU.  Each
+// row-pass workgroup leaves one maximum, and the block pass's first workgroup (as many rows)
+// reduces them: 4096 rows of one wave leave 256 maxima for a 1024-thread workgroup, 131072 rows
+// still one round of eight loads per thread.
+int32_t batch_rows_per_block(const rmsq_launch& l, int64_t T) {
+  for (int32_t r = 16; r > l.rows_per_block; r /= 2)
+    if ((int64_t)r * l.threads_per_row <= 1024 && T >= 256 * (int64_t)r) return r;
+  return l.rows_per_block;
+}
+
 int fp4_dynamic_impl(const void* x, const void* res, const void* w, float eps, void* q,
                      void* scales, void* res_out, float* global_scale, int64_t T, int64_t H,
                      unsigned flags, const rmsq_launch* launch, void* start_event,
                      void* stop_event, void* stream) {
   int st = validate_fp4_dynamic(x, res, w, eps, q, scales, res_out, global_scale, T, H, flags);
   if (st != RMSQ_OK) return st;
-  const rmsq_launch l = launch ? *launch : default_fused_launch(T, H);
+  rmsq_launch l = launch ? *launch : default_fused_launch(T, H);
   if (!valid_launch(l, H)) return RMSQ_EINVAL;
   if (T == 0) return RMSQ_OK;
   st = check_device();
   if (st != RMSQ_OK) return st;
+  if (!launch) l.rows_per_block = batch_rows_per_block(l, T);
   const bool exact = exact_fit(l, T, H), f16 = (flags & RMSQ_INPUT_F16) != 0;
   const int vpt = l.chunks_per_thread;
   const bool stage = (H % 64) == 0 && H <= 4096 && aligned(scales, 4);
@@ -308,7 +321,14 @@ int fp4_dynamic_impl(const void* x, const void* res, const void* w, float eps, v
   if (stage) {
     l3 = default_launch(H);  // one wave per row (several rows per workgroup for H <= 1024)
     if (l3.threads_per_row != 64) l3 = rmsq_launch{64, (int32_t)((H / 8 + 63) / 64), 1, 0};
+    l3.rows_per_block = batch_rows_per_block(l3, T);
   }
+  // The row pass leaves one maximum per workgroup.  When the block pass's first workgroup can
+  // reduce them in one round (eight loads per thread), it derives and publishes gs itself while
+  // the other workgroups load their rows, and there is no middle launch; otherwise the
+  // one-workgroup reduction runs between the passes.
+  const int64_t nblk = (T + l.rows_per_block - 1) / l.rows_per_block;
+  const bool fold = nblk <= 8 * (int64_t)l3.threads_per_row * l3.rows_per_block;
   const bool exact3 = exact_fit(l3, T, H);
   const void* pass1 = f16 ? amax_kernel_f16(res != nullptr, vpt, exact)
                           : amax_kernel_bf16(res != nullptr, vpt, exact);
@@ -316,7 +336,6 @@ int fp4_dynamic_impl(const void* x, const void* res, const void* w, float eps, v
       f16 ? fused_kernel_f16(RMSQ_FP4_BLOCK16, false, 16, l3.chunks_per_thread, exact3)
           : fused_kernel_bf16(RMSQ_FP4_BLOCK16, false, 16, l3.chunks_per_thread, exact3);
   if (!pass1 || !pass3) return RMSQ_EINVAL;
-  const int64_t nblk = (T + l.rows_per_block - 1) / l.rows_per_block;
   const int threads = l.threads_per_row * l.rows_per_block;
   KArgs a{};
   a.x = static_cast<const uint16_t*>(x);
@@ -324,7 +343,7 @@ int fp4_dynamic_impl(const void* x, const void* res, const void* w, float eps, v
   a.w = static_cast<const uint16_t*>(w);
   a.res_out = static_cast<uint16_t*>(res_out);
   a.q = nullptr;
-  a.scales = q;  // the row maxima, [T] f32 at the start of out_q
+  a.scales = q;  // the workgroup maxima, [nblk] f32 at the start of out_q
   a.scale_in = nullptr;
   a.T = T;
   a.H = H;
@@ -338,21 +357,27 @@ int fp4_dynamic_impl(const void* x, const void* res, const void* w, float eps, v
   a.xcd_ranges = (l.options & RMSQ_LAUNCH_XCD_RANGES) ? 1 : 0;
   a.inv_rows = stage ? static_cast<uint8_t*>(scales) : nullptr;
   a.inv_stride = H / 16;
+  a.gs_out = fold ? global_scale : nullptr;  // cleared to 0: not yet published
   st = launch_kernel(pass1, nblk, threads, &a, stream, start_event, nullptr);
   if (st != RMSQ_OK) return st;
-  GArgs g;
-  g.row_amax = static_cast<const float*>(q);
-  g.gs = global_scale;
-  g.T = T;
-  st = launch_kernel(fp4_global_scale_kernel_ptr(), 1, 1024, &g, stream, nullptr, nullptr);
-  if (st != RMSQ_OK) return st;
+  if (!fold) {
+    GArgs g;
+    g.row_amax = static_cast<const float*>(q);
+    g.gs = global_scale;
+    g.T = nblk;
+    st = launch_kernel(fp4_global_scale_kernel_ptr(), 1, 1024, &g, stream, nullptr, nullptr);
+    if (st != RMSQ_OK) return st;
+  }
   KArgs b = a;
   b.x = res ? static_cast<const uint16_t*>(res_out) : static_cast<const uint16_t*>(x);
   b.res = nullptr;
   b.res_out = nullptr;
   b.q = static_cast<uint8_t*>(q);
   b.scales = scales;
-  b.scale_in = global_scale;
+  b.scale_in = fold ? nullptr : global_scale;
+  b.amax_parts = fold ? static_cast<const float*>(q) : nullptr;
+  b.n_parts = fold ? nblk : 0;
+  b.gs_out = fold ? global_scale : nullptr;
   b.tpr = l3.threads_per_row;
   b.rpb = l3.rows_per_block;
   const int64_t nblk3 = (T + l3.rows_per_block - 1) / l3.rows_per_block;
@@ -855,13 +880,13 @@ int64_t rmsq_block_to_rowblock(int64_t block, int64_t grid) {
 
 int rmsq_convert(int format, const float* in, void* out, int64_t n, void* stream) {
   if (format != RMSQ_CVT_E4M3 && format != RMSQ_CVT_E2M1 && format != RMSQ_CVT_BF16 &&
-      format != RMSQ_CVT_INV_SQRT)
+      format != RMSQ_CVT_INV_SQRT && format != RMSQ_CVT_E4M3_IN_RANGE)
     return RMSQ_EINVAL;
   if (n < 0 || (n % 8) != 0) return RMSQ_EINVAL;
   if (n == 0) return RMSQ_OK;
   if (!in || !out) return RMSQ_EINVAL;
   if (!aligned(in, 16) || !aligned(out, 16)) return RMSQ_EALIGN;
-  const size_t ob = format == RMSQ_CVT_E4M3   ? (size_t)n
+  const size_t ob = (format == RMSQ_CVT_E4M3 || format == RMSQ_CVT_E4M3_IN_RANGE) ? (size_t)n
                     : format == RMSQ_CVT_E2M1 ? (size_t)n / 2
                     : format == RMSQ_CVT_BF16 ? (size_t)n * 2
                                               : (size_t)n * 4;

@@ -95,6 +95,21 @@ __device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
   return (uint32_t)w;
 }
 
+// Four f32 of magnitude at most 464 -> four e4m3fn bytes, with no clamp.  The conversion rounds
+// the magnitude to nearest even: everything up to 464, the midpoint between 448 and the step
+// above it (whose pattern is the NaN code), gives 448, and only larger magnitudes give NaN
+// (checked on the device; pinned against the oracle's saturating encoder over |v| <= 464 by the
+// converter test).  The per-group scheme meets that bound by construction: with s = RN(m/448)
+// and r = RN(1/s) finite, any |y| <= m gives |y * r| <= 448 (1 + 2^-20), also where s is
+// subnormal (then s >= 2^-128 and its relative error is at most 2^-21); E8M0 scales give at most
+// 448.  (Per-token scaling would too, but its widest rows have no register to spare for the
+// different zero-safe step below, and its headline shape hides the clamp behind memory.)
+__device__ __forceinline__ uint32_t fp8x4_in_range(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
 // One f32 -> one e4m3fn byte.
 __device__ __forceinline__ uint32_t fp8x1(float a) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp_sym(a, kFp8Max), 0.0f, 0, false) & 0xFFu;
@@ -125,6 +140,16 @@ __device__ __forceinline__ void zero_safe(float (&y)[8], float& m, bool inf) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) y[e] = inf ? y[e] * 0x1p64f : y[e];
   m = inf ? 0x1p100f : m;
+}
+
+// The same codes for the unclamped FP8 conversion (fp8x4_in_range), whose input must stay
+// within 464: where `inf` holds, a zero y stays itself, any other y becomes +-448 (what it
+// would saturate to), and m becomes 1.  Runs only in waves that meet an infinite multiplier.
+__device__ __forceinline__ void zero_safe_in_range(float (&y)[8], float& m, bool inf) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    y[e] = (inf && y[e] != 0.0f) ? __builtin_copysignf(kFp8Max, y[e]) : y[e];
+  m = inf ? 1.0f : m;
 }
 
 // ---- FP4 e2m1 ----------------------------------------------------------------------------

@@ -35,8 +35,8 @@ constexpr int kMaxWavesPerBlock = 16;
 // with a padded row stride (ld), the padding columns zero.  Not a quantization scheme, so not in
 // rmsq_mode.
 constexpr int kModePad = 4;
-// Internal mode of fused_kernel: no codes, only the row's largest |y| (f32) to scales[row] -- the
-// first pass of FP4 with the global scale taken from the batch.
+// Internal mode of fused_kernel: no codes, only the workgroup's largest |y| (f32, over all its
+// rows) to scales[blockIdx.x] -- the first pass of FP4 with the global scale taken from the batch.
 constexpr int kModeRowAmax = 5;
 
 struct KArgs {
@@ -62,7 +62,68 @@ struct KArgs {
   // the block pass instead of normalizing again; null otherwise
   uint8_t* inv_rows;
   int64_t inv_stride;
+  // FP4 with a batch global scale, the block pass (scale_in null): the row pass's n_parts
+  // workgroup maxima, and the global scale's word.  Workgroup 0 reduces the maxima and publishes
+  // gs = (448 * 6) / amax there; the other workgroups wait for it (batch_scale_*).  In the row
+  // pass (kModeRowAmax) gs_out, if set, is cleared to 0, the "not yet published" value.
+  const float* amax_parts;
+  int64_t n_parts;
+  float* gs_out;
 };
+
+// The FP4 global scale of a batch from its largest |y| (PR #51925 summary: NVFP4 with block
+// scales and a global scale; its test derives a global scale as 448 * 6 over a tensor's absmax):
+// (448 * 6) / amax by IEEE division, or FLT_MAX where that is not finite (amax == 0).  Always a
+// positive normal value (amax <= FLT_MAX), so 0 can mark a global scale not yet published.
+__device__ __forceinline__ float batch_fp4_scale(float amax) {
+  const float g = (kFp8Max * kFp4Max) / amax;
+  return (g <= __FLT_MAX__) ? g : __FLT_MAX__;
+}
+
+// Workgroup 0 of the block pass: the largest of the n row-pass maxima (every thread takes every
+// blockDim-th one, eight loads in flight per round; the host keeps n within one round), then
+// gs, published to *gs_out by an agent-scope store and returned to every thread.  Workgroup 0 is
+// the first one dispatched, so it is resident whatever the others do while they wait.  Must be
+// called by every thread of the workgroup.
+__device__ float batch_scale_publish(const float* parts, int64_t n, float* gs_out, float* s_red) {
+  constexpr int kLoads = 8;
+  const int64_t stride = blockDim.x;
+  float m = 0.0f;
+  for (int64_t base = threadIdx.x; base < n; base += kLoads * stride) {
+    float v[kLoads];
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+      const int64_t i = base + u * stride;
+      v[u] = (i < n) ? parts[i] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) m = fmaxf(m, v[u]);
+  }
+  m = wave_max(m);
+  const int nw = (int)(blockDim.x >> 6);
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = 0.0f;
+  for (int i = 0; i < nw; ++i) m = fmaxf(m, s_red[i]);
+  const float gs = batch_fp4_scale(m);
+  if (threadIdx.x == 0) __hip_atomic_store(gs_out, gs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return gs;
+}
+
+// The other workgroups of the block pass: `seen` is an agent-scope load of *gs_out issued with the
+// row's loads; while it still reads 0, poll (sleeping between polls) until workgroup 0 has
+// published.  The wait is bounded (2^20 polls, about 0.1 s): every wave ends even if the value
+// never came, and a global scale that never came leaves 0, which the host cannot mistake for a
+// result (codes computed from it are garbage; it does not occur while workgroup 0 runs).
+__device__ __forceinline__ float batch_scale_await(float seen, float* gs_out) {
+  float g = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(seen)));
+  for (int it = 0; g == 0.0f && it < (1 << 20); ++it) {
+    __builtin_amdgcn_s_sleep(4);
+    const float r = __hip_atomic_load(gs_out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    g = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(r)));
+  }
+  return g;
+}
 
 // One element of y = (h * inv) * w from the packed 16-bit chunk dwords (DT: 0 bf16, 1 binary16).
 template <int DT = 0>
@@ -189,10 +250,10 @@ __device__ __forceinline__ void quantize_store(const YF& Y, const bool (&ok)[VPT
 #pragma unroll
       for (int k = k0; k < k0 + KB; ++k) {  // codes; a zero scale (zero group) gives zero codes
         const bool inf = !zero[k] && not_finite(r[k]);
-        if (wave_any(inf)) zero_safe(y[k], r[k], inf);  // uniform over the wave
+        if (wave_any(inf)) zero_safe_in_range(y[k], r[k], inf);  // uniform over the wave
         const float rk = r[k];
-        qc[k] = (u32x2){fp8x4(y[k][0] * rk, y[k][1] * rk, y[k][2] * rk, y[k][3] * rk),
-                        fp8x4(y[k][4] * rk, y[k][5] * rk, y[k][6] * rk, y[k][7] * rk)};
+        qc[k] = (u32x2){fp8x4_in_range(y[k][0] * rk, y[k][1] * rk, y[k][2] * rk, y[k][3] * rk),
+                        fp8x4_in_range(y[k][4] * rk, y[k][5] * rk, y[k][6] * rk, y[k][7] * rk)};
         if (zero[k]) qc[k] = (u32x2){0u, 0u};
       }
 #pragma unroll
@@ -216,13 +277,17 @@ __device__ __forceinline__ void quantize_store(const YF& Y, const bool (&ok)[VPT
 #pragma unroll
       for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(Y(k, e)));
     mx = wave_max(mx);
-    if (o.wpr > 1) {  // uniform over the block
+    // One value per workgroup: the largest |y| over all its rows (rows past T hold zeros), at
+    // scales[blockIdx.x].  Only the batch's maximum is needed, and fewer values make its
+    // reduction short enough for the block pass's first workgroup.
+    const int nw = (int)(blockDim.x >> 6);
+    if (nw > 1) {  // uniform over the block
       if ((o.tid & 63) == 0) s_mx[o.tid >> 6] = mx;
       __syncthreads();
       mx = 0.0f;
-      for (int i = 0; i < o.wpr; ++i) mx = fmaxf(mx, s_mx[o.rib * o.wpr + i]);
+      for (int i = 0; i < nw; ++i) mx = fmaxf(mx, s_mx[i]);
     }
-    if (o.lr == 0 && o.row_ok) static_cast<float*>(o.scales)[o.row] = mx;
+    if (o.tid == 0) static_cast<float*>(o.scales)[blockIdx.x] = mx;
   } else if constexpr (MODE == kModePad) {
     // 16-bit row of n values at a stride of ld elements; chunks n/8 .. ld/8-1 are zero padding.
     // The launch covers ld/8 chunks per row (ok[] marks the chunks below n).
@@ -338,7 +403,17 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
   // The per-tensor scale is fetched first, with the row: fetched later it would cost every
   // workgroup a second memory round trip after the reduction.
   float scale_val = 0.0f;
-  if constexpr (MODE == RMSQ_FP8_STATIC || MODE == RMSQ_FP4_BLOCK16) scale_val = a.scale_in[0];
+  if constexpr (MODE == RMSQ_FP8_STATIC) scale_val = a.scale_in[0];
+  if constexpr (MODE == RMSQ_FP4_BLOCK16) {
+    if (a.amax_parts == nullptr) {  // uniform: a launch either has the scale or derives it
+      scale_val = a.scale_in[0];
+    } else if (blockIdx.x == 0) {  // s_mx: not otherwise used by the FP4 epilogue
+      scale_val = batch_scale_publish(a.amax_parts, a.n_parts, a.gs_out, s_mx);
+    }
+  }
+  if constexpr (MODE == kModeRowAmax) {
+    if (a.gs_out != nullptr && blockIdx.x == 0 && tid == 0) *a.gs_out = 0.0f;
+  }
 
   // ---- load: x (+ residual) first, then the weight (an L2 hit), each byte once ----
   u32x4 hv[VPT], wv[VPT], rv[VPT];
@@ -377,6 +452,13 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
     } else if (ok[k]) {
       wv[k] = *boff(wrow, c << 4);
     }
+  }
+
+  // The published global scale, loaded behind the row (used only by the epilogue).
+  float gs_seen = 0.0f;
+  if constexpr (MODE == RMSQ_FP4_BLOCK16) {
+    if (a.amax_parts != nullptr && blockIdx.x != 0)
+      gs_seen = __hip_atomic_load(a.gs_out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // ---- residual add: h = round16(x + r), written back as the new residual ----
@@ -443,6 +525,9 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
   o.wpr = wpr;
   o.rib = rib;
   o.tid = tid;
+  if constexpr (MODE == RMSQ_FP4_BLOCK16) {
+    if (a.amax_parts != nullptr && blockIdx.x != 0) scale_val = batch_scale_await(gs_seen, a.gs_out);
+  }
   quantize_store<MODE, VPT, GS, DT, (VPT >= 3)>(
       [&](int k, int e) { return y_of<DT>(hv[k], wv[k], e, inv); }, ok, o, scale_val, s_mx);
 }
@@ -450,9 +535,10 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
 // ------------------------------------------------------------------ FP4 global scale of a batch
 // The middle launch of FP4 with the global scale taken from the batch (PR #51925 summary: NVFP4
 // with block scales and a global scale; its test derives a global scale as 448 * 6 over a
-// tensor's absmax): one workgroup reduces the T row maxima to the batch's largest |y| and writes
-// gs = (448 * 6) / amax (IEEE division), or FLT_MAX where that is not finite (amax == 0).  The
-// kernel (fp4_global_scale_kernel) is defined in table_misc.hip.
+// tensor's absmax), where the block pass's first workgroup cannot reduce the row pass's maxima
+// in one round of loads: one workgroup reduces the T maxima to the batch's largest |y| and
+// writes gs (batch_fp4_scale).  The kernel (fp4_global_scale_kernel) is defined in
+// table_misc.hip.
 struct GArgs {
   const float* row_amax;  // [T], non-negative
   float* gs;              // [1]

@@ -57,7 +57,7 @@ def test_library_exports_every_declared_symbol(B):
 
 
 def test_abi_version_and_status_strings(B):
-    assert B.rmsq_abi_version() == B.RMSQ_ABI_VERSION == 4
+    assert B.rmsq_abi_version() == B.RMSQ_ABI_VERSION == 5
     for st in (0, -1, -2, -3, -4, -5, -6):
         assert B.rmsq_status_string(st) and B.rmsq_status_string(st) != "unknown status"
     assert B.rmsq_status_string(-99) == "unknown status"
@@ -190,6 +190,9 @@ def test_block_to_rowblock_is_a_bijection(B, grid):
 def test_convert_argument_checks(B):
     L = B.lib()
     assert L.rmsq_convert(7, X, Q, 8, None) == B.RMSQ_EINVAL
+    assert L.rmsq_convert(5, X, Q, 8, None) == B.RMSQ_EINVAL
+    assert L.rmsq_convert(B.RMSQ_CVT_E4M3_IN_RANGE, X, X + 16, 8, None) == B.RMSQ_EALIAS
+    assert L.rmsq_convert(B.RMSQ_CVT_E4M3_IN_RANGE, X, Q, 12, None) == B.RMSQ_EINVAL
     assert L.rmsq_convert(0, X, Q, 12, None) == B.RMSQ_EINVAL
     assert L.rmsq_convert(0, X, Q, 0, None) == B.RMSQ_OK
     assert L.rmsq_convert(0, X + 4, Q, 8, None) == B.RMSQ_EALIGN

@@ -1,8 +1,8 @@
 """Pin gfx950's conversion instructions, as the kernels use them, against the oracle's formats.
 
-rmsq_convert runs the kernels' own helpers (clamp + v_cvt_pk_fp8_f32; clamp +
-v_cvt_scalef32_pk_fp4_f32 with a unit scale and the nibble packing; v_cvt_pk_bf16_f32) over
-arbitrary f32 inputs.  Checked on every bf16 value, every rounding midpoint of the target
+rmsq_convert runs the kernels' own helpers (clamp + v_cvt_pk_fp8_f32, and v_cvt_pk_fp8_f32
+alone over |v| <= 464; v_cvt_scalef32_pk_fp4_f32 with a unit scale and the nibble packing;
+v_cvt_pk_bf16_f32) over arbitrary f32 inputs.  Checked on every bf16 value, every rounding midpoint of the target
 format and +-1 ulp around it, saturation, signed zeros, and a large random sample of f32 bit
 patterns.  NaN inputs are outside the contract and are left out.
 """
@@ -49,8 +49,8 @@ def _inputs(table, sat):
 def _convert(fmt, v):
     vin = torch.from_numpy(v).to("cuda")
     n = v.size
-    nbytes = {B.RMSQ_CVT_E4M3: n, B.RMSQ_CVT_E2M1: n // 2, B.RMSQ_CVT_BF16: 2 * n,
-              B.RMSQ_CVT_INV_SQRT: 4 * n}[fmt]
+    nbytes = {B.RMSQ_CVT_E4M3: n, B.RMSQ_CVT_E4M3_IN_RANGE: n, B.RMSQ_CVT_E2M1: n // 2,
+              B.RMSQ_CVT_BF16: 2 * n, B.RMSQ_CVT_INV_SQRT: 4 * n}[fmt]
     g = GH.Guarded(nbytes)
     print(f"[convert] fmt={fmt} n={n}", flush=True)
     B.rmsq_convert(fmt, vin, g.data, n)
@@ -65,6 +65,29 @@ def test_e4m3_conversion_matches_oracle():
     exp = O.e4m3_encode(v)
     bad = got != exp
     assert not bad.any(), f"{bad.sum()} mismatches, e.g. {v[bad][:8]} -> {got[bad][:8]} vs {exp[bad][:8]}"
+
+
+def test_e4m3_in_range_conversion_matches_oracle():
+    """The per-group scheme converts without a clamp: its inputs stay within
+    448 (1 + 2^-20).  Up to 464 (the midpoint between 448 and the step above it) the codes are
+    the saturating encoder's; every value in (448, 464], and the first values past 448 in f32
+    steps, included.  Past 464 the instruction gives the NaN code of the value's sign -- the
+    reason the bound matters."""
+    v = _inputs(O.e4m3_table(), 448.0)
+    v = v[np.abs(v) <= 464.0]
+    i = np.arange(1, 4097, dtype=np.uint32)
+    above = (np.uint32(np.float32(448.0).view(np.uint32)) + i).view(np.float32)
+    edge = np.array([464.0, np.nextafter(np.float32(464.0), np.float32(0)), 456.0, 463.5,
+                     448.0 * (1 + 2.0 ** -20)], np.float32)
+    v = _pad8(np.concatenate([v, above[above <= 464.0], edge, -above[above <= 464.0], -edge]))
+    got = _convert(B.RMSQ_CVT_E4M3_IN_RANGE, v)
+    exp = O.e4m3_encode(v)
+    bad = got != exp
+    assert not bad.any(), f"{bad.sum()} mismatches, e.g. {v[bad][:8]} -> {got[bad][:8]} vs {exp[bad][:8]}"
+    past = _pad8(np.array([np.nextafter(np.float32(464.0), np.float32(1e9)), 480.0, 1e30,
+                           -np.nextafter(np.float32(464.0), np.float32(1e9)), -480.0], np.float32))
+    got = _convert(B.RMSQ_CVT_E4M3_IN_RANGE, past)[:5]
+    assert list(got) == [0x7F, 0x7F, 0x7F, 0xFF, 0xFF]
 
 
 def test_e2m1_conversion_and_packing_match_oracle():

@@ -1,8 +1,11 @@
 """GPU parity of FP4 block-16 with the global scale taken from the batch
 (rmsq_fused_fp4_dynamic, through the C ABI) against the oracle.
 
-Three launches: residual add + RMSNorm with each row's largest |y|, the reduction of those to
-gs = (448 * 6) / amax, and the block quantization of the normalized input.  The global scale is
+Two launches: residual add + RMSNorm with each workgroup's largest |y|, and the block
+quantization of the normalized input, whose first workgroup reduces those maxima to
+gs = (448 * 6) / amax and hands it to the others through global_scale; with more maxima than that
+workgroup reduces in one round, a one-workgroup reduction launch runs between the two (covered by
+test_middle_reduction_launch).  The global scale is
 asserted bit-exact (both sides take the same f32 maximum and the same IEEE division); codes,
 block scales and the new residual follow the static FP4 comparison rule of tests/parity.py.
 Guard bands around every output catch stray writes.
@@ -95,6 +98,16 @@ def check(x, r, w, **kw):
 def test_shapes(T, H, residual):
     x, r, w = _inputs(T, H, T * 3 + H, residual=residual)
     check(x, r, w)
+
+
+@pytest.mark.parametrize("launch", [None, (64, 1, 1)])
+def test_middle_reduction_launch(launch):
+    """8200 rows of 64: the default shape takes 16 rows to a workgroup in both passes (513
+    maxima, one round for the block pass's first workgroup: two launches); a caller's one row to
+    a workgroup leaves 8200 maxima, more than eight per thread of a 1024-thread workgroup, so
+    the one-workgroup reduction runs between the passes.  Both against the oracle."""
+    x, r, w = _inputs(8200, 64, 10)
+    check(x, r, w, launch=None if launch is None else B.rmsq_launch(*launch, 0))
 
 
 @pytest.mark.parametrize("T,H", [(1, 2048), (37, 2048), (512, 4096), (1024, 2048)])

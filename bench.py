@@ -321,8 +321,9 @@ def _probe_lib():
         hb.build_probe_library()
     L = ctypes.CDLL(hb.PROBE_LIB)
     p = ctypes.c_void_p
-    L.rmsq_probe_stream.argtypes = [p, p, p, p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
-                                    ctypes.c_int, ctypes.c_int, p, p, p]
+    i32 = ctypes.c_int
+    L.rmsq_probe_stream.argtypes = [p, p, p, p, p, ctypes.c_int64, ctypes.c_int64, i32, i32, i32,
+                                    i32, i32, p, p, p]
     L.rmsq_probe_stream.restype = ctypes.c_int
     return L
 
@@ -347,12 +348,12 @@ def copy_ceiling(dev, stream):
     torch.cuda.synchronize()
     for i in range(4):  # lead-in, no host synchronization before the timed copies
         src, dst = pairs[i % 2]
-        L.rmsq_probe_stream(src.data_ptr(), None, dst.data_ptr(), None, rows, H, 0, 256, 2,
-                            None, None, sh)
+        L.rmsq_probe_stream(src.data_ptr(), None, dst.data_ptr(), None, None, rows, H, 0, 0, 0,
+                            256, 2, None, None, sh)
     for i, (a_, b_) in enumerate(evs):
         src, dst = pairs[i % 2]
-        st = L.rmsq_probe_stream(src.data_ptr(), None, dst.data_ptr(), None, rows, H, 0, 256, 2,
-                                 a_.cuda_event, b_.cuda_event, sh)
+        st = L.rmsq_probe_stream(src.data_ptr(), None, dst.data_ptr(), None, None, rows, H, 0,
+                                 0, 0, 256, 2, a_.cuda_event, b_.cuda_event, sh)
         if st:
             raise RuntimeError(f"rmsq_probe_stream (copy) failed ({st})")
     torch.cuda.synchronize()
@@ -579,7 +580,7 @@ def gpu_leg(args, wl, T, H, mode, G, flags, with_copy=True):
     # per workgroup, exact fit): the practical ceiling for this exact access pattern
     ceiling = None
     if wl.kind == "norm" and shape[2] == 1 and shape[0] * shape[1] * 8 == H:
-        ceiling = probe_leg(args, sets, T, H, mode, shape, stream, evs)
+        ceiling = probe_leg(args, sets, T, H, mode, shape, stream, evs, G=G, flags=flags)
 
     # a plain device copy, for context (practical HBM ceiling)
     copy_gbs = copy_ceiling(dev, stream) if with_copy else None
@@ -662,16 +663,33 @@ def configs_leg(args, main):
     return out
 
 
-def probe_leg(args, sets, T, H, mode, shape, stream, evs):
+def probe_scale_stream(mode, H, G, flags):
+    """The probe's scale-like stream for a scheme: (shift, bytes per element) -- one f32 per row
+    (per-token), per group of G/8 chunks (f32, or a byte for E8M0 bytes), a byte per two chunks
+    (FP4 block-16) -- or None (static: no scales).  Column-major group scales are stored
+    row-major by the probe (the same bytes, another pattern)."""
+    if mode == 1:
+        return (-1, 4)
+    if mode == 2:
+        return ((G // 8).bit_length() - 1, 1 if flags & 4 else 4)
+    if mode == 3:
+        return (1, 1)
+    return None
+
+
+def probe_leg(args, sets, T, H, mode, shape, stream, evs, G=0, flags=0):
     """Time librmsq_probe.so's memory-only kernel over the same buffer sets: it reads x and the
-    residual and writes the new residual and codes-sized output in the fused kernel's layout,
-    with no arithmetic.  Returns its mean dispatch-stamped duration and bytes."""
+    residual and writes the new residual, codes-sized and scales-sized outputs in the fused
+    kernel's layout, with no arithmetic.  Returns its mean dispatch-stamped duration and bytes."""
     L = _probe_lib()
     out1 = 4 if mode == 3 else 8
+    sc = probe_scale_stream(mode, H, G, flags)
+    shift, sbytes = sc if sc else (0, 0)
     ptr = (lambda t: None if t is None else t.data_ptr())
     sh = stream.cuda_stream
-    argsets = [(ptr(s_["x"]), ptr(s_["r"]), ptr(s_["ro"]), ptr(s_["q"]), T, H, out1, shape[0],
-                shape[1]) for s_ in sets]
+    argsets = [(ptr(s_["x"]), ptr(s_["r"]), ptr(s_["ro"]), ptr(s_["q"]),
+                ptr(s_["s"]) if sc else None, T, H, out1, shift, sbytes, shape[0], shape[1])
+               for s_ in sets]
     import torch
 
     torch.cuda.synchronize()
@@ -688,6 +706,8 @@ def probe_leg(args, sets, T, H, mode, shape, stream, evs):
     per = sorted(a.elapsed_time(b) for a, b in evs)
     nbytes = T * (2 * H + (2 * H if sets[0]["r"] is not None else 0)
                   + (2 * H if sets[0]["ro"] is not None else 0) + H * out1 // 8)
+    if sc:
+        nbytes += T * sbytes * (1 if shift < 0 else (H // 8) >> shift)
     return {"kernel_us": sum(per) / len(per) * 1e3, "median_us": per[len(per) // 2] * 1e3,
             "bytes": nbytes}
 

@@ -332,9 +332,8 @@ int fp4_dynamic_impl(const void* x, const void* res, const void* w, float eps, v
   const bool exact3 = exact_fit(l3, T, H);
   const void* pass1 = f16 ? amax_kernel_f16(res != nullptr, vpt, exact)
                           : amax_kernel_bf16(res != nullptr, vpt, exact);
-  const void* pass3 =
-      f16 ? fused_kernel_f16(RMSQ_FP4_BLOCK16, false, 16, l3.chunks_per_thread, exact3)
-          : fused_kernel_bf16(RMSQ_FP4_BLOCK16, false, 16, l3.chunks_per_thread, exact3);
+  const void* pass3 = f16 ? batch_fp4_kernel_f16(l3.chunks_per_thread, exact3)
+                          : batch_fp4_kernel_bf16(l3.chunks_per_thread, exact3);
   if (!pass1 || !pass3) return RMSQ_EINVAL;
   const int threads = l.threads_per_row * l.rows_per_block;
   KArgs a{};

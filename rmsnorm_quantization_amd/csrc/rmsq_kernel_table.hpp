@@ -14,6 +14,9 @@ const void* fused_kernel_f16(int mode, bool res, int gs, int vpt, bool exact);
 // (residual add ->) RMSNorm -> each row's largest |y| (first pass of FP4 with a batch scale)
 const void* amax_kernel_bf16(bool res, int vpt, bool exact);
 const void* amax_kernel_f16(bool res, int vpt, bool exact);
+// the block pass of FP4 with a batch scale (no residual: it reads the new residual or x)
+const void* batch_fp4_kernel_bf16(int vpt, bool exact);
+const void* batch_fp4_kernel_f16(int vpt, bool exact);
 // (residual add ->) RMSNorm -> padded 16-bit output (launches always masked)
 const void* pad_kernel_bf16(bool res, int vpt);
 const void* pad_kernel_f16(bool res, int vpt);

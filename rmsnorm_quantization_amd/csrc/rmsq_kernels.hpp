@@ -38,6 +38,12 @@ constexpr int kModePad = 4;
 // Internal mode of fused_kernel: no codes, only the workgroup's largest |y| (f32, over all its
 // rows) to scales[blockIdx.x] -- the first pass of FP4 with the global scale taken from the batch.
 constexpr int kModeRowAmax = 5;
+// Internal mode of fused_kernel: FP4 block-16 as the block pass of FP4 with the global scale
+// taken from the batch -- the inverse RMS read from the row pass's staging (inv_rows) rather than
+// recomputed where the row pass left it, and the global scale either read (scale_in) or derived by
+// workgroup 0 from the row pass's maxima and waited for by the others (amax_parts).  Its own
+// instantiations, so that plain FP4 carries none of it.
+constexpr int kModeFp4Batch = 6;
 
 struct KArgs {
   const uint16_t* x;
@@ -403,8 +409,8 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
   // The per-tensor scale is fetched first, with the row: fetched later it would cost every
   // workgroup a second memory round trip after the reduction.
   float scale_val = 0.0f;
-  if constexpr (MODE == RMSQ_FP8_STATIC) scale_val = a.scale_in[0];
-  if constexpr (MODE == RMSQ_FP4_BLOCK16) {
+  if constexpr (MODE == RMSQ_FP8_STATIC || MODE == RMSQ_FP4_BLOCK16) scale_val = a.scale_in[0];
+  if constexpr (MODE == kModeFp4Batch) {
     if (a.amax_parts == nullptr) {  // uniform: a launch either has the scale or derives it
       scale_val = a.scale_in[0];
     } else if (blockIdx.x == 0) {  // s_mx: not otherwise used by the FP4 epilogue
@@ -456,7 +462,7 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
 
   // The published global scale, loaded behind the row (used only by the epilogue).
   float gs_seen = 0.0f;
-  if constexpr (MODE == RMSQ_FP4_BLOCK16) {
+  if constexpr (MODE == kModeFp4Batch) {
     if (a.amax_parts != nullptr && blockIdx.x != 0)
       gs_seen = __hip_atomic_load(a.gs_out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -477,7 +483,7 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
   }
 
   float inv;
-  if (MODE == RMSQ_FP4_BLOCK16 && a.inv_rows != nullptr) {
+  if (MODE == kModeFp4Batch && a.inv_rows != nullptr) {
     // the block pass of FP4 with a batch scale (one wave per row, uniform branch): the row
     // pass's inverse RMS, staged in this row's own block-scale bytes; every store of this wave
     // depends on it, so the load completes before the wave overwrites those bytes
@@ -525,10 +531,11 @@ __global__ void __launch_bounds__(1024) fused_kernel(KArgs a) {
   o.wpr = wpr;
   o.rib = rib;
   o.tid = tid;
-  if constexpr (MODE == RMSQ_FP4_BLOCK16) {
+  if constexpr (MODE == kModeFp4Batch) {
     if (a.amax_parts != nullptr && blockIdx.x != 0) scale_val = batch_scale_await(gs_seen, a.gs_out);
   }
-  quantize_store<MODE, VPT, GS, DT, (VPT >= 3)>(
+  constexpr int QMODE = (MODE == kModeFp4Batch) ? RMSQ_FP4_BLOCK16 : MODE;
+  quantize_store<QMODE, VPT, GS, DT, (VPT >= 3)>(
       [&](int k, int e) { return y_of<DT>(hv[k], wv[k], e, inv); }, ok, o, scale_val, s_mx);
 }
 

@@ -19,8 +19,10 @@ struct ProbeArgs {
   const u32x4* in1;
   u32x4* out0;
   uint8_t* out1;
+  uint8_t* out2;
   int64_t nch;  // 16-byte chunks per row
   int32_t tpr;
+  int32_t out2_shift;  // an out2 element per 2^shift chunks; -1: one per row
 };
 
 // Row base pointers are uniform over the workgroup (scalar registers) and each lane adds a 32-bit
@@ -36,7 +38,7 @@ __device__ __forceinline__ const T* boff(const T* p, uint32_t bytes) {
 
 // One row; IN1 / OUT0: whether the second input and the first output are present (uniform
 // over the launch, so each combination is its own straight-line body).
-template <int VPT, int OUT1, bool IN1, bool OUT0>
+template <int VPT, int OUT1, int OUT2, bool IN1, bool OUT0>
 __device__ __forceinline__ void probe_row(const ProbeArgs& a) {
   const size_t base = (size_t)blockIdx.x * (size_t)a.nch;  // the row's first chunk
   const uint32_t lr = threadIdx.x;
@@ -58,33 +60,49 @@ __device__ __forceinline__ void probe_row(const ProbeArgs& a) {
       __builtin_nontemporal_store(v[k][0] ^ v[k][1] ^ v[k][2] ^ v[k][3],
                                   boff(reinterpret_cast<uint32_t*>(a.out1) + base, c << 2));
     }
+    if constexpr (OUT2 != 0) {  // scale-like stream: the lane that starts each element's chunks
+      const bool per_row = a.out2_shift < 0;
+      const uint32_t sh = per_row ? 0u : (uint32_t)a.out2_shift;
+      if (per_row ? c == 0 : (c & ((1u << sh) - 1u)) == 0) {
+        const size_t idx = per_row ? (size_t)blockIdx.x
+                                   : (size_t)blockIdx.x * (size_t)(a.nch >> sh) + (c >> sh);
+        const uint32_t val = v[k][0] ^ v[k][3];
+        if constexpr (OUT2 == 4) reinterpret_cast<uint32_t*>(a.out2)[idx] = val;
+        else a.out2[idx] = (uint8_t)val;
+      }
+    }
   }
 }
 
-template <int VPT, int OUT1>
+template <int VPT, int OUT1, int OUT2>
 __global__ void __launch_bounds__(1024) stream_probe_kernel(ProbeArgs a) {
   if (a.in1) {
-    if (a.out0) probe_row<VPT, OUT1, true, true>(a);
-    else probe_row<VPT, OUT1, true, false>(a);
+    if (a.out0) probe_row<VPT, OUT1, OUT2, true, true>(a);
+    else probe_row<VPT, OUT1, OUT2, true, false>(a);
   } else {
-    if (a.out0) probe_row<VPT, OUT1, false, true>(a);
-    else probe_row<VPT, OUT1, false, false>(a);
+    if (a.out0) probe_row<VPT, OUT1, OUT2, false, true>(a);
+    else probe_row<VPT, OUT1, OUT2, false, false>(a);
   }
 }
 
-template <int OUT1>
+template <int OUT1, int OUT2>
 const void* pick(int vpt) {
   switch (vpt) {
-    case 1: return reinterpret_cast<const void*>(&stream_probe_kernel<1, OUT1>);
-    case 2: return reinterpret_cast<const void*>(&stream_probe_kernel<2, OUT1>);
-    case 3: return reinterpret_cast<const void*>(&stream_probe_kernel<3, OUT1>);
-    case 4: return reinterpret_cast<const void*>(&stream_probe_kernel<4, OUT1>);
-    case 5: return reinterpret_cast<const void*>(&stream_probe_kernel<5, OUT1>);
-    case 6: return reinterpret_cast<const void*>(&stream_probe_kernel<6, OUT1>);
-    case 7: return reinterpret_cast<const void*>(&stream_probe_kernel<7, OUT1>);
-    case 8: return reinterpret_cast<const void*>(&stream_probe_kernel<8, OUT1>);
+    case 1: return reinterpret_cast<const void*>(&stream_probe_kernel<1, OUT1, OUT2>);
+    case 2: return reinterpret_cast<const void*>(&stream_probe_kernel<2, OUT1, OUT2>);
+    case 3: return reinterpret_cast<const void*>(&stream_probe_kernel<3, OUT1, OUT2>);
+    case 4: return reinterpret_cast<const void*>(&stream_probe_kernel<4, OUT1, OUT2>);
+    case 5: return reinterpret_cast<const void*>(&stream_probe_kernel<5, OUT1, OUT2>);
+    case 6: return reinterpret_cast<const void*>(&stream_probe_kernel<6, OUT1, OUT2>);
+    case 7: return reinterpret_cast<const void*>(&stream_probe_kernel<7, OUT1, OUT2>);
+    case 8: return reinterpret_cast<const void*>(&stream_probe_kernel<8, OUT1, OUT2>);
     default: return nullptr;
   }
+}
+
+template <int OUT2>
+const void* pick_out1(int ob, int vpt) {
+  return ob == 8 ? pick<8, OUT2>(vpt) : ob == 4 ? pick<4, OUT2>(vpt) : pick<0, OUT2>(vpt);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -92,7 +110,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 }  // namespace
 
 extern "C" int rmsq_probe_stream(const void* in0, const void* in1, void* out0, void* out1,
-                                 int64_t rows, int64_t hidden, int out1_bytes_per_chunk,
+                                 void* out2, int64_t rows, int64_t hidden,
+                                 int out1_bytes_per_chunk, int out2_shift, int out2_bytes,
                                  int threads_per_row, int chunks_per_thread, void* start_event,
                                  void* stop_event, void* stream) {
   if (rows < 0 || rows > 0x7FFFFFFFLL || hidden < 8 || hidden % 8 != 0) return -1;
@@ -101,20 +120,29 @@ extern "C" int rmsq_probe_stream(const void* in0, const void* in1, void* out0, v
   if ((int64_t)threads_per_row * chunks_per_thread * 8 != hidden) return -1;
   if (out1_bytes_per_chunk != 0 && out1_bytes_per_chunk != 4 && out1_bytes_per_chunk != 8)
     return -1;
+  if (out2) {
+    if (out2_bytes != 1 && out2_bytes != 4) return -1;
+    if (out2_shift < -1 || out2_shift > 6) return -1;
+    if (out2_shift >= 0 && ((hidden / 8) & ((int64_t(1) << out2_shift) - 1)) != 0) return -1;
+    if (out2_bytes == 4 && (reinterpret_cast<uintptr_t>(out2) & 3) != 0) return -2;
+  }
   if (rows == 0) return 0;
   if (!in0) return -1;
   if (!aligned16(in0) || !aligned16(in1) || !aligned16(out0) || !aligned16(out1)) return -2;
   const int ob = out1 ? out1_bytes_per_chunk : 0;  // no out1 buffer: nothing written there
-  const void* fn = ob == 8 ? pick<8>(chunks_per_thread)
-                   : ob == 4 ? pick<4>(chunks_per_thread)
-                             : pick<0>(chunks_per_thread);
+  const int o2 = out2 ? out2_bytes : 0;
+  const void* fn = o2 == 4   ? pick_out1<4>(ob, chunks_per_thread)
+                   : o2 == 1 ? pick_out1<1>(ob, chunks_per_thread)
+                             : pick_out1<0>(ob, chunks_per_thread);
   ProbeArgs a;
   a.in0 = static_cast<const u32x4*>(in0);
   a.in1 = static_cast<const u32x4*>(in1);
   a.out0 = static_cast<u32x4*>(out0);
   a.out1 = ob ? static_cast<uint8_t*>(out1) : nullptr;
+  a.out2 = static_cast<uint8_t*>(out2);
   a.nch = hidden / 8;
   a.tpr = threads_per_row;
+  a.out2_shift = out2_shift;
   void* args[] = {&a};
   const hipError_t e = hipExtLaunchKernel(
       fn, dim3((uint32_t)rows), dim3((uint32_t)threads_per_row), args, 0,

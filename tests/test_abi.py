@@ -398,17 +398,23 @@ def test_probe_library_exports_and_checks_arguments():
     assert {e for e in exported if "rmsq" in e} == {"rmsq_probe_stream"}
     L = ctypes.CDLL(build.PROBE_LIB)
     p = ctypes.c_void_p
-    L.rmsq_probe_stream.argtypes = [p, p, p, p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
-                                    ctypes.c_int, ctypes.c_int, p, p, p]
+    i32 = ctypes.c_int
+    L.rmsq_probe_stream.argtypes = [p, p, p, p, p, ctypes.c_int64, ctypes.c_int64, i32, i32, i32,
+                                    i32, i32, p, p, p]
 
-    def call(rows=4, hidden=4096, out1=8, tpr=256, vpt=2, a=X, b=R, c=RO, d=Q):
-        return L.rmsq_probe_stream(a, b, c, d, rows, hidden, out1, tpr, vpt, None, None, None)
+    def call(rows=4, hidden=4096, out1=8, tpr=256, vpt=2, a=X, b=R, c=RO, d=Q, e=None, shift=0,
+             eb=4):
+        return L.rmsq_probe_stream(a, b, c, d, e, rows, hidden, out1, shift, eb, tpr, vpt, None,
+                                   None, None)
 
     assert call(rows=0) == 0
+    assert call(rows=0, e=SC, shift=4) == 0 and call(rows=0, e=SC, shift=-1) == 0
     for kw in (dict(hidden=4000), dict(tpr=96), dict(tpr=2048, vpt=1, hidden=16384),
-               dict(vpt=9), dict(tpr=256, vpt=3), dict(out1=2), dict(rows=-1), dict(a=None)):
+               dict(vpt=9), dict(tpr=256, vpt=3), dict(out1=2), dict(rows=-1), dict(a=None),
+               dict(e=SC, shift=7), dict(e=SC, shift=-2), dict(e=SC, eb=2)):
         assert call(**kw) == -1, kw
-    assert call(a=X + 8) == -2 and call(d=Q + 4) == -2
+    assert call(a=X + 8) == -2 and call(d=Q + 4) == -2 and call(e=SC + 2, shift=3) == -2
+    assert call(rows=0, e=SC + 1, eb=1) == 0  # a byte stream needs no alignment
 
 
 def test_input_f16_flag_is_accepted_by_the_quantizing_ops(B):

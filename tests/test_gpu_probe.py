@@ -17,8 +17,9 @@ def L():
 
     lib = ctypes.CDLL(build.PROBE_LIB)
     p = ctypes.c_void_p
-    lib.rmsq_probe_stream.argtypes = [p, p, p, p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
-                                      ctypes.c_int, ctypes.c_int, p, p, p]
+    i32 = ctypes.c_int
+    lib.rmsq_probe_stream.argtypes = [p, p, p, p, p, ctypes.c_int64, ctypes.c_int64, i32, i32,
+                                      i32, i32, i32, p, p, p]
     return lib
 
 
@@ -32,7 +33,7 @@ def test_probe_outputs(L, H, tpr, vpt, out1):
     c = GH.Guarded(T * H * 2)
     d = GH.Guarded(T * H * out1 // 8)
     st = L.rmsq_probe_stream(a.data_ptr(), b.data_ptr(), c.data.data_ptr(), d.data.data_ptr(),
-                             T, H, out1, tpr, vpt, None, None,
+                             None, T, H, out1, 0, 0, tpr, vpt, None, None,
                              torch.cuda.current_stream().cuda_stream)
     assert st == 0
     torch.cuda.synchronize()
@@ -61,8 +62,8 @@ def test_probe_stream_subsets(L, with_in1, with_out0, out1):
     print(f"[probe] in1={with_in1} out0={with_out0} out1={out1}", flush=True)
     st = L.rmsq_probe_stream(a.data_ptr(), b.data_ptr() if with_in1 else None,
                              c.data.data_ptr() if with_out0 else None,
-                             d.data.data_ptr() if out1 else None, T, H, out1, tpr, vpt, None,
-                             None, torch.cuda.current_stream().cuda_stream)
+                             d.data.data_ptr() if out1 else None, None, T, H, out1, 0, 0, tpr,
+                             vpt, None, None, torch.cuda.current_stream().cuda_stream)
     assert st == 0
     torch.cuda.synchronize()
     c.check("out0")
@@ -78,3 +79,32 @@ def test_probe_stream_subsets(L, with_in1, with_out0, out1):
     elif out1 == 4:
         ref = (x[..., 0] ^ x[..., 1] ^ x[..., 2] ^ x[..., 3])[..., None]
         assert torch.equal(d.data.view(torch.int32).view(T, H // 8, 1), ref)
+
+
+@pytest.mark.parametrize("shift,nbytes", [(-1, 4), (4, 4), (3, 4), (4, 1), (1, 1)])
+def test_probe_scale_stream(L, shift, nbytes):
+    """The scale-like stream: one element per row (shift -1) or per 2^shift chunks, written by
+    the thread of the element's first chunk with the XOR of that chunk's words 0 and 3."""
+    T, H, tpr, vpt = 23, 2048, 128, 2
+    g = torch.Generator().manual_seed(11 + shift)
+    a = torch.randint(-2**31, 2**31 - 1, (T, H // 2), generator=g, dtype=torch.int32).cuda()
+    per_row = 1 if shift < 0 else (H // 8) >> shift
+    e = GH.Guarded(T * per_row * nbytes)
+    print(f"[probe] scale stream shift={shift} bytes={nbytes}", flush=True)
+    st = L.rmsq_probe_stream(a.data_ptr(), None, None, None, e.data.data_ptr(), T, H, 0, shift,
+                             nbytes, tpr, vpt, None, None, torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    e.check("out2")
+    x = a.view(T, H // 8, 4)
+    starts = x[:, :1] if shift < 0 else x[:, ::1 << shift]
+    val = starts[..., 0] ^ starts[..., 3]
+    if nbytes == 4:
+        assert torch.equal(e.data.view(torch.int32).view(T, per_row), val)
+    else:
+        assert torch.equal(e.data.view(T, per_row), (val & 0xFF).to(torch.uint8))
+    # shapes the stream does not fit are refused
+    assert L.rmsq_probe_stream(a.data_ptr(), None, None, None, e.data.data_ptr(), T, H, 0, 7,
+                               nbytes, tpr, vpt, None, None, None) == -1
+    assert L.rmsq_probe_stream(a.data_ptr(), None, None, None, e.data.data_ptr(), T, H, 0, shift,
+                               2, tpr, vpt, None, None, None) == -1

@@ -1027,7 +1027,7 @@ def main():
         wl, T, H, mode, G, flags = workload_spec(args)
         key = f"{args.workload}_T{T}_H{H}_{MODE_NAMES[mode]}_G{G}_f{flags}"
         family = {"act": "silu_mul_kernel", "rope": "qk_norm_rope_kernel",
-                  "fp4dyn": "fused_kernel_x3"}.get(wl.kind, "fused_kernel")
+                  "fp4dyn": "fused_kernel_x2"}.get(wl.kind, "fused_kernel")
         md = args.summary_md or os.path.join(ROOT, "profiles", f"{family}_{key}.md")
         if wl.kind == "rope":
             title = (f"{family}, {wl.name}: {T} tokens x {wl.heads[0]} q + {wl.heads[1]} k heads "

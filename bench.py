@@ -18,7 +18,7 @@ data.  Prints ONE JSON line:
 
 Other workloads (--workload w0..w8; w5 is SiLU+Mul -> quant with --quant
 static|token|group|fp4, w6 add+RMSNorm -> padded bf16, w7 QK-norm + RoPE, w8 add+RMSNorm -> FP4
-with the global scale taken from the batch, three launches timed as one step) and forced launch
+with the global scale taken from the batch, two launches timed as one step) and forced launch
 shapes (--launch tpr,vpt,rpb[,options]; for w7 --launch heads_per_block,heads_per_lane) are
 for exploration;
 only one GPU is supported (--gpus above 1 exits with a message).
@@ -117,18 +117,19 @@ def rope_bytes(T, hq, hkv, D):
 
 
 def fp4dyn_bytes(T, H, residual=True):
-    """FP4 with the global scale from the batch, as three launches: the row pass reads x (and
-    the residual) and the weight and writes the new residual and T row maxima; the reduction
-    reads the maxima and writes gs; the block pass reads the normalized input again (the new
-    residual, or x), the weight and gs and writes codes and block scales.  The second read of
-    the input (2H per token) is inherent: gs depends on every row."""
+    """FP4 with the global scale from the batch: the row pass reads x (and the residual) and the
+    weight and writes the new residual and the row maxima (one per workgroup of rows, counted
+    here as T, an upper bound worth 0.05% of the total); their reduction reads them and writes
+    gs; the block pass reads the normalized input again (the new residual, or x) and the weight
+    and writes codes and block scales.  The second read of the input (2H per token) is
+    inherent: gs depends on every row."""
     rd = 2 * T * H + (2 * T * H if residual else 0) + 2 * H + 4 * T + 2 * T * H + 2 * H + 4
     wr = (2 * T * H if residual else 0) + 4 * T + 4 + T * H // 2 + T * (H // 16)
     return rd, wr
 
 
 def fp4dyn_leg(args, wl, T, H):
-    """GPU timing of rmsq_fused_fp4_dynamic (three launches per step), structured like gpu_leg;
+    """GPU timing of rmsq_fused_fp4_dynamic (two launches per step), structured like gpu_leg;
     the per-step duration runs from the first launch's dispatch to the last one's end."""
     import torch
 

@@ -158,9 +158,14 @@ def test_graph_qk_norm_rope():
     _replay_check(launch, outs, "qk_norm_rope", inplace_source=qkv0)
 
 
-def test_graph_fp4_dynamic():
-    """Three launches (row pass, global-scale reduction, block quantization) in one graph."""
-    T, H = 40, 2048
+@pytest.mark.parametrize("T,H,launch", [(40, 2048, None), (4096, 2048, None),
+                                         (8200, 64, (64, 1, 1))])
+def test_graph_fp4_dynamic(T, H, launch):
+    """Batch-scale FP4 in one graph: two launches (row pass; block quantization, whose first
+    workgroup derives the global scale and hands it to the others through global_scale), or with
+    a caller's one-row workgroups over 8200 rows three (the reduction between them).  Each replay
+    starts from a wiped, non-zero global_scale, which the row pass must clear."""
+    lb = None if launch is None else B.rmsq_launch(*launch, 0)
     g = torch.Generator().manual_seed(81)
     x = torch.randn((T, H), generator=g).to(torch.bfloat16).cuda()
     r = torch.randn((T, H), generator=g).to(torch.bfloat16).cuda()
@@ -171,7 +176,7 @@ def test_graph_fp4_dynamic():
                 torch.empty((T, H // 16), dtype=torch.uint8, device="cuda"),
                 torch.empty_like(r), torch.empty((1,), dtype=torch.float32, device="cuda")]
 
-    def launch(o, stream=None):
-        B.rmsq_fused_fp4_dynamic(x, r, w, 1e-6, o[0], o[1], o[2], o[3], stream=stream)
+    def run(o, stream=None):
+        B.rmsq_fused_fp4_dynamic(x, r, w, 1e-6, o[0], o[1], o[2], o[3], stream=stream, launch=lb)
 
-    _replay_check(launch, outs, "fp4_dynamic")
+    _replay_check(run, outs, f"fp4_dynamic T={T} H={H} launch={launch}")

@@ -151,15 +151,14 @@ def fp4dyn_leg(args, wl, T, H):
         if args.inplace:
             s["ro"] = s["r"]
         sets.append(s)
+    launch = None  # the library's own default shapes for both launches
     if args.launch:
         vals = [int(v) for v in args.launch.split(",")]
         launch = B.rmsq_launch(*(vals + [0] * (4 - len(vals))))
-    else:
-        launch = B.rmsq_query_launch(B.RMSQ_FP4_BLOCK16, T, H, 16)[0]
     import ctypes
 
     lib = B.lib()
-    lref = ctypes.byref(launch)
+    lref = None if launch is None else ctypes.byref(launch)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     status = []
@@ -216,7 +215,7 @@ def fp4dyn_leg(args, wl, T, H):
             "avg_launch_ms": sum(per) / len(per), "median_launch_ms": per[len(per) // 2],
             "p10_launch_ms": per[len(per) // 10], "p90_launch_ms": per[(9 * len(per)) // 10],
             "bytes": rd + wr, "read": rd, "write": wr, "sets": nsets,
-            "launch": launch.as_tuple(), "copy_gbs": copy_gbs,
+            "launch": None if launch is None else launch.as_tuple(), "copy_gbs": copy_gbs,
             "device": torch.cuda.get_device_name(dev)}
 
 
@@ -1092,12 +1091,13 @@ def main():
             "tokens": T, "hidden": H, "mode": MODE_NAMES[mode], "group_size": G,
             "flags": flags, "residual": wl.residual, "eps": wl.eps,
             "io": "bf16 in; " + {3: "e2m1 + e4m3 block scales out",
-                                 6: "e2m1 + e4m3 block scales + f32 global scale out (three "
+                                 6: "e2m1 + e4m3 block scales + f32 global scale out (two "
                                     "launches; the input is read twice)",
                                  4: f"bf16 out, rows padded to a multiple of {wl.pad_multiple}",
                                  5: "q and k heads rewritten in place (bf16), f32 cos/sin cache"
                                  }.get(mode, "e4m3fn out"),
-            "launch": ({"heads_per_block": g["launch"][0], "heads_per_lane": g["launch"][1]}
+            "launch": ("library default" if g["launch"] is None else
+                       {"heads_per_block": g["launch"][0], "heads_per_lane": g["launch"][1]}
                        if rope else
                        {"threads_per_row": g["launch"][0], "chunks_per_thread": g["launch"][1],
                         "rows_per_block": g["launch"][2], "options": g["launch"][3]}),

@@ -368,11 +368,13 @@ RMSQ_API int rmsq_qk_norm_rope_query_launch(int64_t tokens, int num_q_heads, int
                                             int* heads_per_lane, int64_t* grid);
 
 /* The launch shape rmsq_fused picks for (mode, T, H, group_size, flags) and its grid size
- * (number of workgroups); the same shape is the default of rmsq_fused_fp4_dynamic's first
- * pass.  The arguments are checked as rmsq_fused checks them (flags: RMSQ_SCALE_* for
- * FP8_GROUP, RMSQ_INPUT_F16 in any mode).  The shape depends on T and H only: it is the same
- * with and without a residual and for either activation type.  Host only; makes no HIP call.
- * Returns RMSQ_OK, RMSQ_EINVAL or RMSQ_EUNSUPPORTED (a flag the mode does not take). */
+ * (number of workgroups).  The arguments are checked as rmsq_fused checks them (flags:
+ * RMSQ_SCALE_* for FP8_GROUP, RMSQ_INPUT_F16 in any mode).  The shape depends on T, H and
+ * whether the mode is RMSQ_FP8_TOKEN (whose row-wide reduction takes one wave per row for
+ * batches of 1024+ rows of 1536 or 2048 elements); it is the same with and without a residual
+ * and for either activation type.  rmsq_fused_fp4_dynamic's default row pass takes the
+ * per-token shape, with as many rows per workgroup as its block pass needs.  Host only; makes no
+ * HIP call.  Returns RMSQ_OK, RMSQ_EINVAL or RMSQ_EUNSUPPORTED (a flag the mode does not take). */
 RMSQ_API int rmsq_query_launch(int mode, int64_t tokens, int64_t hidden, int group_size,
                                unsigned flags, rmsq_launch* launch, int64_t* grid);
 

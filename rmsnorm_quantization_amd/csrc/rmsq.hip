@@ -52,17 +52,24 @@ rmsq_launch default_launch(int64_t H) {
   return l;
 }
 
-// Default shape of the quantizing launch for a batch of T rows.  A batch that is in flight all
-// at once (at least 1024 rows and at most 2^20 chunks, so every wave is resident from the start)
-// whose rows fill two to four whole waves' worth of single chunks (H = 1536 or 2048) takes one
-// wave per row with 3-4 chunks per lane instead: such a wave reduces its row with DPP alone, no
-// LDS exchange and no barrier.  Measured on MI355X (graph replay, per launch): FP4 block-16 at
-// 4096 x 2048 12.5 us against 12.7 us for 128 x 2; the three launches of FP4 with a batch
-// global scale at 1024 x 2048 10.0 us against 10.7 us.  Rows of 8 chunks per lane (H = 4096)
-// measured 6% slower at 2048 rows than 256 x 2 and keep default_launch, as do larger batches.
-rmsq_launch default_fused_launch(int64_t T, int64_t H) {
+// Default shape of the quantizing launch for a batch of T rows.  For the schemes whose epilogue
+// ends in one row-wide reduction (per-token scaling, and the row pass of FP4 with a batch scale:
+// `row_reduction`), a batch that is in flight all at once (at least 1024 rows and at most 2^20
+// chunks, so every wave is resident from the start) whose rows fill two to four whole waves'
+// worth of single chunks (H = 1536 or 2048) takes one wave per row with 3-4 chunks per lane: such
+// a wave reduces its row with DPP alone, no LDS exchange and no barrier.  Measured on MI355X
+// (median of 300 dispatch-stamped launches, two alternations), 64 x 4 against 128 x 2 at H = 2048:
+// per-token 4.36-4.40 against 4.68-5.16 us at 1024 rows, 11.52 against 11.60 us at 4096; the
+// batch-scale FP4 step 8.84 against 9.03 us at 1024 rows.  The other schemes keep default_launch
+// (128 x 2 there), which the same sweep found as fast or faster now that their epilogues work in
+// phases: per-group-128 4.56-4.64 against 4.96 us at 1024 rows and 11.64 against 12.20-12.24 us
+// at 4096, FP4 block-16 10.76-10.84 against 11.12-11.16 us at 4096, static within 1%.  Rows of
+// 8 chunks per lane (H = 4096) measured 6% slower at 2048 rows than 256 x 2 and keep
+// default_launch, as do larger batches.
+rmsq_launch default_fused_launch(int64_t T, int64_t H, bool row_reduction) {
   const int64_t nch = H / 8;
-  if (nch > 128 && nch <= 256 && (nch % 64) == 0 && T >= 1024 && T * nch <= (int64_t(1) << 20))
+  if (row_reduction && nch > 128 && nch <= 256 && (nch % 64) == 0 && T >= 1024 &&
+      T * nch <= (int64_t(1) << 20))
     return rmsq_launch{64, (int32_t)(nch / 64), 1, 0};
   return default_launch(H);
 }
@@ -231,7 +238,7 @@ int fused_impl(const void* x, const void* res, const void* w, float eps, int mod
                void* start_event = nullptr, void* stop_event = nullptr) {
   int st = validate(x, res, w, eps, mode, scale_in, q, scales, res_out, T, H, gs, flags, ld);
   if (st != RMSQ_OK) return st;
-  const rmsq_launch l = launch ? *launch : default_fused_launch(T, H);
+  const rmsq_launch l = launch ? *launch : default_fused_launch(T, H, mode == RMSQ_FP8_TOKEN);
   if (!valid_launch(l, H)) return RMSQ_EINVAL;
   if (T == 0) return RMSQ_OK;
   st = check_device();
@@ -290,16 +297,25 @@ int validate_fp4_dynamic(const void* x, const void* res, const void* w, float ep
 // stages each row's inverse RMS there and pass 3 runs one wave per row and reads it: only that
 // wave later writes those bytes.  Otherwise both passes use one launch shape, so that both
 // reduce each row's squares in the same order.
-// Rows per workgroup for the two passes of FP4 with a batch global scale when the caller gives
-// no shape: raised from the default shape's up to 16 (within 1024 threads) while the grid keeps at
-// least 256 workgroups, so a batch in flight all at once still spreads over every CU.  Each
-// row-pass workgroup leaves one maximum, and the block pass's first workgroup (as many rows)
-// reduces them: 4096 rows of one wave leave 256 maxima for a 1024-thread workgroup, 131072 rows
-// still one round of eight loads per thread.
+// Rows per workgroup of the block pass of FP4 with a batch global scale: raised from the
+// default shape's up to 16 (within 1024 threads) while the grid keeps at least 256 workgroups,
+// so a batch in flight all at once still spreads over every CU.  Its workgroup 0 reduces the row
+// pass's maxima, eight loads per thread in one round: 16 one-wave rows take up to 8192.
 int32_t batch_rows_per_block(const rmsq_launch& l, int64_t T) {
   for (int32_t r = 16; r > l.rows_per_block; r /= 2)
     if ((int64_t)r * l.threads_per_row <= 1024 && T >= 256 * (int64_t)r) return r;
   return l.rows_per_block;
+}
+
+// Rows per workgroup of the row pass when the caller gives no shape: the default shape's, raised
+// only as far as it takes for its per-workgroup maxima to fit that one round (`cap` of them).
+// More rows per workgroup measured slower for this pass (4096 x 2048, graph replay per step:
+// 18.2-18.5 us with one, 19.1-19.3 us with 16; 16384 x 2048: 54.1-54.5 us with two or four,
+// 58.0 us with 16, 55.4 us with one, which leaves too many maxima and takes the middle launch).
+int32_t row_pass_rows_per_block(const rmsq_launch& l, int64_t T, int64_t cap) {
+  int32_t r = l.rows_per_block;
+  while ((T + r - 1) / r > cap && (int64_t)(2 * r) * l.threads_per_row <= 1024) r *= 2;
+  return r;
 }
 
 int fp4_dynamic_impl(const void* x, const void* res, const void* w, float eps, void* q,
@@ -308,21 +324,26 @@ int fp4_dynamic_impl(const void* x, const void* res, const void* w, float eps, v
                      void* stop_event, void* stream) {
   int st = validate_fp4_dynamic(x, res, w, eps, q, scales, res_out, global_scale, T, H, flags);
   if (st != RMSQ_OK) return st;
-  rmsq_launch l = launch ? *launch : default_fused_launch(T, H);
+  rmsq_launch l = launch ? *launch : default_fused_launch(T, H, true);
   if (!valid_launch(l, H)) return RMSQ_EINVAL;
   if (T == 0) return RMSQ_OK;
   st = check_device();
   if (st != RMSQ_OK) return st;
-  if (!launch) l.rows_per_block = batch_rows_per_block(l, T);
-  const bool exact = exact_fit(l, T, H), f16 = (flags & RMSQ_INPUT_F16) != 0;
-  const int vpt = l.chunks_per_thread;
   const bool stage = (H % 64) == 0 && H <= 4096 && aligned(scales, 4);
-  rmsq_launch l3 = l;  // pass 3's shape
+  // pass 3's shape: one wave per row where it reads the staged inverse RMS; otherwise the row
+  // pass's threads and chunks, so that both passes sum each row's squares in the same order
+  // (rows per workgroup do not enter that order)
+  rmsq_launch l3 = l;
   if (stage) {
     l3 = default_launch(H);  // one wave per row (several rows per workgroup for H <= 1024)
     if (l3.threads_per_row != 64) l3 = rmsq_launch{64, (int32_t)((H / 8 + 63) / 64), 1, 0};
-    l3.rows_per_block = batch_rows_per_block(l3, T);
   }
+  if (stage || !launch) l3.rows_per_block = batch_rows_per_block(l3, T);
+  if (!launch)
+    l.rows_per_block =
+        row_pass_rows_per_block(l, T, 8 * (int64_t)l3.threads_per_row * l3.rows_per_block);
+  const bool exact = exact_fit(l, T, H), f16 = (flags & RMSQ_INPUT_F16) != 0;
+  const int vpt = l.chunks_per_thread;
   // The row pass leaves one maximum per workgroup.  When the block pass's first workgroup can
   // reduce them in one round (eight loads per thread), it derives and publishes gs itself while
   // the other workgroups load their rows, and there is no middle launch; otherwise the
@@ -797,7 +818,7 @@ int rmsq_query_launch(int mode, int64_t tokens, int64_t hidden, int group_size, 
   const int st = check_quant_scalars(tokens, hidden, mode, group_size,
                                      flags & ~(unsigned)RMSQ_INPUT_F16, 0);
   if (st != RMSQ_OK) return st;
-  *launch = default_fused_launch(tokens, hidden);
+  *launch = default_fused_launch(tokens, hidden, mode == RMSQ_FP8_TOKEN);
   if (grid) *grid = (tokens + launch->rows_per_block - 1) / launch->rows_per_block;
   return RMSQ_OK;
 }

@@ -157,7 +157,7 @@ def test_query_launch_takes_the_calls_flags(B):
 
 
 @pytest.mark.parametrize("T,H,shape", [
-    (4096, 2048, (64, 4, 1, 0)),     # in flight at once: one wave per row
+    (4096, 2048, (64, 4, 1, 0)),     # in flight at once: one wave per row (per-token)
     (1024, 2048, (64, 4, 1, 0)),
     (2048, 1536, (64, 3, 1, 0)),
     (8192, 2048, (128, 2, 1, 0)),    # more than 2^20 chunks: several waves per row
@@ -170,10 +170,17 @@ def test_query_launch_takes_the_calls_flags(B):
     (4096, 1024, (64, 2, 4, 0)),     # short rows: four to a workgroup
 ])
 def test_query_launch_batch_rule(B, T, H, shape):
-    for mode in (0, 1, 3):
-        l, grid = B.rmsq_query_launch(mode, T, H, 16 if mode == 3 else 0)
-        assert l.as_tuple() == shape
-        assert grid == -(-T // shape[2])
+    """The per-token scheme's shapes; the others take the plain per-H default except where the
+    per-token batch rule gives one wave per row (H 1536 = 64 x 3 is that default anyway)."""
+    l, grid = B.rmsq_query_launch(B.RMSQ_FP8_TOKEN, T, H, 0)
+    assert l.as_tuple() == shape
+    assert grid == -(-T // shape[2])
+    plain = (128, 2, 1, 0) if H == 2048 else shape
+    G128 = 128 if H % 128 == 0 else 64
+    for mode, G in ((B.RMSQ_FP8_STATIC, 0), (B.RMSQ_FP8_GROUP, G128), (B.RMSQ_FP4_BLOCK16, 16)):
+        l, grid = B.rmsq_query_launch(mode, T, H, G)
+        assert l.as_tuple() == plain, (mode, l.as_tuple())
+        assert grid == -(-T // plain[2])
 
 
 @pytest.mark.parametrize("grid", [1, 2, 7, 8, 9, 15, 16, 17, 255, 256, 1000, 4096, 16385])

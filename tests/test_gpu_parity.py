@@ -108,8 +108,9 @@ def test_w4_add_rmsnorm_fp4_block16(T):
 
 
 # ---------------------------------------------------------------- batch-size launch rule
-# Batches in flight all at once with 1536- or 2048-wide rows run one wave per row (64 x 3 or
-# 64 x 4); every scheme at those default shapes against the oracle.
+# Batches in flight all at once with 1536- or 2048-wide rows: the per-token scheme runs one wave
+# per row (64 x 3 or 64 x 4), the others their per-H default (64 x 3 or 128 x 2); every scheme
+# at those default shapes against the oracle.
 @pytest.mark.parametrize("T,H", [(1024, 1536), (2048, 2048)])
 @pytest.mark.parametrize("mode,G,flags", [(O.FP8_STATIC, 0, 0), (O.FP8_TOKEN, 0, 0),
                                           (O.FP8_GROUP, 128, O.SCALE_COLMAJOR),
@@ -118,7 +119,8 @@ def test_w4_add_rmsnorm_fp4_block16(T):
 def test_one_wave_row_default_shapes(T, H, mode, G, flags):
     from rmsnorm_quantization_amd import binding as B
 
-    assert B.rmsq_query_launch(mode, T, H, G)[0].as_tuple() == (64, H // 512, 1, 0)
+    want = (64, 3, 1, 0) if H == 1536 else (64, 4, 1, 0) if mode == O.FP8_TOKEN else (128, 2, 1, 0)
+    assert B.rmsq_query_launch(mode, T, H, G)[0].as_tuple() == want
     _, _, _, xb, rb, wb = GH.workload_inputs(4, T, H)
     scale_in = 0.0
     if mode == O.FP4_BLOCK16:

@@ -385,8 +385,10 @@ RMSQ_API int rmsq_rms_norm_pad_query_launch(int64_t tokens, int64_t hidden, int6
                                             unsigned flags, rmsq_launch* launch,
                                             int64_t* grid);
 
-/* The launch shape rmsq_silu_mul_quant picks for (mode, T, I, group_size) and its grid size.
- * Host only; makes no HIP call.  Returns RMSQ_OK or RMSQ_EINVAL. */
+/* The launch shape rmsq_silu_mul_quant picks for (mode, T, I, group_size) and its grid size:
+ * row tiles of 64 threads x 2 chunks (RMSQ_LAUNCH_ROW_TILES) for FP4 block-16, whole rows as
+ * rmsq_query_launch's per-H default otherwise.  Host only; makes no HIP call.  Returns RMSQ_OK
+ * or RMSQ_EINVAL. */
 RMSQ_API int rmsq_silu_mul_query_launch(int mode, int64_t tokens, int64_t inter, int group_size,
                                         rmsq_launch* launch, int64_t* grid);
 

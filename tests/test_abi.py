@@ -251,10 +251,15 @@ def test_act_x_extent_is_two_rows_wide(B):
 def test_act_query_launch(B):
     l, grid = B.rmsq_silu_mul_query_launch(B.RMSQ_FP8_TOKEN, 100, 14336)
     assert l.options == 0 and l.threads_per_row * l.chunks_per_thread * 8 >= 14336
-    for mode, G in ((B.RMSQ_FP8_STATIC, 0), (B.RMSQ_FP8_GROUP, 128), (B.RMSQ_FP4_BLOCK16, 16)):
+    for mode, G in ((B.RMSQ_FP8_STATIC, 0), (B.RMSQ_FP8_GROUP, 128)):
         l, grid = B.rmsq_silu_mul_query_launch(mode, 100, 14336, G)
         assert l.as_tuple() == B.rmsq_query_launch(mode, 100, 14336, G)[0].as_tuple()
         assert grid == -(-100 // l.rows_per_block)
+    # FP4: tiles of one wave x 2 chunks, 14 to a 1792-chunk row (11 at I = 11008, the last one partial)
+    l, grid = B.rmsq_silu_mul_query_launch(B.RMSQ_FP4_BLOCK16, 100, 14336, 16)
+    assert l.as_tuple() == (64, 2, 1, B.RMSQ_LAUNCH_ROW_TILES) and grid == 100 * 14
+    l, grid = B.rmsq_silu_mul_query_launch(B.RMSQ_FP4_BLOCK16, 100, 11008, 16)
+    assert l.as_tuple() == (64, 2, 1, B.RMSQ_LAUNCH_ROW_TILES) and grid == 100 * 11
 
 
 # ------------------------------------------------------------------ RMSNorm -> padded bf16

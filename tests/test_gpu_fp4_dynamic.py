@@ -110,6 +110,14 @@ def test_middle_reduction_launch(launch):
     check(x, r, w, launch=None if launch is None else B.rmsq_launch(*launch, 0))
 
 
+def test_row_pass_packs_rows_for_one_round():
+    """65536 rows of 64: the row pass's default four rows per workgroup would leave 16384 maxima,
+    more than the block pass's first 1024-thread workgroup reduces in one round (8192), so the
+    row pass takes eight rows per workgroup (8192 maxima) and there is no middle launch."""
+    x, r, w = _inputs(65536, 64, 12)
+    check(x, r, w)
+
+
 @pytest.mark.parametrize("T,H", [(1, 2048), (37, 2048), (512, 4096), (1024, 2048)])
 def test_binary16(T, H):
     x, r, w = _inputs(T, H, T + H + 1, dtype=torch.float16)

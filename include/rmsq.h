@@ -207,7 +207,9 @@ RMSQ_API int rmsq_fused_timed(const void* x, const void* residual, const void* w
  * (and clearing global_scale); (2) the block quantization, which normalizes the new residual (or
  * x) again.  Launch 2's first workgroup reduces the maxima to gs and stores it to global_scale;
  * the other workgroups load their rows meanwhile and then wait for a non-zero global_scale (a
- * bounded wait: the first workgroup is dispatched before them and does not wait on anything).
+ * bounded wait, ~0.1 s: the first workgroup is dispatched before them and does not wait on
+ * anything; should a wait ever run out, global_scale is left NaN, so every value dequantized
+ * with it is NaN rather than silently wrong).
  * No workgroup writes out_q, where the maxima are, before gs exists.  Where that workgroup could
  * not reduce the maxima in one round of loads (more than eight per thread: very large T, or a
  * caller's shape with one row per workgroup), a one-workgroup reduction launch runs between the

@@ -88,7 +88,8 @@ __device__ __forceinline__ float batch_fp4_scale(float amax) {
 
 // Workgroup 0 of the block pass: the largest of the n row-pass maxima (every thread takes every
 // blockDim-th one, eight loads in flight per round; the host keeps n within one round), then
-// gs, published to *gs_out by an agent-scope store and returned to every thread.  Workgroup 0 is
+// gs, published to *gs_out -- an agent-scope compare-and-swap from 0, so that a NaN left there by
+// a wait that ran out (batch_scale_await) stays -- and returned to every thread.  Workgroup 0 is
 // the first one dispatched, so it is resident whatever the others do while they wait.  Must be
 // called by every thread of the workgroup.
 __device__ float batch_scale_publish(const float* parts, int64_t n, float* gs_out, float* s_red) {
@@ -112,21 +113,35 @@ __device__ float batch_scale_publish(const float* parts, int64_t n, float* gs_ou
   m = 0.0f;
   for (int i = 0; i < nw; ++i) m = fmaxf(m, s_red[i]);
   const float gs = batch_fp4_scale(m);
-  if (threadIdx.x == 0) __hip_atomic_store(gs_out, gs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) {
+    uint32_t expected = 0u;
+    __hip_atomic_compare_exchange_strong(reinterpret_cast<uint32_t*>(gs_out), &expected,
+                                         __float_as_uint(gs), __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+  }
   return gs;
 }
 
 // The other workgroups of the block pass: `seen` is an agent-scope load of *gs_out issued with the
 // row's loads; while it still reads 0, poll (sleeping between polls) until workgroup 0 has
-// published.  The wait is bounded (2^20 polls, about 0.1 s): every wave ends even if the value
-// never came, and a global scale that never came leaves 0, which the host cannot mistake for a
-// result (codes computed from it are garbage; it does not occur while workgroup 0 runs).
+// published.  The wait is bounded (2^20 polls, about 0.1 s) so that every wave ends.  A wave
+// whose wait runs out -- which workgroup 0, resident and waiting on nothing, does not let happen
+// -- swaps a NaN into *gs_out unless the scale arrived meanwhile, and workgroup 0 publishes only
+// over a 0: the call's global scale then reads NaN, and so does every value dequantized with it,
+// instead of codes made with no scale passing for valid ones.
 __device__ __forceinline__ float batch_scale_await(float seen, float* gs_out) {
   float g = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(seen)));
   for (int it = 0; g == 0.0f && it < (1 << 20); ++it) {
     __builtin_amdgcn_s_sleep(4);
     const float r = __hip_atomic_load(gs_out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     g = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(r)));
+  }
+  if (g == 0.0f) {  // uniform; never taken while workgroup 0 runs
+    uint32_t cur = 0u;
+    __hip_atomic_compare_exchange_strong(reinterpret_cast<uint32_t*>(gs_out), &cur, 0x7FC00000u,
+                                         __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    g = __uint_as_float(__builtin_amdgcn_readfirstlane(cur == 0u ? 0x7FC00000u : cur));
   }
   return g;
 }

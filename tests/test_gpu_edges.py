@@ -297,6 +297,30 @@ def test_fp4_multiplier_overflow_keeps_zero_codes():
     assert np.array_equal(gpu["q"], ref["q"])
 
 
+@pytest.mark.parametrize("launch", [None, (64, 2, 1), (128, 1, 1)])
+def test_fp4_block_scale_underflow_gives_zero_codes(launch):
+    """FP4 blocks whose elements are non-zero but ~1e-7 of the row's largest: the block scale
+    encodes to the e4m3 zero and every code of the block is 0x0 (the zero-scale rule), while
+    the other blocks quantize normally; bit-exact, in one- and several-wave rows."""
+    T, H = 6, 1024
+    x = torch.full((T, H), 0.25)
+    x[:, :16] = torch.linspace(-1.0, 1.0, 16)
+    for b in range(1, H // 16, 3):                  # every third block tiny and non-zero
+        x[:, 16 * b:16 * b + 16] = torch.linspace(-1e-7, 1e-7, 16)
+    x = x.to(torch.bfloat16)
+    w = torch.ones(H).to(torch.bfloat16)
+    xb, wb = synth.bits(x), synth.bits(w)
+    y = O.rms_y(xb, None, wb, 1e-6)
+    gs = float(np.float32(448 * 6) / np.abs(y).max())
+    print(f"[edge] FP4 block-scale underflow launch={launch}", flush=True)
+    gpu = GH.run(O.FP4_BLOCK16, GH.to_dev(x), None, GH.to_dev(w), 1e-6, scale_in=gs,
+                 group_size=16, launch=None if launch is None else B.rmsq_launch(*launch, 0))
+    ref = O.fused(xb, None, wb, 1e-6, O.FP4_BLOCK16, scale_in=gs, group_size=16)
+    assert (ref["scales"][:, 1::3] == 0).all() and (y[:, 16:32] != 0).all()  # the case
+    assert np.array_equal(gpu["scales"], ref["scales"])
+    assert np.array_equal(gpu["q"], ref["q"])
+
+
 @pytest.mark.parametrize("mode,G", [(O.FP8_STATIC, 0), (O.FP8_TOKEN, 0), (O.FP8_GROUP, 128)])
 def test_silu_mul_reciprocal_overflow_keeps_zero_codes(mode, G):
     """SiLU+Mul rows whose activations are ~2e-38 or exactly zero (gate 0): the reciprocal scale

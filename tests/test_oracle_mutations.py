@@ -56,6 +56,14 @@ MUTANTS = [
      "return y * mul;", 0),
     ("FP4 elements truncated toward zero", "codes[i] = orc_e2m1_encode(v);",
      "codes[i] = orc_e2m1_encode(truncf(v * 2.0f) * 0.5f);", 0),
+    ("padding repeats the row's last value", "i < H ? f32_to_in16(y[i], f16) : 0",
+     "i < H ? f32_to_in16(y[i], f16) : f32_to_in16(y[H - 1], f16)", 0),
+    ("E8M0 byte biased by 128", "*e8m0_byte = k + 127;", "*e8m0_byte = k + 128;", 0),
+    ("FP4 block whose scale underflows still divided", "if (d > 0.0f) {", "if (d >= 0.0f) {", 0),
+    ("all-zero batch leaves an infinite global scale", "return (gs <= FLT_MAX) ? gs : FLT_MAX;",
+     "return gs;", 0),
+    ("new residual copied from x", "memcpy(residual_out + t * H, h, (size_t)H * sizeof(uint16_t));",
+     "memcpy(residual_out + t * H, x + t * H, (size_t)H * sizeof(uint16_t));", 0),
 ]
 
 

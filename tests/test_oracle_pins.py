@@ -260,6 +260,28 @@ def test_fp4_half_step_invariant(orc):
     assert sat.any() and np.all(ok), f"{int((~ok).sum())} elements off by more than half a step"
 
 
+def test_fp4_block_scale_underflow_gives_zero_codes(orc):
+    """The zero-scale rule for FP4 (readings 6 and 9): a 16-element block whose block scale
+    a * gs / 6 rounds to the e4m3 zero gives the 0x0 code for every element, also when the
+    elements themselves are not zero (here ~1e-7 of the row's largest, with gs fitting the
+    largest to 448 * 6: a * gs / 6 ~ 4.5e-5, under half the smallest e4m3 subnormal)."""
+    H = 64
+    x = np.zeros((1, H), np.float64)
+    x[0, :16] = np.linspace(-1.0, 1.0, 16)          # block 0: the row's scale
+    x[0, 16:32] = np.linspace(-1e-7, 1e-7, 16)      # block 1: non-zero, tiny
+    x[0, 32:] = 0.25                                # blocks 2-3: ordinary
+    xb = bf16_bits(x)
+    w = bf16_bits(np.ones(H))
+    y = orc.rms_y(xb, None, w, 1e-6)
+    assert np.all(y[0, 16:32] != 0)
+    gs = float(np.float32(448 * 6) / np.abs(y).max())
+    out = orc.fused(xb, None, w, 1e-6, orc.FP4_BLOCK16, scale_in=gs, group_size=16)
+    assert out["scales"][0, 1] == 0
+    nib = orc.unpack_fp4(out["q"])
+    assert np.all(nib[0, 16:32] == 0), nib[0, 16:32]
+    assert np.all(out["scales"][0, [0, 2, 3]] != 0) and np.any(nib[0, 32:] != 0)
+
+
 def test_zero_residual_equals_plain(orc):
     rng = np.random.default_rng(41)
     T, H = 4, 384

@@ -64,6 +64,10 @@ MUTANTS = [
      "return gs;", 0),
     ("new residual copied from x", "memcpy(residual_out + t * H, h, (size_t)H * sizeof(uint16_t));",
      "memcpy(residual_out + t * H, x + t * H, (size_t)H * sizeof(uint16_t));", 0),
+    ("RoPE frequencies with exponent -i/D", "pow(base, -2.0 * (double)i / (double)D)",
+     "pow(base, -1.0 * (double)i / (double)D)", 0),
+    ("SiLU applied to the up half", "in16_to_f32(x[i], f16), (double)in16_to_f32(x[I + i], f16)",
+     "in16_to_f32(x[I + i], f16), (double)in16_to_f32(x[i], f16)", 0),
 ]
 
 

@@ -289,14 +289,16 @@ int validate_fp4_dynamic(const void* x, const void* res, const void* w, float ep
   return RMSQ_OK;
 }
 
-// Three launches: (1) residual add + RMSNorm, each row's largest |y| staged as f32 in the first
-// 4T bytes of out_q; (2) one workgroup: the batch's largest |y| -> gs; (3) the FP4 block-16
-// kernel without a residual on the normalized input (the new residual, or x), reading gs from
-// device memory.  Pass 3 must see pass 1's y.  Where a row's block scales can hold an f32
-// (H % 64 == 0, out_scales 4-byte aligned) and a row fits one wave (H <= 4096), pass 1 also
-// stages each row's inverse RMS there and pass 3 runs one wave per row and reads it: only that
-// wave later writes those bytes.  Otherwise both passes use one launch shape, so that both
-// reduce each row's squares in the same order.
+// Two launches: (1) residual add + RMSNorm, each workgroup's largest |y| staged as f32 at the
+// start of out_q, global_scale cleared to 0; (2) the FP4 block-16 kernel without a residual on
+// the normalized input (the new residual, or x), whose workgroup 0 reduces the maxima to gs and
+// hands it to the others through global_scale.  Where that workgroup cannot reduce them in one
+// round, a one-workgroup reduction runs between the two instead and launch 2 reads gs.  Launch
+// 2 must see launch 1's y.  Where a row's block scales can hold an f32 (H % 64 == 0,
+// out_scales 4-byte aligned) and a row fits one wave (H <= 4096), launch 1 also stages each
+// row's inverse RMS there and launch 2 runs one wave per row and reads it: only that wave later
+// writes those bytes.  Otherwise both launches use the same threads and chunks per row, so that
+// both reduce each row's squares in the same order.
 // Rows per workgroup of the block pass of FP4 with a batch global scale: raised from the
 // default shape's up to 16 (within 1024 threads) while the grid keeps at least 256 workgroups,
 // so a batch in flight all at once still spreads over every CU.  Its workgroup 0 reduces the row

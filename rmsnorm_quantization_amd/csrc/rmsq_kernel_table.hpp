@@ -11,7 +11,8 @@ namespace rmsq {
 // fused (residual add ->) RMSNorm -> quantization, bf16 or IEEE binary16 activations
 const void* fused_kernel_bf16(int mode, bool res, int gs, int vpt, bool exact);
 const void* fused_kernel_f16(int mode, bool res, int gs, int vpt, bool exact);
-// (residual add ->) RMSNorm -> each row's largest |y| (first pass of FP4 with a batch scale)
+// (residual add ->) RMSNorm -> each workgroup's largest |y| (first pass of FP4 with a batch
+// scale)
 const void* amax_kernel_bf16(bool res, int vpt, bool exact);
 const void* amax_kernel_f16(bool res, int vpt, bool exact);
 // the block pass of FP4 with a batch scale (no residual: it reads the new residual or x)
@@ -28,7 +29,7 @@ const void* rope_kernel_bf16(int D, bool neox, int hpl);
 const void* rope_kernel_f16(int D, bool neox, int hpl);
 // the diagnostic converters
 const void* convert_kernel_ptr();
-// the reduction of row maxima to the FP4 global scale
+// the one-workgroup reduction of the row pass's maxima to the FP4 global scale
 const void* fp4_global_scale_kernel_ptr();
 
 // The fused_kernel instantiation for (mode, residual, chunks per thread, group, exact, type);

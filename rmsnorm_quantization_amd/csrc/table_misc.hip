@@ -36,9 +36,10 @@ const void* rope_kernel_bf16(int D, bool neox, int hpl) { return pick_rope<0>(D,
 
 const void* convert_kernel_ptr() { return reinterpret_cast<const void*>(&convert_kernel); }
 
-// One workgroup of 1024 threads: the batch's largest row maximum, then its FP4 global scale.
-// Each thread takes every 1024th row maximum, eight loads in flight per round (masked past T):
-// a loop of one load at a time waits out a memory round trip per element (4096 rows: 3.7 us).
+// One workgroup of 1024 threads: the largest of the row pass's T maxima, then the batch's FP4
+// global scale.  Each thread takes every 1024th maximum, eight loads in flight per round (masked
+// past T).  The launch costs ~3.5 us however the loads are arranged (mostly its own dispatch),
+// which is why the block pass takes this reduction over wherever one round of loads suffices.
 __global__ void __launch_bounds__(1024) fp4_global_scale_kernel(GArgs a) {
   __shared__ float s_mx[kMaxWavesPerBlock];
   constexpr int kLoads = 8;

@@ -110,6 +110,35 @@ def test_middle_reduction_launch(launch):
     check(x, r, w, launch=None if launch is None else B.rmsq_launch(*launch, 0))
 
 
+def test_concurrent_calls_on_several_streams():
+    """Four calls in flight at once on four streams (default priority), each with its own
+    buffers: every workgroup 0 hands its global scale to its own call's workgroups only, through
+    that call's global_scale, so each result equals the oracle's for its own batch."""
+    T, H = 2048, 2048
+    batches = [_inputs(T, H, 100 + i) for i in range(4)]
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    outs = []
+    for (x, r, w), st in zip(batches, streams):
+        o = dict(q=torch.empty((T, H // 2), dtype=torch.uint8, device="cuda"),
+                 s=torch.empty((T, H // 16), dtype=torch.uint8, device="cuda"),
+                 ro=torch.empty((T, H), dtype=torch.bfloat16, device="cuda"),
+                 g=torch.full((1,), 7.0, dtype=torch.float32, device="cuda"),
+                 x=GH.to_dev(x), r=GH.to_dev(r), w=GH.to_dev(w))
+        outs.append(o)
+    torch.cuda.synchronize()
+    print("[fp4dyn] four concurrent calls", flush=True)
+    for o, st in zip(outs, streams):
+        B.rmsq_fused_fp4_dynamic(o["x"], o["r"], o["w"], 1e-6, o["q"], o["s"], o["ro"], o["g"],
+                                 stream=st)
+    torch.cuda.synchronize()
+    for (x, r, w), o in zip(batches, outs):
+        ref = O.fused_fp4_dynamic(_bits(x), _bits(r), _bits(w), 1e-6)
+        assert o["g"].cpu().numpy().view(np.uint32)[0] == ref["global_scale"].view(np.uint32)
+        assert np.array_equal(o["q"].cpu().numpy(), ref["q"])
+        assert np.array_equal(o["s"].cpu().numpy(), ref["scales"])
+        assert np.array_equal(_bits(o["ro"].cpu()).reshape(T, H), ref["residual_out"])
+
+
 def test_row_pass_packs_rows_for_one_round():
     """65536 rows of 64: the row pass's default four rows per workgroup would leave 16384 maxima,
     more than the block pass's first 1024-thread workgroup reduces in one round (8192), so the

@@ -344,9 +344,10 @@ __device__ __forceinline__ void quantize_store(const YF& Y, const bool (&ok)[VPT
     // Chunks are taken KB at a time, in phases -- block scales, table exchanges, codes, stores --
     // so that nothing divergent separates one chunk's arithmetic from the next within a batch
     // and the batch's exchanges are in flight together.  Measured on MI355X: all chunks at once
-    // is faster for one-wave rows (3-4 chunks per lane: 4096 x 2048 11.4 -> 11.3 us) and for
-    // SiLU+Mul (4096 x 14336: 51.3 -> 47.4-48.9 us), one at a time for the several-wave rows of
-    // the norm (16384 x 2048 at 128 x 2: 34.6 against 35.6 us).
+    // is faster for one-wave rows (3-4 chunks per lane: 4096 x 2048 at 64 x 4 11.4 -> 11.3 us)
+    // and for SiLU+Mul (4096 x 14336: 51.3 -> 47.4-48.9 us); the norm's rows of two chunks per
+    // lane take them one at a time (16384 x 2048 at 128 x 2: 34.6 against 35.6 us; 4096 x 2048,
+    // now 128 x 2 by default: 10.76 us either way).
     constexpr int KB = (FP4_BATCH && VPT <= 4) ? VPT : 1;  // more would spill registers
     float y[VPT][8], d[VPT], g[VPT];
     uint32_t sf[VPT], qc[VPT];
